@@ -1,0 +1,322 @@
+"""Benchmark of masked scaled dot-product attention over a CSR mask on one MI355X.
+
+A step is one pass of the CSR path over one batch of synthetic input: the row plan,
+SDDMM, sparse softmax and SpMM (scores, weights and context) on the Longformer-style
+workload (12 heads, n=4096, d=64, bf16, window |i-j|<=128 plus global tokens 0 and 1).
+Inputs are resident in HBM before timing starts. The JSON line reports attended pairs/s
+(value), per-kernel durations from HIP events recorded on the stream the kernels run
+on, the roofline of the dominant kernel, the other fused variants measured on their own
+workloads, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extra] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak (packed), TFLOP/s
+METRIC = "attended (i,j) pairs/sec and % of HBM/MFMA roofline, 1×MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "masked_scaled_dot_amd", "csrc")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="longformer_n4096",
+                    choices=["longformer_n4096", "random_n8192"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------ device setup
+
+def to_device(p, torch, sa, element=True):
+    dev = torch.device("cuda:0")
+
+    def qkv(w):
+        bits = getattr(p, w + "_bits")
+        if bits is not None:
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(getattr(p, w)).to(dev)
+
+    rp, ci, block = p.row_ptr, p.col_idx, p.block
+    if element and rp is not None and block != 1:
+        rp, ci = p.element_csr()
+        rp, ci, block = rp.astype(np.int32), ci.astype(np.int32), 1
+    t = dict(q=qkv("q"), k=qkv("k"), v=qkv("v"),
+             row_ptr=None if rp is None else torch.from_numpy(rp).to(dev),
+             col_idx=None if ci is None else torch.from_numpy(ci).to(dev),
+             bias=None if p.bias is None else torch.from_numpy(p.bias).to(dev),
+             key_mask=None if p.key_mask is None else torch.from_numpy(p.key_mask).to(dev))
+    nnz = 0 if rp is None else int(rp[-1])
+    prob = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16 if p.dtype == "bf16" else sa.SA_F32,
+                      t["row_ptr"], t["col_idx"], nnz, block=block, scale=p.scale,
+                      bias=t["bias"], key_mask=t["key_mask"], key_mask_heads=p.key_mask_heads)
+    return prob, t, nnz
+
+
+class EventTimer:
+    """Per-kernel HIP events on the current stream; durations summed per name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, name, a, b):
+        self.pending.append((name, a, b))
+
+    def result(self):
+        self.torch.cuda.synchronize()
+        out = {}
+        for name, a, b in self.pending:
+            out.setdefault(name, []).append(a.elapsed_time(b) * 1e3)  # us
+        return {k: float(np.mean(v)) for k, v in out.items()}
+
+
+# ------------------------------------------------------------------------------ algorithmic bytes
+
+def bytes_pipeline(BH, n, d, nnz, elem):
+    """Unique bytes each kernel must move (every gathered K/V row counted once)."""
+    qkv = BH * n * d * elem
+    csr = 4 * (n + 1) + 4 * nnz
+    return {
+        "plan": 4 * (n + 1) + 16 * (n + nnz // 512 + 1),
+        "sddmm": 2 * qkv + csr + 4 * BH * nnz,
+        "softmax": 4 * (n + 1) + 8 * BH * nnz,
+        "spmm": 4 * BH * nnz + csr + qkv + 4 * BH * n * d,
+    }
+
+
+def bytes_fused(p, nnz_blocks=None):
+    qkv = p.BH * p.n * p.d * (2 if p.dtype == "bf16" else 4)
+    b = 3 * qkv + 4 * p.BH * p.n * p.d + 4 * p.BH * p.n  # q, k, v, out, lse
+    if p.row_ptr is not None:
+        b += 4 * len(p.row_ptr) + 4 * len(p.col_idx)
+    if p.bias is not None:
+        b += p.bias.nbytes
+    if p.key_mask is not None:
+        b += p.key_mask.nbytes
+    return b
+
+
+# ------------------------------------------------------------------------------ measurements
+
+def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
+    scores = torch.empty(BH * nnz, device="cuda:0")
+    weights = torch.empty_like(scores)
+    out = torch.empty(BH, n, d, device="cuda:0")
+    plan = torch.empty(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+
+    def step(tm):
+        e0 = tm.mark() if tm else None
+        sa.sa_plan_build(prob, plan)
+        e1 = tm.mark() if tm else None
+        sa.sa_sddmm(prob, t["q"], t["k"], scores)
+        e2 = tm.mark() if tm else None
+        sa.sa_sparse_softmax(prob, scores, weights)
+        e3 = tm.mark() if tm else None
+        sa.sa_spmm(prob, weights, t["v"], out)
+        e4 = tm.mark() if tm else None
+        if tm:
+            tm.add("plan", e0, e1)
+            tm.add("sddmm", e1, e2)
+            tm.add("softmax", e2, e3)
+            tm.add("spmm", e3, e4)
+
+    prob.set_plan(plan)
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall
+
+
+def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
+    prob, t, nnz = to_device(p, torch, sa, element=element)
+    out = torch.empty(p.BH, p.n, p.d, device="cuda:0")
+    lse = torch.empty(p.BH, p.n, device="cuda:0")
+    for _ in range(warmup):
+        sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+    tm = EventTimer(torch)
+    for _ in range(iters):
+        a = tm.mark()
+        sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+        b = tm.mark()
+        tm.add("fused", a, b)
+    us = tm.result()["fused"]
+    del t, out, lse
+    return us
+
+
+def cpu_baseline(p, budget_s):
+    """The fp64 dense oracle (definition with -inf outside the mask), timed on whole heads
+    until the budget is used; returns attended pairs/s on the host cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    pattern = ("csr", p.row_ptr, p.col_idx)
+    done, t0 = 0, time.perf_counter()
+    while done < p.BH:
+        oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, pattern, heads=[done])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    pairs = done * p.nnz
+    return {"value": pairs / dt, "unit": "pairs/s",
+            "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{done} of {p.BH} heads of {p.name} (all rows of each), dense fp64 "
+                      f"oracle with -inf outside the mask; {dt:.1f} s; exp and masking on one "
+                      f"thread, GEMMs on {blas_threads} BLAS threads; "
+                      f"{len(os.sched_getaffinity(0))} cores in the affinity mask"}
+
+
+def load_traffic(kernel, src_hash):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tr.get(kernel)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gen
+    if not os.path.exists(os.path.join(ROOT, "masked_scaled_dot_amd", "libsa.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    import masked_scaled_dot_amd as sa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    p = gen.make(args.workload)
+    BH, n, d = p.BH, p.n, p.d
+    prob, t, nnz = to_device(p, torch, sa)
+    pairs = BH * nnz
+    log(f"workload {p.name}: BH={BH} n={n} d={d} nnz/head={nnz} pairs/step={pairs}")
+
+    timer = EventTimer(torch)
+    wall = run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, args.steps, args.warmup, timer)
+    kern_us = timer.result()
+    ms_per_step = wall * 1e3 / args.steps
+    value = pairs / (wall / args.steps)
+    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step  " +
+        "  ".join(f"{k}={v:.1f}us" for k, v in kern_us.items()))
+
+    algo = bytes_pipeline(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
+    kernels = {}
+    for k, us in kern_us.items():
+        gbs = algo[k] / (us * 1e-6) / 1e9
+        kernels[k] = {"us": round(us, 2), "algo_bytes": algo[k], "GB_s": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    total_bytes = sum(algo[k] for k in ("sddmm", "softmax", "spmm"))
+    total_us = sum(kern_us[k] for k in ("sddmm", "softmax", "spmm"))
+    dominant = max(("sddmm", "softmax", "spmm"), key=lambda k: kern_us[k])
+    src_of = {"sddmm": ["sddmm.hip", "common.h"], "softmax": ["softmax.hip", "common.h"],
+              "spmm": ["spmm.hip", "common.h"]}
+    dom_hash = source_hash(src_of[dominant])
+    achieved = algo[dominant] / (kern_us[dominant] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dominant, dom_hash),
+                "algo_bytes_per_launch": algo[dominant], "avg_launch_us": round(kern_us[dominant], 2),
+                "source_hash": dom_hash,
+                "pipeline_aggregate_frac": round(total_bytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    extra = {}
+    if not args.no_extra:
+        fused_us = time_fused(torch, sa, p)
+        flops = 4.0 * pairs * d
+        extra["fused_csr_" + p.name] = {
+            "us": round(fused_us, 2), "pairs_per_s": pairs / (fused_us * 1e-6),
+            "TFLOP_s": round(flops / (fused_us * 1e-6) / 1e12, 2),
+            "valu_frac": round(flops / (fused_us * 1e-6) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+            "hbm_frac": round(bytes_fused(p) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del t
+        for name in ("bsr_n16384", "evoformer_l384"):
+            q = gen.make(name)
+            us = time_fused(torch, sa, q)
+            pr = q.attended_pairs() if q.row_ptr is None else q.BH * int(q.element_csr()[0][-1])
+            flops = 4.0 * pr * q.d
+            extra["fused_" + name] = {
+                "us": round(us, 2), "pairs_per_s": pr / (us * 1e-6),
+                "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2),
+                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "warm": True}
+            log(f"fused {name}: {us:.1f} us")
+            del q
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.3e} pairs/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": p.name, "B": p.B, "H": p.H, "n": n, "d": d, "nnz_per_head": nnz,
+                   "pairs_per_step": pairs,
+                   "step": "plan + sddmm + sparse_softmax + spmm (scores, weights, context)",
+                   "inputs": "resident in HBM; caches not flushed between steps"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

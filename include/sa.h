@@ -1,0 +1,173 @@
+/*
+ * sa.h -- masked scaled dot-product attention over a CSR attention mask,
+ *         for AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * What is computed (for every head t = b*H + h and query row i):
+ *
+ *   S[t,i,j] = scale * (q[t,i,:] . k[t,j,:]) + bias[h,i,j] + key_mask[b,hm,j]   for (i,j) in P
+ *   W[t,i,j] = exp(S[t,i,j] - m) / sum_{j' in P_i} exp(S[t,i,j'] - m),  m = max_{j in P_i} S[t,i,j]
+ *   O[t,i,:] = sum_{j in P_i} W[t,i,j] * v[t,j,:]
+ *   lse[t,i] = m + log sum_{j in P_i} exp(S[t,i,j] - m)
+ *
+ * P is the attention pattern: query i attends key j iff the user's (n, n) mask
+ * holds a nonzero at (i, j) (gluon-nlp issue "[Proposal] Unified
+ * Interface/Implementation for Sparse Attention", opening post: the mask is a
+ * CSR/COO matrix of shape (n, n)). The three steps of that post are exported
+ * as sa_sddmm (scores at the nonzeros, same pattern as the mask), sa_sparse_softmax
+ * (softmax over each sparse row, same pattern) and sa_spmm (CSR weights times
+ * dense V). sa_fused_forward computes O in one pass with a running maximum and
+ * a running sum that rescale earlier partial results, dividing once at the end
+ * (the streaming-dataflow SDPA review on nubint.ai, "proposed method" list:
+ * reordering the divide by the distributive law, and running max / running
+ * sum with delta rescaling). The additive bias and key mask follow the shapes
+ * of the flash-attention pull request "support attentions in AlphaFold2"
+ * (the mask [total_size, 1 or head, 1, seq_k] and bias [1, head, seq_q, seq_k]
+ * shape lists).
+ *
+ * Conventions (readings where the pages are silent):
+ *   - The scale multiplies q.k only; bias and key_mask are added unscaled.
+ *   - A row with no stored entry, or whose every score is -inf, has W = 0 at
+ *     its stored entries, O = 0 and lse = -inf.
+ *   - Every output is fp32. Inputs q/k/v are fp32 or bf16 (SA_F32 / SA_BF16).
+ *
+ * Memory: every pointer argument and every pointer inside sa_problem is a
+ * DEVICE pointer (hipMalloc / torch CUDA tensor on the current device),
+ * row-major and contiguous, owned by the caller. The library keeps no pointer
+ * after a call returns. Calls are asynchronous on the given stream (0 = the
+ * null stream); outputs are valid after the stream is synchronised. Calls on
+ * different streams share no library state.
+ *
+ * Errors: every call returns SA_OK (0) or a negative sa_status, and checks its
+ * arguments on the host before touching the device. Host checks cover pointers,
+ * shapes, dtypes, alignment and the descriptor; the CSR content (monotone
+ * row_ptr, nnz == row_ptr[n], columns sorted, unique and in range) is checked on
+ * the device only when flags has SA_FLAG_VALIDATE (that call then synchronises
+ * the stream) or by sa_validate_csr. Without it, kernels clamp every index they
+ * read into range, so a malformed CSR gives wrong numbers but no invalid access.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_NULL = -1,        /* a required pointer is NULL                                  */
+  SA_ERR_SHAPE = -2,       /* B, H, n, d, nnz or a broadcast dimension is inconsistent   */
+  SA_ERR_CSR = -3,         /* device validation found a malformed CSR                     */
+  SA_ERR_DTYPE = -4,       /* dtype is not SA_F32 / SA_BF16                               */
+  SA_ERR_UNSUPPORTED = -5, /* d not in {32,64,128}, block not in {1,64}, or pattern kind
+                              not accepted by this call                                   */
+  SA_ERR_ALIGN = -6,       /* q/k/v/out base pointer not 16-byte aligned                  */
+  SA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed                  */
+  SA_ERR_WORKSPACE = -8    /* plan buffer too small or not built for this problem          */
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+#define SA_FLAG_VALIDATE 1 /* validate the CSR on the device first (synchronises the stream) */
+
+/* Problem descriptor. Field order and sizes are part of the ABI.
+ *
+ * q, k, v are [B*H, n, d] with head t = b*H + h (the q/k/v shape
+ * [total_size * head, seq, head_dim] of the AlphaFold2 pull request).
+ *
+ * Pattern kinds:
+ *   block == 1,  row_ptr != NULL : element CSR. row_ptr [n+1], col_idx [nnz], nnz == row_ptr[n].
+ *   block == 64, row_ptr != NULL : block CSR of 64x64 tiles. row_ptr [ceil(n/64)+1] over
+ *                                  block-rows, col_idx [nnz] block-columns, nnz == stored blocks.
+ *                                  A ragged last tile covers only the rows/columns < n.
+ *   row_ptr == NULL              : dense pattern (every (i, j)); nnz and col_idx ignored.
+ * Columns of a row must be sorted ascending and unique. One pattern serves every head.
+ *
+ * bias     : NULL or fp32 [H, n, n] (the [1, H, seq_q, seq_k] bias), added to S.
+ * key_mask : NULL or fp32 [B, key_mask_heads, n] (the [B, 1 or H, 1, seq_k] additive
+ *            key mask, usually 0 / -inf); key_mask_heads is 1 or H.
+ * plan     : NULL, or a buffer filled by sa_plan_build for this same pattern; calls that
+ *            schedule rows read it instead of building their own. */
+typedef struct sa_problem {
+  int32_t B, H, n, d;
+  int32_t dtype;           /* sa_dtype of q, k, v                                     */
+  int32_t block;           /* 1 or 64                                                 */
+  const int32_t *row_ptr;  /* see pattern kinds                                       */
+  const int32_t *col_idx;
+  int64_t nnz;             /* stored entries of col_idx                               */
+  float scale;             /* multiplies q.k                                          */
+  int32_t key_mask_heads;  /* 1 or H; ignored when key_mask is NULL                   */
+  const float *bias;
+  const float *key_mask;
+  const void *plan;
+  int32_t flags;           /* SA_FLAG_*                                               */
+  int32_t reserved;        /* must be 0                                               */
+} sa_problem;
+
+/* --- CSR row plan (load-balancing schedule) ------------------------------------------
+ * The plan cuts every row of an element CSR into segments of at most a fixed
+ * number of entries, so that rows of very different length (variable per-token
+ * windows and global tokens, gluon-nlp issue replies; global tokens in the
+ * "Sparse Attention" notes) become work units of similar size. It depends on
+ * row_ptr, n and nnz only and serves every head and every call on that pattern.
+ *
+ * sa_plan_bytes: size in bytes of the plan buffer for problem p (host-only; 0 on a bad
+ *   descriptor). Requires block == 1 and row_ptr != NULL.
+ * sa_plan_build: fills plan (device buffer of at least sa_plan_bytes bytes, caller-owned)
+ *   on stream. The plan stays valid while row_ptr's content is unchanged. */
+size_t sa_plan_bytes(const sa_problem *p);
+int sa_plan_build(const sa_problem *p, void *plan, size_t plan_bytes, hipStream_t stream);
+
+/* --- SDDMM: scores at the mask's nonzeros ----------------------------------------------
+ * gluon-nlp issue, opening post, first bullet: a dot product between query i and key j
+ * for each nonzero coordinate of the mask; the scores keep the mask's CSR format.
+ * scores[t * nnz + e] = scale * q[t,i,:].k[t,col_idx[e],:] (+ bias[h,i,col]) (+ key_mask[b,hm,col])
+ * for the row i that holds entry e. scores: fp32 [B*H, nnz], written entirely.
+ * Pattern: element CSR only (else SA_ERR_UNSUPPORTED). */
+int sa_sddmm(const sa_problem *p, const void *q, const void *k, float *scores, hipStream_t stream);
+
+/* --- Sparse row softmax ------------------------------------------------------------------
+ * gluon-nlp issue, opening post, second bullet: a softmax over each sparse row; the weights
+ * keep the scores' pattern. weights[t*nnz + e] over the entries of each row; rows whose
+ * scores are all -inf (or empty rows) get 0. scores and weights: fp32 [B*H, nnz]; they may
+ * be the same buffer (in place). bias/key_mask/q/k are not used.
+ * Pattern: element CSR only. */
+int sa_sparse_softmax(const sa_problem *p, const float *scores, float *weights, hipStream_t stream);
+
+/* --- SpMM: CSR weights times dense V ------------------------------------------------------
+ * gluon-nlp issue, opening post, third bullet: the product of the sparse weights with the
+ * dense value tensor gives the context. out[t,i,:] = sum_{e in row i} weights[t*nnz+e] *
+ * v[t,col_idx[e],:]. out: fp32 [B*H, n, d], written entirely (0 for empty rows).
+ * v has dtype p->dtype. Pattern: element CSR only. */
+int sa_spmm(const sa_problem *p, const float *weights, const void *v, float *out, hipStream_t stream);
+
+/* --- Fused forward --------------------------------------------------------------------------
+ * One pass per row with a running maximum and running sum whose earlier partial sums are
+ * rescaled when the maximum grows, and one division at the end (streaming-dataflow SDPA
+ * review, "proposed method"); never writes S or W. Accepts every pattern kind, bias and
+ * key_mask. out: fp32 [B*H, n, d]. lse: NULL or fp32 [B*H, n].
+ * Element CSR runs on the vector ALUs; block CSR (block == 64) and the dense pattern run
+ * 64-query tiles on bf16 matrix cores when dtype == SA_BF16, as each stored tile is a dense
+ * product (block-sparse replies of the gluon-nlp issue; the AlphaFold2 pull request for
+ * the dense pattern with bias and key mask). */
+int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const void *v,
+                     float *out, float *lse, hipStream_t stream);
+
+/* --- Validation and status ----------------------------------------------------------------
+ * sa_validate_csr: checks the pattern on the device (monotone row_ptr starting at 0,
+ *   row_ptr[last] == nnz, columns in range, strictly ascending within each row) and
+ *   synchronises the stream. Returns SA_OK, SA_ERR_CSR, or an argument error.
+ * sa_status_string: a static, human-readable name for a status code.
+ * sa_last_hip_error_string: the HIP runtime's description of the most recent HIP failure
+ *   behind an SA_ERR_HIP returned to the calling thread ("no HIP error" if none). */
+int sa_validate_csr(const sa_problem *p, hipStream_t stream);
+const char *sa_status_string(int status);
+const char *sa_last_hip_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SA_H */

@@ -1,0 +1,245 @@
+"""ctypes binding of libsa.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls and the same arguments.
+Buffers may be torch tensors on the GPU (their data pointer is passed; their size,
+dtype and contiguity are checked here, since the C side only sees pointers) or raw
+integer device addresses (passed unchecked). A nonzero status raises :class:`SaError`.
+The library is required: importing this module without a built ``libsa.so`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa.so")
+
+SA_OK = 0
+SA_ERR_NULL = -1
+SA_ERR_SHAPE = -2
+SA_ERR_CSR = -3
+SA_ERR_DTYPE = -4
+SA_ERR_UNSUPPORTED = -5
+SA_ERR_ALIGN = -6
+SA_ERR_HIP = -7
+SA_ERR_WORKSPACE = -8
+
+SA_F32 = 0
+SA_BF16 = 1
+SA_FLAG_VALIDATE = 1
+
+EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
+           "sa_fused_forward", "sa_validate_csr", "sa_status_string", "sa_last_hip_error_string")
+
+
+class sa_problem(ctypes.Structure):
+    """Mirror of ``struct sa_problem`` in include/sa.h (field order and sizes are ABI)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("n", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("block", ctypes.c_int32),
+        ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+        ("nnz", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("key_mask_heads", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("key_mask", ctypes.c_void_p), ("plan", ctypes.c_void_p),
+        ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+def _load():
+    # torch provides the device memory and streams, so the library must run on torch's HIP
+    # runtime: importing torch first maps its libamdhip64 (SONAME libamdhip64.so.7), which
+    # the loader then reuses for libsa.so's dependency instead of mapping a second runtime.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python masked_scaled_dot_amd/build.py` "
+            "(hipcc for gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(sa_problem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "sa_plan_bytes": (sz, [P]),
+        "sa_plan_build": (ctypes.c_int, [P, vp, sz, vp]),
+        "sa_sddmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "sa_sparse_softmax": (ctypes.c_int, [P, vp, vp, vp]),
+        "sa_spmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "sa_fused_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
+        "sa_validate_csr": (ctypes.c_int, [P, vp]),
+        "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "sa_last_hip_error_string": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = f" [{_lib.sa_last_hip_error_string().decode()}]" if status == SA_ERR_HIP else ""
+        super().__init__(f"{where}: {sa_status_string(status)} ({status}){detail}")
+
+
+def sa_status_string(status: int) -> str:
+    return _lib.sa_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------------------ marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _is_tensor(x) -> bool:
+    return type(x).__module__.startswith("torch") and hasattr(x, "data_ptr")
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if _is_tensor(x):
+        return x.data_ptr() or None
+    return int(x) or None
+
+
+def _check(x, what: str, numel: int, dtype=None):
+    """Size / dtype / layout checks for torch tensors (raw addresses are trusted)."""
+    if x is None or not _is_tensor(x):
+        return
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if x.numel() < numel:
+        raise ValueError(f"{what} has {x.numel()} elements, needs {numel}")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{what} has dtype {x.dtype}, needs {dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        torch = _torch()
+        if torch.cuda.is_available() and torch.cuda.is_initialized():
+            return torch.cuda.current_stream().cuda_stream or None
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream or None
+    return int(stream) or None
+
+
+class Problem:
+    """Holds an ``sa_problem`` plus references to the tensors it points into."""
+
+    def __init__(self, B, H, n, d, dtype=SA_BF16, row_ptr=None, col_idx=None, nnz=None, block=1,
+                 scale=1.0, bias=None, key_mask=None, key_mask_heads=1, plan=None, flags=0):
+        self._keep = (row_ptr, col_idx, bias, key_mask, plan)
+        if nnz is None:
+            nnz = 0 if col_idx is None else (col_idx.numel() if _is_tensor(col_idx) else 0)
+        self.c = sa_problem(B=B, H=H, n=n, d=d, dtype=dtype, block=block,
+                            row_ptr=_ptr(row_ptr), col_idx=_ptr(col_idx), nnz=nnz,
+                            scale=scale, key_mask_heads=key_mask_heads,
+                            bias=_ptr(bias), key_mask=_ptr(key_mask), plan=_ptr(plan),
+                            flags=flags, reserved=0)
+        torch = _torch()
+        if row_ptr is not None:
+            rows = n if block == 1 else (n + block - 1) // block
+            _check(row_ptr, "row_ptr", rows + 1, torch.int32)
+            _check(col_idx, "col_idx", nnz, torch.int32)
+        _check(bias, "bias", H * n * n, torch.float32)
+        _check(key_mask, "key_mask", B * key_mask_heads * n, torch.float32)
+
+    # convenience sizes
+    @property
+    def BH(self):
+        return self.c.B * self.c.H
+
+    def qkv_dtype(self):
+        torch = _torch()
+        return torch.bfloat16 if self.c.dtype == SA_BF16 else torch.float32
+
+    def set_plan(self, plan):
+        self._keep = self._keep[:4] + (plan,)
+        self.c.plan = _ptr(plan)
+
+
+def _p(prob):
+    return ctypes.byref(prob.c if isinstance(prob, Problem) else prob)
+
+
+def _c(prob) -> sa_problem:
+    return prob.c if isinstance(prob, Problem) else prob
+
+
+def _raise(st, where):
+    if st != SA_OK:
+        raise SaError(st, where)
+
+
+def sa_plan_bytes(prob) -> int:
+    return int(_lib.sa_plan_bytes(_p(prob)))
+
+
+def sa_plan_build(prob, plan, plan_bytes: Optional[int] = None, stream=None):
+    if plan_bytes is None:
+        plan_bytes = plan.numel() * plan.element_size() if _is_tensor(plan) else sa_plan_bytes(prob)
+    _raise(_lib.sa_plan_build(_p(prob), _ptr(plan), plan_bytes, _stream(stream)), "sa_plan_build")
+
+
+def sa_sddmm(prob, q, k, scores, stream=None):
+    c = _c(prob)
+    qkv = _dtype_of(c)
+    _check(q, "q", c.B * c.H * c.n * c.d, qkv)
+    _check(k, "k", c.B * c.H * c.n * c.d, qkv)
+    _check(scores, "scores", c.B * c.H * c.nnz, _torch().float32)
+    _raise(_lib.sa_sddmm(_p(prob), _ptr(q), _ptr(k), _ptr(scores), _stream(stream)), "sa_sddmm")
+
+
+def sa_sparse_softmax(prob, scores, weights, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    _check(scores, "scores", c.B * c.H * c.nnz, f32)
+    _check(weights, "weights", c.B * c.H * c.nnz, f32)
+    _raise(_lib.sa_sparse_softmax(_p(prob), _ptr(scores), _ptr(weights), _stream(stream)),
+           "sa_sparse_softmax")
+
+
+def sa_spmm(prob, weights, v, out, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    _check(weights, "weights", c.B * c.H * c.nnz, f32)
+    _check(v, "v", c.B * c.H * c.n * c.d, _dtype_of(c))
+    _check(out, "out", c.B * c.H * c.n * c.d, f32)
+    _raise(_lib.sa_spmm(_p(prob), _ptr(weights), _ptr(v), _ptr(out), _stream(stream)), "sa_spmm")
+
+
+def sa_fused_forward(prob, q, k, v, out, lse=None, stream=None):
+    c = _c(prob)
+    qkv, f32 = _dtype_of(c), _torch().float32
+    for x, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(x, name, c.B * c.H * c.n * c.d, qkv)
+    _check(out, "out", c.B * c.H * c.n * c.d, f32)
+    _check(lse, "lse", c.B * c.H * c.n, f32)
+    _raise(_lib.sa_fused_forward(_p(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _stream(stream)), "sa_fused_forward")
+
+
+def sa_validate_csr(prob, stream=None) -> int:
+    """Returns the status (SA_OK or SA_ERR_CSR); raises on argument errors."""
+    st = _lib.sa_validate_csr(_p(prob), _stream(stream))
+    if st not in (SA_OK, SA_ERR_CSR):
+        _raise(st, "sa_validate_csr")
+    return st
+
+
+def _dtype_of(c: sa_problem):
+    torch = _torch()
+    return torch.bfloat16 if c.dtype == SA_BF16 else torch.float32
+
+
+def raw(name: str):
+    """The raw ctypes function of an exported symbol (for ABI tests)."""
+    return getattr(_lib, name)

@@ -1,0 +1,209 @@
+// C ABI of the library: host-side argument checks, then dispatch to the gfx950 kernels.
+// Every check here runs before any HIP call, so bad arguments return a status without
+// touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/sa.h"
+#include "kernels.h"
+#include "plan_layout.h"
+
+namespace {
+
+enum Op { kOpSddmm, kOpSoftmax, kOpSpmm, kOpFused, kOpPlan, kOpValidate };
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int check_problem(const sa_problem* p, Op op) {
+  if (!p) return SA_ERR_NULL;
+  if (p->reserved != 0) return SA_ERR_UNSUPPORTED;
+  if (p->flags & ~SA_FLAG_VALIDATE) return SA_ERR_UNSUPPORTED;
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (p->B < 0 || p->H < 0 || p->n < 0 || p->d <= 0) return SA_ERR_SHAPE;
+  if (p->d != 32 && p->d != 64 && p->d != 128) return SA_ERR_UNSUPPORTED;
+  if (p->block != 1 && p->block != 64) return SA_ERR_UNSUPPORTED;
+  if (!std::isfinite(p->scale)) return SA_ERR_SHAPE;
+  const bool dense = p->row_ptr == nullptr;
+  const bool element_csr = !dense && p->block == 1;
+  switch (op) {
+    case kOpSddmm:
+    case kOpSoftmax:
+    case kOpSpmm:
+    case kOpPlan:
+      if (!element_csr) return SA_ERR_UNSUPPORTED;
+      break;
+    case kOpValidate:
+      if (dense) return SA_ERR_NULL;
+      break;
+    case kOpFused:
+      break;
+  }
+  if (!dense) {
+    if (p->nnz < 0 || p->nnz > INT32_MAX) return SA_ERR_SHAPE;
+    if (p->nnz > 0 && !p->col_idx) return SA_ERR_NULL;
+    if (p->block == 64 && p->n > 0) {
+      const long long nb = (p->n + 63) / 64;
+      if (p->nnz > nb * nb) return SA_ERR_SHAPE;
+    } else if ((long long)p->nnz > (long long)p->n * (long long)p->n) {
+      return SA_ERR_SHAPE;
+    }
+  }
+  if (p->key_mask && p->key_mask_heads != 1 && p->key_mask_heads != p->H) return SA_ERR_SHAPE;
+  // Buffer element counts must fit in 64-bit byte offsets used by the kernels.
+  const long long bh = (long long)p->B * p->H;
+  if (bh > INT32_MAX) return SA_ERR_SHAPE;
+  if (bh * p->n > INT32_MAX) return SA_ERR_SHAPE;  // (head, row) units are indexed in 32 bits
+  if (bh * (long long)p->n * p->d > (1ll << 40)) return SA_ERR_SHAPE;
+  if (!dense && bh * (long long)p->nnz > (1ll << 40)) return SA_ERR_SHAPE;
+  if (p->bias && (long long)p->H * p->n * (long long)p->n > (1ll << 40)) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+bool empty_problem(const sa_problem* p) { return p->B == 0 || p->H == 0 || p->n == 0; }
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SA_OK;
+  g_last_hip_error = e;
+  return SA_ERR_HIP;
+}
+
+// An error left pending by unrelated HIP calls in this thread would otherwise be reported
+// as a failure of the next launch; take it off before launching.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+// Device validation of the pattern; synchronises the stream.
+int validate_now(const sa_problem* p, hipStream_t s) {
+  if (empty_problem(p) && p->n == 0) return SA_OK;
+  int* flag = nullptr;
+  clear_stale_error();
+  if (hipMalloc(&flag, sizeof(int)) != hipSuccess) return SA_ERR_HIP;
+  int host = 0;
+  int st = SA_OK;
+  if (hipMemsetAsync(flag, 0, sizeof(int), s) != hipSuccess ||
+      sa::launch_validate(*p, flag, s) != hipSuccess ||
+      hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    st = SA_ERR_HIP;
+  } else if (host != 0) {
+    st = SA_ERR_CSR;
+  }
+  (void)hipFree(flag);
+  return st;
+}
+
+// With SA_FLAG_VALIDATE and a caller plan, check that the plan was built for this pattern.
+int check_plan_now(const sa_problem* p, hipStream_t s) {
+  int hdr[sa::kPlanHeaderWords];
+  if (hipMemcpyAsync(hdr, p->plan, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SA_ERR_HIP;
+  const long long nnz = (long long)(uint32_t)hdr[2] | ((long long)hdr[3] << 32);
+  if (hdr[0] != sa::kPlanMagic || hdr[1] != p->n || nnz != p->nnz) return SA_ERR_WORKSPACE;
+  return SA_OK;
+}
+
+int pre_launch(const sa_problem* p, hipStream_t s) {
+  clear_stale_error();
+  if (p->flags & SA_FLAG_VALIDATE) {
+    if (p->row_ptr) {
+      const int st = validate_now(p, s);
+      if (st != SA_OK) return st;
+    }
+    if (p->plan) {
+      const int st = check_plan_now(p, s);
+      if (st != SA_OK) return st;
+    }
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sa_plan_bytes(const sa_problem* p) {
+  if (check_problem(p, kOpPlan) != SA_OK) return 0;
+  return sa::plan_bytes(p->n, p->nnz);
+}
+
+int sa_plan_build(const sa_problem* p, void* plan, size_t plan_bytes, hipStream_t stream) {
+  int st = check_problem(p, kOpPlan);
+  if (st != SA_OK) return st;
+  if (!plan) return SA_ERR_NULL;
+  if (plan_bytes < sa::plan_bytes(p->n, p->nnz)) return SA_ERR_WORKSPACE;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_plan(*p, plan, plan_bytes, stream));
+}
+
+int sa_sddmm(const sa_problem* p, const void* q, const void* k, float* scores, hipStream_t stream) {
+  int st = check_problem(p, kOpSddmm);
+  if (st != SA_OK) return st;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!q || !k || !scores) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores)) return SA_ERR_ALIGN;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_sddmm(*p, q, k, scores, stream));
+}
+
+int sa_sparse_softmax(const sa_problem* p, const float* scores, float* weights, hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!scores || !weights) return SA_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(weights)) return SA_ERR_ALIGN;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_softmax(*p, scores, weights, stream));
+}
+
+int sa_spmm(const sa_problem* p, const float* weights, const void* v, float* out, hipStream_t stream) {
+  int st = check_problem(p, kOpSpmm);
+  if (st != SA_OK) return st;
+  if (empty_problem(p)) return SA_OK;
+  if (!v || !out || (p->nnz > 0 && !weights)) return SA_ERR_NULL;
+  if (!aligned16(v) || !aligned16(out) || (weights && !aligned16(weights))) return SA_ERR_ALIGN;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_spmm(*p, weights, v, out, stream));
+}
+
+int sa_fused_forward(const sa_problem* p, const void* q, const void* k, const void* v, float* out,
+                     float* lse, hipStream_t stream) {
+  int st = check_problem(p, kOpFused);
+  if (st != SA_OK) return st;
+  if (empty_problem(p)) return SA_OK;
+  if (!q || !k || !v || !out) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_ALIGN;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  if (sa::fused_mfma_supported(*p)) return hip_status(sa::launch_fused_mfma(*p, q, k, v, out, lse, stream));
+  return hip_status(sa::launch_fused_valu(*p, q, k, v, out, lse, stream));
+}
+
+int sa_validate_csr(const sa_problem* p, hipStream_t stream) {
+  const int st = check_problem(p, kOpValidate);
+  if (st != SA_OK) return st;
+  return validate_now(p, stream);
+}
+
+const char* sa_last_hip_error_string(void) {
+  return g_last_hip_error == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip_error);
+}
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL: a required pointer is NULL";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE: inconsistent shape, size or broadcast dimension";
+    case SA_ERR_CSR: return "SA_ERR_CSR: malformed CSR pattern";
+    case SA_ERR_DTYPE: return "SA_ERR_DTYPE: unsupported element type";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: head size, block size, flag or pattern kind not supported by this call";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN: buffer not 16-byte aligned";
+    case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime or launch failure";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: plan buffer too small or built for another pattern";
+  }
+  return "unknown sa status";
+}
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// Internal launchers of the gfx950 kernels. The host-side ABI (api.cpp) validates the
+// arguments and then calls these; each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include "../../include/sa.h"
+
+namespace sa {
+
+hipError_t launch_sddmm(const sa_problem& p, const void* q, const void* k, float* scores,
+                        hipStream_t s);
+hipError_t launch_softmax(const sa_problem& p, const float* scores, float* weights, hipStream_t s);
+hipError_t launch_spmm(const sa_problem& p, const float* weights, const void* v, float* out,
+                       hipStream_t s);
+hipError_t launch_fused_valu(const sa_problem& p, const void* q, const void* k, const void* v,
+                             float* out, float* lse, hipStream_t s);
+hipError_t launch_fused_mfma(const sa_problem& p, const void* q, const void* k, const void* v,
+                             float* out, float* lse, hipStream_t s);
+bool fused_mfma_supported(const sa_problem& p);
+
+// CSR row plan and validation.
+size_t plan_bytes(int n, long long nnz);
+hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_t s);
+hipError_t launch_validate(const sa_problem& p, int* flag_dev, hipStream_t s);
+
+}  // namespace sa

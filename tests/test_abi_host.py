@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point declared in
+include/sa.h, the ctypes struct mirrors the C layout, and host-side argument checks
+return their status codes before any device work (fake non-NULL pointers are never
+dereferenced on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+def _ensure_built():
+    if not os.path.exists(os.path.join(ROOT, "masked_scaled_dot_amd", "libsa.so")):
+        import __graft_entry__
+        __graft_entry__._build_module().build()
+
+
+_ensure_built()
+import masked_scaled_dot_amd as sa  # noqa: E402
+from masked_scaled_dot_amd import _lib  # noqa: E402
+
+FAKE = 0x10000  # aligned, never dereferenced by the paths tested here
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert set(declared) == set(sa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (sa_\w+)", out))
+    assert set(declared) <= exported
+    for name in declared:
+        assert getattr(ctypes.CDLL(sa.LIB_PATH), name) is not None
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f[0] for f in _lib.sa_problem._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(sa_problem, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sa.h"\n'
+                   'int main(void) {\n  printf("size %zu\\n", sizeof(sa_problem));\n'
+                   f"{body}\n  return 0;\n}}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(_lib.sa_problem)
+    for f in fields:
+        assert int(got[f]) == getattr(_lib.sa_problem, f).offset, f
+
+
+def _prob(**kw):
+    base = dict(B=1, H=2, n=100, d=64, dtype=sa.SA_BF16, block=1, row_ptr=FAKE, col_idx=FAKE,
+                nnz=500, scale=0.125, key_mask_heads=1, bias=None, key_mask=None, plan=None,
+                flags=0, reserved=0)
+    base.update(kw)
+    return _lib.sa_problem(**base)
+
+
+def _call(name, p, *ptrs):
+    fn = _lib.raw(name)
+    return fn(ctypes.byref(p) if p is not None else None, *ptrs)
+
+
+PIPE = [("sa_sddmm", 4), ("sa_sparse_softmax", 3), ("sa_spmm", 4), ("sa_fused_forward", 6)]
+
+
+@pytest.mark.parametrize("name,nargs", PIPE)
+def test_null_problem(name, nargs):
+    assert _call(name, None, *([FAKE] * (nargs - 1)), None) == sa.SA_ERR_NULL
+
+
+@pytest.mark.parametrize("name,nargs", PIPE)
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, sa.SA_ERR_DTYPE),
+    ("d", 48, sa.SA_ERR_UNSUPPORTED),
+    ("d", 256, sa.SA_ERR_UNSUPPORTED),
+    ("block", 32, sa.SA_ERR_UNSUPPORTED),
+    ("nnz", -1, sa.SA_ERR_SHAPE),
+    ("nnz", 100 * 100 + 1, sa.SA_ERR_SHAPE),
+    ("n", -5, sa.SA_ERR_SHAPE),
+    ("flags", 8, sa.SA_ERR_UNSUPPORTED),
+    ("reserved", 1, sa.SA_ERR_UNSUPPORTED),
+    ("scale", float("nan"), sa.SA_ERR_SHAPE),
+    ("col_idx", None, sa.SA_ERR_NULL),
+])
+def test_descriptor_errors(name, nargs, field, value, status):
+    p = _prob(**{field: value})
+    assert _call(name, p, *([FAKE] * (nargs - 2)), None, None) == status
+
+
+@pytest.mark.parametrize("name,nargs", PIPE[:3])
+def test_non_csr_patterns_rejected_by_pipeline_calls(name, nargs):
+    assert _call(name, _prob(row_ptr=None), *([FAKE] * (nargs - 1)), None) == sa.SA_ERR_UNSUPPORTED
+    assert _call(name, _prob(block=64, nnz=4), *([FAKE] * (nargs - 1)), None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_key_mask_heads_broadcast_rule():
+    # the key mask's head dimension is 1 or H (AlphaFold2 PR, mask shape list)
+    for kmh, st in ((1, None), (2, None), (3, sa.SA_ERR_SHAPE), (0, sa.SA_ERR_SHAPE)):
+        p = _prob(key_mask=FAKE, key_mask_heads=kmh, n=0, nnz=0)   # n=0: valid calls do nothing
+        got = _call("sa_sddmm", p, FAKE, FAKE, FAKE, None)
+        assert got == (sa.SA_OK if st is None else st)
+
+
+@pytest.mark.parametrize("name,nargs", PIPE)
+def test_null_buffers(name, nargs):
+    for i in range(nargs - 1 - (1 if name == "sa_fused_forward" else 0)):
+        ptrs = [FAKE] * (nargs - 1)
+        ptrs[i] = None
+        assert _call(name, _prob(), *ptrs, None) == sa.SA_ERR_NULL, i
+
+
+@pytest.mark.parametrize("name,nargs", PIPE)
+def test_misaligned_buffers(name, nargs):
+    for i in range(nargs - 1 - (1 if name == "sa_fused_forward" else 0)):
+        ptrs = [FAKE] * (nargs - 1)
+        ptrs[i] = FAKE + 2
+        assert _call(name, _prob(), *ptrs, None) == sa.SA_ERR_ALIGN, i
+
+
+@pytest.mark.parametrize("name,nargs", PIPE)
+def test_empty_problems_do_nothing(name, nargs):
+    for field in ("B", "H", "n"):
+        p = _prob(**{field: 0}, nnz=0)
+        assert _call(name, p, *([None] * (nargs - 1)), None) == sa.SA_OK
+
+
+def test_plan_bytes_and_build_checks():
+    p = _prob(n=4096, nnz=1052026)
+    nb = _lib.raw("sa_plan_bytes")(ctypes.byref(p))
+    assert nb == 4 * (8 + 4 * (4096 + 1052026 // 512 + 1))
+    assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(row_ptr=None))) == 0
+    assert _lib.raw("sa_plan_build")(ctypes.byref(p), None, nb, None) == sa.SA_ERR_NULL
+    assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE, nb - 1, None) == sa.SA_ERR_WORKSPACE
+
+
+def test_validate_requires_a_pattern():
+    assert _lib.raw("sa_validate_csr")(ctypes.byref(_prob(row_ptr=None)), None) == sa.SA_ERR_NULL
+
+
+def test_status_strings():
+    for code in range(0, -9, -1):
+        s = sa.sa_status_string(code)
+        assert s.startswith("SA_")
+    assert "unknown" in sa.sa_status_string(-99)
+
+
+def test_binding_checks_tensor_sizes():
+    import torch
+    rp = torch.zeros(101, dtype=torch.int32)
+    ci = torch.zeros(10, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sa.Problem(1, 1, 100, 64, sa.SA_BF16, rp, ci, nnz=20)
+    prob = sa.Problem(1, 1, 100, 64, sa.SA_BF16, rp, ci, nnz=10)
+    small = torch.zeros(5)
+    with pytest.raises(ValueError):
+        sa.sa_sparse_softmax(prob, small, small)
+
+
+def test_single_hip_runtime_shared_with_torch():
+    """The library must run on the HIP runtime that owns torch's memory and streams."""
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
+    assert len(hip) == 1, hip

@@ -1,0 +1,323 @@
+"""GPU parity: every entry point against the fp64 oracle, through the C ABI.
+
+Small cases are compared element by element with the whole oracle output; they span
+several tiles and a ragged tail. Full-size workloads are compared on sampled rows that
+the oracle evaluates one by one, plus invariants over every row.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import masked_scaled_dot_amd as sa
+import oracle
+from gpu_util import DEV, DevProblem, check, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _elementwise(p):
+    """The same problem with its pattern expanded to element CSR (for the pipeline calls)."""
+    if p.row_ptr is not None and p.block == 1:
+        return p
+    import copy
+    rp, ci = p.element_csr()
+    e = copy.copy(p)
+    e.row_ptr, e.col_idx, e.block = rp.astype(np.int32), ci.astype(np.int32), 1
+    return e
+
+
+def _pattern(p):
+    if p.row_ptr is None:
+        return ("dense",)
+    if p.block == 64:
+        return ("bsr", p.row_ptr, p.col_idx, 64)
+    return ("csr", p.row_ptr, p.col_idx)
+
+
+SMALL = {
+    "window_n128_f32": lambda: gen.make("window_n128"),
+    "window_f32_d64_ragged": lambda: gen.make("window_n128", n=131, d=64, H=2),
+    "window_f32_d128": lambda: gen.make("window_n128", n=77, d=128, window=30),
+    "longformer_bf16_d64": lambda: gen.make("longformer_n4096", n=700, H=3, window=40),
+    "longformer_bf16_d32": lambda: gen.make("longformer_n4096", n=333, H=2, d=32, window=20),
+    "longformer_bf16_d128": lambda: gen.make("longformer_n4096", n=257, H=2, d=128, window=60),
+    "random_bf16_long_rows": lambda: gen.make("random_n8192", n=1000, H=2, kmin=1, kmax=900),
+    "random_f32_d32": lambda: gen.make("random_n8192", n=500, H=2, d=32, dtype="f32", kmin=1, kmax=200),
+    "bsr_bf16_d128_ragged": lambda: gen.make("bsr_n16384", n=64 * 6 + 21, H=2, extra=3),
+    "bsr_bf16_d64": lambda: gen.make("bsr_n16384", n=64 * 8, H=2, d=64, extra=2),
+    "bsr_f32_d32": lambda: gen.make("bsr_n16384", n=64 * 5, H=1, d=32, dtype="f32", extra=2),
+    "evoformer_bf16_odd": lambda: gen.make("evoformer_l384", B=3, H=2, n=97),
+    "evoformer_bf16": lambda: gen.make("evoformer_l384", B=2, H=8, n=384),
+    "evoformer_f32_d64": lambda: gen.make("evoformer_l384", B=2, H=2, n=130, d=64, dtype="f32"),
+    "random_bias_keymask": lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
+                                            bias=True, key_mask=True, pmax=40),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def small(name):
+    return SMALL[name]()
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_pipeline_parity_small(name):
+    p = _elementwise(small(name))
+    say(f"pipeline {name}: BH={p.BH} n={p.n} d={p.d} nnz={p.nnz} {p.dtype}")
+    dp = DevProblem(p)
+    S, W, O = dp.pipeline()
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H, **dp.oracle_args())
+    check(S, ref["S"], p.dtype, "scores")
+    check(W, ref["W"], p.dtype, "weights")
+    refd = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(small(name)),
+                                  want_weights=False, **dp.oracle_args())
+    check(O, refd["O"], p.dtype, "context")
+    # the pattern and indices are the caller's and come back untouched, bit for bit
+    assert np.array_equal(dp.row_ptr.cpu().numpy(), p.row_ptr)
+    assert np.array_equal(dp.col_idx.cpu().numpy(), p.col_idx)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_fused_parity_small(name):
+    p = small(name)
+    say(f"fused {name}: BH={p.BH} n={p.n} d={p.d} block={p.block} dense={p.row_ptr is None}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), want_weights=False,
+                                 **dp.oracle_args())
+    check(O, ref["O"], p.dtype, "context")
+    check(lse, ref["lse"], p.dtype, "lse")
+
+
+def test_fused_without_lse_and_scale_one():
+    p = small("longformer_bf16_d64")
+    dp = DevProblem(p, scale=1.0)
+    O, _ = dp.fused(want_lse=False)
+    ref = oracle.attention_dense(p.q, p.k, p.v, 1.0, p.H, _pattern(p), want_weights=False)
+    check(O, ref["O"], p.dtype, "context scale=1")
+    S, W, O2 = dp.pipeline()
+    check(O2, ref["O"], p.dtype, "pipeline context scale=1")
+
+
+# ------------------------------------------------------------------------------ edge cases
+
+def _custom(rows, n, d, dtype, H=1, B=1, seed=5, key_mask=None):
+    rp, ci = gen.csr_from_rows(rows)
+    rng = np.random.default_rng(seed)
+    qkv = []
+    for _ in range(3):
+        x = rng.standard_normal((B * H, n, d)).astype(np.float32)
+        bits = gen.bf16_round_bits(x) if dtype == "bf16" else None
+        qkv.append((gen.bf16_bits_to_f32(bits).reshape(x.shape) if bits is not None else x,
+                    None if bits is None else bits.reshape(x.shape)))
+    return gen.Problem(name="custom", B=B, H=H, n=n, d=d, dtype=dtype, q=qkv[0][0], k=qkv[1][0],
+                       v=qkv[2][0], row_ptr=rp, col_idx=ci, scale=1 / np.sqrt(d),
+                       key_mask=key_mask, q_bits=qkv[0][1], k_bits=qkv[1][1], v_bits=qkv[2][1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_and_fully_masked_rows(dtype):
+    n, d = 70, 64
+    rng = np.random.default_rng(3)
+    rows = [sorted(rng.choice(n, size=int(rng.integers(1, 20)), replace=False).tolist())
+            for _ in range(n)]
+    for i in (0, 5, 69):
+        rows[i] = []
+    rows[7] = [3]                    # key 3 is masked for batch 1 -> row 7 fully masked there
+    km = np.zeros((2, 1, n), np.float32)
+    km[1, 0, 3] = -np.inf
+    km[0, 0, 40:] = -np.inf
+    p = _custom(rows, n, d, dtype, H=2, B=2, key_mask=km)
+    dp = DevProblem(p)
+    S, W, O = dp.pipeline()
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H, key_mask=km)
+    check(S, ref["S"], dtype, "scores")
+    check(W, ref["W"], dtype, "weights")
+    check(O, ref["O"], dtype, "context")
+    for t in range(p.BH):
+        for i in (0, 5, 69):
+            assert np.all(O[t, i] == 0)
+    assert np.all(O[2:, 7] == 0) and np.all(W[2:, p.row_ptr[7]] == 0)
+    Of, lse = dp.fused()
+    check(Of, ref["O"], dtype, "fused context")
+    check(lse, ref["lse"], dtype, "fused lse")
+    assert lse[2, 7] == -np.inf and lse[0, 0] == -np.inf
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_diagonal_only_rows_are_exact(dtype):
+    n, d = 300, 32
+    p = _custom([[i] for i in range(n)], n, d, dtype, H=3)
+    dp = DevProblem(p)
+    S, W, O = dp.pipeline()
+    assert np.array_equal(W, np.ones_like(W))
+    assert np.array_equal(O, p.v)
+    Of, lse = dp.fused()
+    assert np.array_equal(Of, p.v)
+
+
+def test_zero_queries_give_uniform_weights():
+    p = _elementwise(small("random_bf16_long_rows"))
+    dp = DevProblem(p)
+    dp.q.zero_()
+    S, W, O = dp.pipeline()
+    lens = np.diff(p.row_ptr)
+    row_of = np.repeat(np.arange(p.n), lens)
+    np.testing.assert_allclose(W, np.broadcast_to(1.0 / lens[row_of], W.shape), rtol=2e-6, atol=0)
+    assert np.all(S == 0)
+
+
+def test_determinism_bitwise():
+    p = _elementwise(small("longformer_bf16_d64"))
+    dp = DevProblem(p)
+    a = dp.pipeline()
+    b = dp.pipeline()
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(dp.fused()[0], dp.fused()[0])
+
+
+def test_softmax_alone_long_rows_and_infinities():
+    rows_len = [0, 1, 3, 64, 65, 511, 512, 513, 1000, 4096, 5000, 0, 7]
+    rows_len += [0] * (5001 - len(rows_len))          # a square (n, n) mask: n >= longest row
+    rp = np.zeros(len(rows_len) + 1, np.int32)
+    rp[1:] = np.cumsum(rows_len)
+    nnz = int(rp[-1])
+    BH = 3
+    S = gen.random_scores(BH, nnz, seed=9, spread=4.0)
+    S[0, rp[3]:rp[3] + 10] = -np.inf                  # part of a row masked
+    S[1, rp[8]:rp[9]] = -np.inf                        # a whole long row masked
+    S[2, rp[2]:rp[3]] = -np.inf                        # a whole short row masked
+    n = len(rows_len)
+    prob = sa.Problem(1, BH, n, 32, sa.SA_F32, torch.from_numpy(rp).to(DEV),
+                      torch.zeros(nnz, dtype=torch.int32, device=DEV), nnz)
+    s_dev = torch.from_numpy(S).to(DEV)
+    w_dev = torch.full_like(s_dev, float("nan"))
+    sa.sa_sparse_softmax(prob, s_dev, w_dev)
+    ref = oracle.sparse_softmax(S, rp)
+    check(w_dev.cpu().numpy(), ref, "f32", "softmax")
+    sa.sa_sparse_softmax(prob, s_dev, s_dev)          # in place
+    check(s_dev.cpu().numpy(), ref, "f32", "softmax in place")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 32), ("bf16", 128), ("f32", 128)])
+def test_spmm_alone(dtype, d):
+    p = _elementwise(gen.make("random_n8192", n=400, H=2, d=d, dtype=dtype, kmin=0 + 1, kmax=300))
+    dp = DevProblem(p)
+    Wn = gen.random_weights(p.BH, p.nnz, seed=11)
+    w_dev = torch.from_numpy(Wn).to(DEV)
+    out = torch.full((p.BH, p.n, p.d), float("nan"), device=DEV)
+    sa.sa_spmm(dp.prob, w_dev, dp.v, out)
+    ref = oracle.spmm(Wn, p.row_ptr, p.col_idx, p.v)
+    # unnormalised weights in [0,1): compare relative to the row's weight mass
+    got = out.cpu().numpy()
+    mass = np.zeros((p.BH, p.n))
+    for i in range(p.n):
+        mass[:, i] = Wn[:, p.row_ptr[i]:p.row_ptr[i + 1]].sum(axis=1)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert np.all(np.abs(got - ref) <= tol * np.maximum(mass, 1.0)[:, :, None])
+
+
+# ------------------------------------------------------------------------------ validation / plan
+
+def test_validate_csr():
+    p = small("longformer_bf16_d32")
+    dp = DevProblem(p)
+    assert sa.sa_validate_csr(dp.prob) == sa.SA_OK
+    bad_cols = p.col_idx.copy()
+    bad_cols[10], bad_cols[11] = bad_cols[11], bad_cols[10]          # unsorted row
+    for rp, ci in ((p.row_ptr, bad_cols),
+                   (p.row_ptr, np.where(np.arange(p.nnz) == 5, p.n + 3, p.col_idx).astype(np.int32)),
+                   (np.where(np.arange(p.n + 1) == 50, p.row_ptr[52], p.row_ptr).astype(np.int32),
+                    p.col_idx)):
+        rp_d = torch.from_numpy(rp).to(DEV)
+        ci_d = torch.from_numpy(ci).to(DEV)
+        prob = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16, rp_d, ci_d, p.nnz, scale=p.scale)
+        assert sa.sa_validate_csr(prob) == sa.SA_ERR_CSR
+        probv = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16, rp_d, ci_d, p.nnz, scale=p.scale,
+                           flags=sa.SA_FLAG_VALIDATE)
+        scores = torch.empty(p.BH * p.nnz, device=DEV)
+        with pytest.raises(sa.SaError) as ei:
+            sa.sa_sddmm(probv, dp.q, dp.k, scores)
+        assert ei.value.status == sa.SA_ERR_CSR
+        # without validation a malformed CSR still runs without invalid accesses
+        sa.sa_sddmm(prob, dp.q, dp.k, scores)
+        torch.cuda.synchronize()
+
+
+def test_plan_build_matches_host():
+    p = gen.make("longformer_n4096", n=3000, H=1, window=300)        # rows up to 3000 entries
+    dp = DevProblem(p)
+    nbytes = sa.sa_plan_bytes(dp.prob)
+    plan = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+    sa.sa_plan_build(dp.prob, plan)
+    torch.cuda.synchronize()
+    h = plan.cpu().numpy()
+    assert h[0] == 0x53415031 and h[1] == p.n and h[2] == p.nnz and h[4] == 512
+    items = h[8:8 + 4 * h[5]].reshape(-1, 4)
+    exp = []
+    for i in range(p.n):
+        a, ln = int(p.row_ptr[i]), int(p.row_ptr[i + 1] - p.row_ptr[i])
+        ns = max(1, -(-ln // 512))
+        for s in range(ns):
+            exp.append((i, a + ln * s // ns, a + ln * (s + 1) // ns, (ns << 16) | s))
+    assert np.array_equal(items, np.array(exp, dtype=np.int32))
+    # a problem that carries the plan validates it when asked to
+    dp.prob.set_plan(plan)
+    dp.prob.c.flags = sa.SA_FLAG_VALIDATE
+    S, W, O = dp.pipeline()
+    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), [(0, 0), (0, 1500)])
+    check(O[0, [0, 1500]], ref["O"], p.dtype, "context with plan")
+
+
+# ------------------------------------------------------------------------------ full size
+
+FULL = ["longformer_n4096", "random_n8192", "bsr_n16384", "evoformer_l384"]
+
+
+@functools.lru_cache(maxsize=2)
+def full(name):
+    return gen.make(name)
+
+
+def _sample_rows(p, k=40, seed=0):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (0, 1), (p.BH - 1, p.n - 1), (p.BH // 2, p.n // 2)}
+    while len(pairs) < k:
+        pairs.add((int(rng.integers(p.BH)), int(rng.integers(p.n))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", FULL[:3])
+def test_full_size_pipeline_sampled(name):
+    p = full(name)
+    pe = _elementwise(p)
+    say(f"full pipeline {name}: BH={p.BH} n={p.n} nnz/head={pe.nnz}")
+    dp = DevProblem(pe)
+    S, W, O = dp.pipeline()
+    pairs = _sample_rows(p)
+    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), pairs)
+    got_o = np.stack([O[t, i] for t, i in pairs])
+    check(got_o, ref["O"], p.dtype, "context (sampled rows)")
+    got_w = np.concatenate([W[t, pe.row_ptr[i]:pe.row_ptr[i + 1]] for t, i in pairs])
+    check(got_w, np.concatenate(ref["W"]), p.dtype, "weights (sampled rows)")
+    # every row of every head: weights are nonnegative and sum to one
+    assert np.all(W >= 0)
+    sums = np.add.reduceat(W.astype(np.float64), pe.row_ptr[:-1], axis=1)
+    assert np.abs(sums - 1.0).max() < 1e-5
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_fused_sampled(name):
+    p = full(name)
+    say(f"full fused {name}: BH={p.BH} n={p.n} block={p.block}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    pairs = _sample_rows(p)
+    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), pairs,
+                                **dp.oracle_args())
+    check(np.stack([O[t, i] for t, i in pairs]), ref["O"], p.dtype, "context (sampled rows)")
+    check(np.array([lse[t, i] for t, i in pairs]), ref["lse"], p.dtype, "lse (sampled rows)")
+    assert np.all(np.isfinite(O))
