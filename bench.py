@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--profile", choices=["pipeline", "fused_csr", "fused_bsr", "fused_dense"],
+                    help="run only this kernel family (steps iterations after warmup) and exit; "
+                         "for rocprofv3 runs")
     return ap.parse_args()
 
 
@@ -167,6 +170,7 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     for _ in range(steps):
         step(timer)
     torch.cuda.synchronize()
+
     wall = time.perf_counter() - t0
     return wall
 
@@ -227,6 +231,21 @@ def load_traffic(kernel, src_hash):
     return ent.get("bytes_per_launch")
 
 
+def profile_only(args, torch, sa, gen):
+    """Run one kernel family alone so that a profiler sees only its launches."""
+    if args.profile == "pipeline":
+        p = gen.make(args.workload)
+        prob, t, nnz = to_device(p, torch, sa)
+        run_pipeline_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d, args.steps, args.warmup, None)
+    else:
+        name = {"fused_csr": args.workload, "fused_bsr": "bsr_n16384",
+                "fused_dense": "evoformer_l384"}[args.profile]
+        q = gen.make(name)
+        us = time_fused(torch, sa, q, iters=args.steps, warmup=args.warmup)
+        log(f"{args.profile} {name}: {us:.1f} us")
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -242,6 +261,8 @@ def main():
     import masked_scaled_dot_amd as sa
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile:
+        return profile_only(args, torch, sa, gen)
     p = gen.make(args.workload)
     BH, n, d = p.BH, p.n, p.d
     prob, t, nnz = to_device(p, torch, sa)

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/sa.h"
 #include "kernels.h"
@@ -101,8 +102,12 @@ int check_plan_now(const sa_problem* p, hipStream_t s) {
   if (hipMemcpyAsync(hdr, p->plan, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return SA_ERR_HIP;
-  const long long nnz = (long long)(uint32_t)hdr[2] | ((long long)hdr[3] << 32);
-  if (hdr[0] != sa::kPlanMagic || hdr[1] != p->n || nnz != p->nnz) return SA_ERR_WORKSPACE;
+  const long long nnz = (long long)(uint32_t)hdr[sa::kHNnzLo] | ((long long)hdr[sa::kHNnzHi] << 32);
+  if (hdr[sa::kHMagic] != sa::kPlanMagic || hdr[sa::kHN] != p->n || nnz != p->nnz ||
+      hdr[sa::kHValid] != 1)
+    return SA_ERR_WORKSPACE;
+  // the scratch of split rows is sized for (B*H, d)
+  if ((long long)p->B * p->H > hdr[sa::kHBH] || p->d > hdr[sa::kHD]) return SA_ERR_WORKSPACE;
   return SA_OK;
 }
 
@@ -127,14 +132,32 @@ extern "C" {
 
 size_t sa_plan_bytes(const sa_problem* p) {
   if (check_problem(p, kOpPlan) != SA_OK) return 0;
-  return sa::plan_bytes(p->n, p->nnz);
+  const long long BH = (long long)p->B * p->H;
+  if (p->n == 0) return sa::plan_bytes_for(0, 0, 0, BH, p->d);
+  // Exact count of long rows and their segments: one synchronous copy of row_ptr.
+  std::vector<int32_t> rp((size_t)p->n + 1);
+  clear_stale_error();
+  if (hipMemcpy(rp.data(), p->row_ptr, rp.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return 0;
+  long long L = 0, S = 0;
+  for (int i = 0; i < p->n; ++i) {
+    long long a = rp[i], b = rp[i + 1];
+    a = a < 0 ? 0 : (a > p->nnz ? p->nnz : a);
+    b = b < a ? a : (b > p->nnz ? p->nnz : b);
+    if (b - a > sa::kLongRow) {
+      ++L;
+      S += (b - a + sa::kSeg - 1) / sa::kSeg;
+    }
+  }
+  return sa::plan_bytes_for(p->n, L, S, BH, p->d);
 }
 
 int sa_plan_build(const sa_problem* p, void* plan, size_t plan_bytes, hipStream_t stream) {
   int st = check_problem(p, kOpPlan);
   if (st != SA_OK) return st;
   if (!plan) return SA_ERR_NULL;
-  if (plan_bytes < sa::plan_bytes(p->n, p->nnz)) return SA_ERR_WORKSPACE;
+  if (plan_bytes < sa::plan_bytes_for(p->n, 0, 0, 0, p->d)) return SA_ERR_WORKSPACE;
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_plan(*p, plan, plan_bytes, stream));
 }

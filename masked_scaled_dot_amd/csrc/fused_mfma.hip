@@ -32,6 +32,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v2;
 constexpr int kTile = 64;       // queries per workgroup and keys per block
 constexpr int kThreads = 256;
 constexpr int kVtStride = kTile + 8;  // keys per V^T row in LDS (+16 B padding)
+constexpr float kSlack = 8.f;          // lazy running-max threshold, log2 units
 
 template <int D>
 struct alignas(16) Smem {
@@ -102,41 +103,103 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 #pragma unroll
   for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
+  // Per-thread share of one key block: K chunks (row-major copy) and V 4x8 sub-blocks.
+  constexpr int KCH = (kTile * (D / 8) + kThreads - 1) / kThreads;        // uint4 K chunks
+  constexpr int VT = ((kTile / 4) * (D / 8) + kThreads - 1) / kThreads;   // V tasks
+  uint4 kreg[KCH];
+  uint4 vreg[VT][4];
+  auto load_block = [&](int blk) {
+    int bc = blk;
+    if constexpr (!kDense) bc = clampi(col_idx[blk], 0, ntiles - 1);
+    const int kb0 = bc * kTile;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < kTile * (D / 8)) {
+        const int key = min(kb0 + i / (D / 8), n - 1);
+        kreg[j] = *reinterpret_cast<const uint4*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < (kTile / 4) * (D / 8)) {
+        const int kg = i % (kTile / 4), dg = i / (kTile / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(kb0 + 4 * kg + r, n - 1);
+          vreg[j][r] = *reinterpret_cast<const uint4*>(vt + (size_t)key * D + dg * 8);
+        }
+      }
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < kTile * (D / 8))
+        *reinterpret_cast<uint4*>(&sm.k[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < (kTile / 4) * (D / 8)) {
+        const int kg = i % (kTile / 4), dg = i / (kTile / 4);
+        const uint32_t w0[4] = {vreg[j][0].x, vreg[j][0].y, vreg[j][0].z, vreg[j][0].w};
+        const uint32_t w1[4] = {vreg[j][1].x, vreg[j][1].y, vreg[j][1].z, vreg[j][1].w};
+        const uint32_t w2[4] = {vreg[j][2].x, vreg[j][2].y, vreg[j][2].z, vreg[j][2].w};
+        const uint32_t w3[4] = {vreg[j][3].x, vreg[j][3].y, vreg[j][3].z, vreg[j][3].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 halves
+          uint2 col;
+          col.x = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel);
+          col.y = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel);
+          *reinterpret_cast<uint2*>(&sm.vt[(dg * 8 + e) * kVtStride + 4 * kg]) = col;
+        }
+      }
+    }
+  };
+  const bool vec4 = (n & 3) == 0;  // bias/key-mask rows 16-byte aligned
+
+  if (blk_begin < blk_end) load_block(blk_begin);
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     int bc = blk;
     if constexpr (!kDense) bc = clampi(col_idx[blk], 0, ntiles - 1);
     const int k0 = bc * kTile;
 
     __syncthreads();  // previous block's LDS reads are done
-    // ---- stage K (row-major) and V^T
-    for (int i = threadIdx.x; i < kTile * (D / 8); i += kThreads) {
-      const int r = i / (D / 8), cc = i % (D / 8);
-      const int key = min(k0 + r, n - 1);
-      *reinterpret_cast<uint4*>(&sm.k[r * KS + cc * 8]) =
-          *reinterpret_cast<const uint4*>(kt + (size_t)key * D + cc * 8);
-    }
-    for (int i = threadIdx.x; i < (kTile / 4) * (D / 8); i += kThreads) {
-      const int kg = i / (D / 8), dg = i % (D / 8);   // keys 4kg..4kg+3, dims 8dg..8dg+7
-      uint4 r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = min(k0 + 4 * kg + j, n - 1);
-        r[j] = *reinterpret_cast<const uint4*>(vt + (size_t)key * D + dg * 8);
-      }
-      const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-      const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
-      const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
-      const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 halves
-        uint2 col;
-        col.x = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel);
-        col.y = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel);
-        *reinterpret_cast<uint2*>(&sm.vt[(dg * 8 + e) * kVtStride + 4 * kg]) = col;
-      }
-    }
+    store_block();
     __syncthreads();
+    if (blk + 1 < blk_end) load_block(blk + 1);  // in flight while this block computes
+
+    // additive terms for this lane's 16 keys (issued before the matrix products)
+    float add[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int kk = k0 + 16 * tt + 4 * g;
+      if (vec4 && kk + 3 < n) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (brow) a = *reinterpret_cast<const float4*>(brow + kk);
+        if (kmr) {
+          const float4 m4 = *reinterpret_cast<const float4*>(kmr + kk);
+          a.x += m4.x; a.y += m4.y; a.z += m4.z; a.w += m4.w;
+        }
+        add[tt][0] = a.x; add[tt][1] = a.y; add[tt][2] = a.z; add[tt][3] = a.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = 0.f;
+          if (kk + i < n) {
+            if (brow) a += brow[kk + i];
+            if (kmr) a += kmr[kk + i];
+          } else {
+            a = -INFINITY;
+          }
+          add[tt][i] = a;
+        }
+      }
+    }
 
     // ---- S^T tiles: lane holds keys 16t + 4g + i for query c16
     float s[4][4];
@@ -152,27 +215,21 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[tt][i] = acc[i] * scale2;
     }
-    // ---- additive terms and masking of keys past n
+    // ---- additive terms (keys past n carry -inf)
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int kk = k0 + 16 * tt + 4 * g;  // first of this lane's 4 keys
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x = s[tt][i];
-        if (kk + i < n) {
-          if (brow) x = fmaf(brow[kk + i], kLog2e, x);
-          if (kmr) x = fmaf(kmr[kk + i], kLog2e, x);
-        } else {
-          x = -INFINITY;
-        }
+        const float x = fmaf(add[tt][i], kLog2e, s[tt][i]);
         s[tt][i] = x;
         mx = fmaxf(mx, x);
       }
-    }
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float mn = fmaxf(m2, mx);
+    // The running max moves only when the block max exceeds it by more than kSlack (log2
+    // units): p stays <= 2^kSlack, and the O rescale below is skipped for most blocks.
+    const float mn = (mx > m2 + kSlack) ? mx : m2;
     float alpha = 1.f;
     uint32_t pk[2][4];  // bf16 P: [k-block][dword]
     if (mn == -INFINITY) {
@@ -201,14 +258,16 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
       }
       m2 = mn;
     }
-    // ---- rescale O rows (queries 4g+i live in lane 4g+i's softmax state)
-    float al[4];
+    // ---- rescale O rows when some query's max moved (queries 4g+i live in lane 4g+i)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = bperm(alpha, 4 * g + i);
+      for (int i = 0; i < 4; ++i) al[i] = bperm(alpha, 4 * g + i);
 #pragma unroll
-    for (int c = 0; c < OC; ++c)
+      for (int c = 0; c < OC; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+        for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+    }
     // ---- O += P V
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {

@@ -19,7 +19,7 @@ hipError_t launch_fused_mfma(const sa_problem& p, const void* q, const void* k, 
 bool fused_mfma_supported(const sa_problem& p);
 
 // CSR row plan and validation.
-size_t plan_bytes(int n, long long nnz);
+size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);
 hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_t s);
 hipError_t launch_validate(const sa_problem& p, int* flag_dev, hipStream_t s);
 

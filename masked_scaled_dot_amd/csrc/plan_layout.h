@@ -1,10 +1,51 @@
-// Layout constants of the CSR row plan (see plan.hip).
+// Layout of the CSR row plan (see plan.hip). All offsets are in 32-bit words from the
+// start of the plan buffer.
 #pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace sa {
 
-constexpr int kPlanMagic = 0x53415031;  // "SAP1"
-constexpr int kPlanHeaderWords = 8;     // magic, n, nnz lo, nnz hi, seg, items, 0, 0
-constexpr int kPlanSeg = 512;           // maximum entries per segment
+constexpr int kPlanMagic = 0x53415032;  // "SAP2"
+constexpr int kPlanHeaderWords = 16;
+constexpr int kTileRows = 64;           // rows per tile (and keys per key block)
+constexpr int kLongRow = 1024;          // rows with more entries are split into segments
+constexpr int kSeg = 256;               // entries per long-row segment
+constexpr float kDenseTile = 0.25f;     // tiles at least this dense run on matrix cores
+
+// header words
+enum PlanHeader {
+  kHMagic = 0, kHN, kHNnzLo, kHNnzHi, kHTiles, kHLongRows, kHSegs, kHValid,
+  kHBH, kHD, kHOffRows, kHOffTiles, kHOffSegs, kHOffCounters, kHOffScratch, kHWords
+};
+
+// Word counts of the parts, in layout order: header, rows (2 per row: first and one past
+// the last entry of the row's core range), tiles (4 per tile: first key block, one past
+// the last key block, 1 if dense enough for matrix cores, core entries), long-row
+// segments (8 per segment: row, begin, end, long-row index, segment index within the row,
+// segments of the row, 0, 0), merge counters (one per long row and head), scratch floats
+// (kSlot(d) per segment and head: partial row and, for the fused forward, max and sum),
+// starting on a 16-byte boundary.
+__host__ __device__ constexpr long long slot_floats(long long d) { return d + 4; }
+
+struct PlanSizes {
+  long long rows, tiles, segs, counters, pad, scratch, total;
+};
+
+__host__ __device__ inline PlanSizes plan_sizes(long long n, long long long_rows, long long segs, long long BH,
+                            long long d) {
+  PlanSizes s;
+  const long long tiles = (n + kTileRows - 1) / kTileRows;
+  s.rows = 2 * n;
+  s.tiles = 4 * tiles;
+  s.segs = 8 * segs;
+  s.counters = long_rows * BH;
+  const long long before = kPlanHeaderWords + s.rows + s.tiles + s.segs + s.counters;
+  s.pad = (4 - before % 4) % 4;
+  s.scratch = segs * BH * slot_floats(d);
+  s.total = before + s.pad + s.scratch;
+  return s;
+}
 
 }  // namespace sa

@@ -5,28 +5,41 @@
 // key j, computed only at the mask's nonzeros; the scores keep the mask's CSR order.
 // Here: scores[t*nnz + e] = scale * q_i . k_j (+ bias[h,i,j]) (+ key_mask[b,hm,j]).
 //
-// Work decomposition: one wave64 per (head, row). The row's query vector is loaded once
-// into registers (all lanes hold it; its address is wave-uniform); lane L handles entries
-// e = row_start + L + 64*m, gathers the key row k_j with 16-byte loads and reduces it
-// against q in-lane (v_dot2_f32_bf16 for bf16, fma for fp32), so no cross-lane traffic is
-// needed and the score stores of a wave are one contiguous 256-byte segment.
+// With a row plan (plan.hip), a workgroup owns one 64-row tile of one head:
+//  * if the tile's core entries fill at least a quarter of their 64x64 key blocks and the
+//    inputs are bf16, each key block of the span is staged in LDS and every wave forms the
+//    16x64 score block of its rows with v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, Q held in
+//    registers); the CSR then selects the stored entries: the entries of a row that fall
+//    in one 64-key block are at most 64 consecutive entries, so one lane-parallel pass per
+//    row and block reads them from LDS and writes them contiguously;
+//  * the row's entries outside its core range (e.g. global-token columns), and every row
+//    of a sparse tile, take the vector path: one entry per lane, the key row gathered with
+//    16-byte loads and reduced in-lane with v_dot2_f32_bf16 (fma for fp32);
+//  * rows longer than the plan's long-row threshold are skipped by the tiles and handled as
+//    segments by the first workgroups of the grid, spread over many waves.
+// Without a plan, one wave per (head, row) runs the vector path over the whole row.
 #include "common.h"
 #include "kernels.h"
+#include "plan_layout.h"
 
 namespace sa {
 namespace {
 
-constexpr int kRowsPerBlock = 4;  // 4 waves of 64 = 256 threads
+constexpr int kThreads = 256;
+constexpr int kLongWGs = 256;  // workgroups that walk the long-row segments
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
 template <typename T, int D>
 struct RowVec {
   static constexpr int kWords = D * (int)sizeof(T) / 4;  // 32-bit words per row
-  static constexpr int kVec = kWords / 4;                // 16-byte loads per row
+  static constexpr int kVec = kWords / 4;                // 16-byte chunks per row
 };
 
-template <typename T, int D>
-__device__ __forceinline__ float row_dot(const uint32_t (&qw)[RowVec<T, D>::kWords],
-                                         const uint4* __restrict__ krow) {
+// q . k over one row; q as 32-bit words (packed bf16 pairs or fp32), k from memory.
+template <typename T, int D, typename QW>
+__device__ __forceinline__ float row_dot(const QW& qw, const uint4* krow) {
   constexpr int V = RowVec<T, D>::kVec;
   uint4 kv[V];
 #pragma unroll
@@ -49,63 +62,290 @@ __device__ __forceinline__ float row_dot(const uint32_t (&qw)[RowVec<T, D>::kWor
   return acc0 + acc1;
 }
 
+struct Args {
+  const void* q;
+  const void* k;
+  const int* row_ptr;
+  const int* col_idx;
+  float* scores;
+  const float* bias;
+  const float* key_mask;
+  const int* plan;
+  int B, H, n;
+  long long nnz;
+  int km_heads;
+  float scale;
+};
+
+__device__ __forceinline__ void row_bounds(const Args& a, int row, long long& rs, long long& re) {
+  rs = a.row_ptr[row];
+  re = a.row_ptr[row + 1];
+  rs = rs < 0 ? 0 : (rs > a.nnz ? a.nnz : rs);
+  re = re < rs ? rs : (re > a.nnz ? a.nnz : re);
+}
+
+__device__ __forceinline__ float additive(const Args& a, int h, int b, int row, int col) {
+  float x = 0.f;
+  if (a.bias) x += a.bias[((size_t)h * a.n + row) * a.n + col];
+  if (a.key_mask) x += a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * a.n + col];
+  return x;
+}
+
+// Vector path over entries [e_begin, e_end) of one row, q wave-uniform (scalar registers).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void sddmm_row_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const int* __restrict__ row_ptr,
-    const int* __restrict__ col_idx, float* __restrict__ scores, const float* __restrict__ bias,
-    const float* __restrict__ key_mask, int H, int n, long long nnz, int km_heads, int BH,
-    float scale) {
+__device__ void valu_row(const Args& a, int t, int row, long long e_begin, long long e_end) {
+  if (e_begin >= e_end) return;
   constexpr int W = RowVec<T, D>::kWords;
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const long long unit = (long long)lb * kRowsPerBlock + wave;  // t * n + row
-  if (unit >= (long long)BH * n) return;
-  const int t = (int)(unit / n), row = (int)(unit % n);
-  const int b = t / H, h = t % H;
-
-  long long rs = row_ptr[row], re = row_ptr[row + 1];
-  rs = rs < 0 ? 0 : (rs > nnz ? nnz : rs);
-  re = re < rs ? rs : (re > nnz ? nnz : re);
-  if (rs == re) return;
-
+  const int b = t / a.H, h = t % a.H;
+  const T* qt = static_cast<const T*>(a.q);
+  const T* kt = static_cast<const T*>(a.k) + (size_t)t * a.n * D;
   uint32_t qw[W];
-  const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)t * n + row) * D);
+  const uint4* qrow = reinterpret_cast<const uint4*>(qt + ((size_t)t * a.n + row) * D);
 #pragma unroll
   for (int c = 0; c < W / 4; ++c) {
     const uint4 v = qrow[c];
     qw[4 * c] = v.x; qw[4 * c + 1] = v.y; qw[4 * c + 2] = v.z; qw[4 * c + 3] = v.w;
   }
-  const T* kt = k + (size_t)t * n * D;
-  float* st = scores + (size_t)t * nnz;
-  const float* brow = bias ? bias + ((size_t)h * n + row) * n : nullptr;
-  const float* km = key_mask ? key_mask + ((size_t)b * km_heads + (km_heads > 1 ? h : 0)) * n : nullptr;
-
-  for (long long e0 = rs; e0 < re; e0 += 2 * kWave) {
+  float* st = a.scores + (size_t)t * a.nnz;
+  for (long long e0 = e_begin; e0 < e_end; e0 += 2 * kWave) {
     const long long ea = e0 + lane, eb = e0 + kWave + lane;
-    const bool oka = ea < re, okb = eb < re;
-    const int ja = clampi(col_idx[oka ? ea : rs], 0, n - 1);
-    const int jb = clampi(col_idx[okb ? eb : rs], 0, n - 1);
+    const bool oka = ea < e_end, okb = eb < e_end;
+    const int ja = clampi(a.col_idx[oka ? ea : e_begin], 0, a.n - 1);
+    const int jb = clampi(a.col_idx[okb ? eb : e_begin], 0, a.n - 1);
     float sa_ = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)ja * D));
     float sb_ = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)jb * D));
-    sa_ *= scale;
-    sb_ *= scale;
-    if (brow) { sa_ += brow[ja]; sb_ += brow[jb]; }
-    if (km) { sa_ += km[ja]; sb_ += km[jb]; }
+    sa_ = sa_ * a.scale + additive(a, h, b, row, ja);
+    sb_ = sb_ * a.scale + additive(a, h, b, row, jb);
     if (oka) st[ea] = sa_;
     if (okb) st[eb] = sb_;
   }
 }
 
+// Vector path over a list of entries of different rows (a tile's far entries): each lane
+// gathers its own q row and key row. far_pre[r] = far entries of the tile's rows before
+// row r (r in 0..64, inclusive prefix at r+1); row r's far entries are [rs, lo) and [hi, re).
+template <typename T, int D>
+__device__ void valu_far(const Args& a, int t, int row0, const int* far_pre, const int* far_lo,
+                         const int* far_hi) {
+  const int total = far_pre[kTileRows];
+  const int b = t / a.H, h = t % a.H;
+  const T* qt = static_cast<const T*>(a.q) + (size_t)t * a.n * D;
+  const T* kt = static_cast<const T*>(a.k) + (size_t)t * a.n * D;
+  float* st = a.scores + (size_t)t * a.nnz;
+  constexpr int W = RowVec<T, D>::kWords;
+  for (int f = threadIdx.x; f < total; f += kThreads) {
+    int lo = 0, hi = kTileRows;  // find r with far_pre[r] <= f < far_pre[r+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (far_pre[mid] <= f) lo = mid;
+      else hi = mid;
+    }
+    const int r = lo, row = row0 + r;
+    long long rs, re;
+    row_bounds(a, row, rs, re);
+    const int k_in = f - far_pre[r];
+    const int nleft = far_lo[r] - (int)rs;
+    const long long e = k_in < nleft ? rs + k_in : (long long)far_hi[r] + (k_in - nleft);
+    const int j = clampi(a.col_idx[e], 0, a.n - 1);
+    uint32_t qw[W];
+    const uint4* qrow = reinterpret_cast<const uint4*>(qt + (size_t)row * D);
+#pragma unroll
+    for (int c = 0; c < W / 4; ++c) {
+      const uint4 v = qrow[c];
+      qw[4 * c] = v.x; qw[4 * c + 1] = v.y; qw[4 * c + 2] = v.z; qw[4 * c + 3] = v.w;
+    }
+    const float s = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)j * D));
+    st[e] = s * a.scale + additive(a, h, b, row, j);
+  }
+}
+
+// ---------------------------------------------------------------------------------- kernels
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void sddmm_rows_kernel(Args a, int BH) {
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const long long unit = (long long)lb * (kThreads / kWave) + wave;  // t * n + row
+  if (unit >= (long long)BH * a.n) return;
+  const int t = (int)(unit / a.n), row = (int)(unit % a.n);
+  long long rs, re;
+  row_bounds(a, row, rs, re);
+  valu_row<T, D>(a, t, row, rs, re);
+}
+
+template <int D>
+struct TileSmem {
+  static constexpr int kKStride = D + 8;       // bf16 per K row (+16 B: conflict-free A reads)
+  static constexpr int kSStride = kTileRows + 1;  // fp32 per score row
+  alignas(16) uint16_t k[kTileRows * kKStride];
+  float s[kTileRows * kSStride];
+  int far_pre[kTileRows + 1];
+  int far_lo[kTileRows];
+  int far_hi[kTileRows];
+  int core_lo[kTileRows];
+  int core_hi[kTileRows];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
+  __shared__ TileSmem<D> sm;
+  const int* plan = a.plan;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+
+  const bool segs_ok = plan[kHValid] != 0;  // long-row segments were written
+  // ---- long-row segments
+  if ((int)blockIdx.x < kLongWGs) {
+    if (!segs_ok) return;
+    const int S = plan[kHSegs];
+    const int* segs = plan + plan[kHOffSegs];
+    const long long tasks = (long long)S * BH;
+    for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
+         task += (long long)kLongWGs * (kThreads / kWave)) {
+      const int sg = (int)(task % S), t = (int)(task / S);
+      const int* it = segs + 8 * sg;
+      valu_row<T, D>(a, t, it[0], it[1], it[2]);
+    }
+    return;
+  }
+
+  // ---- tiles
+  const int ntiles = plan[kHTiles];
+  const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
+  const int t = lb / ntiles, tile = lb % ntiles;
+  const int row0 = tile * kTileRows;
+  const int* tinfo = plan + plan[kHOffTiles] + 4 * tile;
+  const int* rows = plan + plan[kHOffRows];
+  const int kb_lo = tinfo[0], kb_hi = tinfo[1];
+  const bool dense = (sizeof(T) == 2) && tinfo[2] != 0;
+
+  if (!dense) {
+    for (int r = wave; r < kTileRows; r += kThreads / kWave) {
+      const int row = row0 + r;
+      if (row >= a.n) break;
+      long long rs, re;
+      row_bounds(a, row, rs, re);
+      if (segs_ok && re - rs > kLongRow) continue;  // a long-row segment task covers it
+      valu_row<T, D>(a, t, row, rs, re);
+    }
+    return;
+  }
+
+  if constexpr (sizeof(T) == 2) {
+    constexpr int KS = TileSmem<D>::kKStride, SS = TileSmem<D>::kSStride;
+    constexpr int KC = D / 32;
+    // per-row core ranges and far-entry prefix (long rows contribute nothing here)
+    if (threadIdx.x < kTileRows) {
+      const int r = threadIdx.x, row = row0 + r;
+      int lo = 0, hi = 0, nfar = 0;
+      if (row < a.n) {
+        long long rs, re;
+        row_bounds(a, row, rs, re);
+        if (re - rs <= kLongRow) {
+          lo = clampi(rows[2 * row], (int)rs, (int)re);
+          hi = clampi(rows[2 * row + 1], lo, (int)re);
+          nfar = (lo - (int)rs) + ((int)re - hi);
+        } else {
+          lo = hi = (int)rs;               // no core range: a long row
+          nfar = segs_ok ? 0 : (int)(re - rs);
+        }
+      }
+      sm.core_lo[r] = lo;
+      sm.core_hi[r] = hi;
+      sm.far_lo[r] = lo;
+      sm.far_hi[r] = hi;
+      sm.far_pre[r + 1] = nfar;
+    }
+    if (threadIdx.x == 0) sm.far_pre[0] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int r = 0; r < kTileRows; ++r) sm.far_pre[r + 1] += sm.far_pre[r];
+    }
+    __syncthreads();
+    valu_far<T, D>(a, t, row0, sm.far_pre, sm.far_lo, sm.far_hi);
+
+    // the wave's 16 queries as the B operand of S^T (lane: query c16, dims 32kc + 8g..)
+    const int g = lane / 16, c16 = lane % 16;
+    const int my_q = min(row0 + wave * 16 + c16, a.n - 1);
+    const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * a.n * D;
+    const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * a.n * D;
+    bf16x8_v qb[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+    const int b = t / a.H, h = t % a.H;
+    float* st = a.scores + (size_t)t * a.nnz;
+    // cursor of the wave's row r (lane r < 16 keeps it)
+    int cur = sm.core_lo[wave * 16 + (lane & 15)];
+
+    for (int kb = kb_lo; kb < kb_hi; ++kb) {
+      const int k0 = kb * kTileRows;
+      // columns of the next (at most 64) core entries of each of the wave's 16 rows; the
+      // loads are in flight while K is staged and the block is multiplied
+      int colv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int start = __builtin_amdgcn_readlane(cur, r);
+        const int e = start + lane;
+        colv[r] = e < sm.core_hi[wave * 16 + r] ? a.col_idx[e] : 0x7fffffff;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < kTileRows * (D / 8); i += kThreads) {
+        const int r = i / (D / 8), cc = i % (D / 8);
+        const int key = min(k0 + r, a.n - 1);
+        *reinterpret_cast<uint4*>(&sm.k[r * KS + cc * 8]) =
+            *reinterpret_cast<const uint4*>(kt + (size_t)key * D + cc * 8);
+      }
+      __syncthreads();
+      // S^T block for the wave's 16 queries; accumulator: query c16, keys 16tt + 4g + i
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8_v av = __builtin_bit_cast(
+              bf16x8_v, *reinterpret_cast<const uint4*>(&sm.k[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kc], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.s[(wave * 16 + c16) * SS + 16 * tt + 4 * g + i] = acc[i];
+      }
+      // select the stored entries of each of the wave's rows that fall in this block
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wave * 16 + r;
+        const int row = row0 + lr;
+        const int start = __builtin_amdgcn_readlane(cur, r);
+        const long long e = (long long)start + lane;
+        const int col = colv[r];
+        const bool in_blk = col < k0 + kTileRows;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(in_blk);
+        const int cnt = __builtin_popcountll(m);
+        if (in_blk && row < a.n) {
+          const int cc = clampi(col - k0, 0, kTileRows - 1);
+          st[e] = sm.s[lr * SS + cc] * a.scale + additive(a, h, b, row, clampi(col, 0, a.n - 1));
+        }
+        if (lane == r) cur = start + cnt;
+      }
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_t(const sa_problem& p, const void* q, const void* k, float* scores, hipStream_t s) {
-  const long long units = (long long)p.B * p.H * p.n;
-  const int blocks = (int)((units + kRowsPerBlock - 1) / kRowsPerBlock);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((sddmm_row_kernel<T, D>), dim3(blocks), dim3(256), 0, s,
-                     static_cast<const T*>(q), static_cast<const T*>(k), p.row_ptr, p.col_idx,
-                     scores, p.bias, p.key_mask, p.H, p.n, (long long)p.nnz, p.key_mask_heads,
-                     p.B * p.H, p.scale);
+  Args a{q, k, p.row_ptr, p.col_idx, scores, p.bias, p.key_mask, static_cast<const int*>(p.plan),
+         p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
+  const int BH = p.B * p.H;
+  if (p.plan) {
+    const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
+    const long long blocks = kLongWGs + ntiles * BH;
+    hipLaunchKernelGGL((sddmm_plan_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, BH);
+  } else {
+    const long long units = (long long)BH * p.n;
+    const int blocks = (int)((units + (kThreads / kWave) - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((sddmm_rows_kernel<T, D>), dim3(blocks), dim3(kThreads), 0, s, a, BH);
+  }
   return hipGetLastError();
 }
 

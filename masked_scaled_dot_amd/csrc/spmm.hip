@@ -4,65 +4,88 @@
 // opening post, third bullet: the context is the product of the sparse weight matrix with
 // the dense value tensor. out[t,i,:] = sum_{e in row i} w[t,e] * v[t,col_idx[e],:].
 //
-// One wave64 per (head, row). A value row of d elements is LPR 16-byte chunks; the wave is
-// split into 64/LPR slots of LPR lanes, lane r of a slot owning chunk r. Slot s walks the
-// entries e = row_start + s + slots*m: its lanes read the entry's column and weight (same
-// address across the slot) and one 16-byte chunk of the gathered value row, accumulating
-// in fp32. The slots' partial rows are then summed with cross-lane reductions and slot 0
-// writes the output row with 16-byte stores.
+// With a row plan (plan.hip), a workgroup owns one 64-row tile of one head:
+//  * a dense-enough tile (bf16) walks the 64-key blocks spanned by its rows' core entries:
+//    the V block is staged row-major in LDS, the block's weights are scattered into a
+//    zero-filled 64x64 tile held as two bf16 planes (w = hi + lo, so the product keeps
+//    about 16 mantissa bits of each weight), and each wave accumulates its 16 rows with
+//    v_mfma_f32_16x16x32_bf16 (A = the weight rows, B = V read with the transposing LDS
+//    load ds_read_b64_tr_b16, which turns row-major V into the k-major operand);
+//  * entries outside a row's core range are then added by the thread that owns the row;
+//  * sparse tiles and rows without a plan run the vector path: the wave is split into lane
+//    slots that each own one 16-byte column chunk of V and walk every slots-th entry;
+//  * rows longer than the plan's threshold are cut into segments handled by the first
+//    workgroups of the grid; each segment writes its partial row to the plan's scratch, and
+//    the last segment to finish (per-row counter, acquire/release at device scope) sums the
+//    partials in segment order, so the result does not depend on timing.
 #include "common.h"
 #include "kernels.h"
+#include "plan_layout.h"
 
 namespace sa {
 namespace {
 
-constexpr int kRowsPerBlock = 4;
+constexpr int kThreads = 256;
+constexpr int kLongWGs = 256;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(4))) short i16x4_v;
+typedef __attribute__((ext_vector_type(2))) float f32x2_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v2;
 
 template <typename T, int D>
 struct Layout {
-  static constexpr int kElemsPerChunk = 16 / (int)sizeof(T);  // 8 bf16 or 4 fp32
-  static constexpr int kLPR = D / kElemsPerChunk;             // lanes per value row
+  static constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int kLPR = D / kEPC;             // lanes per value row
   static constexpr int kSlots = kWave / kLPR;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void spmm_row_kernel(
-    const float* __restrict__ weights, const T* __restrict__ v, const int* __restrict__ row_ptr,
-    const int* __restrict__ col_idx, float* __restrict__ out, int n, long long nnz, int BH) {
-  using L = Layout<T, D>;
-  constexpr int EPC = L::kElemsPerChunk, LPR = L::kLPR, SLOTS = L::kSlots;
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const long long unit = (long long)lb * kRowsPerBlock + wave;
-  if (unit >= (long long)BH * n) return;
-  const int t = (int)(unit / n), row = (int)(unit % n);
-  const int slot = lane / LPR, r = lane % LPR;
-  long long rs = row_ptr[row], re = row_ptr[row + 1];
-  rs = rs < 0 ? 0 : (rs > nnz ? nnz : rs);
-  re = re < rs ? rs : (re > nnz ? nnz : re);
+struct Args {
+  const float* w;
+  const void* v;
+  const int* row_ptr;
+  const int* col_idx;
+  float* out;
+  const int* plan;
+  int n;
+  long long nnz;
+};
 
-  const float* wt = weights + (size_t)t * nnz;
-  const T* vt = v + (size_t)t * n * D;
-  float acc[EPC];
+__device__ __forceinline__ void row_bounds(const Args& a, int row, long long& rs, long long& re) {
+  rs = a.row_ptr[row];
+  re = a.row_ptr[row + 1];
+  rs = rs < 0 ? 0 : (rs > a.nnz ? a.nnz : rs);
+  re = re < rs ? rs : (re > a.nnz ? a.nnz : re);
+}
+
+// Vector path: partial row over entries [e_begin, e_end) in the slot layout; after the
+// cross-slot sum every slot holds the full chunk (lane r of each slot: elements r*EPC..).
+template <typename T, int D>
+__device__ __forceinline__ void valu_segment(const Args& a, int t, long long e_begin, long long e_end,
+                                             float (&acc)[Layout<T, D>::kEPC]) {
+  using L = Layout<T, D>;
+  constexpr int EPC = L::kEPC, LPR = L::kLPR, SLOTS = L::kSlots;
+  const int lane = threadIdx.x % kWave;
+  const int slot = lane / LPR, r = lane % LPR;
+  const float* wt = a.w + (size_t)t * a.nnz;
+  const T* vt = static_cast<const T*>(a.v) + (size_t)t * a.n * D;
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
-
-  constexpr int U = 2;  // entries per slot in flight
-  for (long long e0 = rs + slot; e0 < re; e0 += (long long)U * SLOTS) {
+  constexpr int U = 4;  // entries per slot in flight
+  for (long long e0 = e_begin + slot; e0 < e_end; e0 += (long long)U * SLOTS) {
     int j[U];
     float w[U];
     uint4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long long e = e0 + (long long)u * SLOTS;
-      const bool ok = e < re;
-      j[u] = clampi(col_idx[ok ? e : rs], 0, n - 1);
+      const bool ok = e < e_end;
+      j[u] = clampi(a.col_idx[ok ? e : e_begin], 0, a.n - 1);
       w[u] = ok ? wt[e] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      x[u] = reinterpret_cast<const uint4*>(vt + (size_t)j[u] * D)[r];
+    for (int u = 0; u < U; ++u) x[u] = reinterpret_cast<const uint4*>(vt + (size_t)j[u] * D)[r];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
@@ -78,14 +101,20 @@ __global__ __launch_bounds__(256) void spmm_row_kernel(
       }
     }
   }
-  // Sum the slots: lanes r, r+LPR, r+2*LPR, ... hold partials of the same chunk.
 #pragma unroll
   for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
     for (int c = 0; c < EPC; ++c) acc[c] += shfl_xor(acc[c], m);
   }
-  if (slot == 0) {
-    float4* o = reinterpret_cast<float4*>(out + ((size_t)t * n + row) * D) + r * (EPC / 4);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_chunk(float* orow, const float (&acc)[Layout<T, D>::kEPC]) {
+  using L = Layout<T, D>;
+  constexpr int EPC = L::kEPC, LPR = L::kLPR;
+  const int lane = threadIdx.x % kWave;
+  if (lane < LPR) {
+    float4* o = reinterpret_cast<float4*>(orow) + lane * (EPC / 4);
 #pragma unroll
     for (int c = 0; c < EPC / 4; ++c)
       o[c] = make_float4(acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]);
@@ -93,13 +122,271 @@ __global__ __launch_bounds__(256) void spmm_row_kernel(
 }
 
 template <typename T, int D>
+__device__ void valu_row(const Args& a, int t, int row) {
+  long long rs, re;
+  row_bounds(a, row, rs, re);
+  float acc[Layout<T, D>::kEPC];
+  valu_segment<T, D>(a, t, rs, re, acc);
+  store_chunk<T, D>(a.out + ((size_t)t * a.n + row) * D, acc);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void spmm_rows_kernel(Args a, int BH) {
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const long long unit = (long long)lb * (kThreads / kWave) + wave;
+  if (unit >= (long long)BH * a.n) return;
+  valu_row<T, D>(a, (int)(unit / a.n), (int)(unit % a.n));
+}
+
+template <int D>
+struct TileSmem {
+  static constexpr int kVStride = D + 16;   // bf16 per V row: stride = 32 B mod 256 B
+  static constexpr int kWStride = kTileRows + 8;  // bf16 per weight row (+16 B)
+  static constexpr int kOStride = D + 1;    // fp32 per output row
+  alignas(16) uint16_t v[kTileRows * kVStride];
+  alignas(16) uint16_t whi[kTileRows * kWStride];
+  alignas(16) uint16_t wlo[kTileRows * kWStride];
+  float o[kTileRows * kOStride];
+  int core_lo[kTileRows];
+  int core_hi[kTileRows];
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v2));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
+  __shared__ TileSmem<D> sm;
+  const int* plan = a.plan;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  // long rows are split only if the plan holds their segments and scratch for this shape
+  const bool split = plan[kHValid] != 0 && BH <= plan[kHBH] && D <= plan[kHD];
+
+  // ---- long-row segments: partial rows, merged by the last segment of each row
+  if ((int)blockIdx.x < kLongWGs) {
+    if (!split) return;
+    const int S = plan[kHSegs];
+    const int* segs = plan + plan[kHOffSegs];
+    int* counters = const_cast<int*>(plan) + plan[kHOffCounters];
+    float* scratch = reinterpret_cast<float*>(const_cast<int*>(plan) + plan[kHOffScratch]);
+    const int pBH = plan[kHBH], pD = plan[kHD];
+    const long long tasks = (long long)S * BH;
+    using L = Layout<T, D>;
+    for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
+         task += (long long)kLongWGs * (kThreads / kWave)) {
+      const int sg = (int)(task % S), t = (int)(task / S);
+      const int* it = segs + 8 * sg;
+      const int row = it[0], lr = it[3], sidx = it[4], ns = it[5];
+      float acc[L::kEPC];
+      valu_segment<T, D>(a, t, it[1], it[2], acc);
+      float* slot = scratch + ((size_t)sg * pBH + t) * slot_floats(pD);
+      store_chunk<T, D>(slot, acc);
+      // publish the partial; the last arriving segment of the row merges all of them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      int prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(&counters[(size_t)lr * pBH + t], 1, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev == ns - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int first = sg - sidx;
+        float* orow = a.out + ((size_t)t * a.n + row) * D;
+        for (int c = lane; c < D; c += kWave) {
+          float s = 0.f;
+          for (int q = 0; q < ns; ++q)
+            s += __builtin_nontemporal_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c);
+          orow[c] = s;
+        }
+        if (lane == 0) counters[(size_t)lr * pBH + t] = 0;  // ready for the next call
+      }
+    }
+    return;
+  }
+
+  // ---- tiles
+  const int ntiles = plan[kHTiles];
+  const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
+  const int t = lb / ntiles, tile = lb % ntiles;
+  const int row0 = tile * kTileRows;
+  const int* tinfo = plan + plan[kHOffTiles] + 4 * tile;
+  const int* rows = plan + plan[kHOffRows];
+  const int kb_lo = tinfo[0], kb_hi = tinfo[1];
+  const bool dense = (sizeof(T) == 2) && tinfo[2] != 0;
+
+  if (!dense) {
+    for (int r = wave; r < kTileRows; r += kThreads / kWave) {
+      const int row = row0 + r;
+      if (row >= a.n) break;
+      long long rs, re;
+      row_bounds(a, row, rs, re);
+      if (split && re - rs > kLongRow) continue;
+      valu_row<T, D>(a, t, row);
+    }
+    return;
+  }
+
+  if constexpr (sizeof(T) == 2) {
+    constexpr int VS = TileSmem<D>::kVStride, WS = TileSmem<D>::kWStride, OS = TileSmem<D>::kOStride;
+    constexpr int OC = D / 16;
+    if (threadIdx.x < kTileRows) {
+      const int r = threadIdx.x, row = row0 + r;
+      int lo = 0, hi = 0;
+      if (row < a.n) {
+        long long rs, re;
+        row_bounds(a, row, rs, re);
+        if (re - rs <= kLongRow) {
+          lo = clampi(rows[2 * row], (int)rs, (int)re);
+          hi = clampi(rows[2 * row + 1], lo, (int)re);
+        } else {
+          lo = hi = (int)rs;
+        }
+      }
+      sm.core_lo[r] = lo;
+      sm.core_hi[r] = hi;
+    }
+    __syncthreads();
+    const int g = lane / 16, c16 = lane % 16;
+    const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
+    const float* wt = a.w + (size_t)t * a.nnz;
+    f32x4_v o[OC];
+#pragma unroll
+    for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    int cur = sm.core_lo[wave * 16 + (lane & 15)];
+
+    for (int kb = kb_lo; kb < kb_hi; ++kb) {
+      const int k0 = kb * kTileRows;
+      // this block's core entries of the wave's rows: columns and weights (in flight early)
+      int colv[16];
+      float wv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = __builtin_amdgcn_readlane(cur, r) + lane;
+        const bool ok = e < sm.core_hi[wave * 16 + r];
+        colv[r] = ok ? a.col_idx[e] : 0x7fffffff;
+        wv[r] = ok ? wt[e] : 0.f;
+      }
+      __syncthreads();  // previous block's LDS reads are done
+      for (int i = threadIdx.x; i < kTileRows * (D / 8); i += kThreads) {
+        const int r = i / (D / 8), cc = i % (D / 8);
+        const int key = min(k0 + r, a.n - 1);
+        *reinterpret_cast<uint4*>(&sm.v[r * VS + cc * 8]) =
+            *reinterpret_cast<const uint4*>(vt + (size_t)key * D + cc * 8);
+      }
+      for (int i = threadIdx.x; i < kTileRows * (kTileRows / 8); i += kThreads) {
+        const int r = i / (kTileRows / 8), cc = i % (kTileRows / 8);
+        *reinterpret_cast<uint4*>(&sm.whi[r * WS + cc * 8]) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sm.wlo[r * WS + cc * 8]) = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+      // scatter the wave's rows' weights of this block (hi + lo bf16)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = colv[r];
+        const bool in_blk = col < k0 + kTileRows;
+        const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in_blk));
+        if (in_blk) {
+          const int cc = clampi(col - k0, 0, kTileRows - 1);
+          const float w = wv[r];
+          const uint32_t hi = pack_bf16(w, 0.f) & 0xffffu;
+          const float whi = __uint_as_float(hi << 16);
+          const uint32_t lo = pack_bf16(w - whi, 0.f) & 0xffffu;
+          sm.whi[(wave * 16 + r) * WS + cc] = (uint16_t)hi;
+          sm.wlo[(wave * 16 + r) * WS + cc] = (uint16_t)lo;
+        }
+        if (lane == r) cur = __builtin_amdgcn_readlane(cur, r) + cnt;
+      }
+      __syncthreads();
+      // O(16 rows x D) += W(16 x 64 keys) V(64 keys x D)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int wrow = (wave * 16 + c16) * WS + 32 * kk + 8 * g;
+        const bf16x8_v ahi = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&sm.whi[wrow]));
+        const bf16x8_v alo = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&sm.wlo[wrow]));
+        // lane j of each 16-lane group addresses V[key 32kk + 8g + j/4 (+4)][16c + 4(j%4)];
+        // the transposing read hands lane j the 4 keys of column 16c + j
+        const int vkey = 32 * kk + 8 * g + c16 / 4;
+#pragma unroll
+        for (int c = 0; c < OC; ++c) {
+          const int vcol = 16 * c + 4 * (c16 % 4);
+          typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+          const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4*)(&sm.v[vkey * VS + vcol]));
+          const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4*)(&sm.v[(vkey + 4) * VS + vcol]));
+          const bf16x8_v bv = __builtin_bit_cast(
+              bf16x8_v, (__attribute__((ext_vector_type(8))) short){b0[0], b0[1], b0[2], b0[3],
+                                                                    b1[0], b1[1], b1[2], b1[3]});
+          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, o[c], 0, 0, 0);
+          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, o[c], 0, 0, 0);
+        }
+      }
+    }
+    // accumulator layout: lane: column 16c + c16, rows 4g + i of the wave's 16
+#pragma unroll
+    for (int c = 0; c < OC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.o[(wave * 16 + 4 * g + i) * OS + 16 * c + c16] = o[c][i];
+    __syncthreads();
+    // entries outside the core range: each row is owned by one thread
+    if (threadIdx.x < kTileRows) {
+      const int r = threadIdx.x, row = row0 + r;
+      if (row < a.n) {
+        long long rs, re;
+        row_bounds(a, row, rs, re);
+        if (re - rs <= kLongRow || !split) {
+          const int lo = (re - rs <= kLongRow) ? sm.core_lo[r] : (int)re;
+          const int hi = (re - rs <= kLongRow) ? sm.core_hi[r] : (int)re;
+          for (long long e = rs; e < re; ++e) {
+            if (e == lo) e = hi;
+            if (e >= re) break;
+            const int j = clampi(a.col_idx[e], 0, a.n - 1);
+            const float w = wt[e];
+            const uint4* vrow = reinterpret_cast<const uint4*>(vt + (size_t)j * D);
+#pragma unroll
+            for (int c = 0; c < D / 8; ++c) {
+              const uint4 x = vrow[c];
+              const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                sm.o[r * OS + 8 * c + 2 * q] = fmaf(w, bf16lo(xw[q]), sm.o[r * OS + 8 * c + 2 * q]);
+                sm.o[r * OS + 8 * c + 2 * q + 1] = fmaf(w, bf16hi(xw[q]), sm.o[r * OS + 8 * c + 2 * q + 1]);
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // write the tile; long rows (split) are written by their segments
+    for (int i = threadIdx.x; i < kTileRows * D; i += kThreads) {
+      const int r = i / D, c = i % D, row = row0 + r;
+      if (row >= a.n) continue;
+      long long rs, re;
+      row_bounds(a, row, rs, re);
+      if (split && re - rs > kLongRow) continue;
+      a.out[((size_t)t * a.n + row) * D + c] = sm.o[r * OS + c];
+    }
+  }
+}
+
+template <typename T, int D>
 hipError_t launch_t(const sa_problem& p, const float* w, const void* v, float* out, hipStream_t s) {
-  const long long units = (long long)p.B * p.H * p.n;
-  const int blocks = (int)((units + kRowsPerBlock - 1) / kRowsPerBlock);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((spmm_row_kernel<T, D>), dim3(blocks), dim3(256), 0, s, w,
-                     static_cast<const T*>(v), p.row_ptr, p.col_idx, out, p.n, (long long)p.nnz,
-                     p.B * p.H);
+  Args a{w, v, p.row_ptr, p.col_idx, out, static_cast<const int*>(p.plan), p.n, (long long)p.nnz};
+  const int BH = p.B * p.H;
+  if (p.plan) {
+    const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL((spmm_plan_kernel<T, D>), dim3((unsigned)(kLongWGs + ntiles * BH)),
+                       dim3(kThreads), 0, s, a, BH);
+  } else {
+    const long long units = (long long)BH * p.n;
+    const int blocks = (int)((units + (kThreads / kWave) - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((spmm_rows_kernel<T, D>), dim3(blocks), dim3(kThreads), 0, s, a, BH);
+  }
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def qkv_tensor(p, which):
 class DevProblem:
     """Device copies of a gen.Problem plus the sa.Problem descriptor pointing at them."""
 
-    def __init__(self, p, scale=None, flags=0, with_bias=True, with_mask=True):
+    def __init__(self, p, scale=None, flags=0, with_bias=True, with_mask=True, plan=False):
         self.p = p
         self.q, self.k, self.v = (qkv_tensor(p, w) for w in ("q", "k", "v"))
         self.row_ptr = None if p.row_ptr is None else torch.from_numpy(p.row_ptr).to(DEV)
@@ -39,6 +39,17 @@ class DevProblem:
                                self.row_ptr, self.col_idx, p.nnz, block=p.block, scale=self.scale,
                                bias=self.bias, key_mask=self.key_mask,
                                key_mask_heads=p.key_mask_heads, flags=flags)
+        self.plan = None
+        if plan:
+            self.build_plan()
+
+    def build_plan(self):
+        nbytes = sa.sa_plan_bytes(self.prob)
+        assert nbytes > 0
+        self.plan = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=DEV)
+        sa.sa_plan_build(self.prob, self.plan)
+        self.prob.set_plan(self.plan)
+        return self.plan
 
     def pipeline(self):
         p = self.p

@@ -139,11 +139,13 @@ def test_empty_problems_do_nothing(name, nargs):
 
 def test_plan_bytes_and_build_checks():
     p = _prob(n=4096, nnz=1052026)
-    nb = _lib.raw("sa_plan_bytes")(ctypes.byref(p))
-    assert nb == 4 * (8 + 4 * (4096 + 1052026 // 512 + 1))
+    # bad descriptors size to 0; a valid one needs the device (it reads row_ptr)
     assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(row_ptr=None))) == 0
-    assert _lib.raw("sa_plan_build")(ctypes.byref(p), None, nb, None) == sa.SA_ERR_NULL
-    assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE, nb - 1, None) == sa.SA_ERR_WORKSPACE
+    assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(block=64, nnz=4))) == 0
+    assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(n=0, nnz=0))) == 4 * 16
+    assert _lib.raw("sa_plan_build")(ctypes.byref(p), None, 1 << 20, None) == sa.SA_ERR_NULL
+    minimal = 4 * (16 + 2 * 4096 + 4 * 64)        # header, row core ranges, tiles
+    assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE, minimal - 4, None) == sa.SA_ERR_WORKSPACE
 
 
 def test_validate_requires_a_pattern():

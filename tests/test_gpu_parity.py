@@ -54,6 +54,11 @@ SMALL = {
     "evoformer_f32_d64": lambda: gen.make("evoformer_l384", B=2, H=2, n=130, d=64, dtype="f32"),
     "random_bias_keymask": lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
                                             bias=True, key_mask=True, pmax=40),
+    # rows longer than the plan's split threshold (1024 entries): global-token rows, random
+    "longformer_long_rows": lambda: gen.make("longformer_n4096", n=2500, H=2, window=100),
+    "random_long_rows": lambda: gen.make("random_n8192", n=2100, H=2, kmin=1, kmax=1800),
+    "longformer_bias_keymask": lambda: gen.make("longformer_n4096", n=600, H=2, B=2, window=50,
+                                                bias=True, key_mask=True, pmax=100),
 }
 
 
@@ -62,11 +67,12 @@ def small(name):
     return SMALL[name]()
 
 
+@pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_pipeline_parity_small(name):
+def test_pipeline_parity_small(name, plan):
     p = _elementwise(small(name))
-    say(f"pipeline {name}: BH={p.BH} n={p.n} d={p.d} nnz={p.nnz} {p.dtype}")
-    dp = DevProblem(p)
+    say(f"pipeline {name} plan={plan}: BH={p.BH} n={p.n} d={p.d} nnz={p.nnz} {p.dtype}")
+    dp = DevProblem(p, plan=plan)
     S, W, O = dp.pipeline()
     ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H, **dp.oracle_args())
     check(S, ref["S"], p.dtype, "scores")
@@ -79,11 +85,14 @@ def test_pipeline_parity_small(name):
     assert np.array_equal(dp.col_idx.cpu().numpy(), p.col_idx)
 
 
+@pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_fused_parity_small(name):
+def test_fused_parity_small(name, plan):
     p = small(name)
-    say(f"fused {name}: BH={p.BH} n={p.n} d={p.d} block={p.block} dense={p.row_ptr is None}")
-    dp = DevProblem(p)
+    if plan and (p.row_ptr is None or p.block != 1):
+        pytest.skip("the row plan applies to element CSR only")
+    say(f"fused {name} plan={plan}: BH={p.BH} n={p.n} d={p.d} block={p.block} dense={p.row_ptr is None}")
+    dp = DevProblem(p, plan=plan)
     O, lse = dp.fused()
     ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), want_weights=False,
                                  **dp.oracle_args())
@@ -169,14 +178,16 @@ def test_zero_queries_give_uniform_weights():
     assert np.all(S == 0)
 
 
-def test_determinism_bitwise():
-    p = _elementwise(small("longformer_bf16_d64"))
-    dp = DevProblem(p)
-    a = dp.pipeline()
-    b = dp.pipeline()
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
-    assert np.array_equal(dp.fused()[0], dp.fused()[0])
+@pytest.mark.parametrize("name", ["longformer_bf16_d64", "longformer_long_rows"])
+def test_determinism_bitwise(name):
+    p = _elementwise(small(name))
+    for plan in (False, True):
+        dp = DevProblem(p, plan=plan)
+        a = dp.pipeline()
+        b = dp.pipeline()
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+        assert np.array_equal(dp.fused()[0], dp.fused()[0])
 
 
 def test_softmax_alone_long_rows_and_infinities():
@@ -247,29 +258,79 @@ def test_validate_csr():
         torch.cuda.synchronize()
 
 
-def test_plan_build_matches_host():
-    p = gen.make("longformer_n4096", n=3000, H=1, window=300)        # rows up to 3000 entries
+def _host_plan(p, BH, d):
+    """The plan's contents computed on the host from its definition (core ranges, tiles,
+    long-row segments)."""
+    rp, ci, n = p.row_ptr.astype(np.int64), p.col_idx, p.n
+    rows = np.zeros((n, 2), np.int64)
+    for i in range(n):
+        a, b = rp[i], rp[i + 1]
+        L = b - a
+        if 0 < L <= 1024:
+            med = ci[(a + b) // 2]
+            lo = a + np.searchsorted(ci[a:b], med - L, "left")
+            hi = a + np.searchsorted(ci[a:b], med + L, "right")
+            rows[i] = lo, hi
+        else:
+            rows[i] = a, a
+    tiles = []
+    for t0 in range(0, n, 64):
+        lo, hi, core = None, None, 0
+        for i in range(t0, min(n, t0 + 64)):
+            if rows[i, 1] > rows[i, 0]:
+                c0, c1 = ci[rows[i, 0]], ci[rows[i, 1] - 1]
+                lo = c0 if lo is None else min(lo, c0)
+                hi = c1 if hi is None else max(hi, c1)
+                core += rows[i, 1] - rows[i, 0]
+        if hi is None:
+            tiles.append((0, 0, 0, 0))
+        else:
+            kb0, kb1 = lo // 64, hi // 64 + 1
+            tiles.append((kb0, kb1, int(core >= 0.25 * 64 * 64 * (kb1 - kb0)), core))
+    segs = []
+    lr = 0
+    for i in range(n):
+        a, b = rp[i], rp[i + 1]
+        L = b - a
+        if L > 1024:
+            ns = -(-L // 256)
+            for s_ in range(ns):
+                segs.append((i, a + L * s_ // ns, a + L * (s_ + 1) // ns, lr, s_, ns, 0, 0))
+            lr += 1
+    return rows, np.array(tiles), np.array(segs, dtype=np.int64).reshape(-1, 8), lr
+
+
+@pytest.mark.parametrize("name", ["longformer_long_rows", "random_long_rows", "window_n128_f32"])
+def test_plan_build_matches_host(name):
+    p = _elementwise(small(name))
     dp = DevProblem(p)
-    nbytes = sa.sa_plan_bytes(dp.prob)
-    plan = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
-    sa.sa_plan_build(dp.prob, plan)
+    plan = dp.build_plan()
     torch.cuda.synchronize()
-    h = plan.cpu().numpy()
-    assert h[0] == 0x53415031 and h[1] == p.n and h[2] == p.nnz and h[4] == 512
-    items = h[8:8 + 4 * h[5]].reshape(-1, 4)
-    exp = []
-    for i in range(p.n):
-        a, ln = int(p.row_ptr[i]), int(p.row_ptr[i + 1] - p.row_ptr[i])
-        ns = max(1, -(-ln // 512))
-        for s in range(ns):
-            exp.append((i, a + ln * s // ns, a + ln * (s + 1) // ns, (ns << 16) | s))
-    assert np.array_equal(items, np.array(exp, dtype=np.int32))
+    h = plan.cpu().numpy().astype(np.int64)
+    rows, tiles, segs, L = _host_plan(p, p.BH, p.d)
+    assert h[0] == 0x53415032 and h[1] == p.n and h[2] == p.nnz and h[7] == 1
+    assert h[4] == len(tiles) and h[5] == L and h[6] == len(segs)
+    assert h[8] == p.BH and h[9] == p.d
+    assert np.array_equal(h[h[10]:h[10] + 2 * p.n].reshape(-1, 2), rows)
+    assert np.array_equal(h[h[11]:h[11] + 4 * len(tiles)].reshape(-1, 4), tiles)
+    assert np.array_equal(h[h[12]:h[12] + 8 * len(segs)].reshape(-1, 8), segs)
+    assert np.all(h[h[13]:h[13] + L * p.BH] == 0)                       # merge counters
+    assert h[15] * 4 <= plan.numel() * 4
     # a problem that carries the plan validates it when asked to
-    dp.prob.set_plan(plan)
     dp.prob.c.flags = sa.SA_FLAG_VALIDATE
     S, W, O = dp.pipeline()
-    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), [(0, 0), (0, 1500)])
-    check(O[0, [0, 1500]], ref["O"], p.dtype, "context with plan")
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H)
+    check(O, ref["O"], p.dtype, "context with plan")
+    # a plan built for fewer heads is refused under validation
+    small_prob = sa.Problem(1, 1, p.n, p.d, dp.prob.c.dtype, dp.row_ptr, dp.col_idx, p.nnz)
+    nb = sa.sa_plan_bytes(small_prob)
+    pl = torch.zeros((nb + 3) // 4, dtype=torch.int32, device=DEV)
+    sa.sa_plan_build(small_prob, pl)
+    if p.BH > 1:
+        dp.prob.set_plan(pl)
+        with pytest.raises(sa.SaError) as ei:
+            dp.pipeline()
+        assert ei.value.status == sa.SA_ERR_WORKSPACE
 
 
 # ------------------------------------------------------------------------------ full size
@@ -295,7 +356,7 @@ def test_full_size_pipeline_sampled(name):
     p = full(name)
     pe = _elementwise(p)
     say(f"full pipeline {name}: BH={p.BH} n={p.n} nnz/head={pe.nnz}")
-    dp = DevProblem(pe)
+    dp = DevProblem(pe, plan=True)
     S, W, O = dp.pipeline()
     pairs = _sample_rows(p)
     ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), pairs)
