@@ -157,7 +157,7 @@ int sa_plan_build(const sa_problem* p, void* plan, size_t plan_bytes, hipStream_
   int st = check_problem(p, kOpPlan);
   if (st != SA_OK) return st;
   if (!plan) return SA_ERR_NULL;
-  if (plan_bytes < sa::plan_bytes_for(p->n, 0, 0, 0, p->d)) return SA_ERR_WORKSPACE;
+  if (plan_bytes < sa::plan_bytes_for(p->n, 0, 0, 0, p->d)) return SA_ERR_WORKSPACE;  // header, rows, tiles
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_plan(*p, plan, plan_bytes, stream));
 }

@@ -7,8 +7,10 @@
 // plan records, once per pattern and for every head and call:
 //   * per row, its core entry range: the entries within len columns of the row's median
 //     column (for a windowed row: the window; global-token columns fall outside);
-//   * per 64-row tile, the key blocks spanned by the core entries of its rows and whether
-//     that span is dense enough (>= kDenseTile) to be computed as dense 64x64 products;
+//   * per 64-row tile, the key blocks spanned by the core entries of its rows, the sorted
+//     distinct columns of its other ("far") entries when they fit one gathered 64-key
+//     block (e.g. the global-token columns), and whether these blocks are dense enough
+//     (>= kDenseTile) to be computed as dense 64x64 products;
 //   * rows longer than kLongRow, cut into segments of at most kSeg entries, so that such a
 //     row is spread over many waves; their partial results merge deterministically through
 //     a per-(row, head) counter and scratch space kept in the plan.
@@ -139,34 +141,157 @@ __global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __re
   }
 }
 
-// Kernel C: per-tile key-block span of the core entries, and its density.
-__global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__ col_idx, int n,
-                                                         const int* __restrict__ rows,
-                                                         int* __restrict__ tiles) {
-  const int tile = blockIdx.x * blockDim.x + threadIdx.x;
-  const int ntiles = (n + kTileRows - 1) / kTileRows;
-  if (tile >= ntiles) return;
-  int cmin = 0x7fffffff, cmax = -1;
-  long long core = 0;
-  for (int i = tile * kTileRows; i < min(n, (tile + 1) * kTileRows); ++i) {
-    const int lo = rows[2 * i], hi = rows[2 * i + 1];
-    if (hi > lo) {
-      cmin = min(cmin, col_idx[lo]);
-      cmax = max(cmax, col_idx[hi - 1]);
-      core += hi - lo;
+// Kernel C (one workgroup per tile): key-block span of the rows' core entries, the
+// sorted distinct far columns (entries outside the core ranges, long rows excluded), and
+// whether the tile runs on matrix cores: at most 64 far columns (one gathered key block)
+// and core + far entries filling at least kDenseTile of the blocks' cells.
+__global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__ row_ptr,
+                                                         const int* __restrict__ col_idx, int n,
+                                                         long long nnz, const int* __restrict__ rows,
+                                                         int* __restrict__ tiles, int ntiles) {
+  __shared__ int s_far[kFarMax];
+  __shared__ int s_pre[kTileRows + 1];
+  __shared__ int s_min, s_max, s_core, s_far_total;
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_min = 0x7fffffff;
+    s_max = -1;
+    s_core = 0;
+  }
+  __syncthreads();
+  int nfar = 0, lo = 0, hi = 0;
+  long long rs = 0, re = 0;
+  if (tid < kTileRows) {
+    const int row = tile * kTileRows + tid;
+    if (row < n) {
+      row_range(row_ptr, row, nnz, rs, re);
+      if (re - rs > kLongRow) {
+        rs = re = 0;  // handled by segments: no entries in this tile's records
+      } else {
+        lo = rows[2 * row];
+        hi = rows[2 * row + 1];
+        if (hi > lo) {
+          atomicMin(&s_min, col_idx[lo]);
+          atomicMax(&s_max, col_idx[hi - 1]);
+          atomicAdd(&s_core, hi - lo);
+        }
+        nfar = (int)((lo - rs) + (re - hi));
+      }
+    }
+    s_pre[tid + 1] = nfar;
+  }
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    for (int r = 0; r < kTileRows; ++r) s_pre[r + 1] += s_pre[r];
+    s_far_total = s_pre[kTileRows];
+  }
+  __syncthreads();
+  const int F = s_far_total;
+  int U = 0;
+  bool ok = F <= kFarMax;
+  if (ok && F > 0) {
+    // gather the far columns, pad with INT_MAX, bitonic sort, count distinct values
+    for (int i = tid; i < kFarMax; i += blockDim.x) s_far[i] = 0x7fffffff;
+    __syncthreads();
+    if (tid < kTileRows && nfar > 0) {
+      int o = s_pre[tid];
+      for (long long e = rs; e < lo; ++e) s_far[o++] = col_idx[e];
+      for (long long e = hi; e < re; ++e) s_far[o++] = col_idx[e];
+    }
+    __syncthreads();
+    for (int k = 2; k <= kFarMax; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < kFarMax; i += blockDim.x) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int x = s_far[i], y = s_far[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              s_far[i] = y;
+              s_far[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if (tid == 0) {
+      int u = 0;
+      for (int i = 0; i < F; ++i)
+        if (i == 0 || s_far[i] != s_far[i - 1]) {
+          if (u < kTileRows) tiles[kTileInfo * ntiles + kTileRows * tile + u] = s_far[i];
+          s_far[u] = s_far[i];  // compact in place (u <= i)
+          ++u;
+        }
+      s_far_total = u;
+    }
+    __syncthreads();
+    U = s_far_total;
+    ok = U <= kTileRows;
+  }
+  if (tid == 0) {
+    int kb_lo = 0, kb_hi = 0;
+    const int cmin = s_min, cmax = s_max;
+    if (cmax >= 0) {
+      kb_lo = clampi(cmin, 0, n - 1) / kTileRows;
+      kb_hi = clampi(cmax, 0, n - 1) / kTileRows + 1;
+    }
+    const int nblocks = (kb_hi - kb_lo) + (U > 0 ? 1 : 0);
+    const double cells = (double)kTileRows * kTileRows * nblocks;
+    const bool mfma = ok && nblocks > 0 && kb_hi - kb_lo <= kMaxTileBlocks &&
+                      (double)(s_core + F) >= kDenseTile * cells;
+    int* ti = tiles + kTileInfo * tile;
+    ti[0] = kb_lo;
+    ti[1] = kb_hi;
+    ti[2] = mfma ? 1 : 0;
+    ti[3] = ok ? U : 0;
+    ti[4] = ti[5] = ti[6] = ti[7] = 0;
+    s_far_total = mfma ? 1 : 0;  // reused: broadcast the decision
+  }
+  __syncthreads();
+  // block records of a matrix-core tile: per key block, each row's first entry and key mask
+  if (s_far_total && tid < kTileRows) {
+    const int kb_lo = tiles[kTileInfo * tile], kb_hi = tiles[kTileInfo * tile + 1];
+    const int nfar = tiles[kTileInfo * tile + 3];
+    int* blk = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
+    long long e = lo;
+    for (int j = 0; j < kb_hi - kb_lo; ++j) {
+      const long long k0 = (long long)(kb_lo + j) * kTileRows;
+      unsigned long long m = 0;
+      const long long first = e;
+      while (e < hi && col_idx[e] < k0 + kTileRows) {
+        const long long dk = col_idx[e] - k0;
+        if (dk >= 0) m |= 1ull << dk;
+        ++e;
+      }
+      int* rec = blk + ((long long)j * kTileRows + tid) * kBlkWords;
+      rec[0] = (int)first;
+      rec[1] = (int)(m & 0xffffffffull);
+      rec[2] = (int)(m >> 32);
+    }
+    if (nfar > 0) {  // the gathered block: slots are positions in the far list
+      unsigned long long m = 0;
+      for (int side = 0; side < 2; ++side) {
+        const long long a = side ? hi : rs, b = side ? re : lo;
+        for (long long f = a; f < b; ++f) {
+          const int c = col_idx[f];
+          int l = 0, h = nfar;
+          while (l < h) {
+            const int mid = (l + h) >> 1;
+            if (s_far[mid] < c) l = mid + 1;
+            else h = mid;
+          }
+          m |= 1ull << l;
+        }
+      }
+      int* rec = blk + ((long long)(kb_hi - kb_lo) * kTileRows + tid) * kBlkWords;
+      rec[0] = (int)rs;
+      rec[1] = (int)(m & 0xffffffffull);
+      rec[2] = (int)(m >> 32);
     }
   }
-  int kb_lo = 0, kb_hi = 0, dense = 0;
-  if (cmax >= 0) {
-    kb_lo = clampi(cmin, 0, n - 1) / kTileRows;
-    kb_hi = clampi(cmax, 0, n - 1) / kTileRows + 1;
-    const double cells = (double)kTileRows * kTileRows * (kb_hi - kb_lo);
-    dense = (double)core >= kDenseTile * cells ? 1 : 0;
-  }
-  tiles[4 * tile] = kb_lo;
-  tiles[4 * tile + 1] = kb_hi;
-  tiles[4 * tile + 2] = dense;
-  tiles[4 * tile + 3] = (int)core;
 }
 
 // Kernel D: zero the merge counters (a plain fill kernel, safe under graph capture).
@@ -221,13 +346,15 @@ hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_
   const long long off_rows = kPlanHeaderWords;
   const long long off_tiles = off_rows + 2ll * n;
   const int ntiles = (n + kTileRows - 1) / kTileRows;
-  if (cap < off_tiles + 4ll * ntiles) return hipErrorInvalidValue;
+  if (cap < off_tiles + (long long)(kTileInfo + kTileRows + kBoundsPerTile) * ntiles)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col_idx,
                      n, (long long)p.nnz, pl + off_rows);
   hipLaunchKernelGGL(plan_segs_kernel, dim3(1), dim3(kScanThreads), 0, s, p.row_ptr, n,
                      (long long)p.nnz, BH, p.d, cap, pl);
-  hipLaunchKernelGGL(plan_tiles_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, s, p.col_idx, n,
-                     pl + off_rows, pl + off_tiles);
+  if (ntiles > 0)
+    hipLaunchKernelGGL(plan_tiles_kernel, dim3(ntiles), dim3(256), 0, s, p.row_ptr, p.col_idx, n,
+                       (long long)p.nnz, pl + off_rows, pl + off_tiles, ntiles);
   hipLaunchKernelGGL(plan_zero_kernel, dim3(64), dim3(256), 0, s, pl);
   return hipGetLastError();
 }

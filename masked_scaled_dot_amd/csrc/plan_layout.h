@@ -13,16 +13,29 @@ constexpr int kTileRows = 64;           // rows per tile (and keys per key block
 constexpr int kLongRow = 1024;          // rows with more entries are split into segments
 constexpr int kSeg = 256;               // entries per long-row segment
 constexpr float kDenseTile = 0.25f;     // tiles at least this dense run on matrix cores
+constexpr int kFarMax = 1024;           // far entries a tile may hold and still be gathered
+constexpr int kMaxTileBlocks = 12;      // contiguous key blocks a matrix-core tile may span
+constexpr int kTileInfo = 8;            // words per tile
+constexpr int kBlkWords = 3;            // per row and block: first entry, key mask low, high
+constexpr int kBoundsPerTile = (kMaxTileBlocks + 1) * kTileRows * kBlkWords;
 
 // header words
 enum PlanHeader {
   kHMagic = 0, kHN, kHNnzLo, kHNnzHi, kHTiles, kHLongRows, kHSegs, kHValid,
   kHBH, kHD, kHOffRows, kHOffTiles, kHOffSegs, kHOffCounters, kHOffScratch, kHWords
 };
+// After the tile records (kTileInfo words each) come the far-column lists (kTileRows ints per
+// tile) and the block records (kBoundsPerTile ints per tile, laid out [block][row][3]).
 
 // Word counts of the parts, in layout order: header, rows (2 per row: first and one past
-// the last entry of the row's core range), tiles (4 per tile: first key block, one past
-// the last key block, 1 if dense enough for matrix cores, core entries), long-row
+// the last entry of the row's core range), tiles (kTileInfo per tile: first key block, one
+// past the last key block, 1 if the tile runs on matrix cores, number of far columns, then
+// unused), far columns (64 per tile: the sorted distinct columns of the tile's entries
+// outside the rows' core ranges, when there are at most 64 of them), block records (for a
+// matrix-core tile, per key block j -- the contiguous ones, then the gathered far block --
+// and row r: the row's first entry in the block and a 64-bit mask of the block's key slots
+// the row holds; the row's entries in the block are its set bits in ascending order),
+// long-row
 // segments (8 per segment: row, begin, end, long-row index, segment index within the row,
 // segments of the row, 0, 0), merge counters (one per long row and head), scratch floats
 // (kSlot(d) per segment and head: partial row and, for the fused forward, max and sum),
@@ -38,7 +51,7 @@ __host__ __device__ inline PlanSizes plan_sizes(long long n, long long long_rows
   PlanSizes s;
   const long long tiles = (n + kTileRows - 1) / kTileRows;
   s.rows = 2 * n;
-  s.tiles = 4 * tiles;
+  s.tiles = (long long)(kTileInfo + kTileRows + kBoundsPerTile) * tiles;
   s.segs = 8 * segs;
   s.counters = long_rows * BH;
   const long long before = kPlanHeaderWords + s.rows + s.tiles + s.segs + s.counters;

@@ -12,15 +12,17 @@
 //    registers); the CSR then selects the stored entries: the entries of a row that fall
 //    in one 64-key block are at most 64 consecutive entries, so one lane-parallel pass per
 //    row and block reads them from LDS and writes them contiguously;
-//  * the row's entries outside its core range (e.g. global-token columns), and every row
-//    of a sparse tile, take the vector path: one entry per lane, the key row gathered with
-//    16-byte loads and reduced in-lane with v_dot2_f32_bf16 (fma for fp32);
+//  * the rows' entries outside their core ranges (e.g. global-token columns) form one more,
+//    gathered key block: its keys are the tile's distinct far columns listed in the plan;
+//  * every row of a sparse tile takes the vector path: one entry per lane, the key row
+//    gathered with 16-byte loads and reduced in-lane with v_dot2_f32_bf16 (fma for fp32);
 //  * rows longer than the plan's long-row threshold are skipped by the tiles and handled as
 //    segments by the first workgroups of the grid, spread over many waves.
 // Without a plan, one wave per (head, row) runs the vector path over the whole row.
 #include "common.h"
 #include "kernels.h"
 #include "plan_layout.h"
+#include "tile.h"
 
 namespace sa {
 namespace {
@@ -122,44 +124,6 @@ __device__ void valu_row(const Args& a, int t, int row, long long e_begin, long 
   }
 }
 
-// Vector path over a list of entries of different rows (a tile's far entries): each lane
-// gathers its own q row and key row. far_pre[r] = far entries of the tile's rows before
-// row r (r in 0..64, inclusive prefix at r+1); row r's far entries are [rs, lo) and [hi, re).
-template <typename T, int D>
-__device__ void valu_far(const Args& a, int t, int row0, const int* far_pre, const int* far_lo,
-                         const int* far_hi) {
-  const int total = far_pre[kTileRows];
-  const int b = t / a.H, h = t % a.H;
-  const T* qt = static_cast<const T*>(a.q) + (size_t)t * a.n * D;
-  const T* kt = static_cast<const T*>(a.k) + (size_t)t * a.n * D;
-  float* st = a.scores + (size_t)t * a.nnz;
-  constexpr int W = RowVec<T, D>::kWords;
-  for (int f = threadIdx.x; f < total; f += kThreads) {
-    int lo = 0, hi = kTileRows;  // find r with far_pre[r] <= f < far_pre[r+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (far_pre[mid] <= f) lo = mid;
-      else hi = mid;
-    }
-    const int r = lo, row = row0 + r;
-    long long rs, re;
-    row_bounds(a, row, rs, re);
-    const int k_in = f - far_pre[r];
-    const int nleft = far_lo[r] - (int)rs;
-    const long long e = k_in < nleft ? rs + k_in : (long long)far_hi[r] + (k_in - nleft);
-    const int j = clampi(a.col_idx[e], 0, a.n - 1);
-    uint32_t qw[W];
-    const uint4* qrow = reinterpret_cast<const uint4*>(qt + (size_t)row * D);
-#pragma unroll
-    for (int c = 0; c < W / 4; ++c) {
-      const uint4 v = qrow[c];
-      qw[4 * c] = v.x; qw[4 * c + 1] = v.y; qw[4 * c + 2] = v.z; qw[4 * c + 3] = v.w;
-    }
-    const float s = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)j * D));
-    st[e] = s * a.scale + additive(a, h, b, row, j);
-  }
-}
-
 // ---------------------------------------------------------------------------------- kernels
 
 template <typename T, int D>
@@ -176,15 +140,11 @@ __global__ __launch_bounds__(kThreads) void sddmm_rows_kernel(Args a, int BH) {
 
 template <int D>
 struct TileSmem {
-  static constexpr int kKStride = D + 8;       // bf16 per K row (+16 B: conflict-free A reads)
+  static constexpr int kKStride = D + 8;          // bf16 per K row (+16 B: conflict-free A reads)
   static constexpr int kSStride = kTileRows + 1;  // fp32 per score row
-  alignas(16) uint16_t k[kTileRows * kKStride];
+  alignas(16) uint16_t k[2][kTileRows * kKStride];  // double-buffered K block
   float s[kTileRows * kSStride];
-  int far_pre[kTileRows + 1];
-  int far_lo[kTileRows];
-  int far_hi[kTileRows];
-  int core_lo[kTileRows];
-  int core_hi[kTileRows];
+  TileMeta meta;
 };
 
 template <typename T, int D>
@@ -215,10 +175,10 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const int* tinfo = plan + plan[kHOffTiles] + 4 * tile;
   const int* rows = plan + plan[kHOffRows];
-  const int kb_lo = tinfo[0], kb_hi = tinfo[1];
-  const bool dense = (sizeof(T) == 2) && tinfo[2] != 0;
+  const TileView tv = tile_view(plan, tile);
+  const int kb_lo = tv.kb_lo, kb_hi = tv.kb_hi;
+  const bool dense = (sizeof(T) == 2) && tv.mfma && segs_ok;
 
   if (!dense) {
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
@@ -235,35 +195,11 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
   if constexpr (sizeof(T) == 2) {
     constexpr int KS = TileSmem<D>::kKStride, SS = TileSmem<D>::kSStride;
     constexpr int KC = D / 32;
-    // per-row core ranges and far-entry prefix (long rows contribute nothing here)
-    if (threadIdx.x < kTileRows) {
-      const int r = threadIdx.x, row = row0 + r;
-      int lo = 0, hi = 0, nfar = 0;
-      if (row < a.n) {
-        long long rs, re;
-        row_bounds(a, row, rs, re);
-        if (re - rs <= kLongRow) {
-          lo = clampi(rows[2 * row], (int)rs, (int)re);
-          hi = clampi(rows[2 * row + 1], lo, (int)re);
-          nfar = (lo - (int)rs) + ((int)re - hi);
-        } else {
-          lo = hi = (int)rs;               // no core range: a long row
-          nfar = segs_ok ? 0 : (int)(re - rs);
-        }
-      }
-      sm.core_lo[r] = lo;
-      sm.core_hi[r] = hi;
-      sm.far_lo[r] = lo;
-      sm.far_hi[r] = hi;
-      sm.far_pre[r + 1] = nfar;
-    }
-    if (threadIdx.x == 0) sm.far_pre[0] = 0;
+    constexpr int KCH = kTileRows * (D / 8) / kThreads;  // 16-byte K chunks per thread per block
+    load_tile_meta(sm.meta, tv, a.row_ptr, rows, row0, a.n, a.nnz);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int r = 0; r < kTileRows; ++r) sm.far_pre[r + 1] += sm.far_pre[r];
-    }
-    __syncthreads();
-    valu_far<T, D>(a, t, row0, sm.far_pre, sm.far_lo, sm.far_hi);
+    const int nbc = kb_hi - kb_lo;
+    const int nblk = tile_blocks(tv);
 
     // the wave's 16 queries as the B operand of S^T (lane: query c16, dims 32kc + 8g..)
     const int g = lane / 16, c16 = lane % 16;
@@ -276,57 +212,54 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
       qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
     const int b = t / a.H, h = t % a.H;
     float* st = a.scores + (size_t)t * a.nnz;
-    // cursor of the wave's row r (lane r < 16 keeps it)
-    int cur = sm.core_lo[wave * 16 + (lane & 15)];
 
-    for (int kb = kb_lo; kb < kb_hi; ++kb) {
-      const int k0 = kb * kTileRows;
-      // columns of the next (at most 64) core entries of each of the wave's 16 rows; the
-      // loads are in flight while K is staged and the block is multiplied
-      int colv[16];
+    uint4 kn[KCH];  // next block's K rows, loaded one block ahead
+    auto prefetch = [&](int j) {
+      const bool gathered = j >= nbc;
+      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int start = __builtin_amdgcn_readlane(cur, r);
-        const int e = start + lane;
-        colv[r] = e < sm.core_hi[wave * 16 + r] ? a.col_idx[e] : 0x7fffffff;
+      for (int u = 0; u < KCH; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        const int key = block_key(sm.meta, tv.nfar, gathered, k0, i / (D / 8), a.n);
+        kn[u] = *reinterpret_cast<const uint4*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
       }
-      __syncthreads();
-      for (int i = threadIdx.x; i < kTileRows * (D / 8); i += kThreads) {
-        const int r = i / (D / 8), cc = i % (D / 8);
-        const int key = min(k0 + r, a.n - 1);
-        *reinterpret_cast<uint4*>(&sm.k[r * KS + cc * 8]) =
-            *reinterpret_cast<const uint4*>(kt + (size_t)key * D + cc * 8);
+    };
+
+    if (nblk > 0) prefetch(0);
+    for (int j = 0; j < nblk; ++j) {
+      const bool gathered = j >= nbc;
+      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
+      uint16_t* kbuf = sm.k[j & 1];
+#pragma unroll
+      for (int u = 0; u < KCH; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        *reinterpret_cast<uint4*>(&kbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
       }
-      __syncthreads();
-      // S^T block for the wave's 16 queries; accumulator: query c16, keys 16tt + 4g + i
+      lds_barrier();                       // block j's K is visible to every wave
+      if (j + 1 < nblk) prefetch(j + 1);   // in flight while block j is multiplied
+      // S^T block for the wave's 16 queries; accumulator: query c16, keys 16tt + 4g + i.
+      // The score rows are private to the wave.
+      float* sw = sm.s + wave * 16 * SS;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           const bf16x8_v av = __builtin_bit_cast(
-              bf16x8_v, *reinterpret_cast<const uint4*>(&sm.k[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+              bf16x8_v, *reinterpret_cast<const uint4*>(&kbuf[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kc], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.s[(wave * 16 + c16) * SS + 16 * tt + 4 * g + i] = acc[i];
+        for (int i = 0; i < 4; ++i) sw[c16 * SS + 16 * tt + 4 * g + i] = acc[i];
       }
-      // select the stored entries of each of the wave's rows that fall in this block
+      // lane = key slot: store the score of each of the wave's rows that holds this key
+      const int key = gathered ? clampi(sm.meta.far[lane], 0, a.n - 1) : min(k0 + lane, a.n - 1);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = wave * 16 + r;
-        const int row = row0 + lr;
-        const int start = __builtin_amdgcn_readlane(cur, r);
-        const long long e = (long long)start + lane;
-        const int col = colv[r];
-        const bool in_blk = col < k0 + kTileRows;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(in_blk);
-        const int cnt = __builtin_popcountll(m);
-        if (in_blk && row < a.n) {
-          const int cc = clampi(col - k0, 0, kTileRows - 1);
-          st[e] = sm.s[lr * SS + cc] * a.scale + additive(a, h, b, row, clampi(col, 0, a.n - 1));
-        }
-        if (lane == r) cur = start + cnt;
+        bool present;
+        const int e = slot_entry(sm.meta, j, gathered, lr, lane, present);
+        if (present) st[e] = sw[r * SS + lane] * a.scale + additive(a, h, b, row0 + lr, key);
       }
     }
   }

@@ -11,7 +11,9 @@
 //    about 16 mantissa bits of each weight), and each wave accumulates its 16 rows with
 //    v_mfma_f32_16x16x32_bf16 (A = the weight rows, B = V read with the transposing LDS
 //    load ds_read_b64_tr_b16, which turns row-major V into the k-major operand);
-//  * entries outside a row's core range are then added by the thread that owns the row;
+//  * entries outside the rows' core ranges (e.g. global-token columns) form one more,
+//    gathered block: its keys are the tile's distinct far columns listed in the plan, and it
+//    runs through the same scatter-and-multiply steps;
 //  * sparse tiles and rows without a plan run the vector path: the wave is split into lane
 //    slots that each own one 16-byte column chunk of V and walk every slots-th entry;
 //  * rows longer than the plan's threshold are cut into segments handled by the first
@@ -21,6 +23,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "plan_layout.h"
+#include "tile.h"
 
 namespace sa {
 namespace {
@@ -141,15 +144,12 @@ __global__ __launch_bounds__(kThreads) void spmm_rows_kernel(Args a, int BH) {
 
 template <int D>
 struct TileSmem {
-  static constexpr int kVStride = D + 16;   // bf16 per V row: stride = 32 B mod 256 B
+  static constexpr int kVStride = D + 16;         // bf16 per V row: stride = 32 B mod 256 B
   static constexpr int kWStride = kTileRows + 8;  // bf16 per weight row (+16 B)
-  static constexpr int kOStride = D + 1;    // fp32 per output row
-  alignas(16) uint16_t v[kTileRows * kVStride];
+  alignas(16) uint16_t v[2][kTileRows * kVStride];  // double-buffered V block
   alignas(16) uint16_t whi[kTileRows * kWStride];
   alignas(16) uint16_t wlo[kTileRows * kWStride];
-  float o[kTileRows * kOStride];
-  int core_lo[kTileRows];
-  int core_hi[kTileRows];
+  TileMeta meta;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -213,10 +213,10 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const int* tinfo = plan + plan[kHOffTiles] + 4 * tile;
   const int* rows = plan + plan[kHOffRows];
-  const int kb_lo = tinfo[0], kb_hi = tinfo[1];
-  const bool dense = (sizeof(T) == 2) && tinfo[2] != 0;
+  const TileView tv0 = tile_view(plan, tile);
+  const int kb_lo = tv0.kb_lo, kb_hi = tv0.kb_hi;
+  const bool dense = (sizeof(T) == 2) && tv0.mfma && split;
 
   if (!dense) {
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
@@ -231,82 +231,69 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   }
 
   if constexpr (sizeof(T) == 2) {
-    constexpr int VS = TileSmem<D>::kVStride, WS = TileSmem<D>::kWStride, OS = TileSmem<D>::kOStride;
+    constexpr int VS = TileSmem<D>::kVStride, WS = TileSmem<D>::kWStride;
     constexpr int OC = D / 16;
-    if (threadIdx.x < kTileRows) {
-      const int r = threadIdx.x, row = row0 + r;
-      int lo = 0, hi = 0;
-      if (row < a.n) {
-        long long rs, re;
-        row_bounds(a, row, rs, re);
-        if (re - rs <= kLongRow) {
-          lo = clampi(rows[2 * row], (int)rs, (int)re);
-          hi = clampi(rows[2 * row + 1], lo, (int)re);
-        } else {
-          lo = hi = (int)rs;
-        }
-      }
-      sm.core_lo[r] = lo;
-      sm.core_hi[r] = hi;
-    }
+    constexpr int VCH = kTileRows * (D / 8) / kThreads;  // 16-byte V chunks per thread per block
+    const TileView tv = tile_view(plan, tile);
+    load_tile_meta(sm.meta, tv, a.row_ptr, rows, row0, a.n, a.nnz);
     __syncthreads();
+    const int nbc = kb_hi - kb_lo;
+    const int nblk = tile_blocks(tv);
     const int g = lane / 16, c16 = lane % 16;
     const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
     const float* wt = a.w + (size_t)t * a.nnz;
+
+    // next block's operands, loaded one block ahead: lane = key slot
+    float wn[16];
+    uint4 vn[VCH];
+    auto prefetch = [&](int j) {
+      const bool gathered = j >= nbc;
+      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool present;
+        const int e = slot_entry(sm.meta, j, gathered, wave * 16 + r, lane, present);
+        wn[r] = present ? wt[e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < VCH; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        const int key = block_key(sm.meta, tv.nfar, gathered, k0, i / (D / 8), a.n);
+        vn[u] = *reinterpret_cast<const uint4*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
+      }
+    };
+
     f32x4_v o[OC];
 #pragma unroll
     for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    int cur = sm.core_lo[wave * 16 + (lane & 15)];
-
-    for (int kb = kb_lo; kb < kb_hi; ++kb) {
-      const int k0 = kb * kTileRows;
-      // this block's core entries of the wave's rows: columns and weights (in flight early)
-      int colv[16];
-      float wv[16];
+    if (nblk > 0) prefetch(0);
+    for (int j = 0; j < nblk; ++j) {
+      uint16_t* vb = sm.v[j & 1];
+#pragma unroll
+      for (int u = 0; u < VCH; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        *reinterpret_cast<uint4*>(&vb[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = vn[u];
+      }
+      // the wave's 16 weight rows of block j, one key slot per lane (hi + lo bf16 planes;
+      // absent keys write 0); the rows are private to the wave
+      uint16_t* whi = sm.whi + wave * 16 * WS;
+      uint16_t* wlo = sm.wlo + wave * 16 * WS;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int e = __builtin_amdgcn_readlane(cur, r) + lane;
-        const bool ok = e < sm.core_hi[wave * 16 + r];
-        colv[r] = ok ? a.col_idx[e] : 0x7fffffff;
-        wv[r] = ok ? wt[e] : 0.f;
+        const float w = wn[r];
+        const uint32_t hi = pack_bf16(w, 0.f) & 0xffffu;
+        const uint32_t lo = pack_bf16(w - __uint_as_float(hi << 16), 0.f) & 0xffffu;
+        whi[r * WS + lane] = (uint16_t)hi;
+        wlo[r * WS + lane] = (uint16_t)lo;
       }
-      __syncthreads();  // previous block's LDS reads are done
-      for (int i = threadIdx.x; i < kTileRows * (D / 8); i += kThreads) {
-        const int r = i / (D / 8), cc = i % (D / 8);
-        const int key = min(k0 + r, a.n - 1);
-        *reinterpret_cast<uint4*>(&sm.v[r * VS + cc * 8]) =
-            *reinterpret_cast<const uint4*>(vt + (size_t)key * D + cc * 8);
-      }
-      for (int i = threadIdx.x; i < kTileRows * (kTileRows / 8); i += kThreads) {
-        const int r = i / (kTileRows / 8), cc = i % (kTileRows / 8);
-        *reinterpret_cast<uint4*>(&sm.whi[r * WS + cc * 8]) = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sm.wlo[r * WS + cc * 8]) = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-      // scatter the wave's rows' weights of this block (hi + lo bf16)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int col = colv[r];
-        const bool in_blk = col < k0 + kTileRows;
-        const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in_blk));
-        if (in_blk) {
-          const int cc = clampi(col - k0, 0, kTileRows - 1);
-          const float w = wv[r];
-          const uint32_t hi = pack_bf16(w, 0.f) & 0xffffu;
-          const float whi = __uint_as_float(hi << 16);
-          const uint32_t lo = pack_bf16(w - whi, 0.f) & 0xffffu;
-          sm.whi[(wave * 16 + r) * WS + cc] = (uint16_t)hi;
-          sm.wlo[(wave * 16 + r) * WS + cc] = (uint16_t)lo;
-        }
-        if (lane == r) cur = __builtin_amdgcn_readlane(cur, r) + cnt;
-      }
-      __syncthreads();
+      lds_barrier();                       // block j's V is visible to every wave
+      if (j + 1 < nblk) prefetch(j + 1);   // in flight while block j is multiplied
       // O(16 rows x D) += W(16 x 64 keys) V(64 keys x D)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int wrow = (wave * 16 + c16) * WS + 32 * kk + 8 * g;
-        const bf16x8_v ahi = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&sm.whi[wrow]));
-        const bf16x8_v alo = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&sm.wlo[wrow]));
+        const int wrow = c16 * WS + 32 * kk + 8 * g;
+        const bf16x8_v ahi = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&whi[wrow]));
+        const bf16x8_v alo = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&wlo[wrow]));
         // lane j of each 16-lane group addresses V[key 32kk + 8g + j/4 (+4)][16c + 4(j%4)];
         // the transposing read hands lane j the 4 keys of column 16c + j
         const int vkey = 32 * kk + 8 * g + c16 / 4;
@@ -314,10 +301,8 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
         for (int c = 0; c < OC; ++c) {
           const int vcol = 16 * c + 4 * (c16 % 4);
           typedef __attribute__((address_space(3))) i16x4_v lds_v4;
-          const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4*)(&sm.v[vkey * VS + vcol]));
-          const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4*)(&sm.v[(vkey + 4) * VS + vcol]));
+          const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[vkey * VS + vcol]));
+          const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[(vkey + 4) * VS + vcol]));
           const bf16x8_v bv = __builtin_bit_cast(
               bf16x8_v, (__attribute__((ext_vector_type(8))) short){b0[0], b0[1], b0[2], b0[3],
                                                                     b1[0], b1[1], b1[2], b1[3]});
@@ -326,50 +311,20 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
         }
       }
     }
-    // accumulator layout: lane: column 16c + c16, rows 4g + i of the wave's 16
+    // accumulator layout: lane holds column 16c + c16 of rows 4g + i (of the wave's 16);
+    // rows handled by long-row segments are written by those
 #pragma unroll
-    for (int c = 0; c < OC; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.o[(wave * 16 + 4 * g + i) * OS + 16 * c + c16] = o[c][i];
-    __syncthreads();
-    // entries outside the core range: each row is owned by one thread
-    if (threadIdx.x < kTileRows) {
-      const int r = threadIdx.x, row = row0 + r;
-      if (row < a.n) {
+    for (int i = 0; i < 4; ++i) {
+      const int lr = wave * 16 + 4 * g + i, row = row0 + lr;
+      if (row >= a.n) continue;
+      if (sm.meta.row_hi[lr] == sm.meta.row_lo[lr]) {
         long long rs, re;
         row_bounds(a, row, rs, re);
-        if (re - rs <= kLongRow || !split) {
-          const int lo = (re - rs <= kLongRow) ? sm.core_lo[r] : (int)re;
-          const int hi = (re - rs <= kLongRow) ? sm.core_hi[r] : (int)re;
-          for (long long e = rs; e < re; ++e) {
-            if (e == lo) e = hi;
-            if (e >= re) break;
-            const int j = clampi(a.col_idx[e], 0, a.n - 1);
-            const float w = wt[e];
-            const uint4* vrow = reinterpret_cast<const uint4*>(vt + (size_t)j * D);
-#pragma unroll
-            for (int c = 0; c < D / 8; ++c) {
-              const uint4 x = vrow[c];
-              const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                sm.o[r * OS + 8 * c + 2 * q] = fmaf(w, bf16lo(xw[q]), sm.o[r * OS + 8 * c + 2 * q]);
-                sm.o[r * OS + 8 * c + 2 * q + 1] = fmaf(w, bf16hi(xw[q]), sm.o[r * OS + 8 * c + 2 * q + 1]);
-              }
-            }
-          }
-        }
+        if (re - rs > kLongRow) continue;
       }
-    }
-    __syncthreads();
-    // write the tile; long rows (split) are written by their segments
-    for (int i = threadIdx.x; i < kTileRows * D; i += kThreads) {
-      const int r = i / D, c = i % D, row = row0 + r;
-      if (row >= a.n) continue;
-      long long rs, re;
-      row_bounds(a, row, rs, re);
-      if (split && re - rs > kLongRow) continue;
-      a.out[((size_t)t * a.n + row) * D + c] = sm.o[r * OS + c];
+      float* orow = a.out + ((size_t)t * a.n + row) * D;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) orow[16 * c + c16] = o[c][i];
     }
   }
 }

@@ -273,20 +273,26 @@ def _host_plan(p, BH, d):
             rows[i] = lo, hi
         else:
             rows[i] = a, a
-    tiles = []
+    tiles, fars = [], []
     for t0 in range(0, n, 64):
-        lo, hi, core = None, None, 0
+        lo, hi, core, farcols = None, None, 0, []
         for i in range(t0, min(n, t0 + 64)):
+            a, b = rp[i], rp[i + 1]
+            if b - a > 1024:
+                continue
             if rows[i, 1] > rows[i, 0]:
                 c0, c1 = ci[rows[i, 0]], ci[rows[i, 1] - 1]
                 lo = c0 if lo is None else min(lo, c0)
                 hi = c1 if hi is None else max(hi, c1)
                 core += rows[i, 1] - rows[i, 0]
-        if hi is None:
-            tiles.append((0, 0, 0, 0))
-        else:
-            kb0, kb1 = lo // 64, hi // 64 + 1
-            tiles.append((kb0, kb1, int(core >= 0.25 * 64 * 64 * (kb1 - kb0)), core))
+            farcols += list(ci[a:rows[i, 0]]) + list(ci[rows[i, 1]:b])
+        uniq = sorted(set(farcols))
+        ok = len(farcols) <= 1024 and len(uniq) <= 64
+        kb0, kb1 = (0, 0) if hi is None else (lo // 64, hi // 64 + 1)
+        nblk = (kb1 - kb0) + (1 if uniq else 0)
+        mfma = ok and nblk > 0 and kb1 - kb0 <= 12 and core + len(farcols) >= 0.25 * 64 * 64 * nblk
+        tiles.append((kb0, kb1, int(mfma), len(uniq) if ok else 0, 0, 0, 0, 0))
+        fars.append(uniq if ok else None)
     segs = []
     lr = 0
     for i in range(n):
@@ -297,7 +303,7 @@ def _host_plan(p, BH, d):
             for s_ in range(ns):
                 segs.append((i, a + L * s_ // ns, a + L * (s_ + 1) // ns, lr, s_, ns, 0, 0))
             lr += 1
-    return rows, np.array(tiles), np.array(segs, dtype=np.int64).reshape(-1, 8), lr
+    return rows, np.array(tiles), fars, np.array(segs, dtype=np.int64).reshape(-1, 8), lr
 
 
 @pytest.mark.parametrize("name", ["longformer_long_rows", "random_long_rows", "window_n128_f32"])
@@ -307,12 +313,52 @@ def test_plan_build_matches_host(name):
     plan = dp.build_plan()
     torch.cuda.synchronize()
     h = plan.cpu().numpy().astype(np.int64)
-    rows, tiles, segs, L = _host_plan(p, p.BH, p.d)
+    rows, tiles, fars, segs, L = _host_plan(p, p.BH, p.d)
     assert h[0] == 0x53415032 and h[1] == p.n and h[2] == p.nnz and h[7] == 1
     assert h[4] == len(tiles) and h[5] == L and h[6] == len(segs)
     assert h[8] == p.BH and h[9] == p.d
     assert np.array_equal(h[h[10]:h[10] + 2 * p.n].reshape(-1, 2), rows)
-    assert np.array_equal(h[h[11]:h[11] + 4 * len(tiles)].reshape(-1, 4), tiles)
+    T = len(tiles)
+    assert np.array_equal(h[h[11]:h[11] + 8 * T].reshape(-1, 8), tiles)
+    far_base = h[11] + 8 * T
+    for ti, uniq in enumerate(fars):
+        if uniq:
+            assert list(h[far_base + 64 * ti:far_base + 64 * ti + len(uniq)]) == uniq
+    # block records of a matrix-core tile: per key block and row, the first entry in the
+    # block and the 64-bit mask of key slots present; the gathered block's slots are the
+    # positions of the tile's far columns
+    blk_base = h[11] + (8 + 64) * T
+    per_tile = 13 * 64 * 3
+    for ti in range(T):
+        if not tiles[ti, 2]:
+            continue
+        kb0, kb1 = tiles[ti, 0], tiles[ti, 1]
+        rec = h[blk_base + per_tile * ti: blk_base + per_tile * (ti + 1)].reshape(13, 64, 3)
+        for r in range(64):
+            i = ti * 64 + r
+            if i >= p.n or p.row_ptr[i + 1] - p.row_ptr[i] > 1024:
+                assert all(rec[j, r, 1] == 0 and rec[j, r, 2] == 0 for j in range(kb1 - kb0))
+                continue
+            lo, hi = rows[i]
+            core = p.col_idx[lo:hi].astype(np.int64)
+            for j in range(kb1 - kb0):
+                k0 = (kb0 + j) * 64
+                first = lo + int(np.searchsorted(core, k0))
+                m = 0
+                for c in core[(core >= k0) & (core < k0 + 64)]:
+                    m |= 1 << int(c - k0)
+                got = (int(rec[j, r, 0]), int(rec[j, r, 1]) & 0xffffffff, int(rec[j, r, 2]) & 0xffffffff)
+                assert got == (first, m & 0xffffffff, m >> 32), (ti, r, j)
+            if fars[ti]:
+                a, b = p.row_ptr[i], p.row_ptr[i + 1]
+                far_cols = list(p.col_idx[a:lo]) + list(p.col_idx[hi:b])
+                m = 0
+                for c in far_cols:
+                    m |= 1 << fars[ti].index(int(c))
+                g = rec[kb1 - kb0, r]
+                assert (int(g[0]), int(g[1]) & 0xffffffff, int(g[2]) & 0xffffffff) == (a, m & 0xffffffff, m >> 32)
+    if name == "longformer_long_rows":
+        assert tiles[20, 2] == 1 and fars[20] == [0, 1]      # global-token columns gathered
     assert np.array_equal(h[h[12]:h[12] + 8 * len(segs)].reshape(-1, 8), segs)
     assert np.all(h[h[13]:h[13] + L * p.BH] == 0)                       # merge counters
     assert h[15] * 4 <= plan.numel() * 4
