@@ -14,6 +14,10 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each, ow
 struct bf16_t { uint16_t bits; };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+// Native 16-byte vectors: copies of these stay in registers (HIP's uint4 is a class type
+// whose copies can go through private memory).
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_v;
+typedef __attribute__((ext_vector_type(4))) int i32x4_v;
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -270,6 +270,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
       rec[0] = (int)first;
       rec[1] = (int)(m & 0xffffffffull);
       rec[2] = (int)(m >> 32);
+      rec[3] = 0;
     }
     if (nfar > 0) {  // the gathered block: slots are positions in the far list
       unsigned long long m = 0;
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
       rec[0] = (int)rs;
       rec[1] = (int)(m & 0xffffffffull);
       rec[2] = (int)(m >> 32);
+      rec[3] = (int)((lo - rs) | ((long long)(hi - lo) << 16));
     }
   }
 }
@@ -343,11 +345,11 @@ hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_
   const int n = p.n;
   const int BH = p.B * p.H;
   const long long cap = (long long)(bytes / sizeof(int));
+  const PlanSizes sz = plan_sizes(n, 0, 0, 0, p.d);
   const long long off_rows = kPlanHeaderWords;
-  const long long off_tiles = off_rows + 2ll * n;
+  const long long off_tiles = off_rows + sz.rows;
   const int ntiles = (n + kTileRows - 1) / kTileRows;
-  if (cap < off_tiles + (long long)(kTileInfo + kTileRows + kBoundsPerTile) * ntiles)
-    return hipErrorInvalidValue;
+  if (cap < off_tiles + sz.tiles) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col_idx,
                      n, (long long)p.nnz, pl + off_rows);
   hipLaunchKernelGGL(plan_segs_kernel, dim3(1), dim3(kScanThreads), 0, s, p.row_ptr, n,

@@ -16,7 +16,7 @@ constexpr float kDenseTile = 0.25f;     // tiles at least this dense run on matr
 constexpr int kFarMax = 1024;           // far entries a tile may hold and still be gathered
 constexpr int kMaxTileBlocks = 12;      // contiguous key blocks a matrix-core tile may span
 constexpr int kTileInfo = 8;            // words per tile
-constexpr int kBlkWords = 3;            // per row and block: first entry, key mask low, high
+constexpr int kBlkWords = 4;            // per row and block: first entry, key mask low, high, aux
 constexpr int kBoundsPerTile = (kMaxTileBlocks + 1) * kTileRows * kBlkWords;
 
 // header words
@@ -25,17 +25,21 @@ enum PlanHeader {
   kHBH, kHD, kHOffRows, kHOffTiles, kHOffSegs, kHOffCounters, kHOffScratch, kHWords
 };
 // After the tile records (kTileInfo words each) come the far-column lists (kTileRows ints per
-// tile) and the block records (kBoundsPerTile ints per tile, laid out [block][row][3]).
+// tile) and the block records (kBoundsPerTile ints per tile, laid out [block][row][4]).
 
 // Word counts of the parts, in layout order: header, rows (2 per row: first and one past
-// the last entry of the row's core range), tiles (kTileInfo per tile: first key block, one
+// the last entry of the row's core range; padded to a multiple of 4 words so that the
+// records below are 16-byte aligned), tiles (kTileInfo per tile: first key block, one
 // past the last key block, 1 if the tile runs on matrix cores, number of far columns, then
 // unused), far columns (64 per tile: the sorted distinct columns of the tile's entries
 // outside the rows' core ranges, when there are at most 64 of them), block records (for a
 // matrix-core tile, per key block j -- the contiguous ones, then the gathered far block --
 // and row r: the row's first entry in the block and a 64-bit mask of the block's key slots
-// the row holds; the row's entries in the block are its set bits in ascending order),
-// long-row
+// the row holds; the row's entries in the block are its set bits in ascending order; the
+// fourth word is 0 for a contiguous block and, for the gathered block, the number of the
+// row's entries before its core range plus 65536 times the length of the core range, so
+// that the entry of set bit k (counted from 0) is first + k, plus the core length once k
+// reaches that number), long-row
 // segments (8 per segment: row, begin, end, long-row index, segment index within the row,
 // segments of the row, 0, 0), merge counters (one per long row and head), scratch floats
 // (kSlot(d) per segment and head: partial row and, for the fused forward, max and sum),
@@ -50,7 +54,7 @@ __host__ __device__ inline PlanSizes plan_sizes(long long n, long long long_rows
                             long long d) {
   PlanSizes s;
   const long long tiles = (n + kTileRows - 1) / kTileRows;
-  s.rows = 2 * n;
+  s.rows = (2 * n + 3) / 4 * 4;
   s.tiles = (long long)(kTileInfo + kTileRows + kBoundsPerTile) * tiles;
   s.segs = 8 * segs;
   s.counters = long_rows * BH;

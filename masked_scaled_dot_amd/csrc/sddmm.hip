@@ -140,19 +140,134 @@ __global__ __launch_bounds__(kThreads) void sddmm_rows_kernel(Args a, int BH) {
 
 template <int D>
 struct TileSmem {
-  static constexpr int kKStride = D + 8;          // bf16 per K row (+16 B: conflict-free A reads)
-  static constexpr int kSStride = kTileRows + 1;  // fp32 per score row
+  static constexpr int kKStride = D + 8;          // bf16 per K row (+16 B: conflict-free reads)
   alignas(16) uint16_t k[2][kTileRows * kKStride];  // double-buffered K block
-  float s[kTileRows * kSStride];
-  TileMeta meta;
+  int far[kTileRows];                               // the gathered block's key rows
 };
+
+// Matrix-core tile: S = Q K^T per 16x16 tile, A = the wave's 16 queries (lane: query c16,
+// dims 32kc + 8g..), B = K^T (lane: key 16tt + c16, dims 32kc + 8g..); the accumulator holds
+// key 16tt + c16 of the wave's rows 4g + i. Each value is stored if its row holds the key: the
+// entry is the row's first entry in the block plus the number of the row's keys in lower
+// slots; absent keys get an offset past the end of the tile's score range, which the buffer
+// store drops. kAdd: a bias or key mask is added (values loaded one block ahead with K).
+template <int D, bool kAdd>
+__device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, int t, int row0,
+                           long long e_lo, long long e_hi) {
+  constexpr int KS = TileSmem<D>::kKStride;
+  constexpr int KC = D / 32;
+  constexpr int KCH = kTileRows * (D / 8) / kThreads;  // 16-byte K chunks per thread per block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  if (threadIdx.x < kTileRows)
+    sm.far[threadIdx.x] = clampi(tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))], 0, a.n - 1);
+  __syncthreads();
+  const int nbc = tv.kb_hi - tv.kb_lo;
+  const int nblk = tile_blocks(tv);
+  const int g = lane / 16, c16 = lane % 16;
+  const int b = t / a.H, h = t % a.H;
+
+  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * a.n * D;
+  const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * a.n * D;
+  const int my_q = min(row0 + wave * 16 + c16, a.n - 1);
+  bf16x8_v qa[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qa[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+
+  const __amdgpu_buffer_rsrc_t out = make_rsrc(a.scores + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
+  const int lr0 = wave * 16 + 4 * g;  // the lane's first accumulator row within the tile
+  const unsigned below16 = (1u << c16) - 1u, below32 = (0x10000u << c16) - 1u;
+
+  // next block's K rows, the lane's four row records and (kAdd) additive terms, loaded one
+  // block ahead; the last block is loaded again at the end (unused) so the loads are
+  // unconditional
+  u32x4_v kn[KCH];
+  i32x4_v rn[4];
+  float an[kAdd ? 16 : 1];
+  auto prefetch = [&](int jj) {
+    const bool gat = jj >= nbc;
+    const int k0 = (tv.kb_lo + jj) * kTileRows;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const int r = i / (D / 8);
+      const int kf = sm.far[r], kc = min(k0 + r, a.n - 1);
+      const int key = gat ? kf : kc;
+      kn[u] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rn[i] = tv.rec[jj * kTileRows + lr0 + i];
+    if constexpr (kAdd) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int kf = sm.far[16 * tt + c16], kc = min(k0 + 16 * tt + c16, a.n - 1);
+        const int key = gat ? kf : kc;
+        float km = 0.f;
+        if (a.key_mask)
+          km = a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * a.n + key];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(row0 + lr0 + i, a.n - 1);
+          an[4 * i + tt] = km + (a.bias ? a.bias[((size_t)h * a.n + row) * a.n + key] : 0.f);
+        }
+      }
+    }
+  };
+
+  prefetch(0);
+  for (int j = 0; j < nblk; ++j) {
+    uint16_t* kbuf = sm.k[j & 1];
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&kbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
+    }
+    i32x4_v rc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rc[i] = rn[i];
+    float ac[kAdd ? 16 : 1];
+#pragma unroll
+    for (int i = 0; i < (kAdd ? 16 : 1); ++i) ac[i] = an[i];
+    lds_barrier();                  // block j's K is visible to every wave
+    prefetch(min(j + 1, nblk - 1));  // in flight while block j is multiplied
+    f32x4_v acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      acc[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v kb = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kbuf[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], kb, acc[tt], 0, 0, 0);
+      }
+    }
+    const bool gathered = j >= nbc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned lo32 = (unsigned)rc[i].y, hi32 = (unsigned)rc[i].z;
+      const int base = rc[i].x - (int)e_lo;
+      const int nlo = __builtin_popcount(lo32);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const unsigned word = tt < 2 ? lo32 : hi32;
+        const bool bit = (word >> ((tt & 1) * 16 + c16)) & 1u;
+        int rank = __builtin_popcount(word & ((tt & 1) ? below32 : below16)) + (tt < 2 ? 0 : nlo);
+        if (gathered) rank += gathered_skip(rank, rc[i].w);
+        float s = acc[tt][i] * a.scale;
+        if constexpr (kAdd) s += ac[4 * i + tt];
+        const int off = bit ? (base + rank) * 4 : kOffNone;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), out, off, 0, 0);
+      }
+    }
+  }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
   __shared__ TileSmem<D> sm;
   const int* plan = a.plan;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
 
   const bool segs_ok = plan[kHValid] != 0;  // long-row segments were written
   // ---- long-row segments
@@ -175,10 +290,11 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const int* rows = plan + plan[kHOffRows];
   const TileView tv = tile_view(plan, tile);
-  const int kb_lo = tv.kb_lo, kb_hi = tv.kb_hi;
-  const bool dense = (sizeof(T) == 2) && tv.mfma && segs_ok;
+  long long e_lo, e_hi;
+  tile_entry_span(a.row_ptr, row0, a.n, a.nnz, e_lo, e_hi);
+  const bool dense =
+      (sizeof(T) == 2) && tv.mfma && segs_ok && (e_hi - e_lo) * 4 <= kMaxBufBytes;
 
   if (!dense) {
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
@@ -191,77 +307,9 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     }
     return;
   }
-
   if constexpr (sizeof(T) == 2) {
-    constexpr int KS = TileSmem<D>::kKStride, SS = TileSmem<D>::kSStride;
-    constexpr int KC = D / 32;
-    constexpr int KCH = kTileRows * (D / 8) / kThreads;  // 16-byte K chunks per thread per block
-    load_tile_meta(sm.meta, tv, a.row_ptr, rows, row0, a.n, a.nnz);
-    __syncthreads();
-    const int nbc = kb_hi - kb_lo;
-    const int nblk = tile_blocks(tv);
-
-    // the wave's 16 queries as the B operand of S^T (lane: query c16, dims 32kc + 8g..)
-    const int g = lane / 16, c16 = lane % 16;
-    const int my_q = min(row0 + wave * 16 + c16, a.n - 1);
-    const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * a.n * D;
-    const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * a.n * D;
-    bf16x8_v qb[KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
-    const int b = t / a.H, h = t % a.H;
-    float* st = a.scores + (size_t)t * a.nnz;
-
-    uint4 kn[KCH];  // next block's K rows, loaded one block ahead
-    auto prefetch = [&](int j) {
-      const bool gathered = j >= nbc;
-      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
-#pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        const int key = block_key(sm.meta, tv.nfar, gathered, k0, i / (D / 8), a.n);
-        kn[u] = *reinterpret_cast<const uint4*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
-      }
-    };
-
-    if (nblk > 0) prefetch(0);
-    for (int j = 0; j < nblk; ++j) {
-      const bool gathered = j >= nbc;
-      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
-      uint16_t* kbuf = sm.k[j & 1];
-#pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        *reinterpret_cast<uint4*>(&kbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
-      }
-      lds_barrier();                       // block j's K is visible to every wave
-      if (j + 1 < nblk) prefetch(j + 1);   // in flight while block j is multiplied
-      // S^T block for the wave's 16 queries; accumulator: query c16, keys 16tt + 4g + i.
-      // The score rows are private to the wave.
-      float* sw = sm.s + wave * 16 * SS;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const bf16x8_v av = __builtin_bit_cast(
-              bf16x8_v, *reinterpret_cast<const uint4*>(&kbuf[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kc], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sw[c16 * SS + 16 * tt + 4 * g + i] = acc[i];
-      }
-      // lane = key slot: store the score of each of the wave's rows that holds this key
-      const int key = gathered ? clampi(sm.meta.far[lane], 0, a.n - 1) : min(k0 + lane, a.n - 1);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wave * 16 + r;
-        bool present;
-        const int e = slot_entry(sm.meta, j, gathered, lr, lane, present);
-        if (present) st[e] = sw[r * SS + lane] * a.scale + additive(a, h, b, row0 + lr, key);
-      }
-    }
+    if (a.bias || a.key_mask) sddmm_tile<D, true>(a, sm, tv, t, row0, e_lo, e_hi);
+    else sddmm_tile<D, false>(a, sm, tv, t, row0, e_lo, e_hi);
   }
 }
 

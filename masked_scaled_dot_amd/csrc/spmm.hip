@@ -36,6 +36,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 typedef __attribute__((ext_vector_type(4))) short i16x4_v;
 typedef __attribute__((ext_vector_type(2))) float f32x2_v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v2;
+typedef __attribute__((ext_vector_type(8))) float f32x8_v;
 
 template <typename T, int D>
 struct Layout {
@@ -145,16 +146,141 @@ __global__ __launch_bounds__(kThreads) void spmm_rows_kernel(Args a, int BH) {
 template <int D>
 struct TileSmem {
   static constexpr int kVStride = D + 16;         // bf16 per V row: stride = 32 B mod 256 B
-  static constexpr int kWStride = kTileRows + 8;  // bf16 per weight row (+16 B)
+  static constexpr int kWStride = kTileRows + 4;  // fp32 per weight row: conflict-free 16-row reads
   alignas(16) uint16_t v[2][kTileRows * kVStride];  // double-buffered V block
-  alignas(16) uint16_t whi[kTileRows * kWStride];
-  alignas(16) uint16_t wlo[kTileRows * kWStride];
-  TileMeta meta;
+  alignas(16) float w[kTileRows * kWStride];        // the waves' weight rows of one block
+  i32x4_v rec[(kMaxTileBlocks + 1) * kTileRows];    // the tile's block records
+  int far[kTileRows];                               // the gathered block's key rows
+  int live[kTileRows];                              // 1: the tile writes this row's output
 };
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const f32x2_v v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v2));
+// Matrix-core tile: each wave accumulates O (16 rows x D) += W (16 x 64 keys) V (64 keys x D)
+// per key block with v_mfma_f32_16x16x32_bf16. The weights are loaded one row per load, one
+// key slot per lane (a slot the row does not hold gets an offset past the end of the tile's
+// weight range, which the buffer load reads as 0), written to the wave's rows in LDS as fp32,
+// and read back in the A-operand layout split into two bf16 planes (w = hi + lo, about 16
+// mantissa bits); V is staged row-major and read with the transposing LDS load.
+template <int D>
+__device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, int t, int row0,
+                          long long e_lo, long long e_hi) {
+  constexpr int VS = TileSmem<D>::kVStride, WS = TileSmem<D>::kWStride;
+  constexpr int OC = D / 16;
+  constexpr int VCH = kTileRows * (D / 8) / kThreads;  // 16-byte V chunks per thread per block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int nbc = tv.kb_hi - tv.kb_lo;
+  const int nblk = tile_blocks(tv);
+  {
+    // loads clamped to the tile's records (unconditional, so they are all in flight at once)
+    constexpr int kRecs = (kMaxTileBlocks + 1) * kTileRows;
+    const int last = max(nblk * kTileRows - 1, 0);
+    i32x4_v r[(kRecs + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int u = 0; u < (kRecs + kThreads - 1) / kThreads; ++u)
+      r[u] = tv.rec[min((int)threadIdx.x + u * kThreads, last)];
+#pragma unroll
+    for (int u = 0; u < (kRecs + kThreads - 1) / kThreads; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      if (i < kRecs) sm.rec[i] = r[u];
+    }
+  }
+  if (threadIdx.x < kTileRows) {
+    const int r = threadIdx.x, row = row0 + r;
+    sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, a.n - 1);
+    int live = 0;
+    if (row < a.n) {
+      long long rs, re;
+      row_bounds(a, row, rs, re);
+      live = re - rs <= kLongRow;  // longer rows are written by their segments
+    }
+    sm.live[r] = live;
+  }
+  __syncthreads();
+  const int g = lane / 16, c16 = lane % 16;
+  const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
+  const __amdgpu_buffer_rsrc_t wbuf = make_rsrc(a.w + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
+  const unsigned lane_bit_word = lane < 32 ? 1u : 2u;  // record word holding this lane's slot
+  const unsigned lane_bit = 1u << (lane & 31);
+
+  // next block's V rows and the wave's 16 weight rows (lane = key slot), loaded one block
+  // ahead; the last block is loaded again at the end (unused) so the loads are unconditional
+  u32x4_v vn[VCH];
+  float wn[16];
+  auto prefetch = [&](int jj) {
+    const bool gat = jj >= nbc;
+    const int k0 = (tv.kb_lo + jj) * kTileRows;
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const int r = i / (D / 8);
+      const int kf = sm.far[r], kc = min(k0 + r, a.n - 1);
+      const int key = gat ? kf : kc;
+      vn[u] = *reinterpret_cast<const u32x4_v*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const i32x4_v rc = sm.rec[jj * kTileRows + wave * 16 + r];
+      const unsigned lo32 = (unsigned)rc.y, hi32 = (unsigned)rc.z;
+      int rank = (int)__builtin_amdgcn_mbcnt_hi(hi32, __builtin_amdgcn_mbcnt_lo(lo32, 0u));
+      if (gat) rank += gathered_skip(rank, rc.w);
+      const bool bit = ((lane_bit_word == 1u ? lo32 : hi32) & lane_bit) != 0u;
+      const int off = bit ? (rc.x - (int)e_lo + rank) * 4 : kOffNone;
+      wn[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wbuf, off, 0, 0));
+    }
+  };
+
+  f32x4_v o[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  float* wrows = sm.w + wave * 16 * WS;
+  prefetch(0);
+  for (int j = 0; j < nblk; ++j) {
+    uint16_t* vb = sm.v[j & 1];
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&vb[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = vn[u];
+    }
+    // the wave's own weight rows: no other wave reads them
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wrows[r * WS + lane] = wn[r];
+    lds_barrier();                   // block j's V is visible to every wave
+    prefetch(min(j + 1, nblk - 1));  // in flight while block j is multiplied
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // A operand: row c16, key slots 32kk + 8g .. +8, as hi and lo bf16 planes
+      const f32x4_v w0 = *reinterpret_cast<const f32x4_v*>(&wrows[c16 * WS + 32 * kk + 8 * g]);
+      const f32x4_v w1 = *reinterpret_cast<const f32x4_v*>(&wrows[c16 * WS + 32 * kk + 8 * g + 4]);
+      const f32x8_v wv = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      const bf16x8_v ahi = __builtin_convertvector(wv, bf16x8_v);
+      const f32x8_v rest = wv - __builtin_convertvector(ahi, f32x8_v);
+      const bf16x8_v alo = __builtin_convertvector(rest, bf16x8_v);
+      // B operand: lane j of each 16-lane group addresses V[key 32kk + 8g + j/4 (+4)][16c +
+      // 4(j%4)]; the transposing read hands lane j the 4 keys of column 16c + j
+      const int vkey = 32 * kk + 8 * g + c16 / 4;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) {
+        const int vcol = 16 * c + 4 * (c16 % 4);
+        typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+        const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[vkey * VS + vcol]));
+        const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[(vkey + 4) * VS + vcol]));
+        const bf16x8_v bv = __builtin_bit_cast(
+            bf16x8_v, (__attribute__((ext_vector_type(8))) short){b0[0], b0[1], b0[2], b0[3],
+                                                                  b1[0], b1[1], b1[2], b1[3]});
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, o[c], 0, 0, 0);
+      }
+    }
+  }
+  // accumulator layout: lane holds column 16c + c16 of the wave's rows 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wave * 16 + 4 * g + i;
+    if (!sm.live[lr]) continue;
+    float* orow = a.out + ((size_t)t * a.n + row0 + lr) * D;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) orow[16 * c + c16] = o[c][i];
+  }
 }
 
 template <typename T, int D>
@@ -165,6 +291,7 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   const int lane = threadIdx.x % kWave;
   // long rows are split only if the plan holds their segments and scratch for this shape
   const bool split = plan[kHValid] != 0 && BH <= plan[kHBH] && D <= plan[kHD];
+
 
   // ---- long-row segments: partial rows, merged by the last segment of each row
   if ((int)blockIdx.x < kLongWGs) {
@@ -213,10 +340,10 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const int* rows = plan + plan[kHOffRows];
-  const TileView tv0 = tile_view(plan, tile);
-  const int kb_lo = tv0.kb_lo, kb_hi = tv0.kb_hi;
-  const bool dense = (sizeof(T) == 2) && tv0.mfma && split;
+  const TileView tv = tile_view(plan, tile);
+  long long e_lo, e_hi;
+  tile_entry_span(a.row_ptr, row0, a.n, a.nnz, e_lo, e_hi);
+  const bool dense = (sizeof(T) == 2) && tv.mfma && split && (e_hi - e_lo) * 4 <= kMaxBufBytes;
 
   if (!dense) {
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
@@ -229,104 +356,8 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
     }
     return;
   }
-
-  if constexpr (sizeof(T) == 2) {
-    constexpr int VS = TileSmem<D>::kVStride, WS = TileSmem<D>::kWStride;
-    constexpr int OC = D / 16;
-    constexpr int VCH = kTileRows * (D / 8) / kThreads;  // 16-byte V chunks per thread per block
-    const TileView tv = tile_view(plan, tile);
-    load_tile_meta(sm.meta, tv, a.row_ptr, rows, row0, a.n, a.nnz);
-    __syncthreads();
-    const int nbc = kb_hi - kb_lo;
-    const int nblk = tile_blocks(tv);
-    const int g = lane / 16, c16 = lane % 16;
-    const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
-    const float* wt = a.w + (size_t)t * a.nnz;
-
-    // next block's operands, loaded one block ahead: lane = key slot
-    float wn[16];
-    uint4 vn[VCH];
-    auto prefetch = [&](int j) {
-      const bool gathered = j >= nbc;
-      const int k0 = gathered ? 0 : (kb_lo + j) * kTileRows;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bool present;
-        const int e = slot_entry(sm.meta, j, gathered, wave * 16 + r, lane, present);
-        wn[r] = present ? wt[e] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < VCH; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        const int key = block_key(sm.meta, tv.nfar, gathered, k0, i / (D / 8), a.n);
-        vn[u] = *reinterpret_cast<const uint4*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
-      }
-    };
-
-    f32x4_v o[OC];
-#pragma unroll
-    for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    if (nblk > 0) prefetch(0);
-    for (int j = 0; j < nblk; ++j) {
-      uint16_t* vb = sm.v[j & 1];
-#pragma unroll
-      for (int u = 0; u < VCH; ++u) {
-        const int i = threadIdx.x + u * kThreads;
-        *reinterpret_cast<uint4*>(&vb[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = vn[u];
-      }
-      // the wave's 16 weight rows of block j, one key slot per lane (hi + lo bf16 planes;
-      // absent keys write 0); the rows are private to the wave
-      uint16_t* whi = sm.whi + wave * 16 * WS;
-      uint16_t* wlo = sm.wlo + wave * 16 * WS;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float w = wn[r];
-        const uint32_t hi = pack_bf16(w, 0.f) & 0xffffu;
-        const uint32_t lo = pack_bf16(w - __uint_as_float(hi << 16), 0.f) & 0xffffu;
-        whi[r * WS + lane] = (uint16_t)hi;
-        wlo[r * WS + lane] = (uint16_t)lo;
-      }
-      lds_barrier();                       // block j's V is visible to every wave
-      if (j + 1 < nblk) prefetch(j + 1);   // in flight while block j is multiplied
-      // O(16 rows x D) += W(16 x 64 keys) V(64 keys x D)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int wrow = c16 * WS + 32 * kk + 8 * g;
-        const bf16x8_v ahi = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&whi[wrow]));
-        const bf16x8_v alo = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(&wlo[wrow]));
-        // lane j of each 16-lane group addresses V[key 32kk + 8g + j/4 (+4)][16c + 4(j%4)];
-        // the transposing read hands lane j the 4 keys of column 16c + j
-        const int vkey = 32 * kk + 8 * g + c16 / 4;
-#pragma unroll
-        for (int c = 0; c < OC; ++c) {
-          const int vcol = 16 * c + 4 * (c16 % 4);
-          typedef __attribute__((address_space(3))) i16x4_v lds_v4;
-          const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[vkey * VS + vcol]));
-          const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[(vkey + 4) * VS + vcol]));
-          const bf16x8_v bv = __builtin_bit_cast(
-              bf16x8_v, (__attribute__((ext_vector_type(8))) short){b0[0], b0[1], b0[2], b0[3],
-                                                                    b1[0], b1[1], b1[2], b1[3]});
-          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, o[c], 0, 0, 0);
-          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, o[c], 0, 0, 0);
-        }
-      }
-    }
-    // accumulator layout: lane holds column 16c + c16 of rows 4g + i (of the wave's 16);
-    // rows handled by long-row segments are written by those
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = wave * 16 + 4 * g + i, row = row0 + lr;
-      if (row >= a.n) continue;
-      if (sm.meta.row_hi[lr] == sm.meta.row_lo[lr]) {
-        long long rs, re;
-        row_bounds(a, row, rs, re);
-        if (re - rs > kLongRow) continue;
-      }
-      float* orow = a.out + ((size_t)t * a.n + row) * D;
-#pragma unroll
-      for (int c = 0; c < OC; ++c) orow[16 * c + c16] = o[c][i];
-    }
-  }
+  if constexpr (sizeof(T) == 2) spmm_tile<D>(a, sm, tv, t, row0, e_lo, e_hi);
+  (void)lane;
 }
 
 template <typename T, int D>

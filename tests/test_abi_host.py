@@ -144,7 +144,8 @@ def test_plan_bytes_and_build_checks():
     assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(block=64, nnz=4))) == 0
     assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(n=0, nnz=0))) == 4 * 16
     assert _lib.raw("sa_plan_build")(ctypes.byref(p), None, 1 << 20, None) == sa.SA_ERR_NULL
-    minimal = 4 * (16 + 2 * 4096 + 4 * 64)        # header, row core ranges, tiles
+    # header, row core ranges, per tile: info, far columns, 13 x 64 block records of 4 words
+    minimal = 4 * (16 + 2 * 4096 + (8 + 64 + 13 * 64 * 4) * 64)
     assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE, minimal - 4, None) == sa.SA_ERR_WORKSPACE
 
 

@@ -328,12 +328,12 @@ def test_plan_build_matches_host(name):
     # block and the 64-bit mask of key slots present; the gathered block's slots are the
     # positions of the tile's far columns
     blk_base = h[11] + (8 + 64) * T
-    per_tile = 13 * 64 * 3
+    per_tile = 13 * 64 * 4
     for ti in range(T):
         if not tiles[ti, 2]:
             continue
         kb0, kb1 = tiles[ti, 0], tiles[ti, 1]
-        rec = h[blk_base + per_tile * ti: blk_base + per_tile * (ti + 1)].reshape(13, 64, 3)
+        rec = h[blk_base + per_tile * ti: blk_base + per_tile * (ti + 1)].reshape(13, 64, 4)
         for r in range(64):
             i = ti * 64 + r
             if i >= p.n or p.row_ptr[i + 1] - p.row_ptr[i] > 1024:
@@ -347,16 +347,17 @@ def test_plan_build_matches_host(name):
                 m = 0
                 for c in core[(core >= k0) & (core < k0 + 64)]:
                     m |= 1 << int(c - k0)
-                got = (int(rec[j, r, 0]), int(rec[j, r, 1]) & 0xffffffff, int(rec[j, r, 2]) & 0xffffffff)
-                assert got == (first, m & 0xffffffff, m >> 32), (ti, r, j)
+                got = tuple(int(x) & 0xffffffff for x in rec[j, r])
+                assert got == (first, m & 0xffffffff, m >> 32, 0), (ti, r, j)
             if fars[ti]:
                 a, b = p.row_ptr[i], p.row_ptr[i + 1]
                 far_cols = list(p.col_idx[a:lo]) + list(p.col_idx[hi:b])
                 m = 0
                 for c in far_cols:
                     m |= 1 << fars[ti].index(int(c))
-                g = rec[kb1 - kb0, r]
-                assert (int(g[0]), int(g[1]) & 0xffffffff, int(g[2]) & 0xffffffff) == (a, m & 0xffffffff, m >> 32)
+                got = tuple(int(x) & 0xffffffff for x in rec[kb1 - kb0, r])
+                aux = (lo - a) + 65536 * (hi - lo)
+                assert got == (a, m & 0xffffffff, m >> 32, aux), (ti, r)
     if name == "longformer_long_rows":
         assert tiles[20, 2] == 1 and fars[20] == [0, 1]      # global-token columns gathered
     assert np.array_equal(h[h[12]:h[12] + 8 * len(segs)].reshape(-1, 8), segs)
