@@ -17,9 +17,9 @@
 //  * sparse tiles and rows without a plan run the vector path: the wave is split into lane
 //    slots that each own one 16-byte column chunk of V and walk every slots-th entry;
 //  * rows longer than the plan's threshold are cut into segments handled by the first
-//    workgroups of the grid; each segment writes its partial row to the plan's scratch, and
-//    the last segment to finish (per-row counter, acquire/release at device scope) sums the
-//    partials in segment order, so the result does not depend on timing.
+//    workgroups of the grid; each segment writes its partial row to the plan's scratch with
+//    device-coherent stores and counts itself in on a per-row counter; the last segment to
+//    arrive sums the partials in segment order, so the result does not depend on timing.
 #include "common.h"
 #include "kernels.h"
 #include "plan_layout.h"
@@ -65,46 +65,64 @@ __device__ __forceinline__ void row_bounds(const Args& a, int row, long long& rs
 
 // Vector path: partial row over entries [e_begin, e_end) in the slot layout; after the
 // cross-slot sum every slot holds the full chunk (lane r of each slot: elements r*EPC..).
+// Entries go in chunks of kU * SLOTS: lane i loads the column and weight of the chunk's entry
+// i (coalesced, one chunk ahead), and slot s gathers the V rows of entries s, s + SLOTS, ...
+// after fetching their columns and weights from the loading lanes with ds_bpermute.
 template <typename T, int D>
 __device__ __forceinline__ void valu_segment(const Args& a, int t, long long e_begin, long long e_end,
                                              float (&acc)[Layout<T, D>::kEPC]) {
   using L = Layout<T, D>;
   constexpr int EPC = L::kEPC, LPR = L::kLPR, SLOTS = L::kSlots;
+  constexpr int U = (kWave / SLOTS) < 8 ? (kWave / SLOTS) : 8;  // entries per slot per chunk
+  constexpr int CH = U * SLOTS;                                  // entries per chunk (<= 64)
   const int lane = threadIdx.x % kWave;
   const int slot = lane / LPR, r = lane % LPR;
   const float* wt = a.w + (size_t)t * a.nnz;
   const T* vt = static_cast<const T*>(a.v) + (size_t)t * a.n * D;
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
-  constexpr int U = 4;  // entries per slot in flight
-  for (long long e0 = e_begin + slot; e0 < e_end; e0 += (long long)U * SLOTS) {
-    int j[U];
-    float w[U];
-    uint4 x[U];
+  if (e_begin >= e_end) goto reduce;
+  {
+    int cn;
+    float wn;
+    auto load = [&](long long e0) {
+      const long long e = e0 + (lane < CH ? lane : 0);
+      const bool ok = lane < CH && e < e_end;
+      const long long ec = ok ? e : e_begin;
+      cn = clampi(a.col_idx[ec], 0, a.n - 1);
+      wn = wt[ec];
+      wn = ok ? wn : 0.f;
+    };
+    load(e_begin);
+    for (long long e0 = e_begin; e0 < e_end; e0 += CH) {
+      const int cc = cn;
+      const float wc = wn;
+      load(e0 + CH < e_end ? e0 + CH : e0);  // next chunk (this one again past the end: unused)
+      u32x4_v x[U];
+      float w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long long e = e0 + (long long)u * SLOTS;
-      const bool ok = e < e_end;
-      j[u] = clampi(a.col_idx[ok ? e : e_begin], 0, a.n - 1);
-      w[u] = ok ? wt[e] : 0.f;
-    }
+      for (int u = 0; u < U; ++u) {
+        const int src = (u * SLOTS + slot) << 2;
+        const int j = __builtin_amdgcn_ds_bpermute(src, cc);
+        w[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(wc)));
+        x[u] = reinterpret_cast<const u32x4_v*>(vt + (size_t)j * D)[r];
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = reinterpret_cast<const uint4*>(vt + (size_t)j[u] * D)[r];
+      for (int u = 0; u < U; ++u) {
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t xw[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-      if constexpr (sizeof(T) == 2) {
+          for (int c = 0; c < 4; ++c) {
+            acc[2 * c] = fmaf(w[u], bf16lo(x[u][c]), acc[2 * c]);
+            acc[2 * c + 1] = fmaf(w[u], bf16hi(x[u][c]), acc[2 * c + 1]);
+          }
+        } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[2 * c] = fmaf(w[u], bf16lo(xw[c]), acc[2 * c]);
-          acc[2 * c + 1] = fmaf(w[u], bf16hi(xw[c]), acc[2 * c + 1]);
+          for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], __uint_as_float(x[u][c]), acc[c]);
         }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = fmaf(w[u], __uint_as_float(xw[c]), acc[c]);
       }
     }
   }
+reduce:
 #pragma unroll
   for (int m = LPR; m < kWave; m <<= 1) {
 #pragma unroll
@@ -311,25 +329,44 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
       float acc[L::kEPC];
       valu_segment<T, D>(a, t, it[1], it[2], acc);
       float* slot = scratch + ((size_t)sg * pBH + t) * slot_floats(pD);
-      store_chunk<T, D>(slot, acc);
-      // publish the partial; the last arriving segment of the row merges all of them
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      // Publish the partial with agent-scope atomic stores, which are written through to
+      // the memory level shared by all XCDs (so no L2 writeback is needed), wait until they
+      // have completed, then count the segment in; the last arriving segment of the row
+      // reads the partials with agent-scope atomic loads and sums them.
+      if (lane < L::kLPR) {
+#pragma unroll
+        for (int c = 0; c < L::kEPC; ++c)
+          __hip_atomic_store(slot + lane * L::kEPC + c, acc[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
       int prev = 0;
       if (lane == 0)
-        prev = __hip_atomic_fetch_add(&counters[(size_t)lr * pBH + t], 1, __ATOMIC_ACQ_REL,
+        prev = __hip_atomic_fetch_add(&counters[(size_t)lr * pBH + t], 1, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
       prev = __builtin_amdgcn_readfirstlane(prev);
       if (prev == ns - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         const int first = sg - sidx;
         float* orow = a.out + ((size_t)t * a.n + row) * D;
+        // eight partials in flight per lane; the summation order depends only on ns
         for (int c = lane; c < D; c += kWave) {
-          float s = 0.f;
-          for (int q = 0; q < ns; ++q)
-            s += __builtin_nontemporal_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c);
-          orow[c] = s;
+          float s8[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s8[u] = 0.f;
+          for (int q0 = 0; q0 < ns; q0 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int q = min(q0 + u, ns - 1);
+              const float x = __hip_atomic_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              s8[u] += q0 + u < ns ? x : 0.f;
+            }
+          }
+          orow[c] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
         }
-        if (lane == 0) counters[(size_t)lr * pBH + t] = 0;  // ready for the next call
+        if (lane == 0)  // ready for the next call
+          __hip_atomic_store(&counters[(size_t)lr * pBH + t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     return;
