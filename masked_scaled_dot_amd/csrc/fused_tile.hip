@@ -1,0 +1,551 @@
+// Fused forward over 64-query tiles on bf16 matrix cores, for three pattern kinds:
+//  * element CSR with a row plan (plan.hip): a tile walks the 64-key blocks spanned by its
+//    rows' core entries plus one gathered block of its far columns; which keys a row holds
+//    in a block is the 64-bit mask of the plan's block record, and absent keys score -inf;
+//    sparse tiles run the vector routine of fused_row.h per row, and long rows are cut into
+//    segments whose partial states are merged by the last segment to finish;
+//  * block CSR of 64x64 tiles: the block-row's stored blocks (each a dense 64x64 product,
+//    block-sparse attention in the gluon-nlp issue replies);
+//  * dense with additive pair bias [H, n, n] and key mask [B, 1|H, n] (flash-attention PR
+//    "support attentions in AlphaFold2": bias [1,H,Lq,Lk], key mask [B,1|H,1,Lk]).
+// The softmax is the running-max / running-sum form with one division at the end
+// (streaming-dataflow SDPA review on nubint.ai, "proposed method").
+//
+// A workgroup (4 waves) owns 64 queries of one head; wave w owns queries 16w..16w+15. For
+// every key block:
+//   1. the block's K and V rows (loaded into registers one block ahead) are stored
+//      row-major in a double-buffered LDS stage, behind one LDS-only barrier;
+//   2. each wave forms S^T = K Q^T for its 16 queries with v_mfma_f32_16x16x32_bf16
+//      (A = K rows from LDS, B = the wave's Q held in registers); the accumulator gives lane
+//      l query l%16 and keys 16t + 4(l/16) + {0..3};
+//   3. scale, bias and key mask are added, absent keys get -inf, the running max is updated
+//      (in-lane over 16 keys, then across the 4 lanes that share a query, lazily: only when
+//      the block max exceeds it by more than kSlack) and p = 2^(s*log2e - m) is formed;
+//   4. p packed to bf16 is, without any shuffle, the A operand of O += P V: the k-slots of a
+//      lane hold keys {4g..4g+3, 16+4g..16+4g+3} (g = l/16), and the B operand takes V at
+//      exactly those keys from the row-major stage with the transposing LDS read
+//      ds_read_b64_tr_b16 (lane j of a 16-lane group addresses V[key0 + j/4][dim0 + 4(j%4)]
+//      and receives V[key0 + m][dim0 + j], m = 0..3).
+// The output accumulator is fp32 (lane l: dim 16c + l%16, queries 4g..4g+3); rescaling by
+// the running-max ratio fetches each query's factor from the lane that owns the query.
+#include "common.h"
+#include "fused_row.h"
+#include "kernels.h"
+#include "plan_layout.h"
+#include "tile.h"
+
+#include <type_traits>
+
+namespace sa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(2))) float f32x2_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v2;
+typedef __attribute__((ext_vector_type(4))) short i16x4_v;
+typedef __attribute__((ext_vector_type(8))) short i16x8_v;
+
+constexpr int kThreads = 256;
+constexpr int kLongWGs = 256;   // workgroups that walk the long-row segments (CSR)
+constexpr float kSlack = 8.f;   // lazy running-max threshold, log2 units
+
+template <int D>
+struct FusedSmem {
+  static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
+  static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
+  alignas(16) uint16_t k[2][kTileRows * kKStride];
+  alignas(16) uint16_t v[2][kTileRows * kVStride];
+  int far[kTileRows];   // the gathered block's key rows (CSR)
+  int live[kTileRows];  // 1: the tile writes this query's output
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v2));
+}
+
+__device__ __forceinline__ float bperm(float x, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// Matrix-core tile of 64 queries [row0, row0 + 64) of head t.
+// Kind kFusedCsr: blocks are the plan tile's (tv); kFusedBsr: the stored blocks [bs, be) of
+// the block-row; kFusedDense: all key blocks. kBias / kMask: a bias / key mask is added;
+// kVec4: their rows are 16-byte aligned (n % 4 == 0) and loaded as float4 (contiguous blocks).
+template <int D, int K, bool kBias, bool kMask, bool kVec4>
+__device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView& tv, int t, int row0,
+                           long long bs, long long be) {
+  constexpr int KS = FusedSmem<D>::kKStride, VS = FusedSmem<D>::kVStride;
+  constexpr int KC = D / 32;                           // 32-wide k-chunks of the head dim
+  constexpr int OC = D / 16;                           // 16-wide output column tiles
+  constexpr int CH = kTileRows * (D / 8) / kThreads;   // 16-byte chunks per thread (K, and V)
+  constexpr bool kAdd = kBias || kMask;
+  const int n = a.n;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c16 = lane % 16;
+  const int b = t / a.H, h = t % a.H;
+  const int ntiles = (n + kTileRows - 1) / kTileRows;
+
+  int nbc = 0, nblk = 0;
+  if constexpr (K == kFusedCsr) {
+    nbc = tv.kb_hi - tv.kb_lo;
+    nblk = tile_blocks(tv);
+  } else if constexpr (K == kFusedBsr) {
+    nblk = (int)(be - bs);
+  } else {
+    nblk = ntiles;
+  }
+  if (threadIdx.x < kTileRows) {
+    const int r = threadIdx.x, row = row0 + r;
+    if constexpr (K == kFusedCsr) sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, n - 1);
+    int live = row < n;
+    if constexpr (K == kFusedCsr) {
+      if (live) {
+        long long rs = a.row_ptr[row], re = a.row_ptr[row + 1];
+        rs = rs < 0 ? 0 : (rs > a.nnz ? a.nnz : rs);
+        re = re < rs ? rs : (re > a.nnz ? a.nnz : re);
+        live = re - rs <= kLongRow;  // longer rows are written by their segments
+      }
+    }
+    sm.live[r] = live;
+  }
+  __syncthreads();
+
+  // the wave's 16 queries as the B operand of S^T = K Q^T (lane: query c16, dims 32kc + 8g..)
+  const int my_q = min(row0 + wave * 16 + c16, n - 1);
+  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * n * D;
+  const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * n * D;
+  const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * n * D;
+  bf16x8_v qb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+  const float* brow = a.bias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
+  const float* kmr = a.key_mask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
+  const float scale2 = a.scale * kLog2e;
+
+  // first key of block jj (contiguous kinds)
+  auto block_k0 = [&](int jj) -> int {
+    if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
+    else if constexpr (K == kFusedBsr) return clampi(a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows;
+    else return jj * kTileRows;
+  };
+
+  // A block's K and V rows, the lane's key mask (CSR) and raw additive terms, loaded into
+  // registers two blocks ahead (two stages, used alternately); past the last block the
+  // last block is loaded again (unused), so the loads are unconditional
+  struct Stage {
+    u32x4_v kn[CH], vn[CH];
+    unsigned mlo, mhi;
+    f32x4_v bn[kBias ? 4 : 1], mk[kMask ? 4 : 1];
+  };
+  auto prefetch = [&](Stage& st, int jj) {
+    const bool gat = (K == kFusedCsr) && jj >= nbc;
+    const int k0 = block_k0(jj);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const int r = i / (D / 8);
+      int key = min(k0 + r, n - 1);
+      if constexpr (K == kFusedCsr) {
+        const int kf = sm.far[r];
+        key = gat ? kf : key;
+      }
+      st.kn[u] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
+      st.vn[u] = *reinterpret_cast<const u32x4_v*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
+    }
+    if constexpr (K == kFusedCsr) {
+      const i32x4_v rc = tv.rec[jj * kTileRows + wave * 16 + c16];
+      st.mlo = (unsigned)rc.y;
+      st.mhi = (unsigned)rc.z;
+    }
+    if constexpr (kAdd) {
+      // keys 16tt + 4g + {0..3} of the block, loaded raw (summed after the barrier, so no
+      // wait here); keys past n are masked later, so their loads only need to stay in range
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (kVec4 && !gat) {
+          const int kk = min(k0 + 16 * tt + 4 * g, n - 4);
+          if constexpr (kBias) st.bn[tt] = *reinterpret_cast<const f32x4_v*>(brow + kk);
+          if constexpr (kMask) st.mk[tt] = *reinterpret_cast<const f32x4_v*>(kmr + kk);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int key = min(k0 + 16 * tt + 4 * g + i, n - 1);
+            if constexpr (K == kFusedCsr) {
+              const int kf = sm.far[16 * tt + 4 * g + i];
+              key = gat ? kf : key;
+            }
+            if constexpr (kBias) st.bn[tt][i] = brow[key];
+            if constexpr (kMask) st.mk[tt][i] = kmr[key];
+          }
+        }
+      }
+    }
+  };
+
+  float m2 = -INFINITY;  // running max of the lane's query, log2 units
+  float lsum = 0.f;      // partial running sum over this lane's keys
+  f32x4_v o[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  // One key block: stage st (block j) into LDS buffer j&1, then refill st with block j+2
+  // while block j is computed.
+  auto step = [&](Stage& st, int j) {
+    uint16_t* kb_s = sm.k[j & 1];
+    uint16_t* vb_s = sm.v[j & 1];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&kb_s[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = st.kn[u];
+      *reinterpret_cast<u32x4_v*>(&vb_s[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = st.vn[u];
+    }
+    const unsigned mlo = st.mlo, mhi = st.mhi;
+    f32x4_v ad[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      ad[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBias) ad[tt] += st.bn[tt];
+      if constexpr (kMask) ad[tt] += st.mk[tt];
+    }
+    const int k0 = block_k0(j);
+    lds_barrier();                       // block j is staged for every wave
+    prefetch(st, min(j + 2, nblk - 1));  // in flight while blocks j and j+1 are computed
+
+    // ---- S^T tiles: lane holds keys 16tt + 4g + i of query c16, in log2 units
+    float s[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v ka = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kb_s[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kc], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 16 * tt + 4 * g + i;
+        bool present;
+        if constexpr (K == kFusedCsr) present = (((tt < 2 ? mlo : mhi) >> (slot & 31)) & 1u) != 0u;
+        else present = k0 + slot < n;
+        float x = acc[i] * scale2;
+        if constexpr (kAdd) x = fmaf(ad[tt][i], kLog2e, x);
+        s[tt][i] = present ? x : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    // The running max moves only when the block max exceeds it by more than kSlack: p stays
+    // <= 2^kSlack, and the O rescale below is skipped for most blocks.
+    const float mn = (mx > m2 + kSlack) ? mx : m2;
+    float alpha = 1.f;
+    uint32_t pk[2][4];  // bf16 P: [32-key chunk][dword]
+    if (mn == -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pk[c][w] = 0u;
+    } else {
+      alpha = __builtin_amdgcn_exp2f(m2 - mn);
+      float ps = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[tt][i] = __builtin_amdgcn_exp2f(s[tt][i] - mn);
+          ps += p[tt][i];
+        }
+      lsum = fmaf(lsum, alpha, ps);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        pk[c][0] = pack_bf16(p[2 * c][0], p[2 * c][1]);
+        pk[c][1] = pack_bf16(p[2 * c][2], p[2 * c][3]);
+        pk[c][2] = pack_bf16(p[2 * c + 1][0], p[2 * c + 1][1]);
+        pk[c][3] = pack_bf16(p[2 * c + 1][2], p[2 * c + 1][3]);
+      }
+      m2 = mn;
+    }
+    // ---- rescale O rows when some query's max moved (query 4g+i is owned by lane 4g+i)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = bperm(alpha, 4 * g + i);
+#pragma unroll
+      for (int c = 0; c < OC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+    }
+    // ---- O += P V
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8_v pa = __builtin_bit_cast(bf16x8_v, (u32x4_v){pk[c2][0], pk[c2][1], pk[c2][2], pk[c2][3]});
+      const int key0 = 32 * c2 + 4 * g + c16 / 4;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) {
+        const int col = 16 * c + 4 * (c16 % 4);
+        typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+        const i16x4_v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[key0 * VS + col]));
+        const i16x4_v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[(key0 + 16) * VS + col]));
+        const bf16x8_v vb = __builtin_bit_cast(
+            bf16x8_v, (i16x8_v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+      }
+    }
+  };
+
+  Stage s0, s1;
+  if (nblk > 0) {
+    prefetch(s0, 0);
+    prefetch(s1, min(1, nblk - 1));
+  }
+  for (int j = 0; j < nblk; j += 2) {
+    step(s0, j);
+    if (j + 1 >= nblk) break;
+    step(s1, j + 1);
+  }
+
+  // ---- finish: total sum per query, divide, store O and lse
+  float ltot = lsum + shfl_xor(lsum, 16);
+  ltot += shfl_xor(ltot, 32);
+  const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltot;
+  {
+    const int lr = wave * 16 + c16;
+    if (a.lse && g == 0 && sm.live[lr])
+      a.lse[(size_t)t * n + row0 + lr] = (m2 == -INFINITY) ? -INFINITY : (m2 / kLog2e + logf(ltot));
+  }
+  float iv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) iv[i] = bperm(inv, 4 * g + i);
+  float* ot = a.out + (size_t)t * n * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wave * 16 + 4 * g + i;
+    if (!sm.live[lr]) continue;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) ot[(size_t)(row0 + lr) * D + 16 * c + c16] = o[c][i] * iv[i];
+  }
+}
+
+// Long-row segment of the CSR kind: partial state (acc, max, sum) to the plan's scratch with
+// agent-scope atomic stores, then the last segment of the row to arrive merges them in
+// segment order (the result does not depend on timing).
+template <typename T, int D>
+__device__ void fused_segments(const FusedArgs& a, int BH) {
+  using L = FusedLayout<T, D>;
+  const int* plan = a.plan;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int S = plan[kHSegs];
+  const int* segs = plan + plan[kHOffSegs];
+  int* counters = const_cast<int*>(plan) + plan[kHOffCounters];
+  float* scratch = reinterpret_cast<float*>(const_cast<int*>(plan) + plan[kHOffScratch]);
+  const int pBH = plan[kHBH], pD = plan[kHD];
+  const long long tasks = (long long)S * BH;
+  for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
+       task += (long long)kLongWGs * (kThreads / kWave)) {
+    const int sg = (int)(task % S), t = (int)(task / S);
+    const int* it = segs + 8 * sg;
+    const int row = it[0], lr = it[3], sidx = it[4], ns = it[5];
+    float M, Lsum, acc[L::kEPC];
+    fused_range<T, D, kFusedCsr>(a, t, row, 0, it[1], it[2], M, Lsum, acc);
+    float* slot = scratch + ((size_t)sg * pBH + t) * slot_floats(pD);
+    if (lane < L::kLPR) {
+#pragma unroll
+      for (int c = 0; c < L::kEPC; ++c)
+        __hip_atomic_store(slot + lane * L::kEPC + c, acc[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) {
+      __hip_atomic_store(slot + pD, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot + pD + 1, Lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);  // the partial is complete before the segment counts in
+    int prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&counters[(size_t)lr * pBH + t], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != ns - 1) continue;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int first = sg - sidx;
+    auto part = [&](int q, int c) {
+      return __hip_atomic_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float Mx = -INFINITY;
+    for (int q = 0; q < ns; ++q) Mx = fmaxf(Mx, part(q, pD));
+    float Lt = 0.f;
+    for (int q = 0; q < ns; ++q) {
+      const float mq = part(q, pD);
+      Lt += mq == -INFINITY ? 0.f : part(q, pD + 1) * exp_fast(mq - Mx);
+    }
+    const float inv = Mx == -INFINITY ? 0.f : 1.0f / Lt;
+    float* orow = a.out + ((size_t)t * a.n + row) * D;
+    for (int c = lane; c < D; c += kWave) {
+      float s8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s8[u] = 0.f;
+      for (int q0 = 0; q0 < ns; q0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = min(q0 + u, ns - 1);
+          const float mq = part(q, pD);
+          const float x = part(q, c);
+          const float f = (q0 + u < ns && mq != -INFINITY) ? exp_fast(mq - Mx) : 0.f;
+          s8[u] = fmaf(x, f, s8[u]);
+        }
+      }
+      orow[c] = (((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]))) * inv;
+    }
+    if (a.lse && lane == 0)
+      a.lse[(size_t)t * a.n + row] = Mx == -INFINITY ? -INFINITY : Mx + logf(Lt);
+    if (lane == 0)  // ready for the next call
+      __hip_atomic_store(&counters[(size_t)lr * pBH + t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Element CSR with a row plan: long-row segments in the first kLongWGs workgroups, then one
+// workgroup per (head, tile).
+struct NoSmem {};  // fp32 inputs never take the matrix-core tile
+
+// Occupancy floor for the matrix-core kernels: register allocation is capped so that this
+// many waves fit per SIMD (2 -> 256 registers, 3 -> 168).
+template <int D, bool kAdd>
+constexpr int kFusedWaves = (D == 128 || (D == 64 && kAdd)) ? 2 : 3;
+
+template <typename T, int D, bool kBias, bool kMask>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<D, kBias || kMask>)))
+void fused_plan_kernel(FusedArgs a, int BH) {
+  __shared__ std::conditional_t<sizeof(T) == 2, FusedSmem<D>, NoSmem> sm;
+  const int* plan = a.plan;
+  const bool segs_ok = plan[kHValid] != 0 && BH <= plan[kHBH] && D <= plan[kHD];
+  if ((int)blockIdx.x < kLongWGs) {
+    if (segs_ok) fused_segments<T, D>(a, BH);
+    return;
+  }
+  const int ntiles = plan[kHTiles];
+  const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
+  const int t = lb / ntiles, tile = lb % ntiles;
+  const int row0 = tile * kTileRows;
+  const TileView tv = tile_view(plan, tile);
+  if (sizeof(T) == 2 && tv.mfma && segs_ok) {
+    if constexpr (sizeof(T) == 2) fused_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, 0, 0);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  for (int r = wave; r < kTileRows; r += kThreads / kWave) {
+    const int row = row0 + r;
+    if (row >= a.n) break;
+    long long base, len;
+    fused_row_entries<kFusedCsr>(a, row, base, len);
+    if (segs_ok && len > kLongRow) continue;  // a segment task covers it
+    fused_row<T, D, kFusedCsr>(a, t, row);
+  }
+}
+
+// Block CSR and dense: one workgroup per (head, 64-query tile); workgroups of one head (one
+// bias slice) are adjacent in the XCD-aware order.
+template <int D, int K, bool kBias, bool kMask, bool kVec4>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<D, kBias || kMask>)))
+void fused_block_kernel(FusedArgs a) {
+  __shared__ FusedSmem<D> sm;
+  const int ntiles = (a.n + kTileRows - 1) / kTileRows;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int tile = lb % ntiles, hb = lb / ntiles;
+  const int h = hb / a.B, b = hb % a.B;
+  const int t = b * a.H + h;
+  long long bs = 0, be = 0;
+  if constexpr (K == kFusedBsr) {
+    bs = a.row_ptr[tile];
+    be = a.row_ptr[tile + 1];
+    bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
+    be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
+  }
+  const TileView tv{};
+  fused_tile<D, K, kBias, kMask, kVec4>(a, sm, tv, t, tile * kTileRows, bs, be);
+}
+
+template <typename T, int D>
+hipError_t launch_plan_t(const sa_problem& p, const FusedArgs& a, hipStream_t s) {
+  const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
+  const dim3 grid((unsigned)(kLongWGs + ntiles * p.B * p.H)), block(kThreads);
+  const int BH = p.B * p.H;
+  if constexpr (sizeof(T) == 4) {  // the vector path reads bias and key mask itself
+    hipLaunchKernelGGL((fused_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
+  } else if (p.bias) {
+    if (p.key_mask) hipLaunchKernelGGL((fused_plan_kernel<T, D, true, true>), grid, block, 0, s, a, BH);
+    else hipLaunchKernelGGL((fused_plan_kernel<T, D, true, false>), grid, block, 0, s, a, BH);
+  } else {
+    if (p.key_mask) hipLaunchKernelGGL((fused_plan_kernel<T, D, false, true>), grid, block, 0, s, a, BH);
+    else hipLaunchKernelGGL((fused_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int K>
+hipError_t launch_block_k(const sa_problem& p, const FusedArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(kThreads);
+  const bool v4 = (p.n & 3) == 0;
+  if (!p.bias && !p.key_mask) {
+    hipLaunchKernelGGL((fused_block_kernel<D, K, false, false, false>), grid, block, 0, s, a);
+  } else if (p.bias && p.key_mask) {
+    if (v4) hipLaunchKernelGGL((fused_block_kernel<D, K, true, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_block_kernel<D, K, true, true, false>), grid, block, 0, s, a);
+  } else if (p.bias) {
+    if (v4) hipLaunchKernelGGL((fused_block_kernel<D, K, true, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_block_kernel<D, K, true, false, false>), grid, block, 0, s, a);
+  } else {
+    if (v4) hipLaunchKernelGGL((fused_block_kernel<D, K, false, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_block_kernel<D, K, false, true, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_block_t(const sa_problem& p, const FusedArgs& a, hipStream_t s) {
+  const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
+  const dim3 grid((unsigned)(ntiles * p.B * p.H));
+  return p.row_ptr ? launch_block_k<D, kFusedBsr>(p, a, grid, s) : launch_block_k<D, kFusedDense>(p, a, grid, s);
+}
+
+}  // namespace
+
+bool fused_tile_supported(const sa_problem& p) {
+  if (p.row_ptr && p.block == 1) return p.plan != nullptr;  // plan-driven CSR (both dtypes)
+  return p.dtype == SA_BF16;                                  // block CSR and dense: bf16
+}
+
+hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
+                             float* out, float* lse, hipStream_t s) {
+  const FusedArgs a{q, k, v, p.row_ptr, p.col_idx, out, lse, p.bias, p.key_mask,
+                    static_cast<const int*>(p.plan), p.B, p.H, p.n, (long long)p.nnz,
+                    p.key_mask_heads, p.scale};
+  if (p.B == 0 || p.H == 0 || p.n == 0) return hipSuccess;
+  if (p.row_ptr && p.block == 1) {
+    const bool bf = p.dtype == SA_BF16;
+    switch (p.d) {
+      case 32: return bf ? launch_plan_t<bf16_t, 32>(p, a, s) : launch_plan_t<float, 32>(p, a, s);
+      case 64: return bf ? launch_plan_t<bf16_t, 64>(p, a, s) : launch_plan_t<float, 64>(p, a, s);
+      case 128: return bf ? launch_plan_t<bf16_t, 128>(p, a, s) : launch_plan_t<float, 128>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (p.d) {
+    case 32: return launch_block_t<32>(p, a, s);
+    case 64: return launch_block_t<64>(p, a, s);
+    case 128: return launch_block_t<128>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

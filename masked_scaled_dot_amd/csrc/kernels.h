@@ -14,9 +14,9 @@ hipError_t launch_spmm(const sa_problem& p, const float* weights, const void* v,
                        hipStream_t s);
 hipError_t launch_fused_valu(const sa_problem& p, const void* q, const void* k, const void* v,
                              float* out, float* lse, hipStream_t s);
-hipError_t launch_fused_mfma(const sa_problem& p, const void* q, const void* k, const void* v,
+hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
                              float* out, float* lse, hipStream_t s);
-bool fused_mfma_supported(const sa_problem& p);
+bool fused_tile_supported(const sa_problem& p);
 
 // CSR row plan and validation.
 size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);
