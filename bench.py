@@ -32,6 +32,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak (packed), TFLOP/s
 METRIC = "attended (i,j) pairs/sec and % of HBM/MFMA roofline, 1×MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_BYTES = 256 << 20          # size of the calibration copy (--profile copy)
 CSRC = os.path.join(ROOT, "masked_scaled_dot_amd", "csrc")
 
 
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
-    ap.add_argument("--profile", choices=["pipeline", "fused_csr", "fused_bsr", "fused_dense"],
+    ap.add_argument("--profile", choices=["pipeline", "fused_csr", "fused_bsr", "fused_dense", "copy"],
                     help="run only this kernel family (steps iterations after warmup) and exit; "
                          "for rocprofv3 runs")
     return ap.parse_args()
@@ -181,7 +182,13 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
 
 
 def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
+    """Average HIP-event time of one fused forward; an element CSR gets its row plan first
+    (built once per mask, as for the pipeline)."""
     prob, t, nnz = to_device(p, torch, sa, element=element)
+    if prob.c.row_ptr and prob.c.block == 1:
+        t["plan"] = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+        sa.sa_plan_build(prob, t["plan"])
+        prob.set_plan(t["plan"])
     out = torch.empty(p.BH, p.n, p.d, device="cuda:0")
     lse = torch.empty(p.BH, p.n, device="cuda:0")
     for _ in range(warmup):
@@ -237,8 +244,14 @@ def load_traffic(kernel, src_hash):
 
 
 def profile_only(args, torch, sa, gen):
-    """Run one kernel family alone so that a profiler sees only its launches."""
-    if args.profile == "pipeline":
+    """Run one kernel family alone so that a profiler sees only its launches. "copy" is a
+    plain device-to-device copy of 256 MiB, the reference for scaling the HBM byte counters."""
+    if args.profile == "copy":
+        src = torch.ones(COPY_BYTES // 4, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+    elif args.profile == "pipeline":
         p = gen.make(args.workload)
         prob, t, nnz = to_device(p, torch, sa)
         run_pipeline_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d, args.steps, args.warmup, None)
@@ -293,8 +306,9 @@ def main():
     total_bytes = sum(algo[k] for k in ("sddmm", "softmax", "spmm"))
     total_us = sum(kern_us[k] for k in ("sddmm", "softmax", "spmm"))
     dominant = max(("sddmm", "softmax", "spmm"), key=lambda k: kern_us[k])
-    src_of = {"sddmm": ["sddmm.hip", "common.h"], "softmax": ["softmax.hip", "common.h"],
-              "spmm": ["spmm.hip", "common.h"]}
+    src_of = {"sddmm": ["sddmm.hip", "common.h", "tile.h", "plan_layout.h"],
+              "softmax": ["softmax.hip", "common.h"],
+              "spmm": ["spmm.hip", "common.h", "tile.h", "plan_layout.h"]}
     dom_hash = source_hash(src_of[dominant])
     achieved = algo[dominant] / (kern_us[dominant] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
