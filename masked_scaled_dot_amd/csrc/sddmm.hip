@@ -5,17 +5,18 @@
 // key j, computed only at the mask's nonzeros; the scores keep the mask's CSR order.
 // Here: scores[t*nnz + e] = scale * q_i . k_j (+ bias[h,i,j]) (+ key_mask[b,hm,j]).
 //
-// With a row plan (plan.hip), a workgroup owns one 64-row tile of one head:
-//  * if the tile's core entries fill at least a quarter of their 64x64 key blocks and the
-//    inputs are bf16, each key block of the span is staged in LDS and every wave forms the
-//    16x64 score block of its rows with v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, Q held in
-//    registers); the CSR then selects the stored entries: the entries of a row that fall
-//    in one 64-key block are at most 64 consecutive entries, so one lane-parallel pass per
-//    row and block reads them from LDS and writes them contiguously;
+// With a row plan (plan.hip), the grid is cut into wave units of (head, 64-row tile, key
+// block):
+//  * if the tile's entries fill at least a quarter of their 64x64 key blocks and the inputs
+//    are bf16, unit j forms the 64x64 score block of key block j on the matrix cores
+//    (v_mfma_f32_16x16x32_bf16, operands loaded straight into registers) and stores the
+//    entries the CSR holds; the blocks of one tile are independent and run on different
+//    waves at the same time;
 //  * the rows' entries outside their core ranges (e.g. global-token columns) form one more,
 //    gathered key block: its keys are the tile's distinct far columns listed in the plan;
-//  * every row of a sparse tile takes the vector path: one entry per lane, the key row
-//    gathered with 16-byte loads and reduced in-lane with v_dot2_f32_bf16 (fma for fp32);
+//  * the rows of a sparse tile are spread over its units and take the vector path: one entry
+//    per lane, the key row gathered with 16-byte loads and reduced in-lane with
+//    v_dot2_f32_bf16 (fma for fp32);
 //  * rows longer than the plan's long-row threshold are skipped by the tiles and handled as
 //    segments by the first workgroups of the grid, spread over many waves.
 // Without a plan, one wave per (head, row) runs the vector path over the whole row.
@@ -23,6 +24,8 @@
 #include "kernels.h"
 #include "plan_layout.h"
 #include "tile.h"
+
+#include <type_traits>
 
 namespace sa {
 namespace {
@@ -138,53 +141,71 @@ __global__ __launch_bounds__(kThreads) void sddmm_rows_kernel(Args a, int BH) {
   valu_row<T, D>(a, t, row, rs, re);
 }
 
+// Matrix-core tile: a workgroup owns 64 rows of one head; wave w owns rows 16w..16w+15 and
+// walks the tile's key blocks (the contiguous span of its rows' core entries, then the gathered
+// block of its far columns). Per key block:
+//  1. the block's 64 K rows, loaded one block ahead with lane-contiguous 16-byte loads, are
+//     stored row-major in a double-buffered LDS stage behind one LDS-only barrier;
+//  2. S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the wave's 16 query
+//     rows held in registers): lane (g, c16) gets keys 16tt + 4g + {0..3} of query c16;
+//  3. the stored entries are compacted per row in the wave's own LDS area: a present key slot
+//     goes to position rank = number of the row's keys in lower slots (the block record's
+//     64-bit mask), so the row's entries of this block sit in their CSR order;
+//  4. the wave copies its rows out: the entries of one row in one block are consecutive in the
+//     scores array (first entry from the block record), so 16 lanes write 16 of them per store
+//     instruction, four rows at a time (in the gathered block a row's far entries before and
+//     after its core range are two runs, which only shifts the entry index).
+// Global accesses are lane-contiguous throughout: the cost of a vector memory instruction
+// grows with the number of separate segments its lanes touch.
 template <int D>
 struct TileSmem {
-  static constexpr int kKStride = D + 8;          // bf16 per K row (+16 B: conflict-free reads)
-  alignas(16) uint16_t k[2][kTileRows * kKStride];  // double-buffered K block
-  int far[kTileRows];                               // the gathered block's key rows
+  static constexpr int kKStride = D + 8;     // bf16 per K row (+16 B: conflict-free reads)
+  static constexpr int kOStride = kTileRows + 4;  // fp32 per compacted row
+  alignas(16) uint16_t k[2][kTileRows * kKStride];   // double-buffered K block
+  alignas(16) float out[kTileRows * kOStride];       // compacted scores of one block
+  int far[kTileRows];                                // the gathered block's key rows
+  i32x4_v run[kTileRows];                            // per row: first entry, count, aux
 };
 
-// Matrix-core tile: S = Q K^T per 16x16 tile, A = the wave's 16 queries (lane: query c16,
-// dims 32kc + 8g..), B = K^T (lane: key 16tt + c16, dims 32kc + 8g..); the accumulator holds
-// key 16tt + c16 of the wave's rows 4g + i. Each value is stored if its row holds the key: the
-// entry is the row's first entry in the block plus the number of the row's keys in lower
-// slots; absent keys get an offset past the end of the tile's score range, which the buffer
-// store drops. kAdd: a bias or key mask is added (values loaded one block ahead with K).
-template <int D, bool kAdd>
+template <int D, bool kBias, bool kMask>
 __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, int t, int row0,
                            long long e_lo, long long e_hi) {
-  constexpr int KS = TileSmem<D>::kKStride;
+  constexpr int KS = TileSmem<D>::kKStride, OS = TileSmem<D>::kOStride;
   constexpr int KC = D / 32;
   constexpr int KCH = kTileRows * (D / 8) / kThreads;  // 16-byte K chunks per thread per block
+  constexpr bool kAdd = kBias || kMask;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
+  const int n = a.n;
   if (threadIdx.x < kTileRows)
-    sm.far[threadIdx.x] = clampi(tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))], 0, a.n - 1);
+    sm.far[threadIdx.x] = clampi(tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))], 0, n - 1);
   __syncthreads();
   const int nbc = tv.kb_hi - tv.kb_lo;
   const int nblk = tile_blocks(tv);
   const int g = lane / 16, c16 = lane % 16;
   const int b = t / a.H, h = t % a.H;
+  const int lr = wave * 16 + c16;            // the lane's query row within the tile
+  const int my_q = min(row0 + lr, n - 1);
 
-  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * a.n * D;
-  const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * a.n * D;
-  const int my_q = min(row0 + wave * 16 + c16, a.n - 1);
-  bf16x8_v qa[KC];
+  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * n * D;
+  const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * n * D;
+  bf16x8_v qb[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
-    qa[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+    qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+  const float* brow = kBias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
+  const float* kmr = kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
 
-  const __amdgpu_buffer_rsrc_t out = make_rsrc(a.scores + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
-  const int lr0 = wave * 16 + 4 * g;  // the lane's first accumulator row within the tile
-  const unsigned below16 = (1u << c16) - 1u, below32 = (0x10000u << c16) - 1u;
+  const __amdgpu_buffer_rsrc_t outb = make_rsrc(a.scores + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
+  float* orow = sm.out + lr * OS;                    // this lane's compacted row (step 3)
+  const int cr = wave * 16 + g;                      // copy-out rows cr + 4i (step 4)
+  const int cp = c16;                                // copy-out part: entries 4cp..4cp+3
 
-  // next block's K rows, the lane's four row records and (kAdd) additive terms, loaded one
-  // block ahead; the last block is loaded again at the end (unused) so the loads are
-  // unconditional
+  // next block's K rows, the lane's record and (kAdd) additive terms, loaded one block ahead;
+  // the last block is loaded again at the end (unused) so the loads are unconditional
   u32x4_v kn[KCH];
-  i32x4_v rn[4];
-  float an[kAdd ? 16 : 1];
+  i32x4_v rn;
+  f32x4_v an[kAdd ? 4 : 1];
   auto prefetch = [&](int jj) {
     const bool gat = jj >= nbc;
     const int k0 = (tv.kb_lo + jj) * kTileRows;
@@ -192,30 +213,30 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     for (int u = 0; u < KCH; ++u) {
       const int i = threadIdx.x + u * kThreads;
       const int r = i / (D / 8);
-      const int kf = sm.far[r], kc = min(k0 + r, a.n - 1);
+      const int kf = sm.far[r], kc = min(k0 + r, n - 1);
       const int key = gat ? kf : kc;
       kn[u] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rn[i] = tv.rec[jj * kTileRows + lr0 + i];
+    rn = tv.rec[jj * kTileRows + lr];
     if constexpr (kAdd) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int kf = sm.far[16 * tt + c16], kc = min(k0 + 16 * tt + c16, a.n - 1);
-        const int key = gat ? kf : kc;
-        float km = 0.f;
-        if (a.key_mask)
-          km = a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * a.n + key];
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = min(row0 + lr0 + i, a.n - 1);
-          an[4 * i + tt] = km + (a.bias ? a.bias[((size_t)h * a.n + row) * a.n + key] : 0.f);
+          const int slot = 16 * tt + 4 * g + i;
+          const int kf = sm.far[slot], kc = min(k0 + slot, n - 1);
+          const int key = gat ? kf : kc;
+          an[tt][i] = (kBias ? brow[key] : 0.f) + (kMask ? kmr[key] : 0.f);
         }
-      }
     }
   };
 
   prefetch(0);
+  // Enter the loop with the first block's loads complete, as it loops back with the next
+  // block's loads complete: the wait the compiler places at the top of the loop then has
+  // nothing to wait for, instead of also waiting for the previous block's stores (vector
+  // loads and stores share one in-order counter).
+  vm_wait_all();
   for (int j = 0; j < nblk; ++j) {
     uint16_t* kbuf = sm.k[j & 1];
 #pragma unroll
@@ -223,49 +244,70 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
       const int i = threadIdx.x + u * kThreads;
       *reinterpret_cast<u32x4_v*>(&kbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
     }
-    i32x4_v rc[4];
+    const i32x4_v rc = rn;
+    f32x4_v ac[kAdd ? 4 : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rc[i] = rn[i];
-    float ac[kAdd ? 16 : 1];
-#pragma unroll
-    for (int i = 0; i < (kAdd ? 16 : 1); ++i) ac[i] = an[i];
-    lds_barrier();                  // block j's K is visible to every wave
-    prefetch(min(j + 1, nblk - 1));  // in flight while block j is multiplied
+    for (int i = 0; i < (kAdd ? 4 : 1); ++i) ac[i] = an[i];
+    lds_barrier();                   // block j's K is visible to every wave
+    prefetch(min(j + 1, nblk - 1));  // in flight while block j is computed and written
+    const bool gat = j >= nbc;
+
+    // step 2: all four 16x16 products, then (no branch in between) their use
     f32x4_v acc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       acc[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8_v kb = __builtin_bit_cast(
+        const bf16x8_v ka = __builtin_bit_cast(
             bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kbuf[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], kb, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kc], acc[tt], 0, 0, 0);
       }
     }
-    const bool gathered = j >= nbc;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // step 3: compact the lane's query row; absent slots write to the row's spare word
+    const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int s0 = 16 * tt + 4 * g;
+      const unsigned bits = (unsigned)(m >> s0) & 0xfu;
+      const int r0 = __builtin_popcountll(m & ((1ull << s0) - 1ull));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[tt][i] * a.scale;
+        if constexpr (kAdd) x += ac[tt][i];
+        const int pos = (bits >> i) & 1u ? r0 + __builtin_popcount(bits & ((1u << i) - 1u)) : kTileRows;
+        orow[pos] = x;
+      }
+    }
+    if (g == 0) sm.run[lr] = i32x4_v{rc.x - (int)e_lo, __builtin_popcountll(m), rc.w, 0};
+
+    // step 4: copy the wave's rows out (the wave reads only what it wrote: no barrier). Row
+    // cr + 4i goes to 16 lanes; lane cp stores its entries cp, cp + 16, cp + 32, cp + 48, so
+    // each store instruction writes 64 consecutive bytes of four rows. The sixteen stores are
+    // issued unconditionally (entries past the row's count get an offset the buffer drops):
+    // vector-memory stores and loads share one in-order counter, and a fixed store count lets
+    // the next block's K rows, loaded before these stores, be awaited without waiting for them.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const unsigned lo32 = (unsigned)rc[i].y, hi32 = (unsigned)rc[i].z;
-      const int base = rc[i].x - (int)e_lo;
-      const int nlo = __builtin_popcount(lo32);
+      const i32x4_v ru = sm.run[cr + 4 * i];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const unsigned word = tt < 2 ? lo32 : hi32;
-        const bool bit = (word >> ((tt & 1) * 16 + c16)) & 1u;
-        int rank = __builtin_popcount(word & ((tt & 1) ? below32 : below16)) + (tt < 2 ? 0 : nlo);
-        if (gathered) rank += gathered_skip(rank, rc[i].w);
-        float s = acc[tt][i] * a.scale;
-        if constexpr (kAdd) s += ac[4 * i + tt];
-        const int off = bit ? (base + rank) * 4 : kOffNone;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), out, off, 0, 0);
+      for (int c0 = 0; c0 < kTileRows; c0 += 16) {
+        const int k = c0 + cp;
+        const float v = sm.out[(cr + 4 * i) * OS + k];
+        const int e = ru.x + k + (gat ? gathered_skip(k, ru.z) : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outb, k < ru.y ? e * 4 : kOffNone, 0, 0);
       }
     }
   }
 }
 
-template <typename T, int D>
+// kBias / kMask select the matrix-core variant (the vector path reads both at run time); each
+// is its own kernel so that the plain variant keeps its register budget.
+template <typename T, int D, bool kBias, bool kMask>
 __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
-  __shared__ TileSmem<D> sm;
+  __shared__ std::conditional_t<sizeof(T) == 2, TileSmem<D>, char> sm;
   const int* plan = a.plan;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
@@ -285,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     return;
   }
 
-  // ---- tiles
+  // ---- tiles: one workgroup per (head, tile)
   const int ntiles = plan[kHTiles];
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
@@ -307,10 +349,7 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     }
     return;
   }
-  if constexpr (sizeof(T) == 2) {
-    if (a.bias || a.key_mask) sddmm_tile<D, true>(a, sm, tv, t, row0, e_lo, e_hi);
-    else sddmm_tile<D, false>(a, sm, tv, t, row0, e_lo, e_hi);
-  }
+  if constexpr (sizeof(T) == 2) sddmm_tile<D, kBias, kMask>(a, sm, tv, t, row0, e_lo, e_hi);
 }
 
 template <typename T, int D>
@@ -321,7 +360,17 @@ hipError_t launch_t(const sa_problem& p, const void* q, const void* k, float* sc
   if (p.plan) {
     const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
     const long long blocks = kLongWGs + ntiles * BH;
-    hipLaunchKernelGGL((sddmm_plan_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, BH);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if constexpr (sizeof(T) == 4)
+      hipLaunchKernelGGL((sddmm_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
+    else if (!p.bias && !p.key_mask)
+      hipLaunchKernelGGL((sddmm_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
+    else if (p.bias && p.key_mask)
+      hipLaunchKernelGGL((sddmm_plan_kernel<T, D, true, true>), grid, block, 0, s, a, BH);
+    else if (p.bias)
+      hipLaunchKernelGGL((sddmm_plan_kernel<T, D, true, false>), grid, block, 0, s, a, BH);
+    else
+      hipLaunchKernelGGL((sddmm_plan_kernel<T, D, false, true>), grid, block, 0, s, a, BH);
   } else {
     const long long units = (long long)BH * p.n;
     const int blocks = (int)((units + (kThreads / kWave) - 1) / (kThreads / kWave));

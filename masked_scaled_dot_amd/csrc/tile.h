@@ -16,6 +16,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// every vector-memory load and store of the wave has completed.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // The plan's view of one tile.
 struct TileView {
   int kb_lo, kb_hi, nfar;
