@@ -50,6 +50,8 @@ constexpr int kThreads = 256;
 constexpr int kLongWGs = 256;   // workgroups that walk the long-row segments (CSR)
 constexpr float kSlack = 8.f;   // lazy running-max threshold, log2 units
 
+constexpr int kBsrCached = 512;  // block-columns of a block-row kept in LDS (n <= 32768 fully)
+
 template <int D>
 struct FusedSmem {
   static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
@@ -58,6 +60,7 @@ struct FusedSmem {
   alignas(16) uint16_t v[2][kTileRows * kVStride];
   int far[kTileRows];   // the gathered block's key rows (CSR)
   int live[kTileRows];  // 1: the tile writes this query's output
+  int bcol[kBsrCached]; // the block-row's first stored block-columns (block CSR)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -97,6 +100,10 @@ __device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView&
   } else {
     nblk = ntiles;
   }
+  // block CSR: the block-columns in LDS, so that the addresses of a prefetch never wait for a
+  // load (vector loads complete in order: such a wait would also wait for the other stage)
+  if constexpr (K == kFusedBsr)
+    for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
   if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x, row = row0 + r;
     if constexpr (K == kFusedCsr) sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, n - 1);
@@ -129,7 +136,8 @@ __device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView&
   // first key of block jj (contiguous kinds)
   auto block_k0 = [&](int jj) -> int {
     if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
-    else if constexpr (K == kFusedBsr) return clampi(a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows;
+    else if constexpr (K == kFusedBsr)
+      return clampi(jj < kBsrCached ? sm.bcol[jj] : a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows;
     else return jj * kTileRows;
   };
 
@@ -306,6 +314,10 @@ __device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView&
   Stage s0, s1;
   if (nblk > 0) {
     prefetch(s0, 0);
+    // the first stage complete before the second is issued: the loop is entered, as it loops
+    // back, with one stage's loads outstanding behind the other's, so the wait at the top of
+    // the loop need not cover both
+    vm_wait_all();
     prefetch(s1, min(1, nblk - 1));
   }
   for (int j = 0; j < nblk; j += 2) {
@@ -453,6 +465,235 @@ void fused_plan_kernel(FusedArgs a, int BH) {
   }
 }
 
+// Block CSR and dense kinds, lean form. Same tile and MFMA layouts as fused_tile; differences:
+//  * K/V (and bias/key-mask) rows come through raw buffer loads whose per-block part of the
+//    offset is a scalar (the block's first key), so the loop spends no vector instructions on
+//    addresses, and rows past n read as zero;
+//  * one register stage, loaded one block ahead, and a loop body of one block: the only vector
+//    memory operations after a prefetch are the next prefetch's, so the wait for it at the top
+//    of the loop covers nothing else;
+//  * the softmax is branch-free: a row that has seen no finite score uses 0 as its reference
+//    maximum (exp2(-inf) = 0 keeps its sums at zero), and keys past n are masked only in the
+//    ragged last block (a uniform test).
+template <int D, int K, bool kBias, bool kMask, bool kVec4>
+__device__ void fused_block_tile(const FusedArgs& a, FusedSmem<D>& sm, int t, int row0, long long bs,
+                                 long long be) {
+  constexpr int KS = FusedSmem<D>::kKStride, VS = FusedSmem<D>::kVStride;
+  constexpr int KC = D / 32;
+  constexpr int OC = D / 16;
+  constexpr int CH = kTileRows * (D / 8) / kThreads;  // 16-byte chunks per thread (K, and V)
+  constexpr bool kAdd = kBias || kMask;
+  const int n = a.n;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c16 = lane % 16;
+  const int b = t / a.H, h = t % a.H;
+  const int ntiles = (n + kTileRows - 1) / kTileRows;
+  const int nblk = K == kFusedBsr ? (int)(be - bs) : ntiles;
+  if constexpr (K == kFusedBsr)
+    for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
+  __syncthreads();
+
+  const int my_q = min(row0 + wave * 16 + c16, n - 1);
+  const size_t head = (size_t)t * n * D;
+  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + head;
+  bf16x8_v qb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
+  const long long kv_bytes = (long long)n * D * 2;
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + head, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + head, kv_bytes);
+  // the bias buffer spans the head's [n, n] slice (uniform); the lane's row is in the offset
+  const __amdgpu_buffer_rsrc_t bres = make_rsrc(kBias ? a.bias + (size_t)h * n * n : a.out, kBias ? (long long)n * n * 4 : 0);
+  const int brow_off = my_q * n * 4;
+  const __amdgpu_buffer_rsrc_t mres = make_rsrc(
+      kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : a.out, kMask ? (long long)n * 4 : 0);
+  const float scale2 = a.scale * kLog2e;
+
+  auto block_k0 = [&](int jj) -> int {
+    if constexpr (K == kFusedBsr)
+      return __builtin_amdgcn_readfirstlane(
+          clampi(jj < kBsrCached ? sm.bcol[jj] : a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows);
+    else return jj * kTileRows;
+  };
+  // lane-constant parts of the offsets: chunk u of the thread is row i / (D/8), part i % (D/8)
+  int kvoff[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    kvoff[u] = ((i / (D / 8)) * D + (i % (D / 8)) * 8) * 2;
+  }
+
+  u32x4_v kn[CH], vn[CH];
+  f32x4_v bn[kBias ? 4 : 1], mk[kMask ? 4 : 1];
+  auto prefetch = [&](int jj) {
+    const int k0 = block_k0(jj);
+    const int kvs = k0 * D * 2;  // scalar part of the K/V offsets
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      kn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(kres, kvoff[u], kvs, 0));
+      vn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(vres, kvoff[u], kvs, 0));
+    }
+    if constexpr (kAdd) {
+      // keys 16tt + 4g + {0..3}: 16 consecutive bytes of the bias row and of the key mask
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int off = (16 * tt + 4 * g) * 4;
+        if constexpr (kVec4) {
+          if constexpr (kBias) bn[tt] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(bres, brow_off + off, k0 * 4, 0));
+          if constexpr (kMask) mk[tt] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(mres, off, k0 * 4, 0));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (kBias) bn[tt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, brow_off + off + 4 * i, k0 * 4, 0));
+            if constexpr (kMask) mk[tt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mres, off + 4 * i, k0 * 4, 0));
+          }
+        }
+      }
+    }
+  };
+
+  float m2 = -INFINITY;  // running max of the lane's query, log2 units
+  float lsum = 0.f;      // partial running sum over this lane's keys
+  f32x4_v o[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) prefetch(0);
+  vm_wait_all();
+  for (int j = 0; j < nblk; ++j) {
+    uint16_t* kb_s = sm.k[j & 1];
+    uint16_t* vb_s = sm.v[j & 1];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&kb_s[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
+      *reinterpret_cast<u32x4_v*>(&vb_s[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = vn[u];
+    }
+    f32x4_v ad[kAdd ? 4 : 1];
+    if constexpr (kAdd) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        ad[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBias) ad[tt] += bn[tt];
+        if constexpr (kMask) ad[tt] += mk[tt];
+      }
+    }
+    const int lim = n - block_k0(j);       // keys of this block below n
+    lds_barrier();                         // block j is staged for every wave
+    prefetch(min(j + 1, nblk - 1));        // in flight while block j is computed
+
+    // S^T = K Q^T: lane holds keys 16tt + 4g + i of query c16
+    f32x4_v acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      acc[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v ka = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kb_s[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kc], acc[tt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float sc[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = acc[tt][i] * scale2;
+        if constexpr (kAdd) x = fmaf(ad[tt][i], kLog2e, x);
+        sc[tt][i] = x;
+      }
+    if (lim < kTileRows) {  // ragged last block: keys at or past n score -inf
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tt][i] = 16 * tt + 4 * g + i < lim ? sc[tt][i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[2][0], sc[2][1]), fmaxf(sc[2][2], sc[2][3])),
+                         fmaxf(fmaxf(sc[3][0], sc[3][1]), fmaxf(sc[3][2], sc[3][3]))));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    // The running max moves only when the block max exceeds it by more than kSlack: p stays
+    // <= 2^kSlack, and the O rescale below is skipped for most blocks.
+    const float mn = (mx > m2 + kSlack) ? mx : m2;
+    const float ref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - ref);  // 0 while nothing is accumulated
+    float ps = 0.f;
+    uint32_t pk[2][4];  // bf16 P: [32-key chunk][dword]
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(sc[2 * c][i] - ref);
+        p[4 + i] = __builtin_amdgcn_exp2f(sc[2 * c + 1][i] - ref);
+      }
+      ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pk[c][0] = pack_bf16(p[0], p[1]);
+      pk[c][1] = pack_bf16(p[2], p[3]);
+      pk[c][2] = pack_bf16(p[4], p[5]);
+      pk[c][3] = pack_bf16(p[6], p[7]);
+    }
+    lsum = fmaf(lsum, alpha, ps);
+    m2 = mn;
+    // rescale O rows when some query's max moved (query 4g+i is owned by lane 4g+i)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = bperm(alpha, 4 * g + i);
+#pragma unroll
+      for (int c = 0; c < OC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+    }
+    // the V reads below stay after the branch: their LDS latency separates a rescale's writes
+    // of O from the products that accumulate into it
+    __builtin_amdgcn_sched_barrier(0);
+    // O += P V
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8_v pa = __builtin_bit_cast(bf16x8_v, (u32x4_v){pk[c2][0], pk[c2][1], pk[c2][2], pk[c2][3]});
+      const int key0 = 32 * c2 + 4 * g + c16 / 4;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) {
+        const int col = 16 * c + 4 * (c16 % 4);
+        typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+        const i16x4_v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[key0 * VS + col]));
+        const i16x4_v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[(key0 + 16) * VS + col]));
+        const bf16x8_v vb = __builtin_bit_cast(
+            bf16x8_v, (i16x8_v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // finish: total sum per query, divide, store O and lse
+  float ltot = lsum + shfl_xor(lsum, 16);
+  ltot += shfl_xor(ltot, 32);
+  const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltot;
+  const int lr = wave * 16 + c16;
+  if (a.lse && g == 0 && row0 + lr < n)
+    a.lse[(size_t)t * n + row0 + lr] = (m2 == -INFINITY) ? -INFINITY : (m2 / kLog2e + logf(ltot));
+  float iv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) iv[i] = bperm(inv, 4 * g + i);
+  float* ot = a.out + (size_t)t * n * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + wave * 16 + 4 * g + i;
+    if (r >= n) continue;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) ot[(size_t)r * D + 16 * c + c16] = o[c][i] * iv[i];
+  }
+}
+
 // Block CSR and dense: one workgroup per (head, 64-query tile); workgroups of one head (one
 // bias slice) are adjacent in the XCD-aware order.
 template <int D, int K, bool kBias, bool kMask, bool kVec4>
@@ -471,8 +712,7 @@ void fused_block_kernel(FusedArgs a) {
     bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
     be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
   }
-  const TileView tv{};
-  fused_tile<D, K, kBias, kMask, kVec4>(a, sm, tv, t, tile * kTileRows, bs, be);
+  fused_block_tile<D, K, kBias, kMask, kVec4>(a, sm, t, tile * kTileRows, bs, be);
 }
 
 template <typename T, int D>
@@ -522,7 +762,10 @@ hipError_t launch_block_t(const sa_problem& p, const FusedArgs& a, hipStream_t s
 
 bool fused_tile_supported(const sa_problem& p) {
   if (p.row_ptr && p.block == 1) return p.plan != nullptr;  // plan-driven CSR (both dtypes)
-  return p.dtype == SA_BF16;                                  // block CSR and dense: bf16
+  // block CSR and dense: bf16, with every buffer the tile addresses within 32-bit offsets
+  const long long kv = (long long)p.n * p.d * 2;
+  const long long bias = p.bias ? (long long)p.n * p.n * 4 : 0;
+  return p.dtype == SA_BF16 && kv <= kMaxBufBytes && bias <= kMaxBufBytes;
 }
 
 hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
