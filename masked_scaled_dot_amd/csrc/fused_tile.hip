@@ -63,6 +63,21 @@ struct FusedSmem {
   int bcol[kBsrCached]; // the block-row's first stored block-columns (block CSR)
 };
 
+// LDS of the block-CSR / dense tile: one K/V stage (a second barrier per block guards its
+// reuse), so that four workgroups fit on a compute unit and more loads are in flight.
+template <int D>
+struct FusedSmem1 {
+  static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
+  static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
+  alignas(16) uint16_t k[1][kTileRows * kKStride];
+  alignas(16) uint16_t v[1][kTileRows * kVStride];
+  int bcol[kBsrCached];
+};
+
+// Waves per SIMD the block kernels are compiled for (caps the registers at 512 / waves).
+template <int D, int K, bool kAdd>
+constexpr int kBlockWaves = (D == 32 || (!kAdd && !(D == 128 && K == kFusedDense))) ? 4 : 3;
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2_v v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v2));
@@ -471,14 +486,14 @@ void fused_plan_kernel(FusedArgs a, int BH) {
 //    addresses, and rows past n read as zero;
 //  * one register stage, loaded one block ahead, and a loop body of one block: the only vector
 //    memory operations after a prefetch are the next prefetch's, so the wait for it at the top
-//    of the loop covers nothing else;
+//    of the loop covers nothing else; one LDS stage, for occupancy (four workgroups per CU);
 //  * the softmax is branch-free: a row that has seen no finite score uses 0 as its reference
 //    maximum (exp2(-inf) = 0 keeps its sums at zero), and keys past n are masked only in the
 //    ragged last block (a uniform test).
 template <int D, int K, bool kBias, bool kMask, bool kVec4>
-__device__ void fused_block_tile(const FusedArgs& a, FusedSmem<D>& sm, int t, int row0, long long bs,
+__device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, int row0, long long bs,
                                  long long be) {
-  constexpr int KS = FusedSmem<D>::kKStride, VS = FusedSmem<D>::kVStride;
+  constexpr int KS = FusedSmem1<D>::kKStride, VS = FusedSmem1<D>::kVStride;
   constexpr int KC = D / 32;
   constexpr int OC = D / 16;
   constexpr int CH = kTileRows * (D / 8) / kThreads;  // 16-byte chunks per thread (K, and V)
@@ -563,8 +578,9 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem<D>& sm, int t, in
   if (nblk > 0) prefetch(0);
   vm_wait_all();
   for (int j = 0; j < nblk; ++j) {
-    uint16_t* kb_s = sm.k[j & 1];
-    uint16_t* vb_s = sm.v[j & 1];
+    uint16_t* kb_s = sm.k[0];
+    uint16_t* vb_s = sm.v[0];
+    if (j > 0) lds_barrier();  // every wave is done with block j-1
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int i = threadIdx.x + u * kThreads;
@@ -697,9 +713,9 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem<D>& sm, int t, in
 // Block CSR and dense: one workgroup per (head, 64-query tile); workgroups of one head (one
 // bias slice) are adjacent in the XCD-aware order.
 template <int D, int K, bool kBias, bool kMask, bool kVec4>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<D, kBias || kMask>)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBlockWaves<D, K, kBias || kMask>)))
 void fused_block_kernel(FusedArgs a) {
-  __shared__ FusedSmem<D> sm;
+  __shared__ FusedSmem1<D> sm;
   const int ntiles = (a.n + kTileRows - 1) / kTileRows;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int tile = lb % ntiles, hb = lb / ntiles;
