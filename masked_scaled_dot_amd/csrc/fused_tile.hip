@@ -340,6 +340,7 @@ __device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView&
     if (j + 1 >= nblk) break;
     step(s1, j + 1);
   }
+  mfma_drain();
 
   // ---- finish: total sum per query, divide, store O and lse
   float ltot = lsum + shfl_xor(lsum, 16);
@@ -688,7 +689,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
+  mfma_drain();
 
   // finish: total sum per query, divide, store O and lse
   float ltot = lsum + shfl_xor(lsum, 16);

@@ -290,6 +290,7 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
       }
     }
   }
+  mfma_drain();
   // accumulator layout: lane holds column 16c + c16 of the wave's rows 4g + i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -20,6 +20,16 @@ __device__ __forceinline__ void lds_barrier() {
 // every vector-memory load and store of the wave has completed.
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Wait states after the last matrix-core product of a loop, before code that reads its
+// results behind a branch: the compiler counts the write-to-read distance of a product within
+// straight-line code but has been seen to miss it across a short branch path, so such reads
+// get 24 wait states here, more than a 16x16x32 bf16 product needs.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The plan's view of one tile.
 struct TileView {
   int kb_lo, kb_hi, nfar;
