@@ -173,11 +173,10 @@ struct TileSmem {
 };
 
 // Matrix-core tile: each wave accumulates O (16 rows x D) += W (16 x 64 keys) V (64 keys x D)
-// per key block with v_mfma_f32_16x16x32_bf16. The weights are loaded one row per load, one
-// key slot per lane (a slot the row does not hold gets an offset past the end of the tile's
-// weight range, which the buffer load reads as 0), written to the wave's rows in LDS as fp32,
-// and read back in the A-operand layout split into two bf16 planes (w = hi + lo, about 16
-// mantissa bits); V is staged row-major and read with the transposing LDS load.
+// per key block with v_mfma_f32_16x16x32_bf16. The weights are loaded four key slots per lane,
+// sixteen lanes per row (a slot the row does not hold reads 0), written to the wave's rows in
+// LDS as fp32, and read back in the A-operand layout split into two bf16 planes (w = hi + lo,
+// about 16 mantissa bits); V is staged row-major and read with the transposing LDS load.
 template <int D>
 __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, int t, int row0,
                           long long e_lo, long long e_hi) {
@@ -217,13 +216,15 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
   const int g = lane / 16, c16 = lane % 16;
   const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
   const __amdgpu_buffer_rsrc_t wbuf = make_rsrc(a.w + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
-  const unsigned lane_bit_word = lane < 32 ? 1u : 2u;  // record word holding this lane's slot
-  const unsigned lane_bit = 1u << (lane & 31);
 
   // next block's V rows and the wave's 16 weight rows (lane = key slot), loaded one block
   // ahead; the last block is loaded again at the end (unused) so the loads are unconditional
   u32x4_v vn[VCH];
-  float wn[16];
+  // the wave's 16 weight rows of a block: lane (q, p) takes slots 4p..4p+3 of rows 4i + q;
+  // when the row holds all four, their entries are consecutive (one 16-byte load), otherwise
+  // each present slot is loaded alone and absent ones read 0
+  const int wq_row = lane / 16, wq_part = lane % 16;
+  f32x4_v wn[4];
   auto prefetch = [&](int jj) {
     const bool gat = jj >= nbc;
     const int k0 = (tv.kb_lo + jj) * kTileRows;
@@ -235,15 +236,39 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
       const int key = gat ? kf : kc;
       vn[u] = *reinterpret_cast<const u32x4_v*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
     }
+    int first[4], r0s[4], auxs[4];
+    unsigned slow[4];
+    bool any_slow = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const i32x4_v rc = sm.rec[jj * kTileRows + wave * 16 + r];
-      const unsigned lo32 = (unsigned)rc.y, hi32 = (unsigned)rc.z;
-      int rank = (int)__builtin_amdgcn_mbcnt_hi(hi32, __builtin_amdgcn_mbcnt_lo(lo32, 0u));
-      if (gat) rank += gathered_skip(rank, rc.w);
-      const bool bit = ((lane_bit_word == 1u ? lo32 : hi32) & lane_bit) != 0u;
-      const int off = bit ? (rc.x - (int)e_lo + rank) * 4 : kOffNone;
-      wn[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wbuf, off, 0, 0));
+    for (int i = 0; i < 4; ++i) {
+      const i32x4_v rc = sm.rec[jj * kTileRows + wave * 16 + 4 * i + wq_row];
+      const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+      const int s0 = 4 * wq_part;
+      const unsigned bits = (unsigned)(m >> s0) & 0xfu;
+      const int r0 = __builtin_popcountll(m & ((1ull << s0) - 1ull));
+      const int nb = rc.w & 0xffff;
+      // the gathered block lists the row's far entries before its core range first: four
+      // slots are consecutive entries unless that boundary falls inside them
+      const bool fast = bits == 0xfu && (!gat || r0 >= nb || r0 + 3 < nb);
+      first[i] = rc.x - (int)e_lo;
+      r0s[i] = r0;
+      auxs[i] = rc.w;
+      slow[i] = fast ? 0u : bits;
+      any_slow |= !fast && bits != 0u;
+      const int e0 = first[i] + r0 + (gat ? gathered_skip(r0, rc.w) : 0);
+      wn[i] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(wbuf, fast ? e0 * 4 : kOffNone, 0, 0));
+    }
+    if (__builtin_amdgcn_ballot_w64(any_slow) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int rank = r0s[i] + __builtin_popcount(slow[i] & ((1u << c) - 1u));
+          const int e = first[i] + rank + (gat ? gathered_skip(rank, auxs[i]) : 0);
+          const float x = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(wbuf, (slow[i] >> c) & 1u ? e * 4 : kOffNone, 0, 0));
+          if (slow[i] != 0u) wn[i][c] = x;
+        }
     }
   };
 
@@ -261,7 +286,7 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
     }
     // the wave's own weight rows: no other wave reads them
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wrows[r * WS + lane] = wn[r];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_v*>(&wrows[(4 * i + wq_row) * WS + 4 * wq_part]) = wn[i];
     lds_barrier();                   // block j's V is visible to every wave
     prefetch(min(j + 1, nblk - 1));  // in flight while block j is multiplied
 #pragma unroll
