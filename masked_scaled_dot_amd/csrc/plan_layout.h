@@ -15,6 +15,7 @@ constexpr int kSeg = 256;               // entries per long-row segment
 constexpr float kDenseTile = 0.25f;     // tiles at least this dense run on matrix cores
 constexpr int kFarMax = 1024;           // far entries a tile may hold and still be gathered
 constexpr int kMaxTileBlocks = 12;      // contiguous key blocks a matrix-core tile may span
+constexpr int kFarVec = 8;              // far columns up to this many go to the vector path
 constexpr int kTileInfo = 8;            // words per tile
 constexpr int kBlkWords = 4;            // per row and block: first entry, key mask low, high, aux
 constexpr int kBoundsPerTile = (kMaxTileBlocks + 1) * kTileRows * kBlkWords;

@@ -181,7 +181,10 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     sm.far[threadIdx.x] = clampi(tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))], 0, n - 1);
   __syncthreads();
   const int nbc = tv.kb_hi - tv.kb_lo;
-  const int nblk = tile_blocks(tv);
+  // a few far columns (e.g. global tokens) are cheaper as vector dot products after the block
+  // loop than as one more gathered 64-key block
+  const bool far_vec = tv.nfar > 0 && tv.nfar <= kFarVec;
+  const int nblk = far_vec ? nbc : tile_blocks(tv);
   const int g = lane / 16, c16 = lane % 16;
   const int b = t / a.H, h = t % a.H;
   const int lr = wave * 16 + c16;            // the lane's query row within the tile
@@ -299,6 +302,32 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
         const int e = ru.x + k + (gat ? gathered_skip(k, ru.z) : 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outb, k < ru.y ? e * 4 : kOffNone, 0, 0);
       }
+    }
+  }
+  if (far_vec) {
+    // far column f of query lr: the lane's dims 32kc + 8g..+8 of q . k_f, summed over the
+    // four lanes of the query, stored by the first of them if the row holds the column
+    const i32x4_v rc = tv.rec[nbc * kTileRows + lr];
+    const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+    for (int f = 0; f < tv.nfar; ++f) {
+      const int kf = sm.far[f];
+      float x = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4_v kv = *reinterpret_cast<const u32x4_v*>(kt + (size_t)kf * D + 32 * kc + 8 * g);
+        const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[w], x);
+      }
+      x += shfl_xor(x, 16);
+      x += shfl_xor(x, 32);
+      x *= a.scale;
+      if constexpr (kBias) x += brow[kf];
+      if constexpr (kMask) x += kmr[kf];
+      const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
+      const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
+      const bool st = g == 0 && ((m >> f) & 1ull);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), outb, st ? e * 4 : kOffNone, 0, 0);
     }
   }
 }

@@ -186,11 +186,14 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int nbc = tv.kb_hi - tv.kb_lo;
-  const int nblk = tile_blocks(tv);
+  // a few far columns (e.g. global tokens) are cheaper on the vector ALUs after the block loop
+  // than as one more gathered 64-key block
+  const bool far_vec = tv.nfar > 0 && tv.nfar <= kFarVec;
+  const int nblk = far_vec ? nbc : tile_blocks(tv);
   {
     // loads clamped to the tile's records (unconditional, so they are all in flight at once)
     constexpr int kRecs = (kMaxTileBlocks + 1) * kTileRows;
-    const int last = max(nblk * kTileRows - 1, 0);
+    const int last = max(tile_blocks(tv) * kTileRows - 1, 0);  // the gathered block's records too
     i32x4_v r[(kRecs + kThreads - 1) / kThreads];
 #pragma unroll
     for (int u = 0; u < (kRecs + kThreads - 1) / kThreads; ++u)
@@ -316,6 +319,27 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
     }
   }
   mfma_drain();
+  if (far_vec) {
+    // far column f: O[row] += w[row, f] V[far_f] for the lane's rows 4g + i and columns
+    // 16c + c16 (the accumulator layout), in fp32
+    for (int f = 0; f < tv.nfar; ++f) {
+      const int kf = sm.far[f];
+      float vf[OC];
+#pragma unroll
+      for (int c = 0; c < OC; ++c) vf[c] = __uint_as_float((uint32_t)vt[(size_t)kf * D + 16 * c + c16] << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4_v rc = sm.rec[nbc * kTileRows + wave * 16 + 4 * g + i];
+        const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+        const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
+        const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
+        const float w = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(wbuf, (m >> f) & 1ull ? e * 4 : kOffNone, 0, 0));
+#pragma unroll
+        for (int c = 0; c < OC; ++c) o[c][i] = fmaf(w, vf[c], o[c][i]);
+      }
+    }
+  }
   // accumulator layout: lane holds column 16c + c16 of the wave's rows 4g + i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
