@@ -124,7 +124,7 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
 
-  constexpr int U = 2;
+  constexpr int U = 4;
   for (long long e0 = e_begin + slot; e0 < e_end; e0 += (long long)U * SLOTS) {
     int j[U];
     bool ok[U];

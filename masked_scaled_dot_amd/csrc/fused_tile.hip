@@ -410,30 +410,42 @@ __device__ void fused_segments(const FusedArgs& a, int BH) {
       return __hip_atomic_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
+    // maxima and sums of the partials, one partial per lane (all loads in flight at once)
     float Mx = -INFINITY;
-    for (int q = 0; q < ns; ++q) Mx = fmaxf(Mx, part(q, pD));
+    for (int q = lane; q < ns; q += kWave) Mx = fmaxf(Mx, part(q, pD));
+    Mx = wave_reduce<OpMax>(Mx);
     float Lt = 0.f;
-    for (int q = 0; q < ns; ++q) {
+    for (int q = lane; q < ns; q += kWave) {
       const float mq = part(q, pD);
       Lt += mq == -INFINITY ? 0.f : part(q, pD + 1) * exp_fast(mq - Mx);
     }
+    Lt = wave_reduce<OpSum>(Lt);
     const float inv = Mx == -INFINITY ? 0.f : 1.0f / Lt;
     float* orow = a.out + ((size_t)t * a.n + row) * D;
-    for (int c = lane; c < D; c += kWave) {
-      float s8[8];
+    // rescaled partial rows summed in segment order; each lane's factor of partial q is
+    // fetched from lane q % 64, sixteen partial loads in flight
+    for (int q0 = 0; q0 < ns; q0 += kWave) {
+      const int qm = min(q0 + lane, ns - 1);
+      const float mq = part(qm, pD);
+      const float fq = (q0 + lane < ns && mq != -INFINITY) ? exp_fast(mq - Mx) : 0.f;
+      for (int c = lane; c < D; c += kWave) {
+        float s16[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s8[u] = 0.f;
-      for (int q0 = 0; q0 < ns; q0 += 8) {
+        for (int u = 0; u < 16; ++u) s16[u] = 0.f;
+        for (int q1 = 0; q1 < min(kWave, ns - q0); q1 += 16) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int q = min(q0 + u, ns - 1);
-          const float mq = part(q, pD);
-          const float x = part(q, c);
-          const float f = (q0 + u < ns && mq != -INFINITY) ? exp_fast(mq - Mx) : 0.f;
-          s8[u] = fmaf(x, f, s8[u]);
+          for (int u = 0; u < 16; ++u) {
+            const int q = min(q0 + q1 + u, ns - 1);
+            const float f = bperm(fq, q1 + u);  // 0 past ns (lane q1 + u > ns - 1 - q0)
+            s16[u] = fmaf(part(q, c), f, s16[u]);
+          }
         }
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += s16[u];
+        if (q0 == 0) orow[c] = acc * inv;
+        else orow[c] += acc * inv;
       }
-      orow[c] = (((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]))) * inv;
     }
     if (a.lse && lane == 0)
       a.lse[(size_t)t * a.n + row] = Mx == -INFINITY ? -INFINITY : Mx + logf(Lt);

@@ -346,12 +346,17 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     if (!segs_ok) return;
     const int S = plan[kHSegs];
     const int* segs = plan + plan[kHOffSegs];
-    const long long tasks = (long long)S * BH;
+    // each plan segment as kSegSplit tasks: scores need no merge, so shorter tasks only add
+    // parallelism
+    constexpr int kSegSplit = 2;
+    const long long tasks = (long long)S * BH * kSegSplit;
     for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
          task += (long long)kLongWGs * (kThreads / kWave)) {
-      const int sg = (int)(task % S), t = (int)(task / S);
+      const int part = (int)(task % kSegSplit);
+      const int sg = (int)(task / kSegSplit % S), t = (int)(task / kSegSplit / S);
       const int* it = segs + 8 * sg;
-      valu_row<T, D>(a, t, it[0], it[1], it[2]);
+      const long long len = it[2] - it[1];
+      valu_row<T, D>(a, t, it[0], it[1] + len * part / kSegSplit, it[1] + len * (part + 1) / kSegSplit);
     }
     return;
   }

@@ -399,21 +399,24 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         const int first = sg - sidx;
         float* orow = a.out + ((size_t)t * a.n + row) * D;
-        // eight partials in flight per lane; the summation order depends only on ns
+        // sixteen partials in flight per lane; the summation order depends only on ns
         for (int c = lane; c < D; c += kWave) {
-          float s8[8];
+          float s16[16];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) s8[u] = 0.f;
-          for (int q0 = 0; q0 < ns; q0 += 8) {
+          for (int u = 0; u < 16; ++u) s16[u] = 0.f;
+          for (int q0 = 0; q0 < ns; q0 += 16) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 16; ++u) {
               const int q = min(q0 + u, ns - 1);
               const float x = __hip_atomic_load(scratch + ((size_t)(first + q) * pBH + t) * slot_floats(pD) + c,
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              s8[u] += q0 + u < ns ? x : 0.f;
+              s16[u] += q0 + u < ns ? x : 0.f;
             }
           }
-          orow[c] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+          float acc = 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) acc += s16[u];
+          orow[c] = acc;
         }
         if (lane == 0)  // ready for the next call
           __hip_atomic_store(&counters[(size_t)lr * pBH + t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
