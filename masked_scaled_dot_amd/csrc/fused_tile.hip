@@ -52,26 +52,17 @@ constexpr float kSlack = 8.f;   // lazy running-max threshold, log2 units
 
 constexpr int kBsrCached = 512;  // block-columns of a block-row kept in LDS (n <= 32768 fully)
 
-template <int D>
-struct FusedSmem {
-  static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
-  static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
-  alignas(16) uint16_t k[2][kTileRows * kKStride];
-  alignas(16) uint16_t v[2][kTileRows * kVStride];
-  int far[kTileRows];   // the gathered block's key rows (CSR)
-  int live[kTileRows];  // 1: the tile writes this query's output
-  int bcol[kBsrCached]; // the block-row's first stored block-columns (block CSR)
-};
-
-// LDS of the block-CSR / dense tile: one K/V stage (a second barrier per block guards its
-// reuse), so that four workgroups fit on a compute unit and more loads are in flight.
+// LDS of the matrix-core tile: one K/V stage (a second barrier per block guards its reuse),
+// so that three or four workgroups fit on a compute unit and more loads are in flight.
 template <int D>
 struct FusedSmem1 {
   static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
   static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
   alignas(16) uint16_t k[1][kTileRows * kKStride];
   alignas(16) uint16_t v[1][kTileRows * kVStride];
-  int bcol[kBsrCached];
+  int bcol[kBsrCached];  // block CSR: the block-row's first stored block-columns
+  int far[kTileRows];    // element CSR: the gathered block's key rows
+  int live[kTileRows];   // element CSR: 1 if the tile writes this query's output
 };
 
 // Waves per SIMD the block kernels are compiled for (caps the registers at 512 / waves).
@@ -85,283 +76,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float bperm(float x, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
-}
-
-// Matrix-core tile of 64 queries [row0, row0 + 64) of head t.
-// Kind kFusedCsr: blocks are the plan tile's (tv); kFusedBsr: the stored blocks [bs, be) of
-// the block-row; kFusedDense: all key blocks. kBias / kMask: a bias / key mask is added;
-// kVec4: their rows are 16-byte aligned (n % 4 == 0) and loaded as float4 (contiguous blocks).
-template <int D, int K, bool kBias, bool kMask, bool kVec4>
-__device__ void fused_tile(const FusedArgs& a, FusedSmem<D>& sm, const TileView& tv, int t, int row0,
-                           long long bs, long long be) {
-  constexpr int KS = FusedSmem<D>::kKStride, VS = FusedSmem<D>::kVStride;
-  constexpr int KC = D / 32;                           // 32-wide k-chunks of the head dim
-  constexpr int OC = D / 16;                           // 16-wide output column tiles
-  constexpr int CH = kTileRows * (D / 8) / kThreads;   // 16-byte chunks per thread (K, and V)
-  constexpr bool kAdd = kBias || kMask;
-  const int n = a.n;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int g = lane / 16, c16 = lane % 16;
-  const int b = t / a.H, h = t % a.H;
-  const int ntiles = (n + kTileRows - 1) / kTileRows;
-
-  int nbc = 0, nblk = 0;
-  if constexpr (K == kFusedCsr) {
-    nbc = tv.kb_hi - tv.kb_lo;
-    nblk = tile_blocks(tv);
-  } else if constexpr (K == kFusedBsr) {
-    nblk = (int)(be - bs);
-  } else {
-    nblk = ntiles;
-  }
-  // block CSR: the block-columns in LDS, so that the addresses of a prefetch never wait for a
-  // load (vector loads complete in order: such a wait would also wait for the other stage)
-  if constexpr (K == kFusedBsr)
-    for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
-  if (threadIdx.x < kTileRows) {
-    const int r = threadIdx.x, row = row0 + r;
-    if constexpr (K == kFusedCsr) sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, n - 1);
-    int live = row < n;
-    if constexpr (K == kFusedCsr) {
-      if (live) {
-        long long rs = a.row_ptr[row], re = a.row_ptr[row + 1];
-        rs = rs < 0 ? 0 : (rs > a.nnz ? a.nnz : rs);
-        re = re < rs ? rs : (re > a.nnz ? a.nnz : re);
-        live = re - rs <= kLongRow;  // longer rows are written by their segments
-      }
-    }
-    sm.live[r] = live;
-  }
-  __syncthreads();
-
-  // the wave's 16 queries as the B operand of S^T = K Q^T (lane: query c16, dims 32kc + 8g..)
-  const int my_q = min(row0 + wave * 16 + c16, n - 1);
-  const uint16_t* qt = static_cast<const uint16_t*>(a.q) + (size_t)t * n * D;
-  const uint16_t* kt = static_cast<const uint16_t*>(a.k) + (size_t)t * n * D;
-  const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * n * D;
-  bf16x8_v qb[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
-  const float* brow = a.bias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
-  const float* kmr = a.key_mask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
-  const float scale2 = a.scale * kLog2e;
-
-  // first key of block jj (contiguous kinds)
-  auto block_k0 = [&](int jj) -> int {
-    if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
-    else if constexpr (K == kFusedBsr)
-      return clampi(jj < kBsrCached ? sm.bcol[jj] : a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows;
-    else return jj * kTileRows;
-  };
-
-  // A block's K and V rows, the lane's key mask (CSR) and raw additive terms, loaded into
-  // registers two blocks ahead (two stages, used alternately); past the last block the
-  // last block is loaded again (unused), so the loads are unconditional
-  struct Stage {
-    u32x4_v kn[CH], vn[CH];
-    unsigned mlo, mhi;
-    f32x4_v bn[kBias ? 4 : 1], mk[kMask ? 4 : 1];
-  };
-  auto prefetch = [&](Stage& st, int jj) {
-    const bool gat = (K == kFusedCsr) && jj >= nbc;
-    const int k0 = block_k0(jj);
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int i = threadIdx.x + u * kThreads;
-      const int r = i / (D / 8);
-      int key = min(k0 + r, n - 1);
-      if constexpr (K == kFusedCsr) {
-        const int kf = sm.far[r];
-        key = gat ? kf : key;
-      }
-      st.kn[u] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)key * D + (i % (D / 8)) * 8);
-      st.vn[u] = *reinterpret_cast<const u32x4_v*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
-    }
-    if constexpr (K == kFusedCsr) {
-      const i32x4_v rc = tv.rec[jj * kTileRows + wave * 16 + c16];
-      st.mlo = (unsigned)rc.y;
-      st.mhi = (unsigned)rc.z;
-    }
-    if constexpr (kAdd) {
-      // keys 16tt + 4g + {0..3} of the block, loaded raw (summed after the barrier, so no
-      // wait here); keys past n are masked later, so their loads only need to stay in range
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (kVec4 && !gat) {
-          const int kk = min(k0 + 16 * tt + 4 * g, n - 4);
-          if constexpr (kBias) st.bn[tt] = *reinterpret_cast<const f32x4_v*>(brow + kk);
-          if constexpr (kMask) st.mk[tt] = *reinterpret_cast<const f32x4_v*>(kmr + kk);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int key = min(k0 + 16 * tt + 4 * g + i, n - 1);
-            if constexpr (K == kFusedCsr) {
-              const int kf = sm.far[16 * tt + 4 * g + i];
-              key = gat ? kf : key;
-            }
-            if constexpr (kBias) st.bn[tt][i] = brow[key];
-            if constexpr (kMask) st.mk[tt][i] = kmr[key];
-          }
-        }
-      }
-    }
-  };
-
-  float m2 = -INFINITY;  // running max of the lane's query, log2 units
-  float lsum = 0.f;      // partial running sum over this lane's keys
-  f32x4_v o[OC];
-#pragma unroll
-  for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-
-  // One key block: stage st (block j) into LDS buffer j&1, then refill st with block j+2
-  // while block j is computed.
-  auto step = [&](Stage& st, int j) {
-    uint16_t* kb_s = sm.k[j & 1];
-    uint16_t* vb_s = sm.v[j & 1];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int i = threadIdx.x + u * kThreads;
-      *reinterpret_cast<u32x4_v*>(&kb_s[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = st.kn[u];
-      *reinterpret_cast<u32x4_v*>(&vb_s[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = st.vn[u];
-    }
-    const unsigned mlo = st.mlo, mhi = st.mhi;
-    f32x4_v ad[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      ad[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kBias) ad[tt] += st.bn[tt];
-      if constexpr (kMask) ad[tt] += st.mk[tt];
-    }
-    const int k0 = block_k0(j);
-    lds_barrier();                       // block j is staged for every wave
-    prefetch(st, min(j + 2, nblk - 1));  // in flight while blocks j and j+1 are computed
-
-    // ---- S^T tiles: lane holds keys 16tt + 4g + i of query c16, in log2 units
-    float s[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8_v ka = __builtin_bit_cast(
-            bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kb_s[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kc], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = 16 * tt + 4 * g + i;
-        bool present;
-        if constexpr (K == kFusedCsr) present = (((tt < 2 ? mlo : mhi) >> (slot & 31)) & 1u) != 0u;
-        else present = k0 + slot < n;
-        float x = acc[i] * scale2;
-        if constexpr (kAdd) x = fmaf(ad[tt][i], kLog2e, x);
-        s[tt][i] = present ? x : -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    // The running max moves only when the block max exceeds it by more than kSlack: p stays
-    // <= 2^kSlack, and the O rescale below is skipped for most blocks.
-    const float mn = (mx > m2 + kSlack) ? mx : m2;
-    float alpha = 1.f;
-    uint32_t pk[2][4];  // bf16 P: [32-key chunk][dword]
-    if (mn == -INFINITY) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pk[c][w] = 0u;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m2 - mn);
-      float ps = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[tt][i] = __builtin_amdgcn_exp2f(s[tt][i] - mn);
-          ps += p[tt][i];
-        }
-      lsum = fmaf(lsum, alpha, ps);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        pk[c][0] = pack_bf16(p[2 * c][0], p[2 * c][1]);
-        pk[c][1] = pack_bf16(p[2 * c][2], p[2 * c][3]);
-        pk[c][2] = pack_bf16(p[2 * c + 1][0], p[2 * c + 1][1]);
-        pk[c][3] = pack_bf16(p[2 * c + 1][2], p[2 * c + 1][3]);
-      }
-      m2 = mn;
-    }
-    // ---- rescale O rows when some query's max moved (query 4g+i is owned by lane 4g+i)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = bperm(alpha, 4 * g + i);
-#pragma unroll
-      for (int c = 0; c < OC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
-    }
-    // ---- O += P V
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const bf16x8_v pa = __builtin_bit_cast(bf16x8_v, (u32x4_v){pk[c2][0], pk[c2][1], pk[c2][2], pk[c2][3]});
-      const int key0 = 32 * c2 + 4 * g + c16 / 4;
-#pragma unroll
-      for (int c = 0; c < OC; ++c) {
-        const int col = 16 * c + 4 * (c16 % 4);
-        typedef __attribute__((address_space(3))) i16x4_v lds_v4;
-        const i16x4_v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[key0 * VS + col]));
-        const i16x4_v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb_s[(key0 + 16) * VS + col]));
-        const bf16x8_v vb = __builtin_bit_cast(
-            bf16x8_v, (i16x8_v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
-      }
-    }
-  };
-
-  Stage s0, s1;
-  if (nblk > 0) {
-    prefetch(s0, 0);
-    // the first stage complete before the second is issued: the loop is entered, as it loops
-    // back, with one stage's loads outstanding behind the other's, so the wait at the top of
-    // the loop need not cover both
-    vm_wait_all();
-    prefetch(s1, min(1, nblk - 1));
-  }
-  for (int j = 0; j < nblk; j += 2) {
-    step(s0, j);
-    if (j + 1 >= nblk) break;
-    step(s1, j + 1);
-  }
-  mfma_drain();
-
-  // ---- finish: total sum per query, divide, store O and lse
-  float ltot = lsum + shfl_xor(lsum, 16);
-  ltot += shfl_xor(ltot, 32);
-  const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltot;
-  {
-    const int lr = wave * 16 + c16;
-    if (a.lse && g == 0 && sm.live[lr])
-      a.lse[(size_t)t * n + row0 + lr] = (m2 == -INFINITY) ? -INFINITY : (m2 / kLog2e + logf(ltot));
-  }
-  float iv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) iv[i] = bperm(inv, 4 * g + i);
-  float* ot = a.out + (size_t)t * n * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = wave * 16 + 4 * g + i;
-    if (!sm.live[lr]) continue;
-#pragma unroll
-    for (int c = 0; c < OC; ++c) ot[(size_t)(row0 + lr) * D + 16 * c + c16] = o[c][i] * iv[i];
-  }
 }
 
 // Long-row segment of the CSR kind: partial state (acc, max, sum) to the plan's scratch with
@@ -458,15 +172,10 @@ __device__ void fused_segments(const FusedArgs& a, int BH) {
 // workgroup per (head, tile).
 struct NoSmem {};  // fp32 inputs never take the matrix-core tile
 
-// Occupancy floor for the matrix-core kernels: register allocation is capped so that this
-// many waves fit per SIMD (2 -> 256 registers, 3 -> 168).
-template <int D, bool kAdd>
-constexpr int kFusedWaves = (D == 128 || (D == 64 && kAdd)) ? 2 : 3;
-
 template <typename T, int D, bool kBias, bool kMask>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<D, kBias || kMask>)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : kBlockWaves<D, kFusedCsr, kBias || kMask>)))
 void fused_plan_kernel(FusedArgs a, int BH) {
-  __shared__ std::conditional_t<sizeof(T) == 2, FusedSmem<D>, NoSmem> sm;
+  __shared__ std::conditional_t<sizeof(T) == 2, FusedSmem1<D>, NoSmem> sm;
   const int* plan = a.plan;
   const bool segs_ok = plan[kHValid] != 0 && BH <= plan[kHBH] && D <= plan[kHD];
   if ((int)blockIdx.x < kLongWGs) {
@@ -479,7 +188,7 @@ void fused_plan_kernel(FusedArgs a, int BH) {
   const int row0 = tile * kTileRows;
   const TileView tv = tile_view(plan, tile);
   if (sizeof(T) == 2 && tv.mfma && segs_ok) {
-    if constexpr (sizeof(T) == 2) fused_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, 0, 0);
+    if constexpr (sizeof(T) == 2) fused_block_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, 0, 0);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -493,19 +202,25 @@ void fused_plan_kernel(FusedArgs a, int BH) {
   }
 }
 
-// Block CSR and dense kinds, lean form. Same tile and MFMA layouts as fused_tile; differences:
+// Matrix-core tile of 64 queries [row0, row0 + 64) of head t. Kind kFusedCsr: the blocks are
+// the plan tile's (tv): its contiguous key blocks, then its far columns; kFusedBsr: the
+// stored blocks [bs, be) of the block-row; kFusedDense: all key blocks. kBias / kMask: a bias
+// / key mask is added; kVec4: their rows are 16-byte aligned (n % 4 == 0) and loaded as
+// float4. Each of the four waves owns 16 queries; per 64-key block it forms S^T = K Q^T on
+// the matrix cores (lane g = lane / 16, c16 = lane % 16 holds keys 16tt + 4g + i of query
+// c16), runs the online softmax in registers, and adds P V with V read transposed from LDS.
 //  * K/V (and bias/key-mask) rows come through raw buffer loads whose per-block part of the
 //    offset is a scalar (the block's first key), so the loop spends no vector instructions on
 //    addresses, and rows past n read as zero;
 //  * one register stage, loaded one block ahead, and a loop body of one block: the only vector
 //    memory operations after a prefetch are the next prefetch's, so the wait for it at the top
-//    of the loop covers nothing else; one LDS stage, for occupancy (four workgroups per CU);
+//    of the loop covers nothing else; one LDS stage, for occupancy;
 //  * the softmax is branch-free: a row that has seen no finite score uses 0 as its reference
 //    maximum (exp2(-inf) = 0 keeps its sums at zero), and keys past n are masked only in the
 //    ragged last block (a uniform test).
 template <int D, int K, bool kBias, bool kMask, bool kVec4>
-__device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, int row0, long long bs,
-                                 long long be) {
+__device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const TileView& tv, int t,
+                                 int row0, long long bs, long long be) {
   constexpr int KS = FusedSmem1<D>::kKStride, VS = FusedSmem1<D>::kVStride;
   constexpr int KC = D / 32;
   constexpr int OC = D / 16;
@@ -517,9 +232,27 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
   const int g = lane / 16, c16 = lane % 16;
   const int b = t / a.H, h = t % a.H;
   const int ntiles = (n + kTileRows - 1) / kTileRows;
-  const int nblk = K == kFusedBsr ? (int)(be - bs) : ntiles;
+  // element CSR: the plan tile's contiguous blocks, then its far columns (a few on the vector
+  // ALUs after the loop, more as one gathered block)
+  const int nbc = K == kFusedCsr ? tv.kb_hi - tv.kb_lo : 0;
+  const bool far_vec = K == kFusedCsr && tv.nfar > 0 && tv.nfar <= kFarVec;
+  const int nblk = K == kFusedBsr ? (int)(be - bs) : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv)) : ntiles;
   if constexpr (K == kFusedBsr)
     for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
+  if constexpr (K == kFusedCsr) {
+    if (threadIdx.x < kTileRows) {
+      const int r = threadIdx.x, row = row0 + r;
+      sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, n - 1);
+      int live = row < n;
+      if (live) {
+        long long rs = a.row_ptr[row], re = a.row_ptr[row + 1];
+        rs = rs < 0 ? 0 : (rs > a.nnz ? a.nnz : rs);
+        re = re < rs ? rs : (re > a.nnz ? a.nnz : re);
+        live = re - rs <= kLongRow;  // longer rows are written by their segments
+      }
+      sm.live[r] = live;
+    }
+  }
   __syncthreads();
 
   const int my_q = min(row0 + wave * 16 + c16, n - 1);
@@ -543,6 +276,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
     if constexpr (K == kFusedBsr)
       return __builtin_amdgcn_readfirstlane(
           clampi(jj < kBsrCached ? sm.bcol[jj] : a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows);
+    else if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
     else return jj * kTileRows;
   };
   // lane-constant parts of the offsets: chunk u of the thread is row i / (D/8), part i % (D/8)
@@ -555,15 +289,38 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
 
   u32x4_v kn[CH], vn[CH];
   f32x4_v bn[kBias ? 4 : 1], mk[kMask ? 4 : 1];
+  unsigned mlo = 0u, mhi = 0u;  // element CSR: the key slots the lane's query holds
   auto prefetch = [&](int jj) {
     const int k0 = block_k0(jj);
-    const int kvs = k0 * D * 2;  // scalar part of the K/V offsets
+    const bool gat = K == kFusedCsr && jj >= nbc;  // the gathered block: rows from the far list
+    const int kvs = gat ? 0 : k0 * D * 2;          // scalar part of the K/V offsets
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      kn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(kres, kvoff[u], kvs, 0));
-      vn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(vres, kvoff[u], kvs, 0));
+      int vo = kvoff[u];
+      if constexpr (K == kFusedCsr) {
+        const int i = threadIdx.x + u * kThreads;
+        vo = gat ? (sm.far[i / (D / 8)] * D + (i % (D / 8)) * 8) * 2 : vo;
+      }
+      kn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(kres, vo, kvs, 0));
+      vn[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(vres, vo, kvs, 0));
     }
-    if constexpr (kAdd) {
+    if constexpr (K == kFusedCsr) {
+      const i32x4_v rc = tv.rec[jj * kTileRows + wave * 16 + c16];
+      mlo = (unsigned)rc.y;
+      mhi = (unsigned)rc.z;
+    }
+    if constexpr (kAdd && K == kFusedCsr) {
+      // keys 16tt + 4g + {0..3}, one load each (their columns need not be consecutive)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 16 * tt + 4 * g + i;
+          const int key = gat ? sm.far[slot] : k0 + slot;
+          if constexpr (kBias) bn[tt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, brow_off + key * 4, 0, 0));
+          if constexpr (kMask) mk[tt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mres, key * 4, 0, 0));
+        }
+    } else if constexpr (kAdd) {
       // keys 16tt + 4g + {0..3}: 16 consecutive bytes of the bias row and of the key mask
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -610,6 +367,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
       }
     }
     const int lim = n - block_k0(j);       // keys of this block below n
+    const unsigned blo = mlo, bhi = mhi;   // element CSR: key slots the query holds in block j
     lds_barrier();                         // block j is staged for every wave
     prefetch(min(j + 1, nblk - 1));        // in flight while block j is computed
 
@@ -635,7 +393,13 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
         if constexpr (kAdd) x = fmaf(ad[tt][i], kLog2e, x);
         sc[tt][i] = x;
       }
-    if (lim < kTileRows) {  // ragged last block: keys at or past n score -inf
+    if constexpr (K == kFusedCsr) {  // keys the row does not hold score -inf
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[tt][i] = ((tt < 2 ? blo : bhi) >> ((16 * tt + 4 * g + i) & 31)) & 1u ? sc[tt][i] : -INFINITY;
+    } else if (lim < kTileRows) {  // ragged last block: keys at or past n score -inf
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -703,12 +467,58 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
   }
   mfma_drain();
 
+  if (far_vec) {
+    // far column f of query c16: q . k_f from the lane's dims, summed over the query's four
+    // lanes; then one exact running-max / running-sum update, with V_f added in fp32 to the
+    // output rows 4g + i (their factors come from the lanes that own those queries)
+    const i32x4_v rc = tv.rec[nbc * kTileRows + wave * 16 + c16];
+    const unsigned long long fm = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+    const uint16_t* kt = static_cast<const uint16_t*>(a.k) + head;
+    const uint16_t* vt = static_cast<const uint16_t*>(a.v) + head;
+    for (int f = 0; f < tv.nfar; ++f) {
+      const int kf = sm.far[f];
+      float x = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4_v kv = *reinterpret_cast<const u32x4_v*>(kt + (size_t)kf * D + 32 * kc + 8 * g);
+        const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[w], x);
+      }
+      x += shfl_xor(x, 16);
+      x += shfl_xor(x, 32);
+      x *= scale2;
+      if constexpr (kBias) x = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, brow_off + kf * 4, 0, 0)), kLog2e, x);
+      if constexpr (kMask) x = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mres, kf * 4, 0, 0)), kLog2e, x);
+      x = (fm >> f) & 1ull ? x : -INFINITY;
+      const float mn = fmaxf(m2, x);
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - ref);
+      const float p = __builtin_amdgcn_exp2f(x - ref);
+      lsum = fmaf(lsum, alpha, g == 0 ? p : 0.f);  // the query's four lanes share the sum
+      m2 = mn;
+      float vf[OC];
+#pragma unroll
+      for (int c = 0; c < OC; ++c) vf[c] = __uint_as_float((uint32_t)vt[(size_t)kf * D + 16 * c + c16] << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = bperm(alpha, 4 * g + i), pi = bperm(p, 4 * g + i);
+#pragma unroll
+        for (int c = 0; c < OC; ++c) o[c][i] = fmaf(pi, vf[c], o[c][i] * al);
+      }
+    }
+  }
+
   // finish: total sum per query, divide, store O and lse
   float ltot = lsum + shfl_xor(lsum, 16);
   ltot += shfl_xor(ltot, 32);
   const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltot;
+  auto live = [&](int lr) {
+    if constexpr (K == kFusedCsr) return sm.live[lr] != 0;
+    else return row0 + lr < n;
+  };
   const int lr = wave * 16 + c16;
-  if (a.lse && g == 0 && row0 + lr < n)
+  if (a.lse && g == 0 && live(lr))
     a.lse[(size_t)t * n + row0 + lr] = (m2 == -INFINITY) ? -INFINITY : (m2 / kLog2e + logf(ltot));
   float iv[4];
 #pragma unroll
@@ -716,10 +526,10 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, int t, i
   float* ot = a.out + (size_t)t * n * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = row0 + wave * 16 + 4 * g + i;
-    if (r >= n) continue;
+    const int lr4 = wave * 16 + 4 * g + i;
+    if (!live(lr4)) continue;
 #pragma unroll
-    for (int c = 0; c < OC; ++c) ot[(size_t)r * D + 16 * c + c16] = o[c][i] * iv[i];
+    for (int c = 0; c < OC; ++c) ot[(size_t)(row0 + lr4) * D + 16 * c + c16] = o[c][i] * iv[i];
   }
 }
 
@@ -741,7 +551,8 @@ void fused_block_kernel(FusedArgs a) {
     bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
     be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
   }
-  fused_block_tile<D, K, kBias, kMask, kVec4>(a, sm, t, tile * kTileRows, bs, be);
+  const TileView tv{};
+  fused_block_tile<D, K, kBias, kMask, kVec4>(a, sm, tv, t, tile * kTileRows, bs, be);
 }
 
 template <typename T, int D>
