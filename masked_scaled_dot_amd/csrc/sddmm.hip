@@ -96,35 +96,85 @@ __device__ __forceinline__ float additive(const Args& a, int h, int b, int row, 
   return x;
 }
 
-// Vector path over entries [e_begin, e_end) of one row, q wave-uniform (scalar registers).
-template <typename T, int D>
+// Vector path over entries [e_begin, e_end) of one row. G lanes share an entry: lane p of a
+// group holds the 16-byte chunks p, p + G, ... of q and loads the same chunks of the entry's
+// key row, so each load instruction covers whole key rows (64 / G of them) instead of one
+// chunk of 64 rows. 64 entries go in G rounds: in round c, group r takes entry G*r + c; after
+// the sum over the group, lane G*r + p keeps round p's score, which is that of entry
+// G*r + p = its own lane index, so scores are stored lane-contiguous. kBig: the head's keys
+// exceed one buffer's range, and rows are addressed with 64-bit pointers.
+template <typename T, int D, bool kBig>
 __device__ void valu_row(const Args& a, int t, int row, long long e_begin, long long e_end) {
   if (e_begin >= e_end) return;
-  constexpr int W = RowVec<T, D>::kWords;
+  constexpr int V = RowVec<T, D>::kVec;  // 16-byte chunks per key row
+  constexpr int G = V < 8 ? V : 8;       // lanes per entry
+  constexpr int PL = V / G;              // chunks per lane
+  constexpr int RB = D * (int)sizeof(T); // bytes per key row
   const int lane = threadIdx.x % kWave;
+  const int r = lane / G, p = lane % G;
   const int b = t / a.H, h = t % a.H;
-  const T* qt = static_cast<const T*>(a.q);
-  const T* kt = static_cast<const T*>(a.k) + (size_t)t * a.n * D;
-  uint32_t qw[W];
-  const uint4* qrow = reinterpret_cast<const uint4*>(qt + ((size_t)t * a.n + row) * D);
+  const char* kt = static_cast<const char*>(a.k) + (size_t)t * a.n * RB;
+  const char* qrow = static_cast<const char*>(a.q) + ((size_t)t * a.n + row) * RB;
+  u32x4_v qv[PL];
 #pragma unroll
-  for (int c = 0; c < W / 4; ++c) {
-    const uint4 v = qrow[c];
-    qw[4 * c] = v.x; qw[4 * c + 1] = v.y; qw[4 * c + 2] = v.z; qw[4 * c + 3] = v.w;
+  for (int i = 0; i < PL; ++i) qv[i] = *reinterpret_cast<const u32x4_v*>(qrow + (p + G * i) * 16);
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(kt, (long long)a.n * RB);
+  const long long len = e_end - e_begin;
+  // the row's columns; reads past the row return 0 (a valid key, never stored)
+  const __amdgpu_buffer_rsrc_t cres = make_rsrc(a.col_idx + e_begin, len * 4);
+  float* st = a.scores + (size_t)t * a.nnz + e_begin;
+  i32x4_v cn[G / 4];  // columns of entries G*r .. G*r + G-1 of the next 64
+  auto load_cols = [&](long long s0) {
+#pragma unroll
+    for (int u = 0; u < G / 4; ++u)
+      cn[u] = __builtin_bit_cast(i32x4_v, __builtin_amdgcn_raw_buffer_load_b128(cres, (int)(s0 + G * r + 4 * u) * 4, 0, 0));
+  };
+  load_cols(0);
+  for (long long s0 = 0; s0 < len; s0 += kWave) {
+    int cc[G];
+#pragma unroll
+    for (int c = 0; c < G; ++c) cc[c] = clampi(cn[c / 4][c % 4], 0, a.n - 1);
+    if (s0 + kWave < len) load_cols(s0 + kWave);
+    u32x4_v kv[G][PL];
+#pragma unroll
+    for (int c = 0; c < G; ++c)
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int off = (p + G * i) * 16;
+        if constexpr (kBig)
+          kv[c][i] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)cc[c] * RB + off);
+        else
+          kv[c][i] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(kres, cc[c] * RB + off, 0, 0));
+      }
+    float sel = 0.f;
+    int col = 0;
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (sizeof(T) == 2) {
+            if (w & 1) acc1 = dot2_bf16(qv[i][w], kv[c][i][w], acc1);
+            else acc0 = dot2_bf16(qv[i][w], kv[c][i][w], acc0);
+          } else {
+            if (w & 1) acc1 = fmaf(__uint_as_float(qv[i][w]), __uint_as_float(kv[c][i][w]), acc1);
+            else acc0 = fmaf(__uint_as_float(qv[i][w]), __uint_as_float(kv[c][i][w]), acc0);
+          }
+        }
+      const float acc = group_reduce<G, OpSum>(acc0 + acc1);
+      sel = p == c ? acc : sel;
+      col = p == c ? cc[c] : col;
+    }
+    if (s0 + lane < len) st[s0 + lane] = sel * a.scale + additive(a, h, b, row, col);
   }
-  float* st = a.scores + (size_t)t * a.nnz;
-  for (long long e0 = e_begin; e0 < e_end; e0 += 2 * kWave) {
-    const long long ea = e0 + lane, eb = e0 + kWave + lane;
-    const bool oka = ea < e_end, okb = eb < e_end;
-    const int ja = clampi(a.col_idx[oka ? ea : e_begin], 0, a.n - 1);
-    const int jb = clampi(a.col_idx[okb ? eb : e_begin], 0, a.n - 1);
-    float sa_ = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)ja * D));
-    float sb_ = row_dot<T, D>(qw, reinterpret_cast<const uint4*>(kt + (size_t)jb * D));
-    sa_ = sa_ * a.scale + additive(a, h, b, row, ja);
-    sb_ = sb_ * a.scale + additive(a, h, b, row, jb);
-    if (oka) st[ea] = sa_;
-    if (okb) st[eb] = sb_;
-  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void valu_row(const Args& a, int t, int row, long long e_begin, long long e_end) {
+  if ((long long)a.n * D * (long long)sizeof(T) > kMaxBufBytes) valu_row<T, D, true>(a, t, row, e_begin, e_end);
+  else valu_row<T, D, false>(a, t, row, e_begin, e_end);
 }
 
 // ---------------------------------------------------------------------------------- kernels
