@@ -290,7 +290,9 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
   // nothing to wait for, instead of also waiting for the previous block's stores (vector
   // loads and stores share one in-order counter).
   vm_wait_all();
-  for (int j = 0; j < nblk; ++j) {
+  // one key block; kGat: the gathered block of far columns (last, at most once)
+  auto pass = [&](int j, auto gat_tag) {
+    constexpr bool gat = decltype(gat_tag)::value;
     uint16_t* kbuf = sm.k[j & 1];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
@@ -303,7 +305,6 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     for (int i = 0; i < (kAdd ? 4 : 1); ++i) ac[i] = an[i];
     lds_barrier();                   // block j's K is visible to every wave
     prefetch(min(j + 1, nblk - 1));  // in flight while block j is computed and written
-    const bool gat = j >= nbc;
 
     // step 2: all four 16x16 products, then (no branch in between) their use
     f32x4_v acc[4];
@@ -336,24 +337,50 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     }
     if (g == 0) sm.run[lr] = i32x4_v{rc.x - (int)e_lo, __builtin_popcountll(m), rc.w, 0};
 
-    // step 4: copy the wave's rows out (the wave reads only what it wrote: no barrier). Row
-    // cr + 4i goes to 16 lanes; lane cp stores its entries cp, cp + 16, cp + 32, cp + 48, so
-    // each store instruction writes 64 consecutive bytes of four rows. The sixteen stores are
-    // issued unconditionally (entries past the row's count get an offset the buffer drops):
-    // vector-memory stores and loads share one in-order counter, and a fixed store count lets
+    // step 4: copy the wave's rows out (the wave reads only what it wrote: no barrier). The
+    // store count per block is fixed (entries past a row's count get an offset the buffer
+    // drops): vector-memory stores and loads share one in-order counter, and a fixed count lets
     // the next block's K rows, loaded before these stores, be awaited without waiting for them.
+    if constexpr (!gat) {
+      // A contiguous block: a row's entries are consecutive in the scores array. Four lanes
+      // per row, sixteen rows per instruction: lane qq of row rq moves 4-entry quads
+      // qq, qq + 4, qq + 8, qq + 12 of the compacted row with one LDS read and one 16-byte
+      // store each; the row's last, partial quad (1 to 3 entries) goes out by three single
+      // stores from the lane that read it.
+      const int rq = wave * 16 + lane / 4, qq = lane % 4;
+      const i32x4_v ru = sm.run[rq];
+      const int cnt = ru.y, qp = cnt >> 2, rem = cnt & 3;
+      u32x4_v part = u32x4_v{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x4_v ru = sm.run[cr + 4 * i];
+      for (int u = 0; u < 4; ++u) {
+        const int q = qq + 4 * u;
+        const u32x4_v x = *reinterpret_cast<const u32x4_v*>(&sm.out[rq * OS + 4 * q]);
+        part = q == qp ? x : part;
+        __builtin_amdgcn_raw_buffer_store_b128(x, outb, 4 * q + 3 < cnt ? (ru.x + 4 * q) * 4 : kOffNone, 0, 0);
+      }
+      const bool own = (qp & 3) == qq;  // the lane holds the partial quad (if rem > 0)
 #pragma unroll
-      for (int c0 = 0; c0 < kTileRows; c0 += 16) {
-        const int k = c0 + cp;
-        const float v = sm.out[(cr + 4 * i) * OS + k];
-        const int e = ru.x + k + (gat ? gathered_skip(k, ru.z) : 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outb, k < ru.y ? e * 4 : kOffNone, 0, 0);
+      for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(part[i], outb, own && i < rem ? (ru.x + 4 * qp + i) * 4 : kOffNone, 0, 0);
+    } else {
+      // The gathered block: a row's far entries before and after its core range are two runs.
+      // Row cr + 4i goes to 16 lanes; lane cp stores its entries cp, cp + 16, cp + 32, cp + 48,
+      // so each store instruction writes 64 consecutive bytes of four rows.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4_v ru = sm.run[cr + 4 * i];
+#pragma unroll
+        for (int c0 = 0; c0 < kTileRows; c0 += 16) {
+          const int k = c0 + cp;
+          const float v = sm.out[(cr + 4 * i) * OS + k];
+          const int e = ru.x + k + gathered_skip(k, ru.z);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outb, k < ru.y ? e * 4 : kOffNone, 0, 0);
+        }
       }
     }
-  }
+  };
+  for (int j = 0; j < nbc; ++j) pass(j, std::false_type{});
+  if (nblk > nbc) pass(nbc, std::true_type{});
   if (far_vec) {
     // far column f of query lr: the lane's dims 32kc + 8g..+8 of q . k_f, summed over the
     // four lanes of the query, stored by the first of them if the row holds the column
