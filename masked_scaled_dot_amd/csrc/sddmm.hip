@@ -212,7 +212,8 @@ struct TileSmem {
   static constexpr int kKStride = D + 8;     // bf16 per K row (+16 B: conflict-free reads)
   static constexpr int kOStride = kTileRows + 4;  // fp32 per compacted row
   alignas(16) uint16_t k[2][kTileRows * kKStride];   // double-buffered K block
-  alignas(16) float out[kTileRows * kOStride];       // compacted scores of one block
+  alignas(16) float out[kTileRows * kOStride + kTileRows];  // one block's scores per row (+ slack
+                                                            // for the last row's shifted reads)
   int far[kTileRows];                                // the gathered block's key rows
   i32x4_v run[kTileRows];                            // per row: first entry, count, aux
 };
@@ -227,9 +228,9 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int n = a.n;
-  if (threadIdx.x < kTileRows)
-    sm.far[threadIdx.x] = clampi(tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))], 0, n - 1);
-  __syncthreads();
+  // the far list is needed by the gathered block (last) and the far-column epilogue only:
+  // its load is issued first and its LDS copy made after the first block's loads are out
+  const int farv = threadIdx.x < kTileRows ? tv.far_cols[min((int)threadIdx.x, max(tv.nfar - 1, 0))] : 0;
   const int nbc = tv.kb_hi - tv.kb_lo;
   // a few far columns (e.g. global tokens) are cheaper as vector dot products after the block
   // loop than as one more gathered 64-key block
@@ -284,7 +285,12 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     }
   };
 
-  prefetch(0);
+  // The first block's loads go out before the far list is copied to LDS, unless the first
+  // block is the gathered one. Every later read of the list follows a barrier of the loop.
+  if (nbc > 0) prefetch(0);
+  if (threadIdx.x < kTileRows) sm.far[threadIdx.x] = clampi(farv, 0, n - 1);
+  lds_barrier();
+  if (nbc == 0) prefetch(0);
   // Enter the loop with the first block's loads complete, as it loops back with the next
   // block's loads complete: the wait the compiler places at the top of the loop then has
   // nothing to wait for, instead of also waiting for the previous block's stores (vector
@@ -320,22 +326,48 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // step 3: compact the lane's query row; absent slots write to the row's spare word
+    // step 3: the lane's query row to LDS. If every row of the wave holds one run of
+    // consecutive key slots (banded patterns), the block's scores are stored as they are,
+    // slot by slot, and the row's run starts at slot `lo`; otherwise present slots are
+    // compacted to positions rank = number of the row's keys in lower slots (absent slots
+    // write to the row's spare word) and lo = 0. Either way the row's entries of this block
+    // are at positions lo .. lo + count - 1, in their CSR order.
     const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+    int lo = 0;
+    bool dense = false;
+    if constexpr (!gat) {
+      lo = m ? (int)__builtin_ctzll(m) : 0;
+      const unsigned long long sh = m >> lo;
+      dense = __builtin_amdgcn_ballot_w64((sh & (sh + 1ull)) != 0ull) == 0ull;
+      lo = dense ? lo : 0;
+    }
+    if (dense) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int s0 = 16 * tt + 4 * g;
-      const unsigned bits = (unsigned)(m >> s0) & 0xfu;
-      const int r0 = __builtin_popcountll(m & ((1ull << s0) - 1ull));
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4_v x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = acc[tt][i] * a.scale;
-        if constexpr (kAdd) x += ac[tt][i];
-        const int pos = (bits >> i) & 1u ? r0 + __builtin_popcount(bits & ((1u << i) - 1u)) : kTileRows;
-        orow[pos] = x;
+        for (int i = 0; i < 4; ++i) {
+          x[i] = acc[tt][i] * a.scale;
+          if constexpr (kAdd) x[i] += ac[tt][i];
+        }
+        *reinterpret_cast<f32x4_v*>(&orow[16 * tt + 4 * g]) = x;
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int s0 = 16 * tt + 4 * g;
+        const unsigned bits = (unsigned)(m >> s0) & 0xfu;
+        const int r0 = __builtin_popcountll(m & ((1ull << s0) - 1ull));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = acc[tt][i] * a.scale;
+          if constexpr (kAdd) x += ac[tt][i];
+          const int pos = (bits >> i) & 1u ? r0 + __builtin_popcount(bits & ((1u << i) - 1u)) : kTileRows;
+          orow[pos] = x;
+        }
       }
     }
-    if (g == 0) sm.run[lr] = i32x4_v{rc.x - (int)e_lo, __builtin_popcountll(m), rc.w, 0};
+    if (g == 0) sm.run[lr] = i32x4_v{rc.x - (int)e_lo, __builtin_popcountll(m), rc.w, lo};
 
     // step 4: copy the wave's rows out (the wave reads only what it wrote: no barrier). The
     // store count per block is fixed (entries past a row's count get an offset the buffer
@@ -350,11 +382,14 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
       const int rq = wave * 16 + lane / 4, qq = lane % 4;
       const i32x4_v ru = sm.run[rq];
       const int cnt = ru.y, qp = cnt >> 2, rem = cnt & 3;
+      const float* src = &sm.out[rq * OS + ru.w];
       u32x4_v part = u32x4_v{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int q = qq + 4 * u;
-        const u32x4_v x = *reinterpret_cast<const u32x4_v*>(&sm.out[rq * OS + 4 * q]);
+        u32x4_v x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __float_as_uint(src[4 * q + i]);
         part = q == qp ? x : part;
         __builtin_amdgcn_raw_buffer_store_b128(x, outb, 4 * q + 3 < cnt ? (ru.x + 4 * q) * 4 : kOffNone, 0, 0);
       }
@@ -383,28 +418,43 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
   if (nblk > nbc) pass(nbc, std::true_type{});
   if (far_vec) {
     // far column f of query lr: the lane's dims 32kc + 8g..+8 of q . k_f, summed over the
-    // four lanes of the query, stored by the first of them if the row holds the column
+    // four lanes of the query, stored by the first of them if the row holds the column. The
+    // key rows (and additive terms) of four far columns are loaded together.
     const i32x4_v rc = tv.rec[nbc * kTileRows + lr];
-    const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
-    for (int f = 0; f < tv.nfar; ++f) {
-      const int kf = sm.far[f];
-      float x = 0.f;
+    constexpr int FG = 4;
+    for (int f0 = 0; f0 < tv.nfar; f0 += FG) {
+      u32x4_v kv[FG][KC];
+      float ad[FG];
+      int kf[FG];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const u32x4_v kv = *reinterpret_cast<const u32x4_v*>(kt + (size_t)kf * D + 32 * kc + 8 * g);
-        const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
+      for (int u = 0; u < FG; ++u) {
+        kf[u] = sm.far[min(f0 + u, tv.nfar - 1)];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[w], x);
+        for (int kc = 0; kc < KC; ++kc)
+          kv[u][kc] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)kf[u] * D + 32 * kc + 8 * g);
+        ad[u] = 0.f;
+        if constexpr (kBias) ad[u] += brow[kf[u]];
+        if constexpr (kMask) ad[u] += kmr[kf[u]];
       }
-      x += shfl_xor(x, 16);
-      x += shfl_xor(x, 32);
-      x *= a.scale;
-      if constexpr (kBias) x += brow[kf];
-      if constexpr (kMask) x += kmr[kf];
-      const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
-      const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
-      const bool st = g == 0 && ((m >> f) & 1ull);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), outb, st ? e * 4 : kOffNone, 0, 0);
+      const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+#pragma unroll
+      for (int u = 0; u < FG; ++u) {
+        const int f = f0 + u;
+        float x = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[u][kc][w], x);
+        }
+        x += shfl_xor(x, 16);
+        x += shfl_xor(x, 32);
+        x = x * a.scale + ad[u];
+        const int rank = __builtin_popcountll(m & ((1ull << (f & 63)) - 1ull));
+        const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
+        const bool st = g == 0 && f < tv.nfar && ((m >> (f & 63)) & 1ull);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), outb, st ? e * 4 : kOffNone, 0, 0);
+      }
     }
   }
 }
