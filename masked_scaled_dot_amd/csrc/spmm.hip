@@ -16,7 +16,7 @@
 //    runs through the same scatter-and-multiply steps;
 //  * sparse tiles and rows without a plan run the vector path: the wave is split into lane
 //    slots that each own one 16-byte column chunk of V and walk every slots-th entry;
-//  * rows longer than the plan's threshold are cut into segments handled by the first
+//  * rows longer than the plan's threshold are cut into segments handled by the last
 //    workgroups of the grid; each segment writes its partial row to the plan's scratch with
 //    device-coherent stores and counts itself in on a per-row counter; the last segment to
 //    arrive sums the partials in segment order, so the result does not depend on timing.
@@ -361,8 +361,12 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   const bool split = plan[kHValid] != 0 && BH <= plan[kHBH] && D <= plan[kHD];
 
 
-  // ---- long-row segments: partial rows, merged by the last segment of each row
-  if ((int)blockIdx.x < kLongWGs) {
+  // ---- long-row segments: partial rows, merged by the last segment of each row. These
+  // workgroups come last in the grid: the tiles are dispatched first and hold every LDS slot
+  // they need, and the segments fill compute units as tiles finish.
+  const int ntile_wgs = (int)gridDim.x - kLongWGs;
+  if ((int)blockIdx.x >= ntile_wgs) {
+    const int lwg = (int)blockIdx.x - ntile_wgs;
     if (!split) return;
     const int S = plan[kHSegs];
     const int* segs = plan + plan[kHOffSegs];
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
     const int pBH = plan[kHBH], pD = plan[kHD];
     const long long tasks = (long long)S * BH;
     using L = Layout<T, D>;
-    for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
+    for (long long task = (long long)lwg * (kThreads / kWave) + wave; task < tasks;
          task += (long long)kLongWGs * (kThreads / kWave)) {
       const int sg = (int)(task % S), t = (int)(task / S);
       const int* it = segs + 8 * sg;
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
 
   // ---- tiles
   const int ntiles = plan[kHTiles];
-  const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
+  const int lb = xcd_logical_block(blockIdx.x, ntile_wgs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
   const TileView tv = tile_view(plan, tile);
