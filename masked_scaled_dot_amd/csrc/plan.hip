@@ -5,8 +5,9 @@
 // "Unified Interface/Implementation for Sparse Attention", replies on variable windows and
 // pattern-specific kernels; "Sparse Attention" notes, local window and global tokens). The
 // plan records, once per pattern and for every head and call:
-//   * per row, its core entry range: the entries within len columns of the row's median
-//     column (for a windowed row: the window; global-token columns fall outside);
+//   * per row, its core entry range: the entries within ceil(len / 2) columns of the row's
+//     median column (a run of len consecutive columns lies inside; for a windowed row: the
+//     window; global-token columns fall outside unless they adjoin it);
 //   * per 64-row tile, the key blocks spanned by the core entries of its rows, the sorted
 //     distinct columns of its other ("far") entries when they fit one gathered 64-key
 //     block (e.g. the global-token columns), and whether these blocks are dense enough
@@ -53,9 +54,9 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int* __restrict__ 
   const long long len = b - a;
   long long lo = a, hi = a;
   if (len > 0 && len <= kLongRow) {
-    const long long med = col_idx[(a + b) >> 1];
-    lo = lower_bound(col_idx, a, b, med - len);
-    hi = lower_bound(col_idx, lo, b, med + len + 1);
+    const long long med = col_idx[(a + b) >> 1], half = (len + 1) >> 1;
+    lo = lower_bound(col_idx, a, b, med - half);
+    hi = lower_bound(col_idx, lo, b, med + half + 1);
   }
   rows[2 * i] = (int)lo;
   rows[2 * i + 1] = (int)hi;
@@ -151,13 +152,14 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
                                                          int* __restrict__ tiles, int ntiles) {
   __shared__ int s_far[kFarMax];
   __shared__ int s_pre[kTileRows + 1];
-  __shared__ int s_min, s_max, s_core, s_far_total;
+  __shared__ int s_min, s_max, s_core, s_far_total, s_banded;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid == 0) {
     s_min = 0x7fffffff;
     s_max = -1;
     s_core = 0;
+    s_banded = 1;
   }
   __syncthreads();
   int nfar = 0, lo = 0, hi = 0;
@@ -177,6 +179,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
           atomicAdd(&s_core, hi - lo);
         }
         nfar = (int)((lo - rs) + (re - hi));
+        // banded row: the core range holds consecutive columns, so within every key block
+        // the row's entries are one run of consecutive slots
+        if (hi > lo && col_idx[hi - 1] - col_idx[lo] != hi - lo - 1) atomicAnd(&s_banded, 0);
       }
     }
     s_pre[tid + 1] = nfar;
@@ -247,7 +252,8 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
     ti[1] = kb_hi;
     ti[2] = mfma ? 1 : 0;
     ti[3] = ok ? U : 0;
-    ti[4] = ti[5] = ti[6] = ti[7] = 0;
+    ti[4] = s_banded;
+    ti[5] = ti[6] = ti[7] = 0;
     s_far_total = mfma ? 1 : 0;  // reused: broadcast the decision
   }
   __syncthreads();

@@ -31,8 +31,10 @@ enum PlanHeader {
 // Word counts of the parts, in layout order: header, rows (2 per row: first and one past
 // the last entry of the row's core range; padded to a multiple of 4 words so that the
 // records below are 16-byte aligned), tiles (kTileInfo per tile: first key block, one
-// past the last key block, 1 if the tile runs on matrix cores, number of far columns, then
-// unused), far columns (64 per tile: the sorted distinct columns of the tile's entries
+// past the last key block, 1 if the tile runs on matrix cores, number of far columns, 1 if
+// every row's core range holds consecutive columns (so a row's entries in a key block are one
+// run of slots), then unused), far columns (64 per tile: the sorted distinct columns of the
+// tile's entries
 // outside the rows' core ranges, when there are at most 64 of them), block records (for a
 // matrix-core tile, per key block j -- the contiguous ones, then the gathered far block --
 // and row r: the row's first entry in the block and a 64-bit mask of the block's key slots

@@ -236,6 +236,9 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
   // loop than as one more gathered 64-key block
   const bool far_vec = tv.nfar > 0 && tv.nfar <= kFarVec;
   const int nblk = far_vec ? nbc : tile_blocks(tv);
+  // blocks whose K rows are loaded: with far_vec, the last contiguous block prefetches the far
+  // block (its first rows are the far columns) for the epilogue
+  const int npre = tile_blocks(tv);
   const int g = lane / 16, c16 = lane % 16;
   const int b = t / a.H, h = t % a.H;
   const int lr = wave * 16 + c16;            // the lane's query row within the tile
@@ -310,7 +313,7 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
 #pragma unroll
     for (int i = 0; i < (kAdd ? 4 : 1); ++i) ac[i] = an[i];
     lds_barrier();                   // block j's K is visible to every wave
-    prefetch(min(j + 1, nblk - 1));  // in flight while block j is computed and written
+    prefetch(min(j + 1, npre - 1));  // in flight while block j is computed and written
 
     // step 2: all four 16x16 products, then (no branch in between) their use
     f32x4_v acc[4];
@@ -414,47 +417,101 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
       }
     }
   };
-  for (int j = 0; j < nbc; ++j) pass(j, std::false_type{});
+  // A banded tile's contiguous blocks (no additive terms): S = Q K^T on the matrix cores, so
+  // that lane (g, c16) holds keys 16tt + c16 of queries 4g + i, sixteen consecutive keys of a
+  // row in sixteen lanes. A row's entries in the block are one run of slots [lo, lo + count),
+  // at consecutive entries from the row's first, so each score is stored straight from the
+  // accumulators (no LDS round trip): sixteen stores per block, each 64 consecutive bytes of
+  // four rows; slots outside the run get an offset the buffer drops.
+  auto pass_banded = [&](int j) {
+    uint16_t* kbuf = sm.k[j & 1];
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&kbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
+    }
+    const i32x4_v rc = rn;
+    const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+    const int lo = m ? (int)__builtin_ctzll(m) : 0;
+    // row lr: entry of slot s = x + s, run [lo, lo + count)
+    if (g == 0) sm.run[lr] = i32x4_v{rc.x - (int)e_lo - lo, lo, __builtin_popcountll(m), 0};
+    lds_barrier();                   // block j's K is visible to every wave
+    prefetch(min(j + 1, npre - 1));  // in flight while block j is computed and written
+    f32x4_v acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      acc[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v kb = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const u32x4_v*>(&kbuf[(16 * tt + c16) * KS + 32 * kc + 8 * g]));
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[kc], kb, acc[tt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    i32x4_v pr[4];  // the runs of the lane's rows 4g + i (written by this wave above)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = sm.run[wave * 16 + 4 * g + i];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * tt + c16;
+        const bool in = (unsigned)(key - pr[i].y) < (unsigned)pr[i].z;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[tt][i] * a.scale), outb,
+                                              in ? (pr[i].x + key) * 4 : kOffNone, 0, 0);
+      }
+  };
+  bool done = false;
+  if constexpr (!kAdd) {
+    if (tv.banded) {
+      for (int j = 0; j < nbc; ++j) pass_banded(j);
+      done = true;
+    }
+  }
+  if (!done)
+    for (int j = 0; j < nbc; ++j) pass(j, std::false_type{});
   if (nblk > nbc) pass(nbc, std::true_type{});
   if (far_vec) {
-    // far column f of query lr: the lane's dims 32kc + 8g..+8 of q . k_f, summed over the
-    // four lanes of the query, stored by the first of them if the row holds the column. The
-    // key rows (and additive terms) of four far columns are loaded together.
-    const i32x4_v rc = tv.rec[nbc * kTileRows + lr];
-    constexpr int FG = 4;
-    for (int f0 = 0; f0 < tv.nfar; f0 += FG) {
-      u32x4_v kv[FG][KC];
-      float ad[FG];
-      int kf[FG];
+    // Far column f of query lr: its K row is row f of the far block, which the last pass left
+    // in the stage registers (with the block's record and additive terms); staged in the LDS
+    // buffer the last pass did not use. The lane's dims 32kc + 8g..+8 of q . k_f are summed
+    // over the query's four lanes; lane g = f / 4 holds the additive term of slot f and stores
+    // the score if the row holds the column.
+    uint16_t* fbuf = sm.k[nbc & 1];
 #pragma unroll
-      for (int u = 0; u < FG; ++u) {
-        kf[u] = sm.far[min(f0 + u, tv.nfar - 1)];
+    for (int u = 0; u < KCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&fbuf[(i / (D / 8)) * KS + (i % (D / 8)) * 8]) = kn[u];
+    }
+    const i32x4_v rc = rn;
+    f32x4_v ac[kAdd ? 4 : 1];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          kv[u][kc] = *reinterpret_cast<const u32x4_v*>(kt + (size_t)kf[u] * D + 32 * kc + 8 * g);
-        ad[u] = 0.f;
-        if constexpr (kBias) ad[u] += brow[kf[u]];
-        if constexpr (kMask) ad[u] += kmr[kf[u]];
+    for (int i = 0; i < (kAdd ? 4 : 1); ++i) ac[i] = an[i];
+    lds_barrier();
+    const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+    for (int f = 0; f < tv.nfar; ++f) {
+      float x = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4_v kv = *reinterpret_cast<const u32x4_v*>(&fbuf[f * KS + 32 * kc + 8 * g]);
+        const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[w], x);
       }
-      const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+      x += shfl_xor(x, 16);
+      x += shfl_xor(x, 32);
+      x *= a.scale;
+      if constexpr (kAdd) {
+        float ad = ac[0][0];
 #pragma unroll
-      for (int u = 0; u < FG; ++u) {
-        const int f = f0 + u;
-        float x = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const u32x4_v qv = __builtin_bit_cast(u32x4_v, qb[kc]);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) x = dot2_bf16(qv[w], kv[u][kc][w], x);
-        }
-        x += shfl_xor(x, 16);
-        x += shfl_xor(x, 32);
-        x = x * a.scale + ad[u];
-        const int rank = __builtin_popcountll(m & ((1ull << (f & 63)) - 1ull));
-        const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
-        const bool st = g == 0 && f < tv.nfar && ((m >> (f & 63)) & 1ull);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), outb, st ? e * 4 : kOffNone, 0, 0);
+        for (int i = 1; i < 4; ++i) ad = (f & 3) == i ? ac[0][i] : ad;
+        x += ad;
       }
+      const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
+      const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
+      const bool st = g == (f >> 2) && ((m >> f) & 1ull);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), outb, st ? e * 4 : kOffNone, 0, 0);
     }
   }
 }

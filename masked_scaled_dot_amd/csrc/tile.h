@@ -34,6 +34,7 @@ __device__ __forceinline__ void mfma_drain() {
 struct TileView {
   int kb_lo, kb_hi, nfar;
   bool mfma;
+  bool banded;          // every row's entries in every contiguous block are one run of slots
   const int* far_cols;  // nfar ascending columns
   const i32x4_v* rec;   // block records [block][row]: first entry, mask low, mask high, aux
 };
@@ -47,6 +48,7 @@ __device__ __forceinline__ TileView tile_view(const int* plan, int tile) {
   v.kb_hi = ti[1];
   v.mfma = ti[2] != 0;
   v.nfar = ti[3];
+  v.banded = ti[4] != 0;
   v.far_cols = base + (long long)kTileInfo * ntiles + (long long)kTileRows * tile;
   v.rec = reinterpret_cast<const i32x4_v*>(base + (long long)(kTileInfo + kTileRows) * ntiles +
                                         (long long)kBoundsPerTile * tile);

@@ -267,15 +267,15 @@ def _host_plan(p, BH, d):
         a, b = rp[i], rp[i + 1]
         L = b - a
         if 0 < L <= 1024:
-            med = ci[(a + b) // 2]
-            lo = a + np.searchsorted(ci[a:b], med - L, "left")
-            hi = a + np.searchsorted(ci[a:b], med + L, "right")
+            med, half = ci[(a + b) // 2], (L + 1) // 2
+            lo = a + np.searchsorted(ci[a:b], med - half, "left")
+            hi = a + np.searchsorted(ci[a:b], med + half, "right")
             rows[i] = lo, hi
         else:
             rows[i] = a, a
     tiles, fars = [], []
     for t0 in range(0, n, 64):
-        lo, hi, core, farcols = None, None, 0, []
+        lo, hi, core, farcols, banded = None, None, 0, [], 1
         for i in range(t0, min(n, t0 + 64)):
             a, b = rp[i], rp[i + 1]
             if b - a > 1024:
@@ -285,13 +285,15 @@ def _host_plan(p, BH, d):
                 lo = c0 if lo is None else min(lo, c0)
                 hi = c1 if hi is None else max(hi, c1)
                 core += rows[i, 1] - rows[i, 0]
+                if c1 - c0 != rows[i, 1] - rows[i, 0] - 1:  # core columns not consecutive
+                    banded = 0
             farcols += list(ci[a:rows[i, 0]]) + list(ci[rows[i, 1]:b])
         uniq = sorted(set(farcols))
         ok = len(farcols) <= 1024 and len(uniq) <= 64
         kb0, kb1 = (0, 0) if hi is None else (lo // 64, hi // 64 + 1)
         nblk = (kb1 - kb0) + (1 if uniq else 0)
         mfma = ok and nblk > 0 and kb1 - kb0 <= 12 and core + len(farcols) >= 0.25 * 64 * 64 * nblk
-        tiles.append((kb0, kb1, int(mfma), len(uniq) if ok else 0, 0, 0, 0, 0))
+        tiles.append((kb0, kb1, int(mfma), len(uniq) if ok else 0, banded, 0, 0, 0))
         fars.append(uniq if ok else None)
     segs = []
     lr = 0
@@ -360,6 +362,7 @@ def test_plan_build_matches_host(name):
                 assert got == (a, m & 0xffffffff, m >> 32, aux), (ti, r)
     if name == "longformer_long_rows":
         assert tiles[20, 2] == 1 and fars[20] == [0, 1]      # global-token columns gathered
+        assert tiles[20, 4] == 1                             # window rows: banded
     assert np.array_equal(h[h[12]:h[12] + 8 * len(segs)].reshape(-1, 8), segs)
     assert np.all(h[h[13]:h[13] + L * p.BH] == 0)                       # merge counters
     assert h[15] * 4 <= plan.numel() * 4
