@@ -103,14 +103,15 @@ class EventTimer:
         e.record()
         return e
 
-    def add(self, name, a, b):
-        self.pending.append((name, a, b))
+    def add(self, name, a, b, reps=1):
+        """Events a, b bracket `reps` back-to-back launches of one kernel."""
+        self.pending.append((name, a, b, reps))
 
     def result(self):
         self.torch.cuda.synchronize()
         out = {}
-        for name, a, b in self.pending:
-            out.setdefault(name, []).append(a.elapsed_time(b) * 1e3)  # us
+        for name, a, b, reps in self.pending:
+            out.setdefault(name, []).append(a.elapsed_time(b) * 1e3 / reps)  # us per launch
         return {k: float(np.mean(v)) for k, v in out.items()}
 
 
@@ -144,8 +145,9 @@ def bytes_fused(p, nnz_blocks=None):
 
 def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     """Build the row plan once (it depends on the mask only), then run `steps` passes of
-    SDDMM -> sparse softmax -> SpMM, first launched one call at a time with HIP events around
-    each kernel (per-kernel durations), then as one HIP graph per step (the step rate).
+    SDDMM -> sparse softmax -> SpMM launched one call at a time (the eager rate), time each
+    kernel over `steps` back-to-back launches between HIP events (per-kernel durations), then
+    run the steps as one HIP graph per step (the step rate).
     Returns (wall seconds of the graph-launched steps, wall seconds of the eager steps,
     plan build us)."""
     scores = torch.empty(BH * nnz, device="cuda:0")
@@ -160,33 +162,37 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     plan_us = pt.result()["plan"]
     prob.set_plan(plan)
 
-    def step(tm):
-        e1 = tm.mark() if tm else None
-        sa.sa_sddmm(prob, t["q"], t["k"], scores)
-        e2 = tm.mark() if tm else None
-        sa.sa_sparse_softmax(prob, scores, weights)
-        e3 = tm.mark() if tm else None
-        sa.sa_spmm(prob, weights, t["v"], out)
-        e4 = tm.mark() if tm else None
-        if tm:
-            tm.add("sddmm", e1, e2)
-            tm.add("softmax", e2, e3)
-            tm.add("spmm", e3, e4)
+    calls = {"sddmm": lambda: sa.sa_sddmm(prob, t["q"], t["k"], scores),
+             "softmax": lambda: sa.sa_sparse_softmax(prob, scores, weights),
+             "spmm": lambda: sa.sa_spmm(prob, weights, t["v"], out)}
+
+    def step(_=None):
+        for f in calls.values():
+            f()
 
     for _ in range(warmup):
-        step(None)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(timer)
+        step()
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t0
+    # per-kernel durations: each call `steps` times back to back between two HIP events on the
+    # stream the kernels run on (the inputs are the pipeline's own: the step above left them),
+    # so the launch gaps between calls stay hidden, as in a kernel trace
+    for name, f in calls.items():
+        a = timer.mark()
+        for _ in range(steps):
+            f()
+        b = timer.mark()
+        timer.add(name, a, b, steps)
 
     # the same three calls captured once as a HIP graph (the kernels allocate nothing and
     # take no host decision after the plan is built), replayed once per step
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step(None)
+        step()
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -199,8 +205,8 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
 
 
 def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
-    """Average HIP-event time of one fused forward; an element CSR gets its row plan first
-    (built once per mask, as for the pipeline)."""
+    """Average HIP-event time of one fused forward over `iters` back-to-back launches; an
+    element CSR gets its row plan first (built once per mask, as for the pipeline)."""
     prob, t, nnz = to_device(p, torch, sa, element=element)
     if prob.c.row_ptr and prob.c.block == 1:
         t["plan"] = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
@@ -211,11 +217,11 @@ def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
     for _ in range(warmup):
         sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
     tm = EventTimer(torch)
+    a = tm.mark()
     for _ in range(iters):
-        a = tm.mark()
         sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
-        b = tm.mark()
-        tm.add("fused", a, b)
+    b = tm.mark()
+    tm.add("fused", a, b, iters)
     us = tm.result()["fused"]
     del t, out, lse
     return us
