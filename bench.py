@@ -1,8 +1,9 @@
 """Benchmark of masked scaled dot-product attention over a CSR mask on one MI355X.
 
 A step is one pass of the CSR path over one batch of synthetic input: SDDMM, sparse
-softmax and SpMM (scores, weights and context), launched as one HIP graph, on the Longformer-style
-workload (12 heads, n=4096, d=64, bf16, window |i-j|<=128 plus global tokens 0 and 1).
+softmax and SpMM (scores, weights and context), replayed from a HIP graph of several steps,
+on the Longformer-style workload (12 heads, n=4096, d=64, bf16, window |i-j|<=128 plus
+global tokens 0 and 1).
 The row plan (a function of the mask alone) is built once before timing and reported
 separately. Inputs are resident in HBM before timing starts. The JSON line reports attended pairs/s
 (value), per-kernel durations from HIP events recorded on the stream the kernels run
@@ -147,9 +148,9 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     """Build the row plan once (it depends on the mask only), then run `steps` passes of
     SDDMM -> sparse softmax -> SpMM launched one call at a time (the eager rate), time each
     kernel over `steps` back-to-back launches between HIP events (per-kernel durations), then
-    run the steps as one HIP graph per step (the step rate).
+    run the steps again from a HIP graph of several steps (the step rate).
     Returns (wall seconds of the graph-launched steps, wall seconds of the eager steps,
-    plan build us)."""
+    plan build us, steps per graph)."""
     scores = torch.empty(BH * nnz, device="cuda:0")
     weights = torch.empty_like(scores)
     out = torch.empty(BH, n, d, device="cuda:0")
@@ -188,20 +189,23 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
         b = timer.mark()
         timer.add(name, a, b, steps)
 
-    # the same three calls captured once as a HIP graph (the kernels allocate nothing and
-    # take no host decision after the plan is built), replayed once per step
+    # the same calls captured as a HIP graph of `chunk` steps (the kernels allocate nothing and
+    # take no host decision after the plan is built; chunk is the largest divisor of `steps`
+    # up to 10, so the replays run exactly `steps` steps), replayed steps / chunk times
+    chunk = max(c for c in range(1, min(steps, 10) + 1) if steps % c == 0)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step()
-    for _ in range(warmup):
+        for _ in range(chunk):
+            step()
+    for _ in range(max(1, warmup // chunk)):
         graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(steps // chunk):
         graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, eager_wall, plan_us
+    return wall, eager_wall, plan_us, chunk
 
 
 def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
@@ -311,13 +315,13 @@ def main():
     log(f"workload {p.name}: BH={BH} n={n} d={d} nnz/head={nnz} pairs/step={pairs}")
 
     timer = EventTimer(torch)
-    wall, eager_wall, plan_us = run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, args.steps,
-                                                   args.warmup, timer)
+    wall, eager_wall, plan_us, chunk = run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d,
+                                                          args.steps, args.warmup, timer)
     kern_us = timer.result()
     ms_per_step = wall * 1e3 / args.steps
     value = pairs / (wall / args.steps)
-    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step (graph), {eager_wall * 1e6 / args.steps:.1f} "
-        f"us/step (eager)  " +
+    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step (graph of {chunk} steps), "
+        f"{eager_wall * 1e6 / args.steps:.1f} us/step (eager)  " +
         "  ".join(f"{k}={v:.1f}us" for k, v in kern_us.items()))
 
     algo = bytes_pipeline(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
@@ -377,8 +381,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "config": {"workload": p.name, "B": p.B, "H": p.H, "n": n, "d": d, "nnz_per_head": nnz,
                    "pairs_per_step": pairs,
-                   "step": "sddmm + sparse_softmax + spmm (scores, weights, context), launched as one "
-                           "HIP graph per step; the row plan is built once per mask before timing",
+                   "step": "sddmm + sparse_softmax + spmm (scores, weights, context); the row plan "
+                           "is built once per mask before timing",
+                   "launch": f"HIP graph of {chunk} steps, replayed {args.steps // chunk} times",
                    "eager_ms_per_step": round(eager_wall * 1e3 / args.steps, 5),
                    "inputs": "resident in HBM; caches not flushed between steps"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "extra": extra,
