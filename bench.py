@@ -356,6 +356,27 @@ def main():
             "valu_frac": round(flops / (fused_us * 1e-6) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
             "hbm_frac": round(bytes_fused(p) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del t
+        # the random-row workload (rows of 32-512 random columns): every tile takes the
+        # vector path, whose key/value row gathers bound it
+        rq = gen.make("random_n8192")
+        rprob, rt, rnnz = to_device(rq, torch, sa)
+        rtimer = EventTimer(torch)
+        _, reager, _, _ = run_pipeline_steps(torch, sa, rprob, rt, rnnz, rq.BH, rq.n, rq.d, 10, 2, rtimer)
+        rk = rtimer.result()
+        ralgo = bytes_pipeline(rq.BH, rq.n, rq.d, rnnz, 2)
+        rpairs = rq.BH * rnnz
+        extra["pipeline_" + rq.name] = {
+            "us_per_step_eager": round(reager * 1e6 / 10, 2), "pairs_per_s": rpairs / (reager / 10),
+            "kernels_us": {k: round(v, 2) for k, v in rk.items()},
+            "hbm_frac": {k: round(ralgo[k] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k, v in rk.items()}}
+        fr = time_fused(torch, sa, rq)
+        extra["fused_csr_" + rq.name] = {
+            "us": round(fr, 2), "pairs_per_s": rpairs / (fr * 1e-6),
+            "TFLOP_s": round(4.0 * rpairs * rq.d / (fr * 1e-6) / 1e12, 2),
+            "hbm_frac": round(bytes_fused(rq) / (fr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"random_n8192: pipeline {reager * 1e6 / 10:.1f} us/step (eager) " +
+            "  ".join(f"{k}={v:.1f}us" for k, v in rk.items()) + f", fused {fr:.1f} us")
+        del rt, rprob
         for name in ("bsr_n16384", "evoformer_l384"):
             q = gen.make(name)
             us = time_fused(torch, sa, q)
