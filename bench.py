@@ -353,6 +353,9 @@ def main():
         extra["fused_csr_" + p.name] = {
             "us": round(fused_us, 2), "pairs_per_s": pairs / (fused_us * 1e-6),
             "TFLOP_s": round(flops / (fused_us * 1e-6) / 1e12, 2),
+            # the tiles of this workload run on the matrix cores (bf16); the vector-ALU
+            # fraction is the bound for tiles that take the vector path
+            "mfma_frac": round(flops / (fused_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "valu_frac": round(flops / (fused_us * 1e-6) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
             "hbm_frac": round(bytes_fused(p) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del t
