@@ -13,10 +13,13 @@ Two evaluations of the same definition are provided:
   ("Unified Interface/Implementation for Sparse Attention", the three bullet
   points of the opening post): scores at the mask's nonzeros, a softmax over
   each sparse row, and the sparse-times-dense product, in fp64.
+* :mod:`oracle.backward` -- the gradients with respect to q, k and v: the chain
+  rule through the three steps, and torch autograd (fp64, CPU) of the dense
+  definition.
 
 Both follow the same conventions (see the module docstrings). Every function
 here has a pin in ``tests/test_oracle_pins.py`` other than itself.
 """
-from . import dense, csr  # noqa: F401
+from . import dense, csr, backward  # noqa: F401
 from .dense import attention_dense, attention_rows, pattern_rows  # noqa: F401
 from .csr import sddmm, sparse_softmax, spmm, attention_csr  # noqa: F401
