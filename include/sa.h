@@ -149,12 +149,44 @@ int sa_spmm(const sa_problem *p, const float *weights, const void *v, float *out
  * rescaled when the maximum grows, and one division at the end (streaming-dataflow SDPA
  * review, "proposed method"); never writes S or W. Accepts every pattern kind, bias and
  * key_mask. out: fp32 [B*H, n, d]. lse: NULL or fp32 [B*H, n].
- * Element CSR runs on the vector ALUs; block CSR (block == 64) and the dense pattern run
- * 64-query tiles on bf16 matrix cores when dtype == SA_BF16, as each stored tile is a dense
- * product (block-sparse replies of the gluon-nlp issue; the AlphaFold2 pull request for
- * the dense pattern with bias and key mask). */
+ * Element CSR with a plan runs the plan's dense-enough 64-row tiles on bf16 matrix cores
+ * (dtype == SA_BF16) and the other rows on the vector ALUs (without a plan: all rows on the
+ * vector ALUs); block CSR (block == 64) and the dense pattern run 64-query tiles on bf16
+ * matrix cores when dtype == SA_BF16, as each stored tile is a dense product (block-sparse
+ * replies of the gluon-nlp issue; the AlphaFold2 pull request for the dense pattern with
+ * bias and key mask). */
 int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const void *v,
                      float *out, float *lse, hipStream_t stream);
+
+/* --- Backward pass of the CSR pipeline -----------------------------------------------------
+ * With dO the gradient of a loss with respect to the context, the chain rule through the
+ * three steps of the gluon-nlp proposal (opening post), taken in reverse, is, per head and
+ * stored entry (i, j):  dW = dO[i].v[j] (sa_sddmm of dO and V at scale 1, no bias/mask),
+ * dS = W (dW - sum_row W dW) (sa_sparse_softmax_backward), dQ = scale * dS K (sa_spmm),
+ * dK = scale * dS^T Q and dV = W^T dO (sa_spmm over the transposed pattern, with dS and W
+ * gathered into its order by sa_gather_entries). dS is also the gradient of the additive
+ * bias and key mask at the stored entries. Element CSR only.
+ *
+ * sa_transpose_workspace_bytes: device workspace bytes sa_csr_transpose needs (host-only;
+ *   0 on a bad descriptor).
+ * sa_csr_transpose: the transposed pattern, built on the device on stream: row_ptr_t
+ *   int32 [n+1], col_idx_t int32 [nnz] (each column's rows, ascending) and perm int32 [nnz]
+ *   (perm[k] = index in the original CSR of transposed entry k). Depends on the pattern
+ *   only: build it once per mask. All buffers are caller-owned; workspace is scratch for the
+ *   duration of the call (SA_ERR_WORKSPACE if smaller than the size above).
+ * sa_gather_entries: dst[t*nnz + k] = src[t*nnz + perm[k]] for every head t; src and dst
+ *   are fp32 [B*H, nnz] and must not alias.
+ * sa_sparse_softmax_backward: dscores[t*nnz + e] = out_scale * W[e] * (dW[e] - D_row),
+ *   D_row = sum over the row's entries of W * dW; weights, dweights and dscores are fp32
+ *   [B*H, nnz] (dscores may alias dweights). out_scale = scale gives the operand of dQ
+ *   and dK; out_scale = 1 gives the gradient of the scores. */
+size_t sa_transpose_workspace_bytes(const sa_problem *p);
+int sa_csr_transpose(const sa_problem *p, int32_t *row_ptr_t, int32_t *col_idx_t, int32_t *perm,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+int sa_gather_entries(const sa_problem *p, const int32_t *perm, const float *src, float *dst,
+                      hipStream_t stream);
+int sa_sparse_softmax_backward(const sa_problem *p, const float *weights, const float *dweights,
+                               float out_scale, float *dscores, hipStream_t stream);
 
 /* --- Validation and status ----------------------------------------------------------------
  * sa_validate_csr: checks the pattern on the device (monotone row_ptr starting at 0,

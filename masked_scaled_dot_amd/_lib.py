@@ -30,7 +30,9 @@ SA_BF16 = 1
 SA_FLAG_VALIDATE = 1
 
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
-           "sa_fused_forward", "sa_validate_csr", "sa_status_string", "sa_last_hip_error_string")
+           "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
+           "sa_gather_entries", "sa_sparse_softmax_backward", "sa_validate_csr",
+           "sa_status_string", "sa_last_hip_error_string")
 
 
 class sa_problem(ctypes.Structure):
@@ -65,6 +67,10 @@ def _load():
         "sa_sparse_softmax": (ctypes.c_int, [P, vp, vp, vp]),
         "sa_spmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_fused_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
+        "sa_transpose_workspace_bytes": (sz, [P]),
+        "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
         "sa_validate_csr": (ctypes.c_int, [P, vp]),
         "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "sa_last_hip_error_string": (ctypes.c_char_p, []),
@@ -225,6 +231,41 @@ def sa_fused_forward(prob, q, k, v, out, lse=None, stream=None):
     _check(lse, "lse", c.B * c.H * c.n, f32)
     _raise(_lib.sa_fused_forward(_p(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                  _stream(stream)), "sa_fused_forward")
+
+
+def sa_transpose_workspace_bytes(prob) -> int:
+    return int(_lib.sa_transpose_workspace_bytes(_p(prob)))
+
+
+def sa_csr_transpose(prob, row_ptr_t, col_idx_t, perm, workspace, stream=None):
+    c = _c(prob)
+    i32 = _torch().int32
+    _check(row_ptr_t, "row_ptr_t", c.n + 1, i32)
+    _check(col_idx_t, "col_idx_t", c.nnz, i32)
+    _check(perm, "perm", c.nnz, i32)
+    nbytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else 0
+    _raise(_lib.sa_csr_transpose(_p(prob), _ptr(row_ptr_t), _ptr(col_idx_t), _ptr(perm),
+                                 _ptr(workspace), nbytes, _stream(stream)), "sa_csr_transpose")
+
+
+def sa_gather_entries(prob, perm, src, dst, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    _check(perm, "perm", c.nnz, _torch().int32)
+    _check(src, "src", c.B * c.H * c.nnz, f32)
+    _check(dst, "dst", c.B * c.H * c.nnz, f32)
+    _raise(_lib.sa_gather_entries(_p(prob), _ptr(perm), _ptr(src), _ptr(dst), _stream(stream)),
+           "sa_gather_entries")
+
+
+def sa_sparse_softmax_backward(prob, weights, dweights, out_scale, dscores, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    for x, name in ((weights, "weights"), (dweights, "dweights"), (dscores, "dscores")):
+        _check(x, name, c.B * c.H * c.nnz, f32)
+    _raise(_lib.sa_sparse_softmax_backward(_p(prob), _ptr(weights), _ptr(dweights),
+                                           float(out_scale), _ptr(dscores), _stream(stream)),
+           "sa_sparse_softmax_backward")
 
 
 def sa_validate_csr(prob, stream=None) -> int:

@@ -204,6 +204,44 @@ int sa_fused_forward(const sa_problem* p, const void* q, const void* k, const vo
   return hip_status(sa::launch_fused_valu(*p, q, k, v, out, lse, stream));
 }
 
+size_t sa_transpose_workspace_bytes(const sa_problem* p) {
+  if (check_problem(p, kOpSoftmax) != SA_OK) return 0;
+  return sa::transpose_workspace_bytes(p->n, p->nnz);
+}
+
+int sa_csr_transpose(const sa_problem* p, int32_t* row_ptr_t, int32_t* col_idx_t, int32_t* perm,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);  // element CSR
+  if (st != SA_OK) return st;
+  if (!row_ptr_t || (p->nnz > 0 && (!col_idx_t || !perm || !workspace))) return SA_ERR_NULL;
+  if (p->n == 0) return SA_OK;
+  if (p->nnz > 0 && workspace_bytes < sa::transpose_workspace_bytes(p->n, p->nnz)) return SA_ERR_WORKSPACE;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_csr_transpose(*p, row_ptr_t, col_idx_t, perm, workspace, workspace_bytes, stream));
+}
+
+int sa_gather_entries(const sa_problem* p, const int32_t* perm, const float* src, float* dst,
+                      hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!perm || !src || !dst) return SA_ERR_NULL;
+  if (src == dst) return SA_ERR_SHAPE;  // a permutation cannot be applied in place here
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_gather_entries(*p, perm, src, dst, stream));
+}
+
+int sa_sparse_softmax_backward(const sa_problem* p, const float* weights, const float* dweights,
+                               float out_scale, float* dscores, hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (!std::isfinite(out_scale)) return SA_ERR_SHAPE;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!weights || !dweights || !dscores) return SA_ERR_NULL;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_softmax_backward(*p, weights, dweights, out_scale, dscores, stream));
+}
+
 int sa_validate_csr(const sa_problem* p, hipStream_t stream) {
   const int st = check_problem(p, kOpValidate);
   if (st != SA_OK) return st;

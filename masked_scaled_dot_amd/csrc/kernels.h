@@ -18,6 +18,15 @@ hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, 
                              float* out, float* lse, hipStream_t s);
 bool fused_tile_supported(const sa_problem& p);
 
+// Backward pass pieces: pattern transpose, per-entry gather, softmax gradient.
+size_t transpose_workspace_bytes(long long n, long long nnz);
+hipError_t launch_csr_transpose(const sa_problem& p, int* row_ptr_t, int* col_idx_t, int* perm,
+                                void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_gather_entries(const sa_problem& p, const int* perm, const float* src, float* dst,
+                                 hipStream_t s);
+hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const float* dw,
+                                   float out_scale, float* ds, hipStream_t s);
+
 // CSR row plan and validation.
 size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);
 hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_t s);

@@ -177,3 +177,37 @@ def test_single_hip_runtime_shared_with_torch():
     maps = open("/proc/self/maps").read().splitlines()
     hip = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
     assert len(hip) == 1, hip
+
+
+# ---- backward-pass entry points (host checks only)
+
+BWD = [("sa_gather_entries", 4), ("sa_csr_transpose", 6)]
+
+
+def test_backward_calls_reject_bad_descriptors():
+    f = _lib.raw
+    for p, st in ((None, sa.SA_ERR_NULL), (_prob(row_ptr=None), sa.SA_ERR_UNSUPPORTED),
+                  (_prob(block=64, nnz=4), sa.SA_ERR_UNSUPPORTED), (_prob(dtype=7), sa.SA_ERR_DTYPE)):
+        ref = ctypes.byref(p) if p is not None else None
+        assert f("sa_gather_entries")(ref, FAKE, FAKE, FAKE + 64, None) == st
+        assert f("sa_sparse_softmax_backward")(ref, FAKE, FAKE, 1.0, FAKE, None) == st
+        assert f("sa_csr_transpose")(ref, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == st
+        if p is not None:
+            assert f("sa_transpose_workspace_bytes")(ref) == 0
+
+
+def test_backward_calls_check_buffers_and_arguments():
+    f, p = _lib.raw, ctypes.byref(_prob())
+    assert f("sa_gather_entries")(p, None, FAKE, FAKE + 64, None) == sa.SA_ERR_NULL
+    assert f("sa_gather_entries")(p, FAKE, FAKE, FAKE, None) == sa.SA_ERR_SHAPE  # in place
+    assert f("sa_sparse_softmax_backward")(p, FAKE, None, 1.0, FAKE, None) == sa.SA_ERR_NULL
+    assert f("sa_sparse_softmax_backward")(p, FAKE, FAKE, float("inf"), FAKE, None) == sa.SA_ERR_SHAPE
+    assert f("sa_csr_transpose")(p, None, FAKE, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
+    assert f("sa_csr_transpose")(p, FAKE, FAKE, FAKE, None, 1 << 30, None) == sa.SA_ERR_NULL
+    assert f("sa_csr_transpose")(p, FAKE, FAKE, FAKE, FAKE, 64, None) == sa.SA_ERR_WORKSPACE
+    # keys and values are sorted out of place: at least 2 x (8 + 4) bytes per entry
+    assert f("sa_transpose_workspace_bytes")(p) >= 24 * 500
+    for field in ("B", "H"):
+        q = ctypes.byref(_prob(**{field: 0}, nnz=0))
+        assert f("sa_gather_entries")(q, None, None, None, None) == sa.SA_OK
+        assert f("sa_sparse_softmax_backward")(q, None, None, 1.0, None, None) == sa.SA_OK
