@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
-    ap.add_argument("--profile", choices=["pipeline", "fused_csr", "fused_bsr", "fused_dense", "copy"],
+    ap.add_argument("--profile", choices=["pipeline", "backward", "fused_csr", "fused_bsr", "fused_dense", "copy"],
                     help="run only this kernel family (steps iterations after warmup) and exit; "
                          "for rocprofv3 runs")
     return ap.parse_args()
@@ -182,7 +182,7 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     # per-kernel durations: each call `steps` times back to back between two HIP events on the
     # stream the kernels run on (the inputs are the pipeline's own: the step above left them),
     # so the launch gaps between calls stay hidden, as in a kernel trace
-    for name, f in calls.items():
+    for name, f in calls.items() if timer is not None else ():
         a = timer.mark()
         for _ in range(steps):
             f()
@@ -206,6 +206,81 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, eager_wall, plan_us, chunk
+
+
+def run_backward_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
+    """The backward pass of the CSR pipeline for an upstream gradient dO (bf16, N(0,1)):
+    dW = SDDMM(dO, V) at scale 1, dS = softmax gradient (times the scale), dQ = SpMM(dS, K),
+    dS and W gathered into the transposed pattern's order, dK = SpMM^T(dS, Q),
+    dV = SpMM^T(W, dO). The transposed pattern and both row plans are built once per mask
+    before timing; the forward weights come from one forward pass. Returns (wall seconds of
+    `steps` eager backward steps, us per kernel call from back-to-back launches)."""
+    dtype = prob.c.dtype
+    plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+    sa.sa_plan_build(prob, plan)
+    prob.set_plan(plan)
+    rpt = torch.empty(n + 1, dtype=torch.int32, device="cuda:0")
+    cit = torch.empty(nnz, dtype=torch.int32, device="cuda:0")
+    perm = torch.empty(nnz, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(sa.sa_transpose_workspace_bytes(prob), dtype=torch.uint8, device="cuda:0")
+    sa.sa_csr_transpose(prob, rpt, cit, perm, ws)
+    del ws
+    c = prob.c
+    prob_dw = sa.Problem(c.B, c.H, n, d, dtype, t["row_ptr"], t["col_idx"], nnz, scale=1.0)
+    prob_t = sa.Problem(c.B, c.H, n, d, dtype, rpt, cit, nnz, scale=c.scale)
+    keep = []
+    for pr in (prob_dw, prob_t):
+        buf = torch.zeros(sa.sa_plan_bytes(pr) // 4 + 1, dtype=torch.int32, device="cuda:0")
+        sa.sa_plan_build(pr, buf)
+        pr.set_plan(buf)
+        keep.append(buf)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    dO = torch.randn(BH, n, d, generator=g).to("cuda:0", t["q"].dtype)
+    S = torch.empty(BH * nnz, device="cuda:0")
+    W = torch.empty_like(S)
+    sa.sa_sddmm(prob, t["q"], t["k"], S)
+    sa.sa_sparse_softmax(prob, S, W)
+    dW, dS, Wt, dSt = (torch.empty_like(S) for _ in range(4))
+    dQ, dK, dV = (torch.empty(BH, n, d, device="cuda:0") for _ in range(3))
+    calls = {"sddmm_dO_V": lambda: sa.sa_sddmm(prob_dw, dO, t["v"], dW),
+             "softmax_backward": lambda: sa.sa_sparse_softmax_backward(prob, W, dW, c.scale, dS),
+             "spmm_dS_K": lambda: sa.sa_spmm(prob, dS, t["k"], dQ),
+             "gather_dS": lambda: sa.sa_gather_entries(prob, perm, dS, dSt),
+             "gather_W": lambda: sa.sa_gather_entries(prob, perm, W, Wt),
+             "spmmT_dS_Q": lambda: sa.sa_spmm(prob_t, dSt, t["q"], dK),
+             "spmmT_W_dO": lambda: sa.sa_spmm(prob_t, Wt, dO, dV)}
+
+    def step():
+        for f in calls.values():
+            f()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for name, f in calls.items() if timer is not None else ():
+        a = timer.mark()
+        for _ in range(steps):
+            f()
+        b = timer.mark()
+        timer.add(name, a, b, steps)
+    del keep
+    return wall
+
+
+def bytes_backward(BH, n, d, nnz, elem):
+    """Unique bytes of each backward call (as bytes_pipeline: gathered rows counted once)."""
+    qkv = BH * n * d * elem
+    csr = 4 * (n + 1) + 4 * nnz
+    e4 = 4 * BH * nnz
+    spmm = e4 + csr + qkv + 4 * BH * n * d
+    return {"sddmm_dO_V": 2 * qkv + csr + e4, "softmax_backward": 4 * (n + 1) + 3 * e4,
+            "spmm_dS_K": spmm, "gather_dS": 2 * e4 + 4 * nnz, "gather_W": 2 * e4 + 4 * nnz,
+            "spmmT_dS_Q": spmm, "spmmT_W_dO": spmm}
 
 
 def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
@@ -282,6 +357,10 @@ def profile_only(args, torch, sa, gen):
         p = gen.make(args.workload)
         prob, t, nnz = to_device(p, torch, sa)
         run_pipeline_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d, args.steps, args.warmup, None)
+    elif args.profile == "backward":
+        p = gen.make(args.workload)
+        prob, t, nnz = to_device(p, torch, sa)
+        run_backward_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d, args.steps, args.warmup, None)
     else:
         name = {"fused_csr": args.workload, "fused_bsr": "bsr_n16384",
                 "fused_dense": "evoformer_l384"}[args.profile]
@@ -359,6 +438,20 @@ def main():
             "valu_frac": round(flops / (fused_us * 1e-6) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
             "hbm_frac": round(bytes_fused(p) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del t
+        # the backward pass of the CSR pipeline on the main workload
+        bprob, bt, _ = to_device(p, torch, sa)
+        btimer = EventTimer(torch)
+        bwall = run_backward_steps(torch, sa, bprob, bt, nnz, BH, n, d, 20, 3, btimer)
+        bk = btimer.result()
+        balgo = bytes_backward(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
+        extra["backward_" + p.name] = {
+            "us_per_step_eager": round(bwall * 1e6 / 20, 2), "pairs_per_s": pairs / (bwall / 20),
+            "kernels_us": {k: round(v, 2) for k, v in bk.items()},
+            "hbm_frac": {k: round(balgo[k] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k, v in bk.items()},
+            "aggregate_hbm_frac": round(sum(balgo.values()) / (sum(bk.values()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"backward {p.name}: {bwall * 1e6 / 20:.1f} us/step (eager) " +
+            "  ".join(f"{k}={v:.1f}us" for k, v in bk.items()))
+        del bt, bprob
         # the random-row workload (rows of 32-512 random columns): every tile takes the
         # vector path, whose key/value row gathers bound it
         rq = gen.make("random_n8192")
