@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "plan_layout.h"
 
 namespace sa {
 namespace {
@@ -61,40 +62,135 @@ __global__ __launch_bounds__(kThreads) void transpose_finish_kernel(const unsign
   }
 }
 
-// dst[t, k] = src[t, perm[k]] for every head t.
+// dst[t, k] = src[t, perm[k]]. A workgroup takes 256 consecutive k of four heads, and each XCD
+// runs a contiguous range of (heads, k) blocks: consecutive k of a banded pattern read the
+// same source lines one entry apart (the rows crossing consecutive columns), so those lines
+// are fetched once into one L2 instead of into every XCD's.
+constexpr int kGatherHeads = 4;  // heads per thread: four independent loads per perm read
+
 __global__ __launch_bounds__(kThreads) void gather_kernel(const int* __restrict__ perm,
                                                           const float* __restrict__ src,
                                                           float* __restrict__ dst, long long nnz,
-                                                          int BH) {
-  const long long k = (long long)blockIdx.x * kThreads + threadIdx.x;
+                                                          long long kblocks, int BH) {
+  const long long lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int t0 = (int)(lb / kblocks) * kGatherHeads;
+  const long long k = (lb % kblocks) * kThreads + threadIdx.x;
   if (k >= nnz) return;
   long long from = perm[k];
   from = from < 0 ? 0 : (from >= nnz ? nnz - 1 : from);
-  for (int t = (int)blockIdx.y; t < BH; t += (int)gridDim.y)
-    dst[(size_t)t * nnz + k] = src[(size_t)t * nnz + from];
+  float x[kGatherHeads];
+#pragma unroll
+  for (int u = 0; u < kGatherHeads; ++u)
+    x[u] = t0 + u < BH ? src[(size_t)(t0 + u) * nnz + from] : 0.f;
+#pragma unroll
+  for (int u = 0; u < kGatherHeads; ++u)
+    if (t0 + u < BH) dst[(size_t)(t0 + u) * nnz + k] = x[u];
 }
 
-// dS = out_scale * W * (dW - D), D = sum over the row of W * dW; one wave per (head, row):
-// a first pass forms D (DPP sum), a second writes dS (its reads hit the cache).
+// dS = out_scale * W * (dW - D), D = sum over the row of W * dW, for one row of len entries
+// by kT threads (a wave or the workgroup; `rsum` all-reduces over them). Rows of up to
+// kPerLane * kT entries are read once into registers and written once; longer rows take a
+// pass for D (kPerLane loads in flight per thread) and a pass that writes.
+constexpr int kPerLane = 8;
+constexpr int kLongWGs = 64;  // workgroups that take the plan's long rows
+constexpr int kRowsPerBlock = kThreads / kWave;
+
+template <int kT, class ReduceSum>
+__device__ __forceinline__ void row_softmax_backward(const float* wt, const float* dwt, float* dst,
+                                                     long long len, int tid, float out_scale,
+                                                     ReduceSum rsum) {
+  constexpr int kCap = kPerLane * kT;
+  if (len <= kCap) {
+    float x[kPerLane], y[kPerLane];
+    float d = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const long long e = tid + (long long)u * kT;
+      x[u] = e < len ? wt[e] : 0.f;
+      y[u] = e < len ? dwt[e] : 0.f;
+      d = fmaf(x[u], y[u], d);
+    }
+    d = rsum(d);
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const long long e = tid + (long long)u * kT;
+      if (e < len) dst[e] = out_scale * x[u] * (y[u] - d);
+    }
+    return;
+  }
+  float dp[kPerLane];
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) dp[u] = 0.f;
+  for (long long e0 = 0; e0 < len; e0 += kCap)
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const long long e = e0 + tid + (long long)u * kT;
+      if (e < len) dp[u] = fmaf(wt[e], dwt[e], dp[u]);
+    }
+  float d = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) d += dp[u];
+  d = rsum(d);
+  for (long long e0 = 0; e0 < len; e0 += kCap)
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const long long e = e0 + tid + (long long)u * kT;
+      if (e < len) dst[e] = out_scale * wt[e] * (dwt[e] - d);
+    }
+}
+
+// One wave per (head, row); with a row plan, the plan's long rows (e.g. global-token rows)
+// go to the first kLongWGs workgroups instead, one whole workgroup per (head, long row).
 __global__ __launch_bounds__(kThreads) void softmax_backward_kernel(const int* __restrict__ row_ptr,
                                                                     int n, long long nnz, int BH,
-                                                                    const float* __restrict__ w,
-                                                                    const float* __restrict__ dw,
-                                                                    float out_scale,
-                                                                    float* __restrict__ ds) {
-  const long long unit = (long long)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+                                                                    const float* w, const float* dw,
+                                                                    float out_scale, float* ds,
+                                                                    const int* __restrict__ plan,
+                                                                    int long_wgs) {
+  __shared__ float red[kRowsPerBlock];
+  const bool use_plan = long_wgs > 0 && plan[kHValid] != 0;
+  auto range = [&](int row, long long& a, long long& b) {
+    a = row_ptr[row];
+    b = row_ptr[row + 1];
+    a = a < 0 ? 0 : (a > nnz ? nnz : a);
+    b = b < a ? a : (b > nnz ? nnz : b);
+  };
+  if ((int)blockIdx.x < long_wgs) {
+    if (!use_plan) return;
+    const int L = plan[kHLongRows], S = plan[kHSegs];
+    const int* segs = plan + plan[kHOffSegs];
+    for (long long task = blockIdx.x; task < (long long)L * BH; task += long_wgs) {
+      const int lr = (int)(task % L), t = (int)(task / L);
+      int lo = 0, hi = S - 1;  // the first segment of long row lr (segments are in row order)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (segs[8 * mid + 3] < lr) lo = mid + 1;
+        else hi = mid;
+      }
+      long long a, b;
+      range(segs[8 * lo], a, b);
+      const size_t off = (size_t)t * nnz + a;
+      row_softmax_backward<kThreads>(w + off, dw + off, ds + off, b - a, (int)threadIdx.x, out_scale,
+                                     [&](float x) {
+                                       x = wave_reduce<OpSum>(x);
+                                       __syncthreads();  // red[] is free
+                                       if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
+                                       __syncthreads();
+                                       return (red[0] + red[1]) + (red[2] + red[3]);
+                                     });
+    }
+    return;
+  }
+  const int lb = xcd_logical_block(blockIdx.x - long_wgs, gridDim.x - long_wgs);
+  const long long unit = (long long)lb * kRowsPerBlock + threadIdx.x / kWave;
   if (unit >= (long long)BH * n) return;
   const int t = (int)(unit / n), row = (int)(unit % n), lane = threadIdx.x % kWave;
-  long long a = row_ptr[row], b = row_ptr[row + 1];
-  a = a < 0 ? 0 : (a > nnz ? nnz : a);
-  b = b < a ? a : (b > nnz ? nnz : b);
-  const float* wt = w + (size_t)t * nnz;
-  const float* dwt = dw + (size_t)t * nnz;
-  float* dst = ds + (size_t)t * nnz;
-  float d = 0.f;
-  for (long long e = a + lane; e < b; e += kWave) d = fmaf(wt[e], dwt[e], d);
-  d = wave_reduce<OpSum>(d);
-  for (long long e = a + lane; e < b; e += kWave) dst[e] = out_scale * wt[e] * (dwt[e] - d);
+  long long a, b;
+  range(row, a, b);
+  if (a == b || (use_plan && b - a > kLongRow)) return;  // empty, or a long-row workgroup's
+  const size_t off = (size_t)t * nnz + a;
+  row_softmax_backward<kWave>(w + off, dw + off, ds + off, b - a, lane, out_scale,
+                              [](float x) { return wave_reduce<OpSum>(x); });
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -155,8 +251,11 @@ hipError_t launch_gather_entries(const sa_problem& p, const int* perm, const flo
                                  hipStream_t s) {
   const int BH = p.B * p.H;
   if (p.nnz == 0 || BH == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.nnz + kThreads - 1) / kThreads), (unsigned)(BH < 65535 ? BH : 65535));
-  hipLaunchKernelGGL(gather_kernel, grid, dim3(kThreads), 0, s, perm, src, dst, (long long)p.nnz, BH);
+  const long long kblocks = (p.nnz + kThreads - 1) / kThreads;
+  const long long groups = (BH + kGatherHeads - 1) / kGatherHeads;
+  if (kblocks * groups > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(kblocks * groups)), dim3(kThreads), 0, s, perm,
+                     src, dst, (long long)p.nnz, kblocks, BH);
   return hipGetLastError();
 }
 
@@ -165,9 +264,11 @@ hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const fl
   const int BH = p.B * p.H;
   const long long units = (long long)BH * p.n;
   if (units == 0) return hipSuccess;
-  const int per_wg = kThreads / kWave;
-  hipLaunchKernelGGL(softmax_backward_kernel, dim3((unsigned)((units + per_wg - 1) / per_wg)),
-                     dim3(kThreads), 0, s, p.row_ptr, p.n, (long long)p.nnz, BH, w, dw, out_scale, ds);
+  const long long blocks = (units + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int long_wgs = p.plan ? kLongWGs : 0;
+  hipLaunchKernelGGL(softmax_backward_kernel, dim3((unsigned)(long_wgs + blocks)), dim3(kThreads), 0,
+                     s, p.row_ptr, p.n, (long long)p.nnz, BH, w, dw, out_scale, ds,
+                     static_cast<const int*>(p.plan), long_wgs);
   return hipGetLastError();
 }
 
