@@ -211,10 +211,11 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
 def run_backward_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     """The backward pass of the CSR pipeline for an upstream gradient dO (bf16, N(0,1)):
     dW = SDDMM(dO, V) at scale 1, dS = softmax gradient (times the scale), dQ = SpMM(dS, K),
-    dS and W gathered into the transposed pattern's order, dK = SpMM^T(dS, Q),
-    dV = SpMM^T(W, dO). The transposed pattern and both row plans are built once per mask
-    before timing; the forward weights come from one forward pass. Returns (wall seconds of
-    `steps` eager backward steps, us per kernel call from back-to-back launches)."""
+    dS and W gathered together into the transposed pattern's order (block read order),
+    dK = SpMM^T(dS, Q), dV = SpMM^T(W, dO). The transposed pattern, its gather order and
+    both row plans are built once per mask before timing; the forward weights come from one
+    forward pass. Returns the wall seconds of `steps` eager backward steps; with a timer,
+    each call is then also timed over `steps` back-to-back launches."""
     dtype = prob.c.dtype
     plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
     sa.sa_plan_build(prob, plan)
@@ -224,6 +225,8 @@ def run_backward_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     perm = torch.empty(nnz, dtype=torch.int32, device="cuda:0")
     ws = torch.empty(sa.sa_transpose_workspace_bytes(prob), dtype=torch.uint8, device="cuda:0")
     sa.sa_csr_transpose(prob, rpt, cit, perm, ws)
+    order = torch.empty(2 * nnz, dtype=torch.int32, device="cuda:0")
+    sa.sa_gather_order_build(prob, perm, order, ws)
     del ws
     c = prob.c
     prob_dw = sa.Problem(c.B, c.H, n, d, dtype, t["row_ptr"], t["col_idx"], nnz, scale=1.0)
@@ -245,8 +248,7 @@ def run_backward_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     calls = {"sddmm_dO_V": lambda: sa.sa_sddmm(prob_dw, dO, t["v"], dW),
              "softmax_backward": lambda: sa.sa_sparse_softmax_backward(prob, W, dW, c.scale, dS),
              "spmm_dS_K": lambda: sa.sa_spmm(prob, dS, t["k"], dQ),
-             "gather_dS": lambda: sa.sa_gather_entries(prob, perm, dS, dSt),
-             "gather_W": lambda: sa.sa_gather_entries(prob, perm, W, Wt),
+             "gather_dS_W": lambda: sa.sa_gather_entries_ordered(prob, order, dS, dSt, W, Wt),
              "spmmT_dS_Q": lambda: sa.sa_spmm(prob_t, dSt, t["q"], dK),
              "spmmT_W_dO": lambda: sa.sa_spmm(prob_t, Wt, dO, dV)}
 
@@ -279,7 +281,7 @@ def bytes_backward(BH, n, d, nnz, elem):
     e4 = 4 * BH * nnz
     spmm = e4 + csr + qkv + 4 * BH * n * d
     return {"sddmm_dO_V": 2 * qkv + csr + e4, "softmax_backward": 4 * (n + 1) + 3 * e4,
-            "spmm_dS_K": spmm, "gather_dS": 2 * e4 + 4 * nnz, "gather_W": 2 * e4 + 4 * nnz,
+            "spmm_dS_K": spmm, "gather_dS_W": 4 * e4 + 8 * nnz,
             "spmmT_dS_Q": spmm, "spmmT_W_dO": spmm}
 
 

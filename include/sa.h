@@ -164,7 +164,7 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  * stored entry (i, j):  dW = dO[i].v[j] (sa_sddmm of dO and V at scale 1, no bias/mask),
  * dS = W (dW - sum_row W dW) (sa_sparse_softmax_backward), dQ = scale * dS K (sa_spmm),
  * dK = scale * dS^T Q and dV = W^T dO (sa_spmm over the transposed pattern, with dS and W
- * gathered into its order by sa_gather_entries). dS is also the gradient of the additive
+ * gathered into its order by sa_gather_entries or sa_gather_entries_ordered). dS is also the gradient of the additive
  * bias and key mask at the stored entries. Element CSR only.
  *
  * sa_transpose_workspace_bytes: device workspace bytes sa_csr_transpose needs (host-only;
@@ -176,6 +176,14 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  *   duration of the call (SA_ERR_WORKSPACE if smaller than the size above).
  * sa_gather_entries: dst[t*nnz + k] = src[t*nnz + perm[k]] for every head t; src and dst
  *   are fp32 [B*H, nnz] and must not alias.
+ * sa_gather_order_build: from perm, the read order of sa_gather_entries_ordered: order is
+ *   int32 [2*nnz], caller-owned; within each block of 4096 consecutive positions k, the
+ *   sources perm[k] ascending (first half) and the position each goes to (second half).
+ *   Depends on the pattern only; workspace as for sa_csr_transpose (same size).
+ * sa_gather_entries_ordered: the same result as sa_gather_entries with the perm that order
+ *   was built from, for one array (src_b = dst_b = NULL) or two at once (e.g. dS and W);
+ *   reads the sources in ascending runs, which is faster when the pattern is banded. No
+ *   destination may alias a source or the other destination (SA_ERR_SHAPE).
  * sa_sparse_softmax_backward: dscores[t*nnz + e] = out_scale * W[e] * (dW[e] - D_row),
  *   D_row = sum over the row's entries of W * dW; weights, dweights and dscores are fp32
  *   [B*H, nnz] (dscores may alias dweights). out_scale = scale gives the operand of dQ
@@ -185,6 +193,10 @@ int sa_csr_transpose(const sa_problem *p, int32_t *row_ptr_t, int32_t *col_idx_t
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 int sa_gather_entries(const sa_problem *p, const int32_t *perm, const float *src, float *dst,
                       hipStream_t stream);
+int sa_gather_order_build(const sa_problem *p, const int32_t *perm, int32_t *order,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+int sa_gather_entries_ordered(const sa_problem *p, const int32_t *order, const float *src_a,
+                              float *dst_a, const float *src_b, float *dst_b, hipStream_t stream);
 int sa_sparse_softmax_backward(const sa_problem *p, const float *weights, const float *dweights,
                                float out_scale, float *dscores, hipStream_t stream);
 

@@ -31,7 +31,8 @@ SA_FLAG_VALIDATE = 1
 
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
            "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
-           "sa_gather_entries", "sa_sparse_softmax_backward", "sa_validate_csr",
+           "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
+           "sa_sparse_softmax_backward", "sa_validate_csr",
            "sa_status_string", "sa_last_hip_error_string")
 
 
@@ -70,6 +71,8 @@ def _load():
         "sa_transpose_workspace_bytes": (sz, [P]),
         "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "sa_gather_order_build": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
+        "sa_gather_entries_ordered": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
         "sa_validate_csr": (ctypes.c_int, [P, vp]),
         "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -256,6 +259,27 @@ def sa_gather_entries(prob, perm, src, dst, stream=None):
     _check(dst, "dst", c.B * c.H * c.nnz, f32)
     _raise(_lib.sa_gather_entries(_p(prob), _ptr(perm), _ptr(src), _ptr(dst), _stream(stream)),
            "sa_gather_entries")
+
+
+def sa_gather_order_build(prob, perm, order, workspace, stream=None):
+    c = _c(prob)
+    i32 = _torch().int32
+    _check(perm, "perm", c.nnz, i32)
+    _check(order, "order", 2 * c.nnz, i32)
+    nbytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else 0
+    _raise(_lib.sa_gather_order_build(_p(prob), _ptr(perm), _ptr(order), _ptr(workspace), nbytes,
+                                      _stream(stream)), "sa_gather_order_build")
+
+
+def sa_gather_entries_ordered(prob, order, src_a, dst_a, src_b=None, dst_b=None, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    _check(order, "order", 2 * c.nnz, _torch().int32)
+    for x, name in ((src_a, "src_a"), (dst_a, "dst_a"), (src_b, "src_b"), (dst_b, "dst_b")):
+        _check(x, name, c.B * c.H * c.nnz, f32)
+    _raise(_lib.sa_gather_entries_ordered(_p(prob), _ptr(order), _ptr(src_a), _ptr(dst_a),
+                                          _ptr(src_b), _ptr(dst_b), _stream(stream)),
+           "sa_gather_entries_ordered")
 
 
 def sa_sparse_softmax_backward(prob, weights, dweights, out_scale, dscores, stream=None):

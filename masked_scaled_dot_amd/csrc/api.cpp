@@ -231,6 +231,30 @@ int sa_gather_entries(const sa_problem* p, const int32_t* perm, const float* src
   return hip_status(sa::launch_gather_entries(*p, perm, src, dst, stream));
 }
 
+int sa_gather_order_build(const sa_problem* p, const int32_t* perm, int32_t* order, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (p->nnz == 0) return SA_OK;
+  if (!perm || !order || !workspace) return SA_ERR_NULL;
+  if (workspace_bytes < sa::transpose_workspace_bytes(p->n, p->nnz)) return SA_ERR_WORKSPACE;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_gather_order_build(*p, perm, order, workspace, workspace_bytes, stream));
+}
+
+int sa_gather_entries_ordered(const sa_problem* p, const int32_t* order, const float* src_a,
+                              float* dst_a, const float* src_b, float* dst_b, hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!order || !src_a || !dst_a || (src_b == nullptr) != (dst_b == nullptr)) return SA_ERR_NULL;
+  // no destination may alias a source or the other destination
+  if (src_a == dst_a || (src_b && (src_b == dst_b || src_a == dst_b || src_b == dst_a || dst_a == dst_b)))
+    return SA_ERR_SHAPE;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_gather_ordered(*p, order, src_a, dst_a, src_b, dst_b, stream));
+}
+
 int sa_sparse_softmax_backward(const sa_problem* p, const float* weights, const float* dweights,
                                float out_scale, float* dscores, hipStream_t stream) {
   int st = check_problem(p, kOpSoftmax);

@@ -11,7 +11,11 @@
 //   dV[j]   = sum_i W[i,j] dO[i]                   -> SpMM over the transposed pattern
 // The transposed pattern (csr_transpose, here) lists each column's entries by ascending row
 // with perm[k] = the entry's index in the original CSR order, and gather_entries (here)
-// reorders per-entry values (W, dS) into the transposed order.
+// reorders per-entry values (W, dS) into the transposed order. gather_order_build (here)
+// prepares, once per pattern, each 4096-entry block of the transposed order sorted by source
+// index, so that gather_entries_ordered reads the sources in ascending runs (a banded
+// pattern's rows give runs of one block's columns), scatters them into LDS and writes the
+// block out contiguously.
 #include <hipcub/hipcub.hpp>
 
 #include "common.h"
@@ -22,6 +26,7 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kOrderBlock = 4096;  // positions of the transposed order per gather block
 
 // Keys (column << 32 | row) and values (entry index) of every stored entry; one wave per row.
 __global__ __launch_bounds__(kThreads) void transpose_keys_kernel(const int* __restrict__ row_ptr,
@@ -85,6 +90,96 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const int* __restrict_
 #pragma unroll
   for (int u = 0; u < kGatherHeads; ++u)
     if (t0 + u < BH) dst[(size_t)(t0 + u) * nnz + k] = x[u];
+}
+
+// Keys (block of k << 32 | perm[k]) and values k: sorted, each block of the transposed order
+// lists its sources ascending, with the positions (slots) they go to.
+__global__ __launch_bounds__(kThreads) void order_keys_kernel(const int* __restrict__ perm,
+                                                              long long nnz,
+                                                              unsigned long long* __restrict__ keys,
+                                                              int* __restrict__ vals) {
+  const long long k = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= nnz) return;
+  long long from = perm[k];
+  from = from < 0 ? 0 : (from >= nnz ? nnz - 1 : from);
+  keys[k] = ((unsigned long long)(k / kOrderBlock) << 32) | (unsigned long long)from;
+  vals[k] = (int)k;
+}
+
+// order[k] = the k-th smallest source of k's block, order[nnz + k] = its slot in the block.
+// Sorting keeps every block's entries inside the block, so sorted position k is in block
+// k / kOrderBlock and the slots of a block are a permutation of its positions.
+__global__ __launch_bounds__(kThreads) void order_finish_kernel(const unsigned long long* __restrict__ keys,
+                                                                const int* __restrict__ vals,
+                                                                long long nnz, int* __restrict__ order) {
+  const long long k = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= nnz) return;
+  order[k] = (int)(keys[k] & 0xffffffffull);
+  order[nnz + k] = (int)(vals[k] - (k / kOrderBlock) * kOrderBlock);
+}
+
+// dst_a[t, k] = src_a[t, perm[k]] (and the same for b, when given) through the block order: a
+// workgroup takes one block of kOrderBlock positions and a group of heads, and runs one
+// phase per (array, head): read the block's sources in ascending order (kOrderPer loads in
+// flight per thread), write each value to its slot in LDS and, after a barrier, store the
+// block contiguously. The next phase's loads are issued before this phase's stores, and the
+// phases alternate between two LDS buffers, so one barrier per phase suffices: a thread
+// writes a buffer only after the barrier of the phase in between, which every thread passes
+// after it has read that buffer out. Consecutive blocks (neighbouring columns, which read the
+// same source lines) run on one XCD.
+constexpr int kOrderPer = kOrderBlock / kThreads;
+
+__global__ __launch_bounds__(kThreads) void gather_ordered_kernel(const int* __restrict__ order,
+                                                                  long long nnz, long long nblocks,
+                                                                  int BH, int heads_per_wg,
+                                                                  const float* __restrict__ src_a,
+                                                                  float* __restrict__ dst_a,
+                                                                  const float* __restrict__ src_b,
+                                                                  float* __restrict__ dst_b) {
+  __shared__ float buf[2][kOrderBlock];
+  const long long lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const long long blk = lb % nblocks;
+  const int t0 = (int)(lb / nblocks) * heads_per_wg;
+  const int t1 = t0 + heads_per_wg < BH ? t0 + heads_per_wg : BH;
+  if (t0 >= t1) return;
+  const long long k0 = blk * kOrderBlock;
+  const int cnt = nnz - k0 < kOrderBlock ? (int)(nnz - k0) : kOrderBlock;
+  const int arrays = src_b != nullptr ? 2 : 1;
+  const int phases = (t1 - t0) * arrays;
+  int from[kOrderPer], slot[kOrderPer];
+#pragma unroll
+  for (int u = 0; u < kOrderPer; ++u) {
+    const int r = threadIdx.x + u * kThreads;
+    from[u] = r < cnt ? order[k0 + r] : 0;
+    from[u] = from[u] < 0 ? 0 : (from[u] >= nnz ? (int)(nnz - 1) : from[u]);
+    slot[u] = r < cnt ? clampi(order[nnz + k0 + r], 0, kOrderBlock - 1) : 0;
+  }
+  const int nh = t1 - t0;  // phases: every head of a, then every head of b
+  auto src_of = [&](int ph) {
+    return (ph < nh ? src_a : src_b) + (size_t)(t0 + ph % nh) * nnz;
+  };
+  float x[kOrderPer];
+  const float* src = src_of(0);
+#pragma unroll
+  for (int u = 0; u < kOrderPer; ++u) x[u] = threadIdx.x + u * kThreads < cnt ? src[from[u]] : 0.f;
+  for (int ph = 0; ph < phases; ++ph) {
+    float* lds = buf[ph & 1];
+#pragma unroll
+    for (int u = 0; u < kOrderPer; ++u)
+      if (threadIdx.x + u * kThreads < cnt) lds[slot[u]] = x[u];
+    __syncthreads();
+    if (ph + 1 < phases) {
+      src = src_of(ph + 1);
+#pragma unroll
+      for (int u = 0; u < kOrderPer; ++u) x[u] = threadIdx.x + u * kThreads < cnt ? src[from[u]] : 0.f;
+    }
+    float* dst = (ph < nh ? dst_a : dst_b) + (size_t)(t0 + ph % nh) * nnz + k0;
+#pragma unroll
+    for (int u = 0; u < kOrderPer; ++u) {
+      const int r = threadIdx.x + u * kThreads;
+      if (r < cnt) dst[r] = lds[r];
+    }
+  }
 }
 
 // dS = out_scale * W * (dW - D), D = sum over the row of W * dW, for one row of len entries
@@ -195,26 +290,49 @@ __global__ __launch_bounds__(kThreads) void softmax_backward_kernel(const int* _
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int end_bit(int n) {  // bits of the sort keys: 32 (row) + enough for columns < n
+int end_bit(long long n) {  // bits of the sort keys: 32 (low word) + enough for values < n
   int bits = 1;
-  while (bits < 31 && (1ll << bits) < (long long)n) ++bits;
+  while (bits < 31 && (1ll << bits) < n) ++bits;
   return 32 + bits;
 }
 
-size_t cub_temp_bytes(long long nnz, int n) {
+long long order_blocks(long long nnz) { return (nnz + kOrderBlock - 1) / kOrderBlock; }
+
+size_t cub_temp_bytes(long long nnz, int bits) {
   size_t temp = 0;
   if (hipcub::DeviceRadixSort::SortPairs(nullptr, temp, (const unsigned long long*)nullptr,
                                          (unsigned long long*)nullptr, (const int*)nullptr,
-                                         (int*)nullptr, (int)nnz, 0, end_bit(n)) != hipSuccess)
+                                         (int*)nullptr, (int)nnz, 0, bits) != hipSuccess)
     return 0;
   return temp;
+}
+
+struct SortBuffers {
+  unsigned long long *k_in, *k_out;
+  int *v_in, *v_out;
+  void* temp;
+  size_t temp_bytes;
+};
+
+SortBuffers sort_buffers(void* ws, size_t ws_bytes, long long nnz) {
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+  const size_t keys = align256((size_t)nnz * 8), vals = align256((size_t)nnz * 4);
+  SortBuffers b;
+  b.k_in = reinterpret_cast<unsigned long long*>(base);
+  b.k_out = reinterpret_cast<unsigned long long*>(base + keys);
+  b.v_in = reinterpret_cast<int*>(base + 2 * keys);
+  b.v_out = reinterpret_cast<int*>(base + 2 * keys + vals);
+  b.temp = base + 2 * keys + 2 * vals;
+  b.temp_bytes = ws_bytes - (size_t)(static_cast<char*>(b.temp) - static_cast<char*>(ws));
+  return b;
 }
 
 }  // namespace
 
 size_t transpose_workspace_bytes(long long n, long long nnz) {
   const size_t keys = align256((size_t)nnz * 8), vals = align256((size_t)nnz * 4);
-  return 2 * keys + 2 * vals + align256(cub_temp_bytes(nnz, (int)n)) + 256;
+  const size_t t1 = cub_temp_bytes(nnz, end_bit(n)), t2 = cub_temp_bytes(nnz, end_bit(order_blocks(nnz)));
+  return 2 * keys + 2 * vals + align256(t1 > t2 ? t1 : t2) + 256;
 }
 
 hipError_t launch_csr_transpose(const sa_problem& p, int* row_ptr_t, int* col_idx_t, int* perm,
@@ -226,14 +344,11 @@ hipError_t launch_csr_transpose(const sa_problem& p, int* row_ptr_t, int* col_id
                        n, 0ll, row_ptr_t, col_idx_t, perm);
     return hipGetLastError();
   }
-  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
-  const size_t keys = align256((size_t)nnz * 8), vals = align256((size_t)nnz * 4);
-  auto* k_in = reinterpret_cast<unsigned long long*>(base);
-  auto* k_out = reinterpret_cast<unsigned long long*>(base + keys);
-  auto* v_in = reinterpret_cast<int*>(base + 2 * keys);
-  auto* v_out = reinterpret_cast<int*>(base + 2 * keys + vals);
-  void* temp = base + 2 * keys + 2 * vals;
-  size_t temp_bytes = ws_bytes - (size_t)(static_cast<char*>(temp) - static_cast<char*>(ws));
+  SortBuffers sb = sort_buffers(ws, ws_bytes, nnz);
+  auto *k_in = sb.k_in, *k_out = sb.k_out;
+  int *v_in = sb.v_in, *v_out = sb.v_out;
+  void* temp = sb.temp;
+  size_t temp_bytes = sb.temp_bytes;
   const int rows_per_wg = kThreads / kWave;
   hipLaunchKernelGGL(transpose_keys_kernel, dim3((unsigned)((n + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kThreads), 0, s, p.row_ptr, p.col_idx, n, nnz, k_in, v_in);
@@ -256,6 +371,38 @@ hipError_t launch_gather_entries(const sa_problem& p, const int* perm, const flo
   if (kblocks * groups > 0x7fffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(kblocks * groups)), dim3(kThreads), 0, s, perm,
                      src, dst, (long long)p.nnz, kblocks, BH);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_order_build(const sa_problem& p, const int* perm, int* order, void* ws,
+                                     size_t ws_bytes, hipStream_t s) {
+  const long long nnz = p.nnz;
+  if (nnz == 0) return hipSuccess;
+  SortBuffers sb = sort_buffers(ws, ws_bytes, nnz);
+  const unsigned grid = (unsigned)((nnz + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(order_keys_kernel, dim3(grid), dim3(kThreads), 0, s, perm, nnz, sb.k_in, sb.v_in);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipcub::DeviceRadixSort::SortPairs(sb.temp, sb.temp_bytes, sb.k_in, sb.k_out, sb.v_in, sb.v_out,
+                                         (int)nnz, 0, end_bit(order_blocks(nnz)), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(order_finish_kernel, dim3(grid), dim3(kThreads), 0, s, sb.k_out, sb.v_out, nnz, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_ordered(const sa_problem& p, const int* order, const float* src_a,
+                                 float* dst_a, const float* src_b, float* dst_b, hipStream_t s) {
+  const int BH = p.B * p.H;
+  if (p.nnz == 0 || BH == 0) return hipSuccess;
+  const long long nblocks = order_blocks(p.nnz);
+  // Head groups until there are about eight workgroups per CU; each group re-reads the order.
+  long long groups = (2048 + nblocks - 1) / nblocks;
+  groups = groups < BH ? groups : BH;
+  const int heads_per_wg = (int)((BH + groups - 1) / groups);
+  groups = (BH + heads_per_wg - 1) / heads_per_wg;
+  if (nblocks * groups > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_ordered_kernel, dim3((unsigned)(nblocks * groups)), dim3(kThreads), 0, s,
+                     order, (long long)p.nnz, nblocks, BH, heads_per_wg, src_a, dst_a, src_b, dst_b);
   return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@ hipError_t launch_csr_transpose(const sa_problem& p, int* row_ptr_t, int* col_id
                                 void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_gather_entries(const sa_problem& p, const int* perm, const float* src, float* dst,
                                  hipStream_t s);
+hipError_t launch_gather_order_build(const sa_problem& p, const int* perm, int* order, void* ws,
+                                     size_t ws_bytes, hipStream_t s);
+hipError_t launch_gather_ordered(const sa_problem& p, const int* order, const float* src_a,
+                                 float* dst_a, const float* src_b, float* dst_b, hipStream_t s);
 hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const float* dw,
                                    float out_scale, float* ds, hipStream_t s);
 

@@ -192,6 +192,8 @@ def test_backward_calls_reject_bad_descriptors():
         assert f("sa_gather_entries")(ref, FAKE, FAKE, FAKE + 64, None) == st
         assert f("sa_sparse_softmax_backward")(ref, FAKE, FAKE, 1.0, FAKE, None) == st
         assert f("sa_csr_transpose")(ref, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == st
+        assert f("sa_gather_order_build")(ref, FAKE, FAKE, FAKE, 1 << 30, None) == st
+        assert f("sa_gather_entries_ordered")(ref, FAKE, FAKE, FAKE + 64, None, None, None) == st
         if p is not None:
             assert f("sa_transpose_workspace_bytes")(ref) == 0
 
@@ -207,7 +209,17 @@ def test_backward_calls_check_buffers_and_arguments():
     assert f("sa_csr_transpose")(p, FAKE, FAKE, FAKE, FAKE, 64, None) == sa.SA_ERR_WORKSPACE
     # keys and values are sorted out of place: at least 2 x (8 + 4) bytes per entry
     assert f("sa_transpose_workspace_bytes")(p) >= 24 * 500
+    assert f("sa_gather_order_build")(p, FAKE, None, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
+    assert f("sa_gather_order_build")(p, FAKE, FAKE, FAKE, 64, None) == sa.SA_ERR_WORKSPACE
+    g = f("sa_gather_entries_ordered")
+    A, B, C, D = FAKE, FAKE + 64, FAKE + 128, FAKE + 192
+    assert g(p, None, A, B, None, None, None) == sa.SA_ERR_NULL
+    assert g(p, FAKE, A, B, C, None, None) == sa.SA_ERR_NULL  # src_b without dst_b
+    assert g(p, FAKE, A, A, None, None, None) == sa.SA_ERR_SHAPE
+    for aliased in ((A, B, C, B), (A, B, B, C), (A, B, C, A), (A, B, C, C)):
+        assert g(p, FAKE, *aliased, None) == sa.SA_ERR_SHAPE, aliased
     for field in ("B", "H"):
         q = ctypes.byref(_prob(**{field: 0}, nnz=0))
+        assert g(q, None, None, None, None, None, None) == sa.SA_OK
         assert f("sa_gather_entries")(q, None, None, None, None) == sa.SA_OK
         assert f("sa_sparse_softmax_backward")(q, None, None, 1.0, None, None) == sa.SA_OK

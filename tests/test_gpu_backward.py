@@ -49,6 +49,11 @@ class Backward:
         self.perm = torch.empty(max(p.nnz, 1), dtype=torch.int32, device=DEV)
         ws = torch.empty(max(sa.sa_transpose_workspace_bytes(dp.prob), 1), dtype=torch.uint8, device=DEV)
         sa.sa_csr_transpose(dp.prob, self.rpt, self.cit[:p.nnz], self.perm[:p.nnz], ws)
+        # the ordered gather runs with the plan, the plain one without: both take part
+        self.order = None
+        if plan and p.nnz:
+            self.order = torch.empty(2 * p.nnz, dtype=torch.int32, device=DEV)
+            sa.sa_gather_order_build(dp.prob, self.perm[:p.nnz], self.order, ws)
         dtype = sa.SA_BF16 if p.dtype == "bf16" else sa.SA_F32
         # dW = dO . v at the pattern: SDDMM at scale 1 without additive terms
         self.prob_dw = sa.Problem(p.B, p.H, p.n, p.d, dtype, dp.row_ptr, dp.col_idx, p.nnz, scale=1.0)
@@ -68,8 +73,11 @@ class Backward:
         sa.sa_sddmm(self.prob_dw, dO, dp.v, dW)
         sa.sa_sparse_softmax_backward(dp.prob, W, dW, dp.scale, dS)
         sa.sa_spmm(dp.prob, dS, dp.k, dQ)
-        sa.sa_gather_entries(dp.prob, self.perm[:p.nnz], dS, dSt)
-        sa.sa_gather_entries(dp.prob, self.perm[:p.nnz], W, Wt)
+        if self.order is not None:
+            sa.sa_gather_entries_ordered(dp.prob, self.order, dS, dSt, W, Wt)
+        else:
+            sa.sa_gather_entries(dp.prob, self.perm[:p.nnz], dS, dSt)
+            sa.sa_gather_entries(dp.prob, self.perm[:p.nnz], W, Wt)
         sa.sa_spmm(self.prob_t, dSt, dp.q, dK)
         sa.sa_spmm(self.prob_t, Wt, dO, dV)
         return dict(dW=dW, dS=dS, dQ=dQ, dK=dK, dV=dV)
@@ -115,6 +123,45 @@ def test_backward_parity(name, plan):
     check(got["dS"].view(p.BH, p.nnz).cpu().numpy(), dp.scale * ref["dS"], p.dtype, "scale*dS")
     for g in ("dQ", "dK", "dV"):
         check(got[g].cpu().numpy(), ref[g], p.dtype, g)
+
+
+ORDER_CASES = dict(CASES, longformer_full=lambda: gen.make("longformer_n4096"))
+
+
+@pytest.mark.parametrize("name", sorted(ORDER_CASES))
+def test_ordered_gather_equals_permutation(name):
+    """The block read order: every block of 4096 transposed positions lists its sources
+    ascending with a permutation of its slots, and the ordered gather (one array or two)
+    equals dst[t, k] = src[t, perm[k]] bit for bit, including the ragged last block."""
+    p = ORDER_CASES[name]()
+    say(f"ordered gather {name}: BH={p.BH} nnz={p.nnz}")
+    dp = DevProblem(p, plan=False)
+    bw = Backward(dp, plan=True)
+    nnz = p.nnz
+    perm = bw.perm[:nnz].long()
+    order = bw.order.cpu().numpy().astype(np.int64)
+    src_o, slot = order[:nnz], order[nnz:]
+    perm_h = perm.cpu().numpy()
+    for b0 in range(0, nnz, 4096):
+        b1 = min(nnz, b0 + 4096)
+        assert np.all(np.diff(src_o[b0:b1]) > 0)
+        assert np.array_equal(np.sort(slot[b0:b1]), np.arange(b1 - b0))
+        assert np.array_equal(perm_h[b0 + slot[b0:b1]], src_o[b0:b1])
+    g = torch.Generator(device=DEV).manual_seed(3)
+    a = torch.randn(p.BH * nnz, device=DEV, generator=g)
+    b = torch.randn(p.BH * nnz, device=DEV, generator=g)
+    want_a = a.view(p.BH, nnz)[:, perm].reshape(-1)
+    want_b = b.view(p.BH, nnz)[:, perm].reshape(-1)
+    da, db = torch.full_like(a, float("nan")), torch.full_like(b, float("nan"))
+    sa.sa_gather_entries_ordered(dp.prob, bw.order, a, da, b, db)
+    torch.cuda.synchronize()
+    assert torch.equal(da, want_a) and torch.equal(db, want_b)
+    da.fill_(float("nan"))
+    sa.sa_gather_entries_ordered(dp.prob, bw.order, b, da)
+    plain = torch.full_like(a, float("nan"))
+    sa.sa_gather_entries(dp.prob, bw.perm[:nnz], b, plain)
+    torch.cuda.synchronize()
+    assert torch.equal(da, want_b) and torch.equal(plain, want_b)
 
 
 def test_backward_full_size_identities():
