@@ -200,6 +200,44 @@ int sa_gather_entries_ordered(const sa_problem *p, const int32_t *order, const f
 int sa_sparse_softmax_backward(const sa_problem *p, const float *weights, const float *dweights,
                                float out_scale, float *dscores, hipStream_t stream);
 
+/* --- Mask construction ---------------------------------------------------------------------
+ * The gluon-nlp proposal (opening post) takes the mask as a sparse (n, n) matrix in CSR or
+ * COO form, possibly generated at run time; the flash-attention pull request "support
+ * attentions in AlphaFold2" (key-padding discussion) proposes one int per batch, the number
+ * of valid keys, when the masked keys are a suffix, and packs variable-length sequences by a
+ * prefix of their starts (cu_seqlens). These calls turn those forms into the inputs the
+ * kernels above read. All run on stream, take device pointers and allocate nothing.
+ *
+ * sa_mask_workspace_bytes: device workspace bytes for sa_coo_to_csr with n and nnz pairs,
+ *   and for sa_varlen_row_ptr with total = n (host-only; 0 on bad sizes).
+ * sa_coo_to_csr: rows, cols int32 [nnz] (any order) -> row_ptr int32 [n+1] and col_idx
+ *   int32 (capacity nnz): the CSR of the set of pairs with 0 <= row, col < n, each row's
+ *   columns ascending and unique. Pairs outside [0, n) are dropped and repeated pairs are
+ *   merged; counts int32 [3] receives {stored entries (= row_ptr[n]), pairs dropped, pairs
+ *   merged}. nnz < 2^31 - 1 (SA_ERR_SHAPE), SA_ERR_WORKSPACE if the workspace is short.
+ * sa_key_mask_from_lengths: key_mask fp32 [B, n] (the layout of sa_problem.key_mask with
+ *   key_mask_heads = 1): 0 for keys j < seqlen_k[b] (clamped to [0, n]), -inf after.
+ * sa_varlen_row_ptr / sa_varlen_col_idx: the pattern of a packed batch of B sequences,
+ *   sequence b holding tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of total (cu_seqlens int32
+ *   [B+1], ascending, cu_seqlens[0] = 0): token i attends the keys of its own sequence, and
+ *   only those with |i - j| <= window when window >= 0. Tokens outside every sequence get
+ *   empty rows. The first call writes row_ptr int32 [total+1] (read row_ptr[total] for the
+ *   entry count); the second writes col_idx (writing nothing at or past col_capacity). Used
+ *   with B = 1 and n = total in sa_problem, q/k/v laid out [H, total, d]. SA_ERR_SHAPE if
+ *   the pattern could exceed 2^31 - 1 entries (total * min(total, 2 window + 1)). */
+size_t sa_mask_workspace_bytes(int32_t n, int64_t nnz);
+int sa_coo_to_csr(int32_t n, int64_t nnz, const int32_t *rows, const int32_t *cols,
+                  int32_t *row_ptr, int32_t *col_idx, int32_t *counts, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+int sa_key_mask_from_lengths(int32_t B, int32_t n, const int32_t *seqlen_k, float *key_mask,
+                             hipStream_t stream);
+int sa_varlen_row_ptr(int32_t B, int32_t total, const int32_t *cu_seqlens, int32_t window,
+                      int32_t *row_ptr, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+int sa_varlen_col_idx(int32_t B, int32_t total, const int32_t *cu_seqlens, int32_t window,
+                      const int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                      hipStream_t stream);
+
 /* --- Validation and status ----------------------------------------------------------------
  * sa_validate_csr: checks the pattern on the device (monotone row_ptr starting at 0,
  *   row_ptr[last] == nnz, columns in range, strictly ascending within each row) and

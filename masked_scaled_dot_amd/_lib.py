@@ -32,7 +32,8 @@ SA_FLAG_VALIDATE = 1
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
            "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
-           "sa_sparse_softmax_backward", "sa_validate_csr",
+           "sa_sparse_softmax_backward", "sa_mask_workspace_bytes", "sa_coo_to_csr",
+           "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_validate_csr",
            "sa_status_string", "sa_last_hip_error_string")
 
 
@@ -61,6 +62,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(sa_problem)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
     sig = {
         "sa_plan_bytes": (sz, [P]),
         "sa_plan_build": (ctypes.c_int, [P, vp, sz, vp]),
@@ -72,6 +74,11 @@ def _load():
         "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_gather_order_build": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
+        "sa_mask_workspace_bytes": (sz, [i32, i64]),
+        "sa_coo_to_csr": (ctypes.c_int, [i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sa_key_mask_from_lengths": (ctypes.c_int, [i32, i32, vp, vp, vp]),
+        "sa_varlen_row_ptr": (ctypes.c_int, [i32, i32, vp, i32, vp, vp, sz, vp]),
+        "sa_varlen_col_idx": (ctypes.c_int, [i32, i32, vp, i32, vp, vp, i64, vp]),
         "sa_gather_entries_ordered": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
         "sa_validate_csr": (ctypes.c_int, [P, vp]),
@@ -290,6 +297,55 @@ def sa_sparse_softmax_backward(prob, weights, dweights, out_scale, dscores, stre
     _raise(_lib.sa_sparse_softmax_backward(_p(prob), _ptr(weights), _ptr(dweights),
                                            float(out_scale), _ptr(dscores), _stream(stream)),
            "sa_sparse_softmax_backward")
+
+
+def sa_mask_workspace_bytes(n, nnz) -> int:
+    return int(_lib.sa_mask_workspace_bytes(int(n), int(nnz)))
+
+
+def _nbytes(x):
+    return x.numel() * x.element_size() if _is_tensor(x) else 0
+
+
+def sa_coo_to_csr(n, rows, cols, row_ptr, col_idx, counts, workspace, stream=None):
+    """CSR of the set of (rows[k], cols[k]) pairs inside [0, n); counts gets {stored,
+    dropped out of range, merged repeats}."""
+    i32 = _torch().int32
+    nnz = rows.numel() if _is_tensor(rows) else 0
+    _check(rows, "rows", nnz, i32)
+    _check(cols, "cols", nnz, i32)
+    _check(row_ptr, "row_ptr", n + 1, i32)
+    _check(col_idx, "col_idx", nnz, i32)
+    _check(counts, "counts", 3, i32)
+    _raise(_lib.sa_coo_to_csr(int(n), int(nnz), _ptr(rows), _ptr(cols), _ptr(row_ptr), _ptr(col_idx),
+                              _ptr(counts), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "sa_coo_to_csr")
+
+
+def sa_key_mask_from_lengths(B, n, seqlen_k, key_mask, stream=None):
+    _check(seqlen_k, "seqlen_k", B, _torch().int32)
+    _check(key_mask, "key_mask", B * n, _torch().float32)
+    _raise(_lib.sa_key_mask_from_lengths(int(B), int(n), _ptr(seqlen_k), _ptr(key_mask),
+                                         _stream(stream)), "sa_key_mask_from_lengths")
+
+
+def sa_varlen_row_ptr(B, total, cu_seqlens, window, row_ptr, workspace, stream=None):
+    i32 = _torch().int32
+    _check(cu_seqlens, "cu_seqlens", B + 1, i32)
+    _check(row_ptr, "row_ptr", total + 1, i32)
+    _raise(_lib.sa_varlen_row_ptr(int(B), int(total), _ptr(cu_seqlens), int(window), _ptr(row_ptr),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "sa_varlen_row_ptr")
+
+
+def sa_varlen_col_idx(B, total, cu_seqlens, window, row_ptr, col_idx, stream=None):
+    i32 = _torch().int32
+    _check(cu_seqlens, "cu_seqlens", B + 1, i32)
+    _check(row_ptr, "row_ptr", total + 1, i32)
+    _check(col_idx, "col_idx", 0, i32)
+    cap = col_idx.numel() if _is_tensor(col_idx) else 0
+    _raise(_lib.sa_varlen_col_idx(int(B), int(total), _ptr(cu_seqlens), int(window), _ptr(row_ptr),
+                                  _ptr(col_idx), int(cap), _stream(stream)), "sa_varlen_col_idx")
 
 
 def sa_validate_csr(prob, stream=None) -> int:

@@ -266,6 +266,67 @@ int sa_sparse_softmax_backward(const sa_problem* p, const float* weights, const 
   return hip_status(sa::launch_softmax_backward(*p, weights, dweights, out_scale, dscores, stream));
 }
 
+size_t sa_mask_workspace_bytes(int32_t n, int64_t nnz) {
+  if (n < 0 || nnz < 0 || nnz > INT32_MAX - 1) return 0;
+  return sa::mask_workspace_bytes(n, nnz);
+}
+
+int sa_coo_to_csr(int32_t n, int64_t nnz, const int32_t* rows, const int32_t* cols, int32_t* row_ptr,
+                  int32_t* col_idx, int32_t* counts, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (n < 0 || nnz < 0 || nnz > INT32_MAX - 1) return SA_ERR_SHAPE;
+  if (!row_ptr || !counts || (nnz > 0 && (!rows || !cols || !col_idx || !workspace))) return SA_ERR_NULL;
+  if (nnz > 0 && workspace_bytes < sa::mask_workspace_bytes(n, nnz)) return SA_ERR_WORKSPACE;
+  clear_stale_error();
+  return hip_status(sa::launch_coo_to_csr(n, nnz, rows, cols, row_ptr, col_idx, counts, workspace,
+                                          workspace_bytes, stream));
+}
+
+int sa_key_mask_from_lengths(int32_t B, int32_t n, const int32_t* seqlen_k, float* key_mask,
+                             hipStream_t stream) {
+  if (B < 0 || n < 0 || (long long)B * n > INT32_MAX) return SA_ERR_SHAPE;
+  if ((long long)B * n == 0) return SA_OK;
+  if (!seqlen_k || !key_mask) return SA_ERR_NULL;
+  clear_stale_error();
+  return hip_status(sa::launch_key_mask_from_lengths(B, n, seqlen_k, key_mask, stream));
+}
+
+namespace {
+// Largest pattern a packed batch can give: every token attends at most min(total, 2w + 1) keys.
+int check_varlen(int32_t B, int32_t total, int32_t window) {
+  if (B < 0 || total < 0) return SA_ERR_SHAPE;
+  const long long per_row = window >= 0 && 2ll * window + 1 < total ? 2ll * window + 1 : total;
+  if ((long long)total * per_row > INT32_MAX) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+}  // namespace
+
+int sa_varlen_row_ptr(int32_t B, int32_t total, const int32_t* cu_seqlens, int32_t window,
+                      int32_t* row_ptr, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_varlen(B, total, window);
+  if (st != SA_OK) return st;
+  if (!row_ptr || (total > 0 && (!cu_seqlens || !workspace))) return SA_ERR_NULL;
+  if (total > 0 && workspace_bytes < sa::mask_workspace_bytes(total, 0)) return SA_ERR_WORKSPACE;
+  if (total > 0 && B == 0) return SA_ERR_SHAPE;  // tokens but no sequence
+  clear_stale_error();
+  return hip_status(sa::launch_varlen_row_ptr(B, total, cu_seqlens, window, row_ptr, workspace,
+                                              workspace_bytes, stream));
+}
+
+int sa_varlen_col_idx(int32_t B, int32_t total, const int32_t* cu_seqlens, int32_t window,
+                      const int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                      hipStream_t stream) {
+  const int st = check_varlen(B, total, window);
+  if (st != SA_OK) return st;
+  if (col_capacity < 0) return SA_ERR_SHAPE;
+  if (total == 0 || col_capacity == 0) return SA_OK;
+  if (!cu_seqlens || !row_ptr || !col_idx) return SA_ERR_NULL;
+  if (B == 0) return SA_ERR_SHAPE;
+  clear_stale_error();
+  return hip_status(sa::launch_varlen_col_idx(B, total, cu_seqlens, window, row_ptr, col_idx,
+                                              col_capacity, stream));
+}
+
 int sa_validate_csr(const sa_problem* p, hipStream_t stream) {
   const int st = check_problem(p, kOpValidate);
   if (st != SA_OK) return st;

@@ -31,6 +31,17 @@ hipError_t launch_gather_ordered(const sa_problem& p, const int* order, const fl
 hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const float* dw,
                                    float out_scale, float* ds, hipStream_t s);
 
+// Mask construction: COO -> CSR, key mask from key lengths, packed variable-length batches.
+size_t mask_workspace_bytes(long long n, long long nnz);
+hipError_t launch_coo_to_csr(int n, long long nnz, const int* rows, const int* cols, int* row_ptr,
+                             int* col_idx, int* counts, void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_key_mask_from_lengths(int B, int n, const int* seqlen_k, float* key_mask,
+                                        hipStream_t s);
+hipError_t launch_varlen_row_ptr(int B, int total, const int* cu, int window, int* row_ptr,
+                                 void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_varlen_col_idx(int B, int total, const int* cu, int window, const int* row_ptr,
+                                 int* col_idx, long long cap, hipStream_t s);
+
 // CSR row plan and validation.
 size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);
 hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_t s);

@@ -16,10 +16,12 @@ Two evaluations of the same definition are provided:
 * :mod:`oracle.backward` -- the gradients with respect to q, k and v: the chain
   rule through the three steps, and torch autograd (fp64, CPU) of the dense
   definition.
+* :mod:`oracle.mask` -- masks given as COO pairs, per-batch key lengths or packed
+  variable-length sequences, turned into the CSR pattern and key mask.
 
 Both follow the same conventions (see the module docstrings). Every function
 here has a pin in ``tests/test_oracle_pins.py`` other than itself.
 """
-from . import dense, csr, backward  # noqa: F401
+from . import dense, csr, backward, mask  # noqa: F401
 from .dense import attention_dense, attention_rows, pattern_rows  # noqa: F401
 from .csr import sddmm, sparse_softmax, spmm, attention_csr  # noqa: F401

@@ -223,3 +223,31 @@ def test_backward_calls_check_buffers_and_arguments():
         assert g(q, None, None, None, None, None, None) == sa.SA_OK
         assert f("sa_gather_entries")(q, None, None, None, None) == sa.SA_OK
         assert f("sa_sparse_softmax_backward")(q, None, None, 1.0, None, None) == sa.SA_OK
+
+
+# ---- mask construction entry points (host checks only)
+
+def test_mask_calls_check_sizes_and_buffers():
+    f = _lib.raw
+    ws = f("sa_mask_workspace_bytes")
+    assert ws(-1, 10) == 0 and ws(10, -1) == 0 and ws(10, 1 << 31) == 0
+    assert ws(4096, 1000) >= 2 * 8 * 1000  # keys sorted out of place
+    coo = f("sa_coo_to_csr")
+    assert coo(-1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_SHAPE
+    assert coo(10, 1 << 31, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_SHAPE
+    assert coo(10, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
+    assert coo(10, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
+    assert coo(10, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == sa.SA_ERR_WORKSPACE
+    km = f("sa_key_mask_from_lengths")
+    assert km(-1, 4, FAKE, FAKE, None) == sa.SA_ERR_SHAPE
+    assert km(2, 4, None, FAKE, None) == sa.SA_ERR_NULL
+    assert km(0, 4, None, None, None) == sa.SA_OK
+    rp, ci = f("sa_varlen_row_ptr"), f("sa_varlen_col_idx")
+    assert rp(2, -1, FAKE, -1, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_SHAPE
+    assert rp(2, 100000, FAKE, -1, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_SHAPE  # 1e10 pairs
+    assert rp(0, 10, FAKE, -1, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_SHAPE  # no sequence
+    assert rp(2, 10, None, -1, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
+    assert rp(2, 10, FAKE, -1, FAKE, FAKE, 8, None) == sa.SA_ERR_WORKSPACE
+    assert ci(2, 10, FAKE, -1, FAKE, FAKE, -1, None) == sa.SA_ERR_SHAPE
+    assert ci(2, 10, FAKE, -1, None, FAKE, 100, None) == sa.SA_ERR_NULL
+    assert ci(2, 10, FAKE, -1, FAKE, FAKE, 0, None) == sa.SA_OK  # nothing to write

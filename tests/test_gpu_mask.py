@@ -1,0 +1,161 @@
+"""GPU parity of mask construction: COO -> CSR, key mask from key lengths, and the pattern
+of packed variable-length batches, against oracle.mask (pinned in test_oracle_mask_pins.py).
+
+Patterns and key masks are integer / exact results and are compared bit for bit. At full
+size the COO input is a generated pattern scattered back as shuffled pairs with repeats
+and pairs outside the matrix, so the expected CSR is the generator's own. A packed batch is
+also run through the pipeline and the fused forward and compared with the oracle's
+attention over the same pattern.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import masked_scaled_dot_amd as sa
+from oracle import dense as odense
+from oracle import mask as omask
+from gpu_util import DEV, DevProblem, check, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+def _coo_to_csr(n, rows, cols):
+    nnz = len(rows)
+    R, C = _i32(rows), _i32(cols)
+    row_ptr = torch.full((n + 1,), -7, dtype=torch.int32, device=DEV)
+    col_idx = torch.full((max(nnz, 1),), -7, dtype=torch.int32, device=DEV)
+    counts = torch.full((3,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(sa.sa_mask_workspace_bytes(n, nnz), 1), dtype=torch.uint8, device=DEV)
+    sa.sa_coo_to_csr(n, R, C, row_ptr, col_idx[:nnz], counts, ws)
+    torch.cuda.synchronize()
+    rp = row_ptr.cpu().numpy()
+    return rp, col_idx.cpu().numpy()[:rp[-1]], tuple(counts.cpu().numpy().tolist())
+
+
+def _small_coo(seed, n, nnz, lo=-3, hi=None):
+    rng = np.random.default_rng(seed)
+    hi = n + 3 if hi is None else hi
+    return rng.integers(lo, hi, nnz), rng.integers(lo, hi, nnz)
+
+
+SMALL = {
+    "hand": (4, [2, 0, 2, 5, 0, 1, -1, 2], [1, 3, 1, 0, 0, 2, 1, 0]),
+    "random_dups": (1000, *_small_coo(1, 1000, 20000)),
+    "dense_small": (37, *_small_coo(2, 37, 5000)),  # nearly every pair, many repeats
+    "all_outside": (10, [10, -1, 11], [0, 3, 99]),
+    "empty": (5, [], []),
+    "one_row": (1, [0, 0, 0, 1], [0, 0, 0, 0]),
+    "no_rows": (0, [0, 1], [0, 0]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_coo_to_csr_small(name):
+    n, rows, cols = SMALL[name]
+    say(f"coo_to_csr {name}: n={n} pairs={len(rows)}")
+    got = _coo_to_csr(n, np.asarray(rows), np.asarray(cols))
+    want = omask.coo_to_csr(n, rows, cols)
+    assert np.array_equal(got[0], want[0])
+    assert np.array_equal(got[1], want[1])
+    assert got[2] == tuple(want[2])
+
+
+@pytest.mark.parametrize("name", ["longformer_n4096", "random_n8192"])
+def test_coo_to_csr_full_size_round_trip(name):
+    p = gen.make(name, H=1)
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    cols = p.col_idx.astype(np.int64)
+    rng = np.random.default_rng(9)
+    extra = rng.integers(0, len(rows), 100_000)
+    R = np.concatenate([rows, rows[extra], [-1, p.n, 5]])
+    C = np.concatenate([cols, cols[extra], [0, 0, p.n]])
+    order = rng.permutation(len(R))
+    say(f"coo_to_csr round trip {name}: n={p.n} pairs={len(R)}")
+    rp, ci, counts = _coo_to_csr(p.n, R[order], C[order])
+    assert np.array_equal(rp, p.row_ptr)
+    assert np.array_equal(ci, p.col_idx)
+    assert counts == (len(rows), 3, 100_000)
+
+
+def test_key_mask_from_lengths():
+    lens = np.array([0, 1, 383, 384, 500, -4, 200], np.int32)
+    B, n = len(lens), 384
+    km = torch.full((B, n), float("nan"), device=DEV)
+    sa.sa_key_mask_from_lengths(B, n, _i32(lens), km)
+    torch.cuda.synchronize()
+    assert np.array_equal(km.cpu().numpy(), omask.key_mask_from_lengths(lens, n))
+
+
+def test_key_mask_from_lengths_reproduces_the_padding_mask():
+    """The key-padding mask of the Evoformer-style workload (the last p_b keys masked) is
+    exactly the mask of the lengths n - p_b, and the fused forward gives the same bits."""
+    p = gen.make("evoformer_l384", B=4, H=2)
+    lens = np.isfinite(p.key_mask[:, 0, :]).sum(axis=1).astype(np.int32)
+    assert np.array_equal(p.key_mask[:, 0, :], omask.key_mask_from_lengths(lens, p.n))
+    km = torch.empty((p.B, 1, p.n), device=DEV)
+    sa.sa_key_mask_from_lengths(p.B, p.n, _i32(lens), km)
+    dp = DevProblem(p)
+    ref, ref_lse = dp.fused()
+    dp2 = DevProblem(p)
+    dp2.key_mask = km
+    dp2.prob = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16, None, None, 0, scale=p.scale,
+                          bias=dp2.bias, key_mask=km, key_mask_heads=1)
+    got, got_lse = dp2.fused()
+    assert np.array_equal(got, ref) and np.array_equal(got_lse, ref_lse)
+
+
+VARLEN = {
+    "full": ([0, 5, 6, 14, 14, 300, 301, 700], 700, -1),
+    "window": ([0, 200, 260, 700, 1000], 1000, 16),
+    "trailing_tokens": ([0, 64, 100], 130, -1),
+    "one_sequence": ([0, 513], 513, -1),
+}
+
+
+def _varlen(cu, total, window):
+    cu_d = _i32(cu)
+    B = len(cu) - 1
+    row_ptr = torch.full((total + 1,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(sa.sa_mask_workspace_bytes(total, 0), dtype=torch.uint8, device=DEV)
+    sa.sa_varlen_row_ptr(B, total, cu_d, window, row_ptr, ws)
+    nnz = int(row_ptr[total].item())
+    col_idx = torch.full((max(nnz, 1),), -7, dtype=torch.int32, device=DEV)
+    sa.sa_varlen_col_idx(B, total, cu_d, window, row_ptr, col_idx[:nnz])
+    torch.cuda.synchronize()
+    return row_ptr.cpu().numpy(), col_idx.cpu().numpy()[:nnz]
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN))
+def test_varlen_pattern(name):
+    cu, total, window = VARLEN[name]
+    say(f"varlen {name}: total={total} sequences={len(cu) - 1} window={window}")
+    rp, ci = _varlen(cu, total, window)
+    want_rp, want_ci = omask.varlen_csr(cu, total, window)
+    assert np.array_equal(rp, want_rp)
+    assert np.array_equal(ci, want_ci)
+
+
+@pytest.mark.parametrize("name", ["full", "window"])
+def test_varlen_attention(name):
+    """A packed batch (B = 1, n = total tokens) through the pipeline and the fused forward,
+    against the oracle's attention over the same pattern."""
+    cu, total, window = VARLEN[name]
+    rp, ci = _varlen(cu, total, window)
+    p = gen.make("longformer_n4096", n=total, H=2)
+    p = dataclasses.replace(p, row_ptr=rp, col_idx=ci)
+    say(f"varlen attention {name}: total={total} nnz={p.nnz}")
+    ref = odense.attention_dense(p.q, p.k, p.v, p.scale, p.H, ("csr", rp, ci))
+    for plan in (False, True):
+        dp = DevProblem(p, plan=plan)
+        _, W, O = dp.pipeline()
+        check(O, ref["O"], p.dtype, f"pipeline O plan={plan}")
+        Of, lse = dp.fused()
+        check(Of, ref["O"], p.dtype, f"fused O plan={plan}")
+        check(lse, ref["lse"], p.dtype, f"fused lse plan={plan}")
