@@ -16,6 +16,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -285,10 +286,71 @@ def bytes_backward(BH, n, d, nnz, elem):
             "spmmT_dS_Q": spmm, "spmmT_W_dO": spmm}
 
 
-def time_fused(torch, sa, p, iters=20, warmup=3, element=False):
+def _avg_us(torch, f, iters=10, warmup=2):
+    """Average HIP-event time of f over `iters` back-to-back calls on the current stream."""
+    for _ in range(warmup):
+        f()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(iters):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+def time_mask_construction(torch, sa, p):
+    """Mask construction on the device: the workload's pattern given as shuffled COO pairs
+    (COO -> CSR), a packed batch of 8 sequences of 4096 tokens in all (both varlen calls),
+    key masks from 32 key lengths of 384 keys, and the fused dense kernel on evoformer_l384
+    with its key padding given as the mask vector, as per-batch key lengths, and absent."""
+    import gen
+    dev = "cuda:0"
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    order = np.random.default_rng(5).permutation(len(rows))
+    R = torch.from_numpy(rows[order].astype(np.int32)).to(dev)
+    C = torch.from_numpy(p.col_idx[order].astype(np.int32)).to(dev)
+    rp = torch.empty(p.n + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(len(rows), dtype=torch.int32, device=dev)
+    counts = torch.empty(3, dtype=torch.int32, device=dev)
+    ws = torch.empty(sa.sa_mask_workspace_bytes(p.n, len(rows)), dtype=torch.uint8, device=dev)
+    coo_us = _avg_us(torch, lambda: sa.sa_coo_to_csr(p.n, R, C, rp, ci, counts, ws))
+    lens = np.random.default_rng(6).multinomial(4096 - 8, [1 / 8] * 8) + 1
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    vrp = torch.empty(4097, dtype=torch.int32, device=dev)
+    vws = torch.empty(sa.sa_mask_workspace_bytes(4096, 0), dtype=torch.uint8, device=dev)
+    sa.sa_varlen_row_ptr(8, 4096, cu, -1, vrp, vws)
+    vnnz = int(vrp[-1].item())
+    vci = torch.empty(vnnz, dtype=torch.int32, device=dev)
+    varlen_us = _avg_us(torch, lambda: (sa.sa_varlen_row_ptr(8, 4096, cu, -1, vrp, vws),
+                                        sa.sa_varlen_col_idx(8, 4096, cu, -1, vrp, vci)))
+    seqlen = torch.from_numpy(np.random.default_rng(7).integers(320, 385, 32).astype(np.int32)).to(dev)
+    km = torch.empty(32, 384, device=dev)
+    km_us = _avg_us(torch, lambda: sa.sa_key_mask_from_lengths(32, 384, seqlen, km))
+    evo = gen.make("evoformer_l384")
+    with_mask = time_fused(torch, sa, evo)
+    without = time_fused(torch, sa, dataclasses.replace(evo, key_mask=None))
+    evo_lens = np.isfinite(evo.key_mask[:, 0, :]).sum(axis=1)  # the same padding as lengths
+    with_lens = time_fused(torch, sa, dataclasses.replace(evo, key_mask=None), seqlen_k=evo_lens)
+    return {"coo_to_csr_" + p.name: {"pairs": len(rows), "us": round(coo_us, 2),
+                                     "pairs_per_s": len(rows) / (coo_us * 1e-6)},
+            "varlen_8_sequences_4096_tokens": {"nnz": vnnz, "us": round(varlen_us, 2),
+                                               "entries_per_s": vnnz / (varlen_us * 1e-6)},
+            "key_mask_from_lengths_32x384": {"us": round(km_us, 2)},
+            "fused_evoformer_l384_key_padding": {"key_mask_vector_us": round(with_mask, 2),
+                                                 "seqlen_k_us": round(with_lens, 2),
+                                                 "no_padding_us": round(without, 2)}}
+
+
+def time_fused(torch, sa, p, iters=20, warmup=3, element=False, seqlen_k=None):
     """Average HIP-event time of one fused forward over `iters` back-to-back launches; an
-    element CSR gets its row plan first (built once per mask, as for the pipeline)."""
+    element CSR gets its row plan first (built once per mask, as for the pipeline).
+    seqlen_k: optional per-batch key lengths (host ints) read by the kernel."""
     prob, t, nnz = to_device(p, torch, sa, element=element)
+    if seqlen_k is not None:
+        t["seqlen_k"] = torch.tensor(np.asarray(seqlen_k, np.int32), device="cuda:0")
+        prob.c.seqlen_k = t["seqlen_k"].data_ptr()
     if prob.c.row_ptr and prob.c.block == 1:
         t["plan"] = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
         sa.sa_plan_build(prob, t["plan"])
@@ -488,6 +550,10 @@ def main():
                 "warm": True}
             log(f"fused {name}: {us:.1f} us")
             del q
+
+        mc = time_mask_construction(torch, sa, p)
+        extra["mask_construction"] = mc
+        log("mask construction: " + ", ".join(f"{k} {v.get('us', v)}" for k, v in mc.items()))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -90,7 +90,14 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  * key_mask : NULL or fp32 [B, key_mask_heads, n] (the [B, 1 or H, 1, seq_k] additive
  *            key mask, usually 0 / -inf); key_mask_heads is 1 or H.
  * plan     : NULL, or a buffer filled by sa_plan_build for this same pattern; calls that
- *            schedule rows read it instead of building their own. */
+ *            schedule rows read it instead of building their own.
+ * seqlen_k : NULL or int32 [B] on the device: keys j >= seqlen_k[b] (clamped to [0, n]) are
+ *            masked for every head and query of batch b, as if the key mask held -inf there
+ *            (the one-int-per-batch key padding of the AlphaFold2 pull request, key-padding
+ *            discussion). Read by sa_sddmm and sa_fused_forward (the dense and block-CSR
+ *            tiles skip the key blocks past the length); it may be combined with key_mask.
+ *            With an element-CSR plan, sa_sddmm and sa_fused_forward take their row
+ *            kernels (no plan) when seqlen_k is set. */
 typedef struct sa_problem {
   int32_t B, H, n, d;
   int32_t dtype;           /* sa_dtype of q, k, v                                     */
@@ -103,6 +110,7 @@ typedef struct sa_problem {
   const float *bias;
   const float *key_mask;
   const void *plan;
+  const int32_t *seqlen_k; /* NULL or [B] valid keys per batch                        */
   int32_t flags;           /* SA_FLAG_*                                               */
   int32_t reserved;        /* must be 0                                               */
 } sa_problem;

@@ -46,6 +46,7 @@ class sa_problem(ctypes.Structure):
         ("nnz", ctypes.c_int64),
         ("scale", ctypes.c_float), ("key_mask_heads", ctypes.c_int32),
         ("bias", ctypes.c_void_p), ("key_mask", ctypes.c_void_p), ("plan", ctypes.c_void_p),
+        ("seqlen_k", ctypes.c_void_p),
         ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
@@ -151,15 +152,17 @@ class Problem:
     """Holds an ``sa_problem`` plus references to the tensors it points into."""
 
     def __init__(self, B, H, n, d, dtype=SA_BF16, row_ptr=None, col_idx=None, nnz=None, block=1,
-                 scale=1.0, bias=None, key_mask=None, key_mask_heads=1, plan=None, flags=0):
+                 scale=1.0, bias=None, key_mask=None, key_mask_heads=1, plan=None, flags=0,
+                 seqlen_k=None):
         self._keep = (row_ptr, col_idx, bias, key_mask, plan)
+        self._seqlen_k = seqlen_k
         if nnz is None:
             nnz = 0 if col_idx is None else (col_idx.numel() if _is_tensor(col_idx) else 0)
         self.c = sa_problem(B=B, H=H, n=n, d=d, dtype=dtype, block=block,
                             row_ptr=_ptr(row_ptr), col_idx=_ptr(col_idx), nnz=nnz,
                             scale=scale, key_mask_heads=key_mask_heads,
                             bias=_ptr(bias), key_mask=_ptr(key_mask), plan=_ptr(plan),
-                            flags=flags, reserved=0)
+                            seqlen_k=_ptr(seqlen_k), flags=flags, reserved=0)
         torch = _torch()
         if row_ptr is not None:
             rows = n if block == 1 else (n + block - 1) // block
@@ -167,6 +170,7 @@ class Problem:
             _check(col_idx, "col_idx", nnz, torch.int32)
         _check(bias, "bias", H * n * n, torch.float32)
         _check(key_mask, "key_mask", B * key_mask_heads * n, torch.float32)
+        _check(seqlen_k, "seqlen_k", B, torch.int32)
 
     # convenience sizes
     @property

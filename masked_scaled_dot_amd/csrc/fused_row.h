@@ -32,6 +32,7 @@ struct FusedArgs {
   const float* bias;
   const float* key_mask;
   const int* plan;
+  const int* seqlen_k;  // NULL or valid keys per batch
   int B, H, n;
   long long nnz;
   int km_heads;
@@ -119,6 +120,8 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
   const T* vt = static_cast<const T*>(a.v) + (size_t)t * n * D;
   const float* brow = a.bias ? a.bias + ((size_t)h * n + row) * n : nullptr;
   const float* km = a.key_mask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
+  const int ncols = a.seqlen_k ? clampi(a.seqlen_k[b], 0, n) : n;  // keys at or past it are masked
+  if constexpr (K == kFusedDense) e_end = e_end < ncols ? e_end : ncols;
 
   float m = -INFINITY, l = 0.f;
 #pragma unroll
@@ -141,7 +144,7 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
       } else {
         col = (int)ee;
       }
-      ok[u] = e < e_end && col >= 0 && col < n;
+      ok[u] = e < e_end && col >= 0 && col < ncols;
       j[u] = clampi(col, 0, n - 1);
       kc[u] = reinterpret_cast<const u32x4_v*>(kt + (size_t)j[u] * D)[r];
       vc[u] = reinterpret_cast<const u32x4_v*>(vt + (size_t)j[u] * D)[r];

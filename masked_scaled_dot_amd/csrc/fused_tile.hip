@@ -236,7 +236,12 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   // ALUs after the loop, more as one gathered block)
   const int nbc = K == kFusedCsr ? tv.kb_hi - tv.kb_lo : 0;
   const bool far_vec = K == kFusedCsr && tv.nfar > 0 && tv.nfar <= kFarVec;
-  const int nblk = K == kFusedBsr ? (int)(be - bs) : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv)) : ntiles;
+  // dense and block CSR: keys at or past the batch's key length (n without one) are masked,
+  // and the dense kind stops at the block that holds the last valid key
+  const int nvalid = K != kFusedCsr && a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
+  const int nblk = K == kFusedBsr ? (int)(be - bs)
+                   : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv))
+                                    : (nvalid + kTileRows - 1) / kTileRows;
   if constexpr (K == kFusedBsr)
     for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
   if constexpr (K == kFusedCsr) {
@@ -366,7 +371,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
         if constexpr (kMask) ad[tt] += mk[tt];
       }
     }
-    const int lim = n - block_k0(j);       // keys of this block below n
+    const int lim = nvalid - block_k0(j);  // keys of this block below n (or the key length)
     const unsigned blo = mlo, bhi = mhi;   // element CSR: key slots the query holds in block j
     lds_barrier();                         // block j is staged for every wave
     prefetch(min(j + 1, nblk - 1));        // in flight while block j is computed
@@ -399,7 +404,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sc[tt][i] = ((tt < 2 ? blo : bhi) >> ((16 * tt + 4 * g + i) & 31)) & 1u ? sc[tt][i] : -INFINITY;
-    } else if (lim < kTileRows) {  // ragged last block: keys at or past n score -inf
+    } else if (lim < kTileRows) {  // ragged or last valid block: keys at or past lim score -inf
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -601,7 +606,8 @@ hipError_t launch_block_t(const sa_problem& p, const FusedArgs& a, hipStream_t s
 }  // namespace
 
 bool fused_tile_supported(const sa_problem& p) {
-  if (p.row_ptr && p.block == 1) return p.plan != nullptr;  // plan-driven CSR (both dtypes)
+  // plan-driven CSR (both dtypes); its tiles do not read key lengths
+  if (p.row_ptr && p.block == 1) return p.plan != nullptr && p.seqlen_k == nullptr;
   // block CSR and dense: bf16, with every buffer the tile addresses within 32-bit offsets
   const long long kv = (long long)p.n * p.d * 2;
   const long long bias = p.bias ? (long long)p.n * p.n * 4 : 0;
@@ -611,7 +617,7 @@ bool fused_tile_supported(const sa_problem& p) {
 hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
                              float* out, float* lse, hipStream_t s) {
   const FusedArgs a{q, k, v, p.row_ptr, p.col_idx, out, lse, p.bias, p.key_mask,
-                    static_cast<const int*>(p.plan), p.B, p.H, p.n, (long long)p.nnz,
+                    static_cast<const int*>(p.plan), p.seqlen_k, p.B, p.H, p.n, (long long)p.nnz,
                     p.key_mask_heads, p.scale};
   if (p.B == 0 || p.H == 0 || p.n == 0) return hipSuccess;
   if (p.row_ptr && p.block == 1) {

@@ -40,7 +40,7 @@ hipError_t launch_kind(const sa_problem& p, const FusedArgs& a, hipStream_t s) {
 hipError_t launch_fused_valu(const sa_problem& p, const void* q, const void* k, const void* v,
                              float* out, float* lse, hipStream_t s) {
   const FusedArgs a{q, k, v, p.row_ptr, p.col_idx, out, lse, p.bias, p.key_mask, nullptr,
-                    p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
+                    p.seqlen_k, p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
   const bool bf = p.dtype == SA_BF16;
   switch (p.d) {
     case 32: return bf ? launch_kind<bf16_t, 32>(p, a, s) : launch_kind<float, 32>(p, a, s);

@@ -76,6 +76,7 @@ struct Args {
   const float* bias;
   const float* key_mask;
   const int* plan;
+  const int* seqlen_k;
   int B, H, n;
   long long nnz;
   int km_heads;
@@ -93,6 +94,7 @@ __device__ __forceinline__ float additive(const Args& a, int h, int b, int row, 
   float x = 0.f;
   if (a.bias) x += a.bias[((size_t)h * a.n + row) * a.n + col];
   if (a.key_mask) x += a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * a.n + col];
+  if (a.seqlen_k && col >= clampi(a.seqlen_k[b], 0, a.n)) x = -INFINITY;
   return x;
 }
 
@@ -573,9 +575,9 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
 template <typename T, int D>
 hipError_t launch_t(const sa_problem& p, const void* q, const void* k, float* scores, hipStream_t s) {
   Args a{q, k, p.row_ptr, p.col_idx, scores, p.bias, p.key_mask, static_cast<const int*>(p.plan),
-         p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
+         p.seqlen_k, p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
   const int BH = p.B * p.H;
-  if (p.plan) {
+  if (p.plan && !p.seqlen_k) {  // the plan's tiles do not read key lengths
     const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
     const long long blocks = kLongWGs + ntiles * BH;
     const dim3 grid((unsigned)blocks), block(kThreads);

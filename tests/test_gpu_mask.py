@@ -159,3 +159,92 @@ def test_varlen_attention(name):
         Of, lse = dp.fused()
         check(Of, ref["O"], p.dtype, f"fused O plan={plan}")
         check(lse, ref["lse"], p.dtype, f"fused lse plan={plan}")
+
+
+# ---- key lengths read by the kernels (sa_problem.seqlen_k)
+
+def _with_lengths(dp, lens, use_key_mask=True):
+    p = dp.p
+    sl = _i32(lens)
+    km = dp.key_mask if use_key_mask else None
+    dp.prob = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16 if p.dtype == "bf16" else sa.SA_F32,
+                         dp.row_ptr, dp.col_idx, p.nnz, block=p.block, scale=dp.scale,
+                         bias=dp.bias, key_mask=km, key_mask_heads=p.key_mask_heads,
+                         seqlen_k=sl)
+    if dp.plan is not None:
+        dp.prob.set_plan(dp.plan)
+    return dp
+
+
+def _oracle_with_lengths(p, lens, use_key_mask=True):
+    km = omask.key_mask_from_lengths(lens, p.n)[:, None, :]
+    if use_key_mask and p.key_mask is not None:
+        km = km + p.key_mask  # both masks apply
+    return odense.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), bias=p.bias,
+                                  key_mask=km, km_heads=1)
+
+
+def _pattern(p):
+    if p.row_ptr is None:
+        return ("dense",)
+    if p.block == 64:
+        return ("bsr", p.row_ptr, p.col_idx, 64)
+    return ("csr", p.row_ptr, p.col_idx)
+
+
+SEQLEN = {
+    # name: (problem, lengths per batch, keep the generator's key mask too)
+    "dense_bias": (lambda: gen.make("evoformer_l384", B=5, H=2), [384, 0, 1, 200, 320], False),
+    "dense_bias_and_mask": (lambda: gen.make("evoformer_l384", B=3, H=2), [300, 64, 384], True),
+    "dense_ragged_n": (lambda: gen.make("evoformer_l384", B=2, H=2, n=200), [130, 200], False),
+    "dense_f32": (lambda: gen.make("evoformer_l384", B=2, H=2, n=160, dtype="f32"), [100, 7], False),
+    "bsr": (lambda: gen.make("bsr_n16384", n=640, H=2, d=64, extra=3), [500], False),
+    "csr": (lambda: gen.make("longformer_n4096", n=700, H=2, window=40), [650], False),
+    "csr_with_key_mask": (lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
+                                           bias=True, key_mask=True, pmax=40), [250, 299], True),
+}
+
+
+@pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
+@pytest.mark.parametrize("name", sorted(SEQLEN))
+def test_seqlen_k_fused(name, plan):
+    make, lens, keep_km = SEQLEN[name]
+    p = make()
+    if plan and (p.row_ptr is None or p.block != 1):
+        pytest.skip("plans are for element CSR")
+    say(f"seqlen_k fused {name} plan={plan}: B={p.B} H={p.H} n={p.n} lens={lens}")
+    dp = _with_lengths(DevProblem(p, plan=plan), lens, keep_km)
+    ref = _oracle_with_lengths(p, lens, keep_km)
+    O, lse = dp.fused()
+    check(O, ref["O"], p.dtype, "O")
+    check(lse, ref["lse"], p.dtype, "lse")
+
+
+@pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
+@pytest.mark.parametrize("name", ["csr", "csr_with_key_mask"])
+def test_seqlen_k_pipeline(name, plan):
+    """SDDMM reads the key lengths (masked scores are exactly -inf); softmax and SpMM then
+    need nothing more."""
+    make, lens, keep_km = SEQLEN[name]
+    p = make()
+    say(f"seqlen_k pipeline {name} plan={plan}: B={p.B} H={p.H} n={p.n} lens={lens}")
+    dp = _with_lengths(DevProblem(p, plan=plan), lens, keep_km)
+    ref = _oracle_with_lengths(p, lens, keep_km)
+    S, W, O = dp.pipeline()
+    check(O, ref["O"], p.dtype, "O")
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    for t in range(p.BH):
+        masked = p.col_idx >= lens[t // p.H]
+        assert np.all(S[t][masked] == -np.inf) and np.all(W[t][masked] == 0)
+    assert rows.size == p.nnz
+
+
+def test_seqlen_k_dense_equals_key_mask_vector():
+    """The Evoformer-style workload's key padding given as lengths instead of its mask
+    vector: the dense tiles skip the blocks past the length and give the same result."""
+    p = gen.make("evoformer_l384", B=4, H=2)
+    lens = np.isfinite(p.key_mask[:, 0, :]).sum(axis=1).astype(np.int32)
+    ref_O, ref_lse = DevProblem(p).fused()
+    got_O, got_lse = _with_lengths(DevProblem(p), lens, use_key_mask=False).fused()
+    np.testing.assert_allclose(got_O, ref_O, atol=1e-6, rtol=0)
+    np.testing.assert_allclose(got_lse, ref_lse, atol=1e-6, rtol=0)
