@@ -45,10 +45,12 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="longformer_n4096",
                     choices=["longformer_n4096", "random_n8192"])
+    ap.add_argument("--streams", type=int, default=2,
+                    help="independent batches in flight, one HIP stream (and graph) each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
@@ -207,6 +209,50 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, eager_wall, plan_us, chunk
+
+
+def run_concurrent_steps(torch, sa, p, steps, warmup, streams):
+    """`steps` pipeline steps split evenly over `streams` independent batches, each with its
+    own copy of the inputs, its own plan and outputs, captured as a HIP graph of `chunk` steps
+    on its own stream (default priority); the graphs are replayed round-robin so the streams'
+    kernels overlap. Returns (wall seconds of all `steps` steps, steps per graph)."""
+    per = steps // streams
+    chunk = max(c for c in range(1, min(per, 10) + 1) if per % c == 0)
+    lanes = []
+    for _ in range(streams):
+        prob, t, nnz = to_device(p, torch, sa)
+        plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+        sa.sa_plan_build(prob, plan)
+        prob.set_plan(plan)
+        S = torch.empty(p.BH * nnz, device="cuda:0")
+        W = torch.empty_like(S)
+        O = torch.empty(p.BH, p.n, p.d, device="cuda:0")
+
+        def step(prob=prob, t=t, S=S, W=W, O=O):
+            sa.sa_sddmm(prob, t["q"], t["k"], S)
+            sa.sa_sparse_softmax(prob, S, W)
+            sa.sa_spmm(prob, W, t["v"], O)
+
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(chunk):
+                step()
+        lanes.append((graph, torch.cuda.Stream(), (prob, t, plan, S, W, O)))
+
+    def replay_all(rounds):
+        for _ in range(rounds):
+            for graph, stream, _ in lanes:
+                with torch.cuda.stream(stream):
+                    graph.replay()
+
+    replay_all(max(1, warmup // chunk))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    replay_all(per // chunk)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, chunk
 
 
 def run_backward_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
@@ -461,10 +507,19 @@ def main():
     wall, eager_wall, plan_us, chunk = run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d,
                                                           args.steps, args.warmup, timer)
     kern_us = timer.result()
-    ms_per_step = wall * 1e3 / args.steps
-    value = pairs / (wall / args.steps)
-    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step (graph of {chunk} steps), "
-        f"{eager_wall * 1e6 / args.steps:.1f} us/step (eager)  " +
+    single_ms = wall * 1e3 / args.steps
+    streams = args.streams if args.streams > 1 and args.steps % args.streams == 0 else 1
+    if streams > 1:
+        cwall, cchunk = run_concurrent_steps(torch, sa, p, args.steps, args.warmup, streams)
+        launch = (f"{streams} streams, each a HIP graph of {cchunk} steps on its own inputs, plan "
+                  f"and outputs, {args.steps // streams} steps per stream, replayed concurrently")
+    else:
+        cwall = wall
+        launch = f"one stream: a HIP graph of {chunk} steps, replayed {args.steps // chunk} times"
+    ms_per_step = cwall * 1e3 / args.steps
+    value = pairs / (cwall / args.steps)
+    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step ({streams} streams), {single_ms * 1e3:.1f} us/step "
+        f"(one stream, graph of {chunk} steps), {eager_wall * 1e6 / args.steps:.1f} us/step (eager)  " +
         "  ".join(f"{k}={v:.1f}us" for k, v in kern_us.items()))
 
     algo = bytes_pipeline(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
@@ -568,7 +623,8 @@ def main():
                    "pairs_per_step": pairs,
                    "step": "sddmm + sparse_softmax + spmm (scores, weights, context); the row plan "
                            "is built once per mask before timing",
-                   "launch": f"HIP graph of {chunk} steps, replayed {args.steps // chunk} times",
+                   "launch": launch, "streams": streams,
+                   "single_stream_ms_per_step": round(single_ms, 5),
                    "eager_ms_per_step": round(eager_wall * 1e3 / args.steps, 5),
                    "inputs": "resident in HBM; caches not flushed between steps"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "extra": extra,
