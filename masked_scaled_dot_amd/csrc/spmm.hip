@@ -351,6 +351,169 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
   }
 }
 
+// Banded matrix-core tile (the plan's banded flag: every row's core columns are consecutive,
+// and at most kFarVec far columns): the weights of row r for keys c0 .. c0 + len - 1 are the
+// consecutive entries lo .. lo + len - 1 of its core range (plan rows table), so each lane loads
+// its eight A-operand weights of a 32-key chunk (row c16, keys 8g .. 8g + 7) straight from
+// global memory as two 16-byte loads, one block ahead, and masks the keys outside the run in
+// registers. No block records are staged and the weights make no round trip through LDS; V is
+// staged and read as in spmm_tile. Loads whose 32 bytes would start before or end past the
+// tile's entry span (a row at the edge of the span) take eight 4-byte loads instead.
+template <int D>
+__device__ void spmm_tile_banded(const Args& a, TileSmem<D>& sm, const TileView& tv, int t, int row0,
+                                 long long e_lo, long long e_hi) {
+  constexpr int VS = TileSmem<D>::kVStride;
+  constexpr int OC = D / 16;
+  constexpr int VCH = kTileRows * (D / 8) / kThreads;  // 16-byte V chunks per thread per block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c16 = lane % 16;
+  const int nblk = tv.kb_hi - tv.kb_lo;
+  const int span = (int)(e_hi - e_lo);
+  if (threadIdx.x < kTileRows) {
+    const int r = threadIdx.x, row = row0 + r;
+    sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, a.n - 1);
+    int live = 0;
+    if (row < a.n) {
+      long long rs, re;
+      row_bounds(a, row, rs, re);
+      live = re - rs <= kLongRow;  // longer rows are written by their segments
+    }
+    sm.live[r] = live;
+  }
+  // the lane's A row: its core run of keys [c0, c0 + len) sits at entries base + key
+  // (relative to e_lo); rows past n, long rows and rows without a core hold nothing
+  const int arow = row0 + wave * 16 + c16;
+  int c0 = 0, len = 0, base = 0;
+  if (arow < a.n) {
+    long long rs, re;
+    row_bounds(a, arow, rs, re);
+    const int* prow = a.plan + a.plan[kHOffRows];
+    const long long lo = prow[2 * arow], hi = prow[2 * arow + 1];
+    if (re - rs <= kLongRow && hi > lo && lo >= e_lo && hi <= e_hi) {
+      c0 = clampi(a.col_idx[lo], 0, a.n - 1);
+      len = (int)(hi - lo);
+      base = (int)(lo - e_lo) - c0;
+    }
+  }
+  __syncthreads();
+  const uint16_t* vt = static_cast<const uint16_t*>(a.v) + (size_t)t * a.n * D;
+  const __amdgpu_buffer_rsrc_t wbuf = make_rsrc(a.w + (size_t)t * a.nnz + e_lo, (long long)span * 4);
+
+  u32x4_v vn[VCH];
+  f32x4_v wn[4];  // [2 kk + half]: keys k0 + 32kk + 8g + 4half .. +3 of row c16
+  auto prefetch = [&](int jj) {
+    const int k0 = (tv.kb_lo + jj) * kTileRows;
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const int key = min(k0 + i / (D / 8), a.n - 1);
+      vn[u] = *reinterpret_cast<const u32x4_v*>(vt + (size_t)key * D + (i % (D / 8)) * 8);
+    }
+    bool edge = false;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kf = k0 + 32 * kk + 8 * g;
+      const bool any = kf + 7 >= c0 && kf < c0 + len;
+      const int e = base + kf;
+      const bool whole = any && e >= 0 && e + 8 <= span;
+      edge |= any && !whole;
+      wn[2 * kk] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(wbuf, whole ? e * 4 : kOffNone, 0, 0));
+      wn[2 * kk + 1] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(wbuf, whole ? e * 4 + 16 : kOffNone, 0, 0));
+    }
+    if (__builtin_amdgcn_ballot_w64(edge) != 0) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kf = k0 + 32 * kk + 8 * g;
+          const int e = base + kf + i;
+          const bool whole = kf + 7 >= c0 && kf < c0 + len && base + kf >= 0 && base + kf + 8 <= span;
+          const bool in = (unsigned)(kf + i - c0) < (unsigned)len;
+          const float x = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(wbuf, in && !whole ? e * 4 : kOffNone, 0, 0));
+          if (!whole) wn[2 * kk + i / 4][i % 4] = x;
+        }
+    }
+  };
+
+  f32x4_v o[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  if (nblk > 0) prefetch(0);
+  for (int j = 0; j < nblk; ++j) {
+    uint16_t* vb = sm.v[j & 1];
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&vb[(i / (D / 8)) * VS + (i % (D / 8)) * 8]) = vn[u];
+    }
+    // block j's A operands as hi and lo bf16 planes, keys outside the row's run set to 0
+    const int k0 = (tv.kb_lo + j) * kTileRows;
+    bf16x8_v ahi[2], alo[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kf = k0 + 32 * kk + 8 * g;
+      f32x8_v wv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = wn[2 * kk + i / 4][i % 4];
+        wv[i] = (unsigned)(kf + i - c0) < (unsigned)len ? x : 0.f;
+      }
+      ahi[kk] = __builtin_convertvector(wv, bf16x8_v);
+      const f32x8_v rest = wv - __builtin_convertvector(ahi[kk], f32x8_v);
+      alo[kk] = __builtin_convertvector(rest, bf16x8_v);
+    }
+    lds_barrier();                   // block j's V is visible to every wave
+    prefetch(min(j + 1, nblk - 1));  // in flight while block j is multiplied
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int vkey = 32 * kk + 8 * g + c16 / 4;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) {
+        const int vcol = 16 * c + 4 * (c16 % 4);
+        typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+        const i16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[vkey * VS + vcol]));
+        const i16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&vb[(vkey + 4) * VS + vcol]));
+        const bf16x8_v bv = __builtin_bit_cast(
+            bf16x8_v, (__attribute__((ext_vector_type(8))) short){b0[0], b0[1], b0[2], b0[3],
+                                                                  b1[0], b1[1], b1[2], b1[3]});
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[kk], bv, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[kk], bv, o[c], 0, 0, 0);
+      }
+    }
+  }
+  mfma_drain();
+  // far column f (at most kFarVec): O[row] += w[row, f] V[far_f] for the lane's rows 4g + i
+  // and columns 16c + c16, the row's entry found from the gathered block's record
+  for (int f = 0; f < tv.nfar; ++f) {
+    const int kf = sm.far[f];
+    float vf[OC];
+#pragma unroll
+    for (int c = 0; c < OC; ++c) vf[c] = __uint_as_float((uint32_t)vt[(size_t)kf * D + 16 * c + c16] << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x4_v rc = tv.rec[nblk * kTileRows + wave * 16 + 4 * g + i];
+      const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
+      const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
+      const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
+      const float w = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(wbuf, (m >> f) & 1ull ? e * 4 : kOffNone, 0, 0));
+#pragma unroll
+      for (int c = 0; c < OC; ++c) o[c][i] = fmaf(w, vf[c], o[c][i]);
+    }
+  }
+  // accumulator layout: lane holds column 16c + c16 of the wave's rows 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = wave * 16 + 4 * g + i;
+    if (!sm.live[lr]) continue;
+    float* orow = a.out + ((size_t)t * a.n + row0 + lr) * D;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) orow[16 * c + c16] = o[c][i];
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
   __shared__ TileSmem<D> sm;
@@ -450,7 +613,10 @@ __global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
     }
     return;
   }
-  if constexpr (sizeof(T) == 2) spmm_tile<D>(a, sm, tv, t, row0, e_lo, e_hi);
+  if constexpr (sizeof(T) == 2) {
+    if (tv.banded && tv.nfar <= kFarVec) spmm_tile_banded<D>(a, sm, tv, t, row0, e_lo, e_hi);
+    else spmm_tile<D>(a, sm, tv, t, row0, e_lo, e_hi);
+  }
   (void)lane;
 }
 
