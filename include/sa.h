@@ -192,6 +192,11 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  *   was built from, for one array (src_b = dst_b = NULL) or two at once (e.g. dS and W);
  *   reads the sources in ascending runs, which is faster when the pattern is banded. No
  *   destination may alias a source or the other destination (SA_ERR_SHAPE).
+ * sa_bias_grad: the gradient of the shared bias [H, n, n] (the flash-attention pull request's
+ *   bias-gradient question): dbias[h, i, j] = factor * sum over b of dscores[(b*H + h)*nnz + e]
+ *   for each stored entry e = (i, j); entries outside the pattern are not written (the caller
+ *   zeroes dbias). With dscores from sa_sparse_softmax_backward at out_scale = scale, pass
+ *   factor = 1 / scale (or out_scale = 1 and factor = 1). dbias fp32 [H, n, n].
  * sa_sparse_softmax_backward: dscores[t*nnz + e] = out_scale * W[e] * (dW[e] - D_row),
  *   D_row = sum over the row's entries of W * dW; weights, dweights and dscores are fp32
  *   [B*H, nnz] (dscores may alias dweights). out_scale = scale gives the operand of dQ
@@ -207,6 +212,8 @@ int sa_gather_entries_ordered(const sa_problem *p, const int32_t *order, const f
                               float *dst_a, const float *src_b, float *dst_b, hipStream_t stream);
 int sa_sparse_softmax_backward(const sa_problem *p, const float *weights, const float *dweights,
                                float out_scale, float *dscores, hipStream_t stream);
+int sa_bias_grad(const sa_problem *p, const float *dscores, float factor, float *dbias,
+                 hipStream_t stream);
 
 /* --- Mask construction ---------------------------------------------------------------------
  * The gluon-nlp proposal (opening post) takes the mask as a sparse (n, n) matrix in CSR or

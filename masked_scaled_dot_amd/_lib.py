@@ -32,7 +32,7 @@ SA_FLAG_VALIDATE = 1
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
            "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
-           "sa_sparse_softmax_backward", "sa_mask_workspace_bytes", "sa_coo_to_csr",
+           "sa_sparse_softmax_backward", "sa_bias_grad", "sa_mask_workspace_bytes", "sa_coo_to_csr",
            "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_validate_csr",
            "sa_status_string", "sa_last_hip_error_string")
 
@@ -82,6 +82,7 @@ def _load():
         "sa_varlen_col_idx": (ctypes.c_int, [i32, i32, vp, i32, vp, vp, i64, vp]),
         "sa_gather_entries_ordered": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
+        "sa_bias_grad": (ctypes.c_int, [P, vp, ctypes.c_float, vp, vp]),
         "sa_validate_csr": (ctypes.c_int, [P, vp]),
         "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "sa_last_hip_error_string": (ctypes.c_char_p, []),
@@ -350,6 +351,15 @@ def sa_varlen_col_idx(B, total, cu_seqlens, window, row_ptr, col_idx, stream=Non
     cap = col_idx.numel() if _is_tensor(col_idx) else 0
     _raise(_lib.sa_varlen_col_idx(int(B), int(total), _ptr(cu_seqlens), int(window), _ptr(row_ptr),
                                   _ptr(col_idx), int(cap), _stream(stream)), "sa_varlen_col_idx")
+
+
+def sa_bias_grad(prob, dscores, factor, dbias, stream=None):
+    c = _c(prob)
+    f32 = _torch().float32
+    _check(dscores, "dscores", c.B * c.H * c.nnz, f32)
+    _check(dbias, "dbias", c.H * c.n * c.n, f32)
+    _raise(_lib.sa_bias_grad(_p(prob), _ptr(dscores), float(factor), _ptr(dbias), _stream(stream)),
+           "sa_bias_grad")
 
 
 def sa_validate_csr(prob, stream=None) -> int:

@@ -255,6 +255,18 @@ int sa_gather_entries_ordered(const sa_problem* p, const int32_t* order, const f
   return hip_status(sa::launch_gather_ordered(*p, order, src_a, dst_a, src_b, dst_b, stream));
 }
 
+int sa_bias_grad(const sa_problem* p, const float* dscores, float factor, float* dbias,
+                 hipStream_t stream) {
+  int st = check_problem(p, kOpSoftmax);
+  if (st != SA_OK) return st;
+  if (!std::isfinite(factor)) return SA_ERR_SHAPE;
+  if ((long long)p->H * p->n * (long long)p->n > (1ll << 40)) return SA_ERR_SHAPE;
+  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (!dscores || !dbias) return SA_ERR_NULL;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_bias_grad(*p, dscores, factor, dbias, stream));
+}
+
 int sa_sparse_softmax_backward(const sa_problem* p, const float* weights, const float* dweights,
                                float out_scale, float* dscores, hipStream_t stream) {
   int st = check_problem(p, kOpSoftmax);

@@ -288,6 +288,33 @@ __global__ __launch_bounds__(kThreads) void softmax_backward_kernel(const int* _
                               [](float x) { return wave_reduce<OpSum>(x); });
 }
 
+// dbias[h, i, col] = factor * sum over b of dscores[(b*H + h) * nnz + e] for each stored entry
+// e = (i, col): the bias is shared by the batches. One wave per (row, head), lanes over the
+// row's entries (coalesced reads of each batch's scores gradient), four batches in flight.
+__global__ __launch_bounds__(kThreads) void bias_grad_kernel(const int* __restrict__ row_ptr,
+                                                             const int* __restrict__ col_idx, int n,
+                                                             long long nnz, int B, int H,
+                                                             const float* __restrict__ ds, float factor,
+                                                             float* __restrict__ dbias) {
+  const long long unit = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (unit >= (long long)H * n) return;
+  const int row = (int)(unit / H), h = (int)(unit % H), lane = threadIdx.x % kWave;
+  long long a = row_ptr[row], b = row_ptr[row + 1];
+  a = a < 0 ? 0 : (a > nnz ? nnz : a);
+  b = b < a ? a : (b > nnz ? nnz : b);
+  float* out = dbias + ((size_t)h * n + row) * n;
+  for (long long e = a + lane; e < b; e += kWave) {
+    const int col = clampi(col_idx[e], 0, n - 1);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int bb = 0;
+    for (; bb + 4 <= B; bb += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += ds[(size_t)((bb + u) * H + h) * nnz + e];
+    for (; bb < B; ++bb) acc[0] += ds[(size_t)(bb * H + h) * nnz + e];
+    out[col] = factor * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int end_bit(long long n) {  // bits of the sort keys: 32 (low word) + enough for values < n
@@ -403,6 +430,16 @@ hipError_t launch_gather_ordered(const sa_problem& p, const int* order, const fl
   if (nblocks * groups > 0x7fffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_ordered_kernel, dim3((unsigned)(nblocks * groups)), dim3(kThreads), 0, s,
                      order, (long long)p.nnz, nblocks, BH, heads_per_wg, src_a, dst_a, src_b, dst_b);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_grad(const sa_problem& p, const float* ds, float factor, float* dbias,
+                            hipStream_t s) {
+  const long long units = (long long)p.H * p.n;
+  if (units == 0 || p.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(bias_grad_kernel, dim3((unsigned)((units + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(kThreads), 0, s, p.row_ptr, p.col_idx, p.n, (long long)p.nnz, p.B, p.H, ds,
+                     factor, dbias);
   return hipGetLastError();
 }
 

@@ -28,6 +28,8 @@ hipError_t launch_gather_order_build(const sa_problem& p, const int* perm, int* 
                                      size_t ws_bytes, hipStream_t s);
 hipError_t launch_gather_ordered(const sa_problem& p, const int* order, const float* src_a,
                                  float* dst_a, const float* src_b, float* dst_b, hipStream_t s);
+hipError_t launch_bias_grad(const sa_problem& p, const float* ds, float factor, float* dbias,
+                            hipStream_t s);
 hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const float* dw,
                                    float out_scale, float* ds, hipStream_t s);
 

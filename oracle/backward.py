@@ -19,8 +19,12 @@ these quantities. For head t and a stored entry e = (i, j):
   dK[j]   = scale * sum over stored (i, j) of dS[i, j] q[i]
 
 dS is also the gradient with respect to the additive bias and key mask at the stored
-entries (they enter S unscaled). Rows without a finite score have W = 0, so all their
-terms vanish.
+entries (they enter S unscaled); the bias is shared by the batches, so its gradient sums
+over them (the flash-attention PR's bias-gradient question):
+
+  dBias[h, i, j] = sum over b of dS[b*H + h, (i, j)]   at stored (i, j); 0 elsewhere.
+
+Rows without a finite score have W = 0, so all their terms vanish.
 
 Two evaluations, pinned against each other and against finite differences in
 ``tests/test_oracle_pins.py``:
@@ -65,9 +69,21 @@ def spmm_transposed(X, row_ptr, col_idx, y, n):
     return out
 
 
+def bias_grad(dS, row_ptr, col_idx, H, n):
+    """dBias[h, i, j] = sum over batches b of dS[b*H + h, e] for the stored entry e = (i, j)."""
+    dS = np.asarray(dS, dtype=np.float64)
+    BH = dS.shape[0]
+    out = np.zeros((H, n, n))
+    for i in range(n):
+        for e in range(int(row_ptr[i]), int(row_ptr[i + 1])):
+            for t in range(BH):
+                out[t % H, i, int(col_idx[e])] += dS[t, e]
+    return out
+
+
 def grads_csr(q, k, v, row_ptr, col_idx, scale, H, dO, bias=None, key_mask=None, km_heads=1):
     """The formulas of the module docstring on the CSR pattern. Returns a dict with the
-    forward's S, W, O and the gradients dW, dS, dQ, dK, dV (fp64)."""
+    forward's S, W, O and the gradients dW, dS, dQ, dK, dV and dBias (fp64)."""
     fwd = _csr.attention_csr(q, k, v, row_ptr, col_idx, scale, H, bias, key_mask, km_heads)
     n = q.shape[1]
     dO = np.asarray(dO, dtype=np.float64)
@@ -76,13 +92,14 @@ def grads_csr(q, k, v, row_ptr, col_idx, scale, H, dO, bias=None, key_mask=None,
     dQ = scale * _csr.spmm(dS, row_ptr, col_idx, k)
     dK = scale * spmm_transposed(dS, row_ptr, col_idx, q, n)
     dV = spmm_transposed(fwd["W"], row_ptr, col_idx, dO, n)
-    return dict(fwd, dW=dW, dS=dS, dQ=dQ, dK=dK, dV=dV)
+    dBias = bias_grad(dS, row_ptr, col_idx, H, n)
+    return dict(fwd, dW=dW, dS=dS, dQ=dQ, dK=dK, dV=dV, dBias=dBias)
 
 
 def grads_autograd(q, k, v, scale, H, pattern, dO, bias=None, key_mask=None, km_heads=1):
-    """Gradients of sum(O * dO) with respect to q, k, v by torch autograd (fp64, CPU) on
-    the dense definition: S = scale q k^T + bias + key mask, -inf outside the pattern, a
-    row softmax whose rows without a finite score are zero, O = W v."""
+    """Gradients of sum(O * dO) with respect to q, k, v (and the bias, when given) by torch
+    autograd (fp64, CPU) on the dense definition: S = scale q k^T + bias + key mask, -inf
+    outside the pattern, a row softmax whose rows without a finite score are zero, O = W v."""
     import torch
 
     BH, n, d = q.shape
@@ -91,8 +108,10 @@ def grads_autograd(q, k, v, scale, H, pattern, dO, bias=None, key_mask=None, km_
     P = torch.tensor(pattern_rows(pattern, 0, n, n))
     S = scale * Q @ K.transpose(1, 2)
     heads = np.arange(BH)
+    Bt = None
     if bias is not None:
-        S = S + t64(bias)[heads % H]
+        Bt = t64(bias).requires_grad_(True)
+        S = S + Bt[heads % H]
     if key_mask is not None:
         km = np.asarray(key_mask, dtype=np.float64)
         S = S + t64(km[heads // H, (heads % H) if km_heads > 1 else 0])[:, None, :]
@@ -105,4 +124,7 @@ def grads_autograd(q, k, v, scale, H, pattern, dO, bias=None, key_mask=None, km_
     W = torch.where(live, x / torch.where(live, l, torch.ones_like(l)), torch.zeros_like(x))
     O = W @ V
     (O * t64(dO)).sum().backward()
-    return {"dQ": Q.grad.numpy(), "dK": K.grad.numpy(), "dV": V.grad.numpy(), "O": O.detach().numpy()}
+    out = {"dQ": Q.grad.numpy(), "dK": K.grad.numpy(), "dV": V.grad.numpy(), "O": O.detach().numpy()}
+    if Bt is not None:
+        out["dBias"] = Bt.grad.numpy()
+    return out

@@ -191,6 +191,7 @@ def test_backward_calls_reject_bad_descriptors():
         ref = ctypes.byref(p) if p is not None else None
         assert f("sa_gather_entries")(ref, FAKE, FAKE, FAKE + 64, None) == st
         assert f("sa_sparse_softmax_backward")(ref, FAKE, FAKE, 1.0, FAKE, None) == st
+        assert f("sa_bias_grad")(ref, FAKE, 1.0, FAKE, None) == st
         assert f("sa_csr_transpose")(ref, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == st
         assert f("sa_gather_order_build")(ref, FAKE, FAKE, FAKE, 1 << 30, None) == st
         assert f("sa_gather_entries_ordered")(ref, FAKE, FAKE, FAKE + 64, None, None, None) == st
@@ -204,6 +205,8 @@ def test_backward_calls_check_buffers_and_arguments():
     assert f("sa_gather_entries")(p, FAKE, FAKE, FAKE, None) == sa.SA_ERR_SHAPE  # in place
     assert f("sa_sparse_softmax_backward")(p, FAKE, None, 1.0, FAKE, None) == sa.SA_ERR_NULL
     assert f("sa_sparse_softmax_backward")(p, FAKE, FAKE, float("inf"), FAKE, None) == sa.SA_ERR_SHAPE
+    assert f("sa_bias_grad")(p, None, 1.0, FAKE, None) == sa.SA_ERR_NULL
+    assert f("sa_bias_grad")(p, FAKE, float("nan"), FAKE, None) == sa.SA_ERR_SHAPE
     assert f("sa_csr_transpose")(p, None, FAKE, FAKE, FAKE, 1 << 30, None) == sa.SA_ERR_NULL
     assert f("sa_csr_transpose")(p, FAKE, FAKE, FAKE, None, 1 << 30, None) == sa.SA_ERR_NULL
     assert f("sa_csr_transpose")(p, FAKE, FAKE, FAKE, FAKE, 64, None) == sa.SA_ERR_WORKSPACE

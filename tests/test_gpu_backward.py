@@ -7,6 +7,8 @@ test_oracle_backward_pins.py) at the forward's tolerances; the transposed patter
 checked bit-exactly against a host sort. At the full Longformer-style size, where the
 oracle's row loops are too slow, identities of the exact gradients are checked instead.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -80,7 +82,16 @@ class Backward:
             sa.sa_gather_entries(dp.prob, self.perm[:p.nnz], W, Wt)
         sa.sa_spmm(self.prob_t, dSt, dp.q, dK)
         sa.sa_spmm(self.prob_t, Wt, dO, dV)
-        return dict(dW=dW, dS=dS, dQ=dQ, dK=dK, dV=dV)
+        got = dict(dW=dW, dS=dS, dQ=dQ, dK=dK, dV=dV)
+        if dp.bias is not None:  # dS above carries the scale; the bias enters S unscaled
+            got["dBias"] = torch.zeros(p.H, p.n, p.n, device=DEV)
+            sa.sa_bias_grad(dp.prob, dS, 1.0 / dp.scale, got["dBias"])
+        return got
+
+
+def _element_csr(p):
+    rp, ci = p.element_csr()
+    return dataclasses.replace(p, row_ptr=rp.astype(np.int32), col_idx=ci.astype(np.int32), block=1)
 
 
 def _forward_weights(dp):
@@ -99,6 +110,8 @@ CASES = {
     "random_bf16": lambda: gen.make("random_n8192", n=1000, H=2, kmin=1, kmax=300),
     "random_bias_keymask": lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
                                             bias=True, key_mask=True, pmax=40),
+    # the Evoformer-style dense pattern with pair bias and key padding, as element CSR
+    "evoformer_dense_bias": lambda: _element_csr(gen.make("evoformer_l384", B=3, H=2, n=96)),
 }
 
 
@@ -123,6 +136,8 @@ def test_backward_parity(name, plan):
     check(got["dS"].view(p.BH, p.nnz).cpu().numpy(), dp.scale * ref["dS"], p.dtype, "scale*dS")
     for g in ("dQ", "dK", "dV"):
         check(got[g].cpu().numpy(), ref[g], p.dtype, g)
+    if "dBias" in got:
+        check(got["dBias"].cpu().numpy(), ref["dBias"], p.dtype, "dBias")
 
 
 ORDER_CASES = dict(CASES, longformer_full=lambda: gen.make("longformer_n4096"))

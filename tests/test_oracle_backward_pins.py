@@ -79,6 +79,27 @@ def test_gradients_match_finite_differences(seed):
         np.testing.assert_allclose(a[name], ref, atol=1e-7, rtol=1e-6, err_msg=name)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bias_gradient_matches_finite_differences(seed):
+    """dBias sums dS over the batches (the bias is shared by them); checked entry by entry
+    against central differences of the forward, inside and outside the pattern."""
+    q, k, v, dO, rp, ci, b, km = _case(seed, B=2, n=5, d=3)
+    scale = 0.6
+    g = obw.grads_csr(q, k, v, rp, ci, scale, 2, dO, bias=b, key_mask=km)
+    a = obw.grads_autograd(q, k, v, scale, 2, ("csr", rp, ci), dO, bias=b, key_mask=km)
+    h = 1e-6
+    fd = np.zeros_like(b)
+    for idx in np.ndindex(*b.shape):
+        bp, bm = b.copy(), b.copy()
+        bp[idx] += h
+        bm[idx] -= h
+        fd[idx] = (_loss(q, k, v, dO, rp, ci, scale, 2, bp, km) -
+                   _loss(q, k, v, dO, rp, ci, scale, 2, bm, km)) / (2 * h)
+    np.testing.assert_allclose(g["dBias"], fd, atol=1e-7, rtol=1e-6)
+    np.testing.assert_allclose(a["dBias"], fd, atol=1e-7, rtol=1e-6)
+    assert np.any(fd != 0)
+
+
 def test_full_mask_equals_library_sdpa_gradients():
     rng = np.random.default_rng(7)
     BH, n, d = 3, 20, 8
@@ -97,7 +118,7 @@ def test_chain_rule_equals_autograd_on_a_larger_pattern():
     q, k, v, dO, rp, ci, b, km = _case(3, B=2, H=2, n=40, d=8, density=0.2)
     g = obw.grads_csr(q, k, v, rp, ci, 0.3, 2, dO, bias=b, key_mask=km)
     a = obw.grads_autograd(q, k, v, 0.3, 2, ("csr", rp, ci), dO, bias=b, key_mask=km)
-    for name in ("dQ", "dK", "dV"):
+    for name in ("dQ", "dK", "dV", "dBias"):
         np.testing.assert_allclose(g[name], a[name], atol=1e-12, rtol=1e-10, err_msg=name)
     np.testing.assert_allclose(g["O"], a["O"], atol=1e-12)
 
@@ -130,6 +151,13 @@ def _mut_no_row_term(W, dW, row_ptr):
     return np.asarray(W) * np.asarray(dW)
 
 
+_REAL_BIAS_GRAD = obw.bias_grad
+
+
+def _mut_bias_grad_first_batch_only(dS, row_ptr, col_idx, H, n):
+    return _REAL_BIAS_GRAD(np.asarray(dS)[:H], row_ptr, col_idx, H, n)
+
+
 def _mut_transpose_uses_column_as_row(X, row_ptr, col_idx, y, n):
     out = np.zeros((y.shape[0], n, y.shape[2]))
     for i in range(n):
@@ -148,6 +176,14 @@ def test_planted_mistakes_are_caught(target, mutation, monkeypatch):
     fd = _finite_difference(q, k, v, dO, rp, ci, 0.7, 2, b, km)
     g = obw.grads_csr(q, k, v, rp, ci, 0.7, 2, dO, bias=b, key_mask=km)
     assert any(not np.allclose(g[name], ref, atol=1e-6) for name, ref in zip(("dQ", "dK", "dV"), fd))
+
+
+def test_planted_bias_gradient_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(obw, "bias_grad", _mut_bias_grad_first_batch_only)
+    q, k, v, dO, rp, ci, b, km = _case(2, B=2, n=5, d=3)
+    g = obw.grads_csr(q, k, v, rp, ci, 0.6, 2, dO, bias=b, key_mask=km)
+    a = obw.grads_autograd(q, k, v, 0.6, 2, ("csr", rp, ci), dO, bias=b, key_mask=km)
+    assert not np.allclose(g["dBias"], a["dBias"], atol=1e-6)
 
 
 def test_planted_missing_scale_is_caught(monkeypatch):
