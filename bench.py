@@ -349,7 +349,8 @@ def _avg_us(torch, f, iters=10, warmup=2):
 def time_mask_construction(torch, sa, p):
     """Mask construction on the device: the workload's pattern given as shuffled COO pairs
     (COO -> CSR), a packed batch of 8 sequences of 4096 tokens in all (both varlen calls),
-    key masks from 32 key lengths of 384 keys, and the fused dense kernel on evoformer_l384
+    key masks from 32 key lengths of 384 keys, a top-256-per-row mask from a 4096 x 4096
+    score matrix, and the fused dense kernel on evoformer_l384
     with its key padding given as the mask vector, as per-batch key lengths, and absent."""
     import gen
     dev = "cuda:0"
@@ -374,6 +375,14 @@ def time_mask_construction(torch, sa, p):
     seqlen = torch.from_numpy(np.random.default_rng(7).integers(320, 385, 32).astype(np.int32)).to(dev)
     km = torch.empty(32, 384, device=dev)
     km_us = _avg_us(torch, lambda: sa.sa_key_mask_from_lengths(32, 384, seqlen, km))
+    # a mask generated at run time: the 256 largest of every row of a 4096 x 4096 score matrix
+    # (q.k of one head of the workload)
+    qh, kh = torch.from_numpy(p.q[0]).to(dev), torch.from_numpy(p.k[0]).to(dev)
+    Sk = (qh @ kh.T).contiguous()
+    trp = torch.empty(p.n + 1, dtype=torch.int32, device=dev)
+    tci = torch.empty(p.n * 256, dtype=torch.int32, device=dev)
+    topk_us = _avg_us(torch, lambda: sa.sa_topk_mask(p.n, 256, Sk, trp, tci))
+    del Sk, qh, kh
     evo = gen.make("evoformer_l384")
     with_mask = time_fused(torch, sa, evo)
     without = time_fused(torch, sa, dataclasses.replace(evo, key_mask=None))
@@ -384,6 +393,7 @@ def time_mask_construction(torch, sa, p):
             "varlen_8_sequences_4096_tokens": {"nnz": vnnz, "us": round(varlen_us, 2),
                                                "entries_per_s": vnnz / (varlen_us * 1e-6)},
             "key_mask_from_lengths_32x384": {"us": round(km_us, 2)},
+            "topk_mask_4096_k256": {"us": round(topk_us, 2), "scores_read_GB_s": round(p.n * p.n * 4 / (topk_us * 1e-6) / 1e9, 1)},
             "fused_evoformer_l384_key_padding": {"key_mask_vector_us": round(with_mask, 2),
                                                  "seqlen_k_us": round(with_lens, 2),
                                                  "no_padding_us": round(without, 2)}}

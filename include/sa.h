@@ -239,7 +239,13 @@ int sa_bias_grad(const sa_problem *p, const float *dscores, float factor, float 
  *   empty rows. The first call writes row_ptr int32 [total+1] (read row_ptr[total] for the
  *   entry count); the second writes col_idx (writing nothing at or past col_capacity). Used
  *   with B = 1 and n = total in sa_problem, q/k/v laid out [H, total, d]. SA_ERR_SHAPE if
- *   the pattern could exceed 2^31 - 1 entries (total * min(total, 2 window + 1)). */
+ *   the pattern could exceed 2^31 - 1 entries (total * min(total, 2 window + 1)).
+ * sa_topk_mask: a mask generated from scores at run time: every query keeps the k keys of
+ *   largest score, a constant number per query (the SPARSEK abstract's selection; the
+ *   scoring network is the caller's). scores fp32 [n, n] row-major; row_ptr int32 [n+1]
+ *   gets i * min(k, n) and col_idx int32 [n * min(k, n)] each row's chosen columns in
+ *   ascending order. Equal scores are taken lowest column first; NaN counts as -inf and -0
+ *   as +0. SA_ERR_SHAPE if n * min(k, n) >= 2^31. */
 size_t sa_mask_workspace_bytes(int32_t n, int64_t nnz);
 int sa_coo_to_csr(int32_t n, int64_t nnz, const int32_t *rows, const int32_t *cols,
                   int32_t *row_ptr, int32_t *col_idx, int32_t *counts, void *workspace,
@@ -252,6 +258,8 @@ int sa_varlen_row_ptr(int32_t B, int32_t total, const int32_t *cu_seqlens, int32
 int sa_varlen_col_idx(int32_t B, int32_t total, const int32_t *cu_seqlens, int32_t window,
                       const int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
                       hipStream_t stream);
+int sa_topk_mask(int32_t n, int32_t k, const float *scores, int32_t *row_ptr, int32_t *col_idx,
+                 hipStream_t stream);
 
 /* --- Validation and status ----------------------------------------------------------------
  * sa_validate_csr: checks the pattern on the device (monotone row_ptr starting at 0,

@@ -33,7 +33,8 @@ EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "s
            "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
            "sa_sparse_softmax_backward", "sa_bias_grad", "sa_mask_workspace_bytes", "sa_coo_to_csr",
-           "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_validate_csr",
+           "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_topk_mask",
+           "sa_validate_csr",
            "sa_status_string", "sa_last_hip_error_string")
 
 
@@ -80,6 +81,7 @@ def _load():
         "sa_key_mask_from_lengths": (ctypes.c_int, [i32, i32, vp, vp, vp]),
         "sa_varlen_row_ptr": (ctypes.c_int, [i32, i32, vp, i32, vp, vp, sz, vp]),
         "sa_varlen_col_idx": (ctypes.c_int, [i32, i32, vp, i32, vp, vp, i64, vp]),
+        "sa_topk_mask": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
         "sa_gather_entries_ordered": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
         "sa_bias_grad": (ctypes.c_int, [P, vp, ctypes.c_float, vp, vp]),
@@ -360,6 +362,17 @@ def sa_bias_grad(prob, dscores, factor, dbias, stream=None):
     _check(dbias, "dbias", c.H * c.n * c.n, f32)
     _raise(_lib.sa_bias_grad(_p(prob), _ptr(dscores), float(factor), _ptr(dbias), _stream(stream)),
            "sa_bias_grad")
+
+
+def sa_topk_mask(n, k, scores, row_ptr, col_idx, stream=None):
+    """Each row keeps the k columns of largest score (ascending in col_idx)."""
+    torch = _torch()
+    kk = max(0, min(int(k), int(n)))
+    _check(scores, "scores", n * n, torch.float32)
+    _check(row_ptr, "row_ptr", n + 1, torch.int32)
+    _check(col_idx, "col_idx", n * kk, torch.int32)
+    _raise(_lib.sa_topk_mask(int(n), int(k), _ptr(scores), _ptr(row_ptr), _ptr(col_idx),
+                             _stream(stream)), "sa_topk_mask")
 
 
 def sa_validate_csr(prob, stream=None) -> int:

@@ -339,6 +339,16 @@ int sa_varlen_col_idx(int32_t B, int32_t total, const int32_t* cu_seqlens, int32
                                               col_capacity, stream));
 }
 
+int sa_topk_mask(int32_t n, int32_t k, const float* scores, int32_t* row_ptr, int32_t* col_idx,
+                 hipStream_t stream) {
+  if (n < 0 || k < 0) return SA_ERR_SHAPE;
+  const int32_t kk = k < n ? k : n;
+  if ((long long)n * kk > INT32_MAX) return SA_ERR_SHAPE;
+  if (!row_ptr || (n > 0 && (!scores || (kk > 0 && !col_idx)))) return SA_ERR_NULL;
+  clear_stale_error();
+  return hip_status(sa::launch_topk_mask(n, kk, scores, row_ptr, col_idx, stream));
+}
+
 int sa_validate_csr(const sa_problem* p, hipStream_t stream) {
   const int st = check_problem(p, kOpValidate);
   if (st != SA_OK) return st;

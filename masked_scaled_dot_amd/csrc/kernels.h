@@ -43,6 +43,8 @@ hipError_t launch_varlen_row_ptr(int B, int total, const int* cu, int window, in
                                  void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_varlen_col_idx(int B, int total, const int* cu, int window, const int* row_ptr,
                                  int* col_idx, long long cap, hipStream_t s);
+hipError_t launch_topk_mask(int n, int k, const float* scores, int* row_ptr, int* col_idx,
+                            hipStream_t s);
 
 // CSR row plan and validation.
 size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);

@@ -11,7 +11,10 @@
 // per-key mask vector when the masked keys are a suffix; key_mask_from_lengths writes the
 // 0 / -inf vector that the kernels read. Packed variable-length batches (the cu_seqlens
 // prefix of sequence starts, same pull request) become one sequence of all tokens whose
-// pattern keeps every token inside its own sequence (optionally within a window).
+// pattern keeps every token inside its own sequence (optionally within a window). A mask can
+// also be generated from scores at run time: every query keeps the k keys of largest score, a
+// constant number of keys per query as in the SPARSEK abstract (the scoring itself is the
+// caller's; SpAtten's top-k engine ranks importance the same way).
 #include <hipcub/hipcub.hpp>
 
 #include "common.h"
@@ -141,6 +144,131 @@ __global__ __launch_bounds__(kThreads) void varlen_cols_kernel(const int* __rest
   }
 }
 
+// ---- top-k per row. Scores become order-preserving keys (NaN as -inf, -0 as +0); larger key
+// = larger score. One wave per row, with no workgroup barrier: the row's columns c = 64u +
+// lane are read once (kept in registers when the row has at most 64 * R of them, re-read from
+// the cache otherwise). The k-th largest key comes from a 4 x 8-bit radix select: per pass,
+// a histogram of the current digit in the wave's LDS counters, then a suffix sum over the 256
+// bins (four bins per lane, scanned across the wave) picks the digit that holds the wanted
+// rank. The chosen columns -- keys larger than it, and the first `need` keys equal to it --
+// are then written in column order, placed with ballots.
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;  // rows per workgroup
+constexpr int kTopkReg = 32;                       // keys per lane in registers (rows up to 2048)
+
+__device__ __forceinline__ unsigned order_key(float x) {
+  unsigned u = __float_as_uint(x);
+  if (x != x) u = 0xff800000u;  // NaN -> -inf
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ scores, int n,
+                                                                 int k, int* __restrict__ row_ptr,
+                                                                 int* __restrict__ col_idx) {
+  __shared__ unsigned hist_all[kTopkWaves][256];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int row = blockIdx.x * kTopkWaves + wave;
+  if (row >= n) return;
+  unsigned* hist = hist_all[wave];
+  const float* s = scores + (size_t)row * n;
+  if (row == 0 && lane == 0) row_ptr[0] = 0;
+  if (lane == 0) row_ptr[row + 1] = (row + 1) * k;
+  const int steps = (n + kWave - 1) / kWave;  // the lane's columns: lane + 64u, u < steps
+  unsigned keys[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+    // every load is issued (clamped into the row), then they are all waited for once
+#pragma unroll
+    for (int u = 0; u < R; ++u) keys[u] = __float_as_uint(s[min(lane + u * kWave, n - 1)]);
+#pragma unroll
+    for (int u = 0; u < R; ++u) keys[u] = lane + u * kWave < n ? order_key(__uint_as_float(keys[u])) : 0u;
+  }
+  // f(c, key) for the lane's columns c = lane + 64u in order of u (key 0 past the row); rows
+  // not held in registers are read in batches of 16 loads in flight
+  auto for_each_key = [&](auto f) {
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        if (u >= steps) break;
+        f(lane + u * kWave, keys[u]);
+      }
+    } else {
+      constexpr int kBatch = 16;
+      for (int u0 = 0; u0 < steps; u0 += kBatch) {
+        unsigned kb[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) kb[i] = __float_as_uint(s[min(lane + (u0 + i) * kWave, n - 1)]);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int c = lane + (u0 + i) * kWave;
+          if (u0 + i < steps) f(c, c < n ? order_key(__uint_as_float(kb[i])) : 0u);
+        }
+      }
+    }
+  };
+  // radix select of the k-th largest key: after pass p the top 8(p+1) bits are fixed
+  unsigned prefix = 0u, rem = (unsigned)k;  // rem: rank (1-based) among keys matching prefix
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const unsigned hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0u;
+    for_each_key([&](int c, unsigned key) {
+      if (c < n && (key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+    });
+    // lane l holds bins 255 - 4l .. 252 - 4l (largest first); inclusive scan over the lanes
+    unsigned h[4], tot = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = hist[255 - 4 * lane - i];
+      tot += h[i];
+    }
+    unsigned x = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const unsigned y = (unsigned)__shfl_up((int)x, off);
+      if (lane >= off) x += y;
+    }
+    // keys in larger bins than this lane's first: x - tot; walk the lane's four bins
+    unsigned acc = x - tot;
+    int found = -1;
+    unsigned found_excl = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (found < 0 && acc < rem && acc + h[i] >= rem) {
+        found = 255 - 4 * lane - i;
+        found_excl = acc;
+      }
+      acc += h[i];
+    }
+    const unsigned long long who = __builtin_amdgcn_ballot_w64(found >= 0);  // exactly one lane
+    const int src = (int)__builtin_ctzll(who | (1ull << 63));
+    const int bin = __builtin_amdgcn_readlane(found, src);
+    const unsigned excl = (unsigned)__builtin_amdgcn_readlane((int)found_excl, src);
+    prefix |= (unsigned)(bin < 0 ? 0 : bin) << shift;
+    rem -= excl;
+  }
+  const unsigned kth = prefix;  // the k-th largest key
+  const unsigned need = rem;    // how many keys equal to it are taken
+  int* out = col_idx + (size_t)row * k;
+  const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  unsigned run_gt = 0u, run_eq = 0u;  // larger / equal keys in the columns before this step's
+  for_each_key([&](int c, unsigned key) {
+    const bool gt = c < n && key > kth, eq = c < n && key == kth;
+    const unsigned long long bgt = __builtin_amdgcn_ballot_w64(gt), beq = __builtin_amdgcn_ballot_w64(eq);
+    const unsigned pre_gt = run_gt + (unsigned)__builtin_popcountll(bgt & below);
+    const unsigned pre_eq = run_eq + (unsigned)__builtin_popcountll(beq & below);
+    // taken before this column: every larger key, and the equal ones up to `need`
+    if (gt || (eq && pre_eq < need)) {
+      const unsigned pos = pre_gt + (pre_eq < need ? pre_eq : need);
+      if (pos < (unsigned)k) out[pos] = c;
+    }
+    run_gt += (unsigned)__builtin_popcountll(bgt);
+    run_eq += (unsigned)__builtin_popcountll(beq);
+  });
+}
+
 size_t sort_temp_bytes(long long nnz, int bits) {
   size_t temp = 0;
   if (hipcub::DeviceRadixSort::SortKeys(nullptr, temp, (const unsigned long long*)nullptr,
@@ -221,6 +349,23 @@ hipError_t launch_varlen_row_ptr(int B, int total, const int* cu, int window, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || total == 0) return e;
   return hipcub::DeviceScan::InclusiveSum(temp, temp_bytes, cnt, row_ptr + 1, total, s);
+}
+
+hipError_t launch_topk_mask(int n, int k, const float* scores, int* row_ptr, int* col_idx,
+                            hipStream_t s) {
+  if (n == 0) {
+    hipLaunchKernelGGL(varlen_counts_kernel, dim3(1), dim3(kThreads), 0, s, nullptr, 0, 0, -1,
+                       nullptr, row_ptr);  // row_ptr[0] = 0 only
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)((n + kTopkWaves - 1) / kTopkWaves);
+  if (n <= kWave * kTopkReg)
+    hipLaunchKernelGGL(topk_rows_kernel<kTopkReg>, dim3(grid), dim3(kTopkThreads), 0, s, scores, n, k,
+                       row_ptr, col_idx);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel<0>, dim3(grid), dim3(kTopkThreads), 0, s, scores, n, k,
+                       row_ptr, col_idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_varlen_col_idx(int B, int total, const int* cu, int window, const int* row_ptr,

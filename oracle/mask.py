@@ -14,7 +14,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   another with the prefix of their starts (cu_seqlens); attention stays inside each
   sequence, here optionally within a window |i - j| <= w.
 
-Each is written from its definition with Python sets and loops, for small inputs.
+* :func:`topk_rows` -- a mask generated from scores at run time: each query keeps the k
+  keys of largest score, a constant number per query (the SPARSEK abstract); equal scores
+  are taken lowest column first, NaN counts as -inf and -0 as +0.
+
+Each is written from its definition with Python sets, sorts and loops, for small inputs.
 """
 from __future__ import annotations
 
@@ -59,3 +63,16 @@ def varlen_csr(cu_seqlens, total, window=-1):
                     cols.append(j)
         row_ptr.append(len(cols))
     return np.array(row_ptr, np.int32), np.array(cols, np.int32)
+
+
+def topk_rows(scores, k):
+    """(row_ptr, col_idx) of the k largest scores of every row, columns ascending."""
+    S = np.asarray(scores, dtype=np.float32)
+    rows, n = S.shape
+    kk = max(0, min(int(k), n))
+    cols = []
+    for i in range(rows):
+        vals = [(-np.inf if np.isnan(x) else float(x) + 0.0, j) for j, x in enumerate(S[i])]
+        best = sorted(vals, key=lambda vj: (-vj[0], vj[1]))[:kk]   # larger first, then lower j
+        cols.extend(sorted(j for _, j in best))
+    return np.arange(rows + 1, dtype=np.int64).astype(np.int32) * kk, np.array(cols, np.int32)

@@ -248,3 +248,76 @@ def test_seqlen_k_dense_equals_key_mask_vector():
     got_O, got_lse = _with_lengths(DevProblem(p), lens, use_key_mask=False).fused()
     np.testing.assert_allclose(got_O, ref_O, atol=1e-6, rtol=0)
     np.testing.assert_allclose(got_lse, ref_lse, atol=1e-6, rtol=0)
+
+
+# ---- masks generated from scores: the k largest of every row
+
+def _topk(S, k):
+    n = S.shape[0]
+    kk = max(0, min(k, n))
+    Sd = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).to(DEV)
+    rp = torch.full((n + 1,), -7, dtype=torch.int32, device=DEV)
+    ci = torch.full((max(n * kk, 1),), -7, dtype=torch.int32, device=DEV)
+    sa.sa_topk_mask(n, k, Sd, rp, ci[:n * kk])
+    torch.cuda.synchronize()
+    return rp.cpu().numpy(), ci.cpu().numpy()[:n * kk]
+
+
+def _topk_case(name):
+    seeds = {"normal": 1, "ties": 2, "specials": 3, "k_past_n": 4, "k_zero": 5, "one_row": 6,
+             "ragged_n": 7}
+    rng = np.random.default_rng(seeds[name])
+    if name == "normal":
+        return rng.standard_normal((300, 300)).astype(np.float32), 17
+    if name == "ties":
+        return rng.integers(0, 6, (200, 200)).astype(np.float32), 50
+    if name == "specials":
+        S = rng.standard_normal((64, 64)).astype(np.float32)
+        pick = rng.random(S.shape)
+        S[pick < 0.1] = np.nan
+        S[(pick >= 0.1) & (pick < 0.2)] = -np.inf
+        S[(pick >= 0.2) & (pick < 0.25)] = np.inf
+        S[(pick >= 0.25) & (pick < 0.35)] = -0.0
+        S[(pick >= 0.35) & (pick < 0.45)] = 0.0
+        return S, 10
+    if name == "k_past_n":
+        return rng.standard_normal((33, 33)).astype(np.float32), 40
+    if name == "k_zero":
+        return rng.standard_normal((20, 20)).astype(np.float32), 0
+    if name == "one_row":
+        return np.array([[2.5]], np.float32), 1
+    if name == "ragged_n":
+        return rng.standard_normal((777, 777)).astype(np.float32), 100
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["normal", "ties", "specials", "k_past_n", "k_zero", "one_row", "ragged_n"])
+def test_topk_mask(name):
+    S, k = _topk_case(name)
+    say(f"topk {name}: n={S.shape[0]} k={k}")
+    rp, ci = _topk(S, k)
+    want_rp, want_ci = omask.topk_rows(S, k)
+    assert np.array_equal(rp, want_rp)
+    assert np.array_equal(ci, want_ci)
+
+
+def test_topk_mask_full_size_sampled_rows_and_attention():
+    """n = 4096, k = 256 from bf16-rounded q.k scores of one head: sampled rows bit-exact
+    against the oracle, every row sorted and of k distinct columns, and attention over the
+    generated mask (pipeline with a plan) against the oracle's on sampled rows."""
+    p = gen.make("longformer_n4096", H=1)
+    S = (p.q[0].astype(np.float64) @ p.k[0].astype(np.float64).T).astype(np.float32)
+    rp, ci = _topk(S, 256)
+    rows = np.random.default_rng(1).choice(p.n, 24, replace=False)
+    want_rp, want_ci = omask.topk_rows(S[rows], 256)
+    got = np.concatenate([ci[256 * r:256 * r + 256] for r in rows])
+    assert np.array_equal(got, want_ci)
+    C = ci.reshape(p.n, 256)
+    assert np.all(np.diff(C, axis=1) > 0) and C.min() >= 0 and C.max() < p.n
+    assert np.array_equal(rp, np.arange(p.n + 1) * 256)
+    pt = dataclasses.replace(p, row_ptr=rp.astype(np.int32), col_idx=ci.astype(np.int32))
+    dp = DevProblem(pt, plan=True)
+    _, W, O = dp.pipeline()
+    pairs = [(0, int(r)) for r in rows]
+    ref = odense.attention_rows(pt.q, pt.k, pt.v, pt.scale, pt.H, ("csr", pt.row_ptr, pt.col_idx), pairs)
+    check(np.stack([O[t, i] for t, i in pairs]), ref["O"], pt.dtype, "context (sampled rows)")

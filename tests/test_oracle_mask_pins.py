@@ -1,10 +1,12 @@
-"""Pins of oracle.mask (masks given as COO pairs, key lengths or packed sequences).
+"""Pins of oracle.mask (masks given as COO pairs, key lengths, packed sequences or generated
+as the top-k scores of every row).
 
 What fixes the expected values: small cases worked out by hand (written out below), a
 pattern drawn by the generators and scattered back as shuffled, repeated COO pairs, the
 dense boolean matrix of the pairs, and attention itself -- a key mask from lengths must
 give the attention over the first keys only, and a packed batch must give each sequence's
-own attention (torch's library SDPA on each sequence). Planted mistakes must fail a pin.
+own attention (torch's library SDPA on each sequence); top-k rows are checked against
+numpy's stable argsort and the threshold property. Planted mistakes must fail a pin.
 """
 import numpy as np
 import pytest
@@ -105,7 +107,48 @@ def pin_varlen_per_sequence_attention(f, seed=3):
     return bool(ok)
 
 
+def pin_topk_hand(f):
+    nan, inf = np.nan, np.inf
+    S = np.array([[1, 3, 3, 2],
+                  [-0.0, 0.0, nan, -inf],
+                  [5, -inf, nan, 5],
+                  [0, 0, 0, 0]], np.float32)
+    rp, ci = f(S, 2)
+    ok = list(rp) == [0, 2, 4, 6, 8] and list(ci) == [1, 2, 0, 1, 0, 3, 0, 1]
+    rp, ci = f(S, 3)
+    ok = ok and list(ci) == [1, 2, 3, 0, 1, 2, 0, 1, 3, 0, 1, 2]
+    rp, ci = f(S, 9)   # k past n keeps every column
+    return ok and list(rp) == [0, 4, 8, 12, 16] and list(ci) == [0, 1, 2, 3] * 4
+
+
+def pin_topk_stable_argsort(f, seed=4):
+    """Against numpy's stable argsort of the negated scores (ties: lower column first)."""
+    rng = np.random.default_rng(seed)
+    S = rng.integers(-3, 4, (40, 57)).astype(np.float32)   # many ties
+    S[rng.random(S.shape) < 0.05] = -np.inf
+    rp, ci = f(S, 11)
+    ok = list(rp) == list(range(0, 41 * 11, 11))
+    for i in range(40):
+        want = np.sort(np.argsort(-S[i], kind="stable")[:11])
+        ok = ok and np.array_equal(ci[11 * i:11 * i + 11], want)
+    return bool(ok)
+
+
+def pin_topk_threshold(f, seed=5):
+    """Every kept score is >= every dropped score of the row."""
+    rng = np.random.default_rng(seed)
+    S = rng.standard_normal((30, 100)).astype(np.float32)
+    rp, ci = f(S, 13)
+    ok = True
+    for i in range(30):
+        kept = np.zeros(100, bool)
+        kept[ci[13 * i:13 * i + 13]] = True
+        ok = ok and kept.sum() == 13 and S[i][kept].min() >= S[i][~kept].max()
+    return bool(ok)
+
+
 COO_PINS = [pin_coo_hand, pin_coo_round_trip, pin_coo_dense_matrix]
+TOPK_PINS = [pin_topk_hand, pin_topk_stable_argsort, pin_topk_threshold]
 KM_PINS = [pin_key_mask_hand, pin_key_mask_truncation]
 VARLEN_PINS = [pin_varlen_hand, pin_varlen_per_sequence_attention]
 
@@ -113,6 +156,11 @@ VARLEN_PINS = [pin_varlen_hand, pin_varlen_per_sequence_attention]
 @pytest.mark.parametrize("pin", COO_PINS)
 def test_coo_to_csr(pin):
     assert pin(omask.coo_to_csr)
+
+
+@pytest.mark.parametrize("pin", TOPK_PINS)
+def test_topk_rows(pin):
+    assert pin(omask.topk_rows)
 
 
 @pytest.mark.parametrize("pin", KM_PINS)
@@ -155,7 +203,27 @@ def _varlen_end_inclusive(cu, total, window=-1):
     return np.array(rp), np.array(cols)
 
 
+def _topk_ties_high_first(scores, k):
+    S = np.asarray(scores, np.float32)
+    rows, n = S.shape
+    kk = min(k, n)
+    cols = []
+    for i in range(rows):
+        v = np.where(np.isnan(S[i]), -np.inf, S[i])
+        order = sorted(range(n), key=lambda j: (-v[j], -j))[:kk]
+        cols.extend(sorted(order))
+    return np.arange(rows + 1) * kk, np.array(cols)
+
+
+def _topk_nan_as_largest(scores, k):
+    S = np.array(scores, np.float32)
+    S[np.isnan(S)] = np.inf
+    return omask.topk_rows(S, k)
+
+
 @pytest.mark.parametrize("mutant,pins", [
+    (_topk_ties_high_first, TOPK_PINS),
+    (_topk_nan_as_largest, TOPK_PINS),
     (_coo_keeps_repeats, COO_PINS),
     (_coo_clamps_instead_of_dropping, COO_PINS),
     (_key_mask_off_by_one, KM_PINS),
