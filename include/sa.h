@@ -196,11 +196,28 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  *   bias-gradient question): dbias[h, i, j] = factor * sum over b of dscores[(b*H + h)*nnz + e]
  *   for each stored entry e = (i, j); entries outside the pattern are not written (the caller
  *   zeroes dbias). With dscores from sa_sparse_softmax_backward at out_scale = scale, pass
- *   factor = 1 / scale (or out_scale = 1 and factor = 1). dbias fp32 [H, n, n].
+ *   factor = 1 / scale (or out_scale = 1 and factor = 1). dbias fp32 [H, n, n]. With
+ *   row_ptr = NULL (the dense pattern) dscores is [B*H, n, n], as sa_fused_backward writes
+ *   it, and every (i, j) is written.
  * sa_sparse_softmax_backward: dscores[t*nnz + e] = out_scale * W[e] * (dW[e] - D_row),
  *   D_row = sum over the row's entries of W * dW; weights, dweights and dscores are fp32
  *   [B*H, nnz] (dscores may alias dweights). out_scale = scale gives the operand of dQ
  *   and dK; out_scale = 1 gives the gradient of the scores. */
+/* --- Backward of the fused dense forward -------------------------------------------------
+ * sa_fused_backward: the gradients of the fused forward over the dense pattern (additive
+ *   bias, key mask and key lengths as in sa_fused_forward; the AlphaFold2 pull request's
+ *   training and bias-gradient questions), from its outputs: out fp32 [B*H, n, d] and lse
+ *   fp32 [B*H, n]. dout is the gradient of out, in the dtype of q/k/v (bf16 only). The
+ *   weights are recomputed from lse (P = exp(S - lse)), never stored: dQ = scale dS K,
+ *   dK = scale dS^T Q, dV = P^T dO with dS = P (dO V^T - rowsum(dO * O)). dq, dk, dv fp32
+ *   [B*H, n, d]. dscores (optional, fp32 [B*H, n, n]) receives dS, the gradient of the
+ *   scores and so of the bias and key mask at each pair (sa_bias_grad with row_ptr = NULL
+ *   sums it over the batches). workspace: fp32 [B*H*n], caller-owned scratch.
+ *   Pattern: dense only (row_ptr = NULL); dtype bf16 (else SA_ERR_UNSUPPORTED). */
+int sa_fused_backward(const sa_problem *p, const void *q, const void *k, const void *v,
+                      const float *out, const float *lse, const void *dout, float *dq, float *dk,
+                      float *dv, float *dscores, float *workspace, hipStream_t stream);
+
 size_t sa_transpose_workspace_bytes(const sa_problem *p);
 int sa_csr_transpose(const sa_problem *p, int32_t *row_ptr_t, int32_t *col_idx_t, int32_t *perm,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);

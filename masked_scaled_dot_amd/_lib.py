@@ -30,7 +30,7 @@ SA_BF16 = 1
 SA_FLAG_VALIDATE = 1
 
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
-           "sa_fused_forward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
+           "sa_fused_forward", "sa_fused_backward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
            "sa_sparse_softmax_backward", "sa_bias_grad", "sa_mask_workspace_bytes", "sa_coo_to_csr",
            "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_topk_mask",
@@ -72,6 +72,7 @@ def _load():
         "sa_sparse_softmax": (ctypes.c_int, [P, vp, vp, vp]),
         "sa_spmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_fused_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
+        "sa_fused_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "sa_transpose_workspace_bytes": (sz, [P]),
         "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
@@ -250,6 +251,23 @@ def sa_fused_forward(prob, q, k, v, out, lse=None, stream=None):
                                  _stream(stream)), "sa_fused_forward")
 
 
+def sa_fused_backward(prob, q, k, v, out, lse, dout, dq, dk, dv, workspace, dscores=None,
+                      stream=None):
+    c = _c(prob)
+    qkv, f32 = _dtype_of(c), _torch().float32
+    N = c.B * c.H * c.n * c.d
+    for x, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(x, name, N, qkv)
+    for x, name in ((out, "out"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(x, name, N, f32)
+    _check(lse, "lse", c.B * c.H * c.n, f32)
+    _check(workspace, "workspace", c.B * c.H * c.n, f32)
+    _check(dscores, "dscores", c.B * c.H * c.n * c.n, f32)
+    _raise(_lib.sa_fused_backward(_p(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dscores),
+                                  _ptr(workspace), _stream(stream)), "sa_fused_backward")
+
+
 def sa_transpose_workspace_bytes(prob) -> int:
     return int(_lib.sa_transpose_workspace_bytes(_p(prob)))
 
@@ -358,7 +376,8 @@ def sa_varlen_col_idx(B, total, cu_seqlens, window, row_ptr, col_idx, stream=Non
 def sa_bias_grad(prob, dscores, factor, dbias, stream=None):
     c = _c(prob)
     f32 = _torch().float32
-    _check(dscores, "dscores", c.B * c.H * c.nnz, f32)
+    per_head = c.nnz if c.row_ptr else c.n * c.n  # the dense pattern: [B*H, n, n]
+    _check(dscores, "dscores", c.B * c.H * per_head, f32)
     _check(dbias, "dbias", c.H * c.n * c.n, f32)
     _raise(_lib.sa_bias_grad(_p(prob), _ptr(dscores), float(factor), _ptr(dbias), _stream(stream)),
            "sa_bias_grad")

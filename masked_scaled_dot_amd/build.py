@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libsa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["api.cpp", "plan.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "fused_valu.hip",
-           "fused_tile.hip", "backward.hip", "mask.hip"]
+           "fused_tile.hip", "backward.hip", "mask.hip",
+           "fused_backward.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,

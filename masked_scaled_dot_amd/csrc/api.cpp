@@ -204,6 +204,24 @@ int sa_fused_forward(const sa_problem* p, const void* q, const void* k, const vo
   return hip_status(sa::launch_fused_valu(*p, q, k, v, out, lse, stream));
 }
 
+int sa_fused_backward(const sa_problem* p, const void* q, const void* k, const void* v,
+                      const float* out, const float* lse, const void* dout, float* dq, float* dk,
+                      float* dv, float* dscores, float* workspace, hipStream_t stream) {
+  int st = check_problem(p, kOpFused);
+  if (st != SA_OK) return st;
+  if (p->row_ptr) return SA_ERR_UNSUPPORTED;     // dense pattern only
+  if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (dscores && (long long)p->B * p->H * (long long)p->n * p->n > (1ll << 40)) return SA_ERR_SHAPE;
+  if (empty_problem(p)) return SA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(out))
+    return SA_ERR_ALIGN;
+  if ((long long)p->n * p->d * 2 > 0x7ffffff0ll) return SA_ERR_SHAPE;  // raw buffer range of a head
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_fused_backward(*p, q, k, v, out, lse, dout, dq, dk, dv, dscores,
+                                              workspace, stream));
+}
+
 size_t sa_transpose_workspace_bytes(const sa_problem* p) {
   if (check_problem(p, kOpSoftmax) != SA_OK) return 0;
   return sa::transpose_workspace_bytes(p->n, p->nnz);
@@ -257,11 +275,13 @@ int sa_gather_entries_ordered(const sa_problem* p, const int32_t* order, const f
 
 int sa_bias_grad(const sa_problem* p, const float* dscores, float factor, float* dbias,
                  hipStream_t stream) {
-  int st = check_problem(p, kOpSoftmax);
+  if (!p) return SA_ERR_NULL;
+  int st = check_problem(p, p->row_ptr ? kOpSoftmax : kOpFused);  // element CSR or dense
   if (st != SA_OK) return st;
+  if (!p->row_ptr && p->block != 1) return SA_ERR_UNSUPPORTED;
   if (!std::isfinite(factor)) return SA_ERR_SHAPE;
   if ((long long)p->H * p->n * (long long)p->n > (1ll << 40)) return SA_ERR_SHAPE;
-  if (empty_problem(p) || p->nnz == 0) return SA_OK;
+  if (empty_problem(p) || (p->row_ptr && p->nnz == 0)) return SA_OK;
   if (!dscores || !dbias) return SA_ERR_NULL;
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_bias_grad(*p, dscores, factor, dbias, stream));

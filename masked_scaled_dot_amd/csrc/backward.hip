@@ -315,6 +315,25 @@ __global__ __launch_bounds__(kThreads) void bias_grad_kernel(const int* __restri
   }
 }
 
+// Dense pattern: dbias[h, i, j] = factor * sum over b of dscores[b*H + h, i, j], one thread per
+// (h, i, j), consecutive threads on consecutive j.
+__global__ __launch_bounds__(kThreads) void bias_grad_dense_kernel(int n, int B, int H,
+                                                                   const float* __restrict__ ds,
+                                                                   float factor, float* __restrict__ dbias) {
+  const long long cell = (long long)blockIdx.x * kThreads + threadIdx.x;  // (h, i, j)
+  const long long nn = (long long)n * n;
+  if (cell >= (long long)H * nn) return;
+  const int h = (int)(cell / nn);
+  const long long ij = cell % nn;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int bb = 0;
+  for (; bb + 4 <= B; bb += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += ds[(size_t)((bb + u) * H + h) * nn + ij];
+  for (; bb < B; ++bb) acc[0] += ds[(size_t)(bb * H + h) * nn + ij];
+  dbias[cell] = factor * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int end_bit(long long n) {  // bits of the sort keys: 32 (low word) + enough for values < n
@@ -437,6 +456,12 @@ hipError_t launch_bias_grad(const sa_problem& p, const float* ds, float factor, 
                             hipStream_t s) {
   const long long units = (long long)p.H * p.n;
   if (units == 0 || p.B == 0) return hipSuccess;
+  if (!p.row_ptr) {  // dense: dscores [B*H, n, n]
+    const long long cells = units * p.n;
+    hipLaunchKernelGGL(bias_grad_dense_kernel, dim3((unsigned)((cells + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, p.n, p.B, p.H, ds, factor, dbias);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(bias_grad_kernel, dim3((unsigned)((units + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(kThreads), 0, s, p.row_ptr, p.col_idx, p.n, (long long)p.nnz, p.B, p.H, ds,
                      factor, dbias);

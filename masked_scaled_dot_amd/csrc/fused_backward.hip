@@ -1,0 +1,385 @@
+// Backward of the fused dense forward (the dense pattern with additive pair bias [H, n, n],
+// key mask [B, 1|H, n] and key lengths), from the forward's saved lse: the gradients of the
+// flash-attention pull request "support attentions in AlphaFold2" (its training question and
+// the bias gradient). The weights are recomputed, never stored: with s = scale q.k + bias +
+// mask (natural units) and P = exp(s - lse),
+//   D[q]  = dO[q] . O[q]                                   (delta_kernel)
+//   dP    = dO V^T,  dS = P (dP - D)                       (both kernels)
+//   dQ    = scale dS K                                     (dq_kernel, one 64-query tile)
+//   dK    = scale dS^T Q,  dV = P^T dO                     (dkdv_kernel, one 64-key tile)
+// and dS itself, if asked for, is the gradient of the scores (of the bias and key mask at
+// each pair). Splitting dQ from dK/dV recomputes P once more but needs no atomics, so the
+// results do not depend on timing.
+//
+// Layouts follow the forward tile (v_mfma_f32_16x16x32_bf16): the dQ tile forms S^T = K Q^T
+// and dP^T = V dO^T with K, V rows staged in LDS, so lane (g, c16) holds keys 16tt + 4g + i of
+// query c16, and dS^T packed to bf16 is the A operand of dQ += dS K with K read transposed
+// from LDS. The dK/dV tile swaps the roles: S = Q K^T and dP = dO V^T with the 64-query
+// block in LDS and the wave's 16 keys in registers, so lane (g, c16) holds queries
+// 16tt + 4g + i of key c16, and P, dS packed to bf16 are the A operands of dV += P^T dO and
+// dK += dS^T Q with dO, Q read transposed from LDS.
+#include "common.h"
+#include "kernels.h"
+#include "tile.h"
+
+namespace sa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(2))) float f32x2_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v2;
+typedef __attribute__((ext_vector_type(4))) short i16x4_v;
+typedef __attribute__((ext_vector_type(8))) short i16x8_v;
+typedef __attribute__((address_space(3))) i16x4_v lds_v4;
+
+constexpr int kThreads = 256;
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* out;
+  const float* lse;
+  const float* bias;      // [H, n, n] or null
+  const float* key_mask;  // [B, km_heads, n] or null
+  const int* seqlen_k;    // [B] or null
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dscores;  // [B*H, n, n] or null
+  float* delta;    // [B*H, n]
+  int B, H, n, km_heads;
+  float scale;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v2));
+}
+
+__device__ __forceinline__ int valid_keys(const BwdArgs& a, int b) {
+  return a.seqlen_k ? clampi(a.seqlen_k[b], 0, a.n) : a.n;
+}
+
+// lse in log2 units; a row without a finite score (lse = -inf) gets +inf so that its
+// recomputed weights exp2(s - lse2) are 0
+__device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// D[t, q] = dO[t, q, :] . O[t, q, :], one thread per row
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a, long long rows) {
+  const long long r = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= rows) return;
+  const uint16_t* dor = a.dout + r * D;
+  const float* orow = a.out + r * D;
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const u32x4_v d8 = *reinterpret_cast<const u32x4_v*>(dor + c);
+    const float4 o0 = *reinterpret_cast<const float4*>(orow + c);
+    const float4 o1 = *reinterpret_cast<const float4*>(orow + c + 4);
+    acc0 = fmaf(__uint_as_float(d8.x << 16), o0.x, acc0);
+    acc1 = fmaf(__uint_as_float(d8.x & 0xffff0000u), o0.y, acc1);
+    acc0 = fmaf(__uint_as_float(d8.y << 16), o0.z, acc0);
+    acc1 = fmaf(__uint_as_float(d8.y & 0xffff0000u), o0.w, acc1);
+    acc0 = fmaf(__uint_as_float(d8.z << 16), o1.x, acc0);
+    acc1 = fmaf(__uint_as_float(d8.z & 0xffff0000u), o1.y, acc1);
+    acc0 = fmaf(__uint_as_float(d8.w << 16), o1.z, acc0);
+    acc1 = fmaf(__uint_as_float(d8.w & 0xffff0000u), o1.w, acc1);
+  }
+  a.delta[r] = acc0 + acc1;
+}
+
+template <int D>
+struct BwdSmem {
+  static constexpr int kTStride = D + 16;  // bf16 per row: read transposed and as A operands
+  alignas(16) uint16_t x[kTileRows * kTStride];  // K (dQ tile) or Q (dK/dV tile)
+  alignas(16) uint16_t y[kTileRows * kTStride];  // V (dQ tile) or dO (dK/dV tile)
+  float lse2[kTileRows];                         // dK/dV tile: the query block's lse (log2)
+  float delta[kTileRows];                        // dK/dV tile: the query block's D
+};
+
+// 64 rows x D of a [n, D] bf16 matrix, rows from r0, staged row-major in LDS with stride ST;
+// rows past n read 0 (raw buffer bounds)
+template <int D, int ST>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const __amdgpu_buffer_rsrc_t& res, int r0) {
+  constexpr int CH = kTileRows * (D / 8) / kThreads;
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    const int r = i / (D / 8), part = i % (D / 8);
+    const u32x4_v x = __builtin_bit_cast(
+        u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(res, ((r0 + r) * D + part * 8) * 2, 0, 0));
+    *reinterpret_cast<u32x4_v*>(&dst[r * ST + part * 8]) = x;
+  }
+}
+
+// B operand of a transposed product (the transposing LDS read): lane j of each 16-lane group
+// gives the address of row k0 = base + j / 4 (and + 16), columns col = 16c + 4 (j % 4) ..
+// +3, and receives column 16c + j of rows base + {0..3} and base + 16 + {0..3}
+template <int ST>
+__device__ __forceinline__ bf16x8_v read_t(const uint16_t* src, int k0, int col) {
+  const i16x4_v x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&src[k0 * ST + col]));
+  const i16x4_v x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(&src[(k0 + 16) * ST + col]));
+  return __builtin_bit_cast(bf16x8_v, (i16x8_v){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
+}
+
+// ------------------------------------------------------------------------- dQ: 64 queries
+template <int D, bool kBias, bool kMask>
+__global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
+  constexpr int ST = BwdSmem<D>::kTStride;
+  constexpr int KC = D / 32, OC = D / 16;
+  __shared__ BwdSmem<D> sm;
+  const int n = a.n, ntiles = (n + kTileRows - 1) / kTileRows;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int tile = lb % ntiles, t = lb / ntiles;
+  const int b = t / a.H, h = t % a.H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, g = lane / 16, c16 = lane % 16;
+  const int row0 = tile * kTileRows;
+  const int my_q = min(row0 + wave * 16 + c16, n - 1);
+  const size_t head = (size_t)t * n * D;
+  const long long kv_bytes = (long long)n * D * 2;
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(a.k + head, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(a.v + head, kv_bytes);
+  bf16x8_v qb[KC], db[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(a.q + head + (size_t)my_q * D + 32 * kc + 8 * g));
+    db[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(a.dout + head + (size_t)my_q * D + 32 * kc + 8 * g));
+  }
+  const float lse2 = lse2_of(a.lse[(size_t)t * n + my_q]);
+  const float dlt = a.delta[(size_t)t * n + my_q];
+  const float scale2 = a.scale * kLog2e;
+  const float* brow = kBias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
+  const float* kmr = kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
+  const int nvalid = valid_keys(a, b);
+  const int nblk = (nvalid + kTileRows - 1) / kTileRows;
+
+  f32x4_v dq[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) dq[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nblk; ++j) {
+    const int k0 = j * kTileRows;
+    if (j > 0) __syncthreads();  // every wave is done with block j-1
+    stage_rows<D, ST>(sm.x, kres, k0);
+    stage_rows<D, ST>(sm.y, vres, k0);
+    __syncthreads();
+    // S^T = K Q^T and dP^T = V dO^T: lane holds keys 16tt + 4g + i of query c16
+    f32x4_v s[4], dp[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      dp[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v ka = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.x[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
+        const bf16x8_v va = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.y[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kc], s[tt], 0, 0, 0);
+        dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, db[kc], dp[tt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t pk[2][4];  // bf16 dS: [32-key chunk][dword]
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float ds[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 2 * c2 + hh, key = k0 + 16 * tt + 4 * g + i;
+          float x = s[tt][i] * scale2;
+          if constexpr (kBias) x = fmaf(brow[min(key, n - 1)], kLog2e, x);
+          if constexpr (kMask) x = fmaf(kmr[min(key, n - 1)], kLog2e, x);
+          const float p = key < nvalid ? __builtin_amdgcn_exp2f(x - lse2) : 0.f;
+          ds[4 * hh + i] = p * (dp[tt][i] - dlt);
+        }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pk[c2][w] = pack_bf16(ds[2 * w], ds[2 * w + 1]);
+    }
+    // dQ += dS K: A = dS (query c16; keys 32c2 + 4g + {0..3}, +16), B = K read transposed
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8_v pa = __builtin_bit_cast(bf16x8_v, (u32x4_v){pk[c2][0], pk[c2][1], pk[c2][2], pk[c2][3]});
+      const int kr = 32 * c2 + 4 * g + c16 / 4;
+#pragma unroll
+      for (int c = 0; c < OC; ++c)
+        dq[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, read_t<ST>(sm.x, kr, 16 * c + 4 * (c16 % 4)), dq[c], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mfma_drain();
+  // accumulator layout: lane holds column 16c + c16 of the wave's queries 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = row0 + wave * 16 + 4 * g + i;
+    if (q >= n) continue;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) a.dq[head + (size_t)q * D + 16 * c + c16] = dq[c][i] * a.scale;
+  }
+}
+
+// --------------------------------------------------------------------- dK, dV: 64 keys
+template <int D, bool kBias, bool kMask>
+__global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
+  constexpr int ST = BwdSmem<D>::kTStride;
+  constexpr int KC = D / 32, OC = D / 16;
+  __shared__ BwdSmem<D> sm;
+  const int n = a.n, ntiles = (n + kTileRows - 1) / kTileRows;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int tile = lb % ntiles, t = lb / ntiles;
+  const int b = t / a.H, h = t % a.H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, g = lane / 16, c16 = lane % 16;
+  const int key0 = tile * kTileRows;
+  const int my_key = key0 + wave * 16 + c16;  // the lane's key (B-operand column)
+  const int kc_key = min(my_key, n - 1);
+  const size_t head = (size_t)t * n * D;
+  const long long qd_bytes = (long long)n * D * 2;
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(a.q + head, qd_bytes);
+  const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dout + head, qd_bytes);
+  bf16x8_v kb[KC], vb[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    kb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(a.k + head + (size_t)kc_key * D + 32 * kc + 8 * g));
+    vb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(a.v + head + (size_t)kc_key * D + 32 * kc + 8 * g));
+  }
+  const float scale2 = a.scale * kLog2e;
+  const int nvalid = valid_keys(a, b);
+  const bool key_ok = my_key < nvalid;  // keys past the length (or n) get no weight
+  float kmask = 0.f;
+  if constexpr (kMask) kmask = a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n + kc_key] * kLog2e;
+  const float* bcol = kBias ? a.bias + (size_t)h * n * n + kc_key : nullptr;  // + q * n
+
+  f32x4_v dk[OC], dv[OC];
+#pragma unroll
+  for (int c = 0; c < OC; ++c) {
+    dk[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    dv[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int jq = 0; jq < ntiles; ++jq) {
+    const int q0 = jq * kTileRows;
+    if (jq > 0) __syncthreads();  // every wave is done with query block jq-1
+    stage_rows<D, ST>(sm.x, qres, q0);
+    stage_rows<D, ST>(sm.y, dres, q0);
+    if (threadIdx.x < kTileRows) {
+      const int q = q0 + threadIdx.x;
+      sm.lse2[threadIdx.x] = q < n ? lse2_of(a.lse[(size_t)t * n + q]) : INFINITY;
+      sm.delta[threadIdx.x] = q < n ? a.delta[(size_t)t * n + q] : 0.f;
+    }
+    __syncthreads();
+    // S = Q K^T and dP = dO V^T: lane holds queries 16tt + 4g + i of key c16
+    f32x4_v s[4], dp[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      dp[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const bf16x8_v qa = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.x[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
+        const bf16x8_v da = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.y[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb[kc], s[tt], 0, 0, 0);
+        dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vb[kc], dp[tt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t pp[2][4], pd[2][4];  // bf16 P and dS: [32-query chunk][dword]
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float p8[8], d8[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 2 * c2 + hh, ql = 16 * tt + 4 * g + i, q = q0 + ql;
+          float x = s[tt][i] * scale2 + kmask;
+          if constexpr (kBias) x = fmaf(bcol[(size_t)min(q, n - 1) * n], kLog2e, x);
+          const float p = key_ok ? __builtin_amdgcn_exp2f(x - sm.lse2[ql]) : 0.f;
+          const float ds = p * (dp[tt][i] - sm.delta[ql]);
+          p8[4 * hh + i] = p;
+          d8[4 * hh + i] = ds;
+          if (a.dscores && q < n && my_key < n) a.dscores[((size_t)t * n + q) * n + my_key] = ds;
+        }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pp[c2][w] = pack_bf16(p8[2 * w], p8[2 * w + 1]);
+        pd[c2][w] = pack_bf16(d8[2 * w], d8[2 * w + 1]);
+      }
+    }
+    // dV += P^T dO and dK += dS^T Q: A = P / dS (key c16; queries 32c2 + 4g + {0..3}, +16),
+    // B = dO / Q read transposed
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8_v pa = __builtin_bit_cast(bf16x8_v, (u32x4_v){pp[c2][0], pp[c2][1], pp[c2][2], pp[c2][3]});
+      const bf16x8_v da = __builtin_bit_cast(bf16x8_v, (u32x4_v){pd[c2][0], pd[c2][1], pd[c2][2], pd[c2][3]});
+      const int qr = 32 * c2 + 4 * g;
+#pragma unroll
+      for (int c = 0; c < OC; ++c) {
+        const int col = 16 * c + 4 * (c16 % 4);
+        dv[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, read_t<ST>(sm.y, qr + c16 / 4, col), dv[c], 0, 0, 0);
+        dk[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, read_t<ST>(sm.x, qr + c16 / 4, col), dk[c], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mfma_drain();
+  // accumulator layout: lane holds column 16c + c16 of the wave's keys 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = key0 + wave * 16 + 4 * g + i;
+    if (key >= n) continue;
+#pragma unroll
+    for (int c = 0; c < OC; ++c) {
+      a.dk[head + (size_t)key * D + 16 * c + c16] = dk[c][i] * a.scale;
+      a.dv[head + (size_t)key * D + 16 * c + c16] = dv[c][i];
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const sa_problem& p, const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)p.B * p.H * p.n;
+  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, s, a, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
+  const dim3 grid((unsigned)(ntiles * p.B * p.H)), block(kThreads);
+  if (p.bias && p.key_mask) {
+    hipLaunchKernelGGL((dq_kernel<D, true, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, true, true>), grid, block, 0, s, a);
+  } else if (p.bias) {
+    hipLaunchKernelGGL((dq_kernel<D, true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, true, false>), grid, block, 0, s, a);
+  } else if (p.key_mask) {
+    hipLaunchKernelGGL((dq_kernel<D, false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, false, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((dq_kernel<D, false, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused_backward(const sa_problem& p, const void* q, const void* k, const void* v,
+                                 const float* out, const float* lse, const void* dout, float* dq,
+                                 float* dk, float* dv, float* dscores, float* delta, hipStream_t s) {
+  if (p.B == 0 || p.H == 0 || p.n == 0) return hipSuccess;
+  const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                  static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), out, lse,
+                  p.bias, p.key_mask, p.seqlen_k, dq, dk, dv, dscores, delta,
+                  p.B, p.H, p.n, p.key_mask_heads, p.scale};
+  switch (p.d) {
+    case 32: return launch_d<32>(p, a, s);
+    case 64: return launch_d<64>(p, a, s);
+    case 128: return launch_d<128>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

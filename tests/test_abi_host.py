@@ -191,7 +191,8 @@ def test_backward_calls_reject_bad_descriptors():
         ref = ctypes.byref(p) if p is not None else None
         assert f("sa_gather_entries")(ref, FAKE, FAKE, FAKE + 64, None) == st
         assert f("sa_sparse_softmax_backward")(ref, FAKE, FAKE, 1.0, FAKE, None) == st
-        assert f("sa_bias_grad")(ref, FAKE, 1.0, FAKE, None) == st
+        if p is None or p.row_ptr:  # the dense pattern is valid for the bias gradient
+            assert f("sa_bias_grad")(ref, FAKE, 1.0, FAKE, None) == st
         assert f("sa_csr_transpose")(ref, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == st
         assert f("sa_gather_order_build")(ref, FAKE, FAKE, FAKE, 1 << 30, None) == st
         assert f("sa_gather_entries_ordered")(ref, FAKE, FAKE, FAKE + 64, None, None, None) == st
@@ -254,3 +255,20 @@ def test_mask_calls_check_sizes_and_buffers():
     assert ci(2, 10, FAKE, -1, FAKE, FAKE, -1, None) == sa.SA_ERR_SHAPE
     assert ci(2, 10, FAKE, -1, None, FAKE, 100, None) == sa.SA_ERR_NULL
     assert ci(2, 10, FAKE, -1, FAKE, FAKE, 0, None) == sa.SA_OK  # nothing to write
+
+
+def test_fused_backward_checks():
+    f = _lib.raw("sa_fused_backward")
+    args = [FAKE] * 10 + [FAKE, None]  # q k v out lse dout dq dk dv dscores workspace stream
+    dense = _prob(row_ptr=None, col_idx=None, nnz=0)
+    assert f(ctypes.byref(_prob()), *args) == sa.SA_ERR_UNSUPPORTED            # CSR pattern
+    assert f(ctypes.byref(_prob(row_ptr=None, col_idx=None, nnz=0, dtype=sa.SA_F32)), *args) \
+        == sa.SA_ERR_UNSUPPORTED                                             # fp32 inputs
+    bad = list(args)
+    bad[10] = None                                                           # no workspace
+    assert f(ctypes.byref(dense), *bad) == sa.SA_ERR_NULL
+    bad = list(args)
+    bad[9] = None                                                            # dscores is optional
+    bad[1] = FAKE + 4                                                        # misaligned k
+    assert f(ctypes.byref(dense), *bad) == sa.SA_ERR_ALIGN
+    assert f(None, *args) == sa.SA_ERR_NULL
