@@ -426,6 +426,27 @@ def time_fused(torch, sa, p, iters=20, warmup=3, element=False, seqlen_k=None):
     return us
 
 
+def time_fused_backward(torch, sa, p, iters=20, warmup=3, with_dscores=False):
+    """Average HIP-event time of sa_fused_backward (dense pattern) over `iters` back-to-back
+    calls, from one forward's O and lse and a N(0,1) bf16 upstream gradient."""
+    prob, t, _ = to_device(p, torch, sa)
+    dev = "cuda:0"
+    shape = (p.BH, p.n, p.d)
+    out = torch.empty(shape, device=dev)
+    lse = torch.empty(p.BH, p.n, device=dev)
+    sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+    g = torch.Generator(device="cpu").manual_seed(78)
+    dO = torch.randn(shape, generator=g).to(dev, torch.bfloat16)
+    dq, dk, dv = (torch.empty(shape, device=dev) for _ in range(3))
+    ws = torch.empty(p.BH * p.n, device=dev)
+    ds = torch.empty(p.BH, p.n, p.n, device=dev) if with_dscores else None
+    call = lambda: sa.sa_fused_backward(prob, t["q"], t["k"], t["v"], out, lse, dO, dq, dk, dv, ws,
+                                        dscores=ds)
+    us = _avg_us(torch, call, iters=iters, warmup=warmup)
+    del t, out, lse, dO, dq, dk, dv, ws, ds
+    return us
+
+
 def cpu_baseline(p, budget_s):
     """The fp64 dense oracle (definition with -inf outside the mask), timed on whole heads
     until the budget is used; returns attended pairs/s on the host cores."""
@@ -614,6 +635,16 @@ def main():
                 "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "warm": True}
             log(f"fused {name}: {us:.1f} us")
+            if q.row_ptr is None:  # the backward of the dense fused forward
+                bus = time_fused_backward(torch, sa, q)
+                bus_ds = time_fused_backward(torch, sa, q, with_dscores=True)
+                bflops = 10.0 * pr * q.d  # S again, dP, dV, dK, dQ: five products of 2 pairs d
+                extra["fused_backward_" + name] = {
+                    "us": round(bus, 2), "us_with_dscores": round(bus_ds, 2),
+                    "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
+                    "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "flops_model": "10 * attended pairs * d (five products of 2 * pairs * d)"}
+                log(f"fused backward {name}: {bus:.1f} us ({bus_ds:.1f} us writing dS)")
             del q
 
         mc = time_mask_construction(torch, sa, p)

@@ -101,21 +101,6 @@ struct BwdSmem {
   float delta[kTileRows];                        // dK/dV tile: the query block's D
 };
 
-// 64 rows x D of a [n, D] bf16 matrix, rows from r0, staged row-major in LDS with stride ST;
-// rows past n read 0 (raw buffer bounds)
-template <int D, int ST>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const __amdgpu_buffer_rsrc_t& res, int r0) {
-  constexpr int CH = kTileRows * (D / 8) / kThreads;
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    const int r = i / (D / 8), part = i % (D / 8);
-    const u32x4_v x = __builtin_bit_cast(
-        u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(res, ((r0 + r) * D + part * 8) * 2, 0, 0));
-    *reinterpret_cast<u32x4_v*>(&dst[r * ST + part * 8]) = x;
-  }
-}
-
 // B operand of a transposed product (the transposing LDS read): lane j of each 16-lane group
 // gives the address of row k0 = base + j / 4 (and + 16), columns col = 16c + 4 (j % 4) ..
 // +3, and receives column 16c + j of rows base + {0..3} and base + 16 + {0..3}
@@ -126,7 +111,34 @@ __device__ __forceinline__ bf16x8_v read_t(const uint16_t* src, int k0, int col)
   return __builtin_bit_cast(bf16x8_v, (i16x8_v){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]});
 }
 
+// 64 rows of a [n, D] bf16 matrix into registers (CH 16-byte chunks per thread; the block's
+// first row goes into the scalar offset); rows past n read 0 (raw buffer bounds)
+template <int D>
+struct RowChunks {
+  static constexpr int CH = kTileRows * (D / 8) / kThreads;
+  u32x4_v x[CH];
+  __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t& res, int r0) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      x[u] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(
+                                             res, ((i / (D / 8)) * D + (i % (D / 8)) * 8) * 2, r0 * D * 2, 0));
+    }
+  }
+  template <int ST>
+  __device__ __forceinline__ void store(uint16_t* dst) const {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      *reinterpret_cast<u32x4_v*>(&dst[(i / (D / 8)) * ST + (i % (D / 8)) * 8]) = x[u];
+    }
+  }
+};
+
 // ------------------------------------------------------------------------- dQ: 64 queries
+// Per key block: K and V (and the query's bias and key-mask values of the block's keys,
+// 16 consecutive bytes per lane) are loaded one block ahead into registers, staged in LDS
+// behind a barrier, and the next block's loads stay in flight while this one is computed.
 template <int D, bool kBias, bool kMask>
 __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
@@ -144,6 +156,11 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
   const long long kv_bytes = (long long)n * D * 2;
   const __amdgpu_buffer_rsrc_t kres = make_rsrc(a.k + head, kv_bytes);
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(a.v + head, kv_bytes);
+  const __amdgpu_buffer_rsrc_t bres =
+      make_rsrc(kBias ? a.bias + (size_t)h * n * n : a.dq, kBias ? (long long)n * n * 4 : 0);
+  const __amdgpu_buffer_rsrc_t mres = make_rsrc(
+      kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : a.dq, kMask ? (long long)n * 4 : 0);
+  const int brow_off = my_q * n * 4;
   bf16x8_v qb[KC], db[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -153,20 +170,40 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
   const float lse2 = lse2_of(a.lse[(size_t)t * n + my_q]);
   const float dlt = a.delta[(size_t)t * n + my_q];
   const float scale2 = a.scale * kLog2e;
-  const float* brow = kBias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
-  const float* kmr = kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
   const int nvalid = valid_keys(a, b);
   const int nblk = (nvalid + kTileRows - 1) / kTileRows;
+
+  RowChunks<D> kn, vn;
+  f32x4_v bn[kBias ? 4 : 1], mn[kMask ? 4 : 1];
+  auto prefetch = [&](int jj) {
+    const int k0 = jj * kTileRows;
+    kn.load(kres, k0);
+    vn.load(vres, k0);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {  // keys k0 + 16tt + 4g .. +3
+      if constexpr (kBias) bn[tt] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(bres, brow_off + (16 * tt + 4 * g) * 4, k0 * 4, 0));
+      if constexpr (kMask) mn[tt] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(mres, (16 * tt + 4 * g) * 4, k0 * 4, 0));
+    }
+  };
 
   f32x4_v dq[OC];
 #pragma unroll
   for (int c = 0; c < OC; ++c) dq[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  if (nblk > 0) prefetch(0);
   for (int j = 0; j < nblk; ++j) {
     const int k0 = j * kTileRows;
-    if (j > 0) __syncthreads();  // every wave is done with block j-1
-    stage_rows<D, ST>(sm.x, kres, k0);
-    stage_rows<D, ST>(sm.y, vres, k0);
-    __syncthreads();
+    if (j > 0) lds_barrier();  // every wave is done with block j-1
+    kn.template store<ST>(sm.x);
+    vn.template store<ST>(sm.y);
+    f32x4_v ad[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      ad[tt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBias) ad[tt] += bn[tt];
+      if constexpr (kMask) ad[tt] += mn[tt];
+    }
+    lds_barrier();                   // block j is staged for every wave
+    prefetch(min(j + 1, nblk - 1));  // in flight while block j is computed
     // S^T = K Q^T and dP^T = V dO^T: lane holds keys 16tt + 4g + i of query c16
     f32x4_v s[4], dp[4];
 #pragma unroll
@@ -192,8 +229,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int tt = 2 * c2 + hh, key = k0 + 16 * tt + 4 * g + i;
           float x = s[tt][i] * scale2;
-          if constexpr (kBias) x = fmaf(brow[min(key, n - 1)], kLog2e, x);
-          if constexpr (kMask) x = fmaf(kmr[min(key, n - 1)], kLog2e, x);
+          if constexpr (kBias || kMask) x = fmaf(ad[tt][i], kLog2e, x);
           const float p = key < nvalid ? __builtin_amdgcn_exp2f(x - lse2) : 0.f;
           ds[4 * hh + i] = p * (dp[tt][i] - dlt);
         }
@@ -223,6 +259,8 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------- dK, dV: 64 keys
+// Per query block: Q and dO rows, the block's lse and D, and the lane's bias column values
+// are loaded one block ahead into registers, then staged in LDS behind a barrier.
 template <int D, bool kBias, bool kMask>
 __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
@@ -241,6 +279,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   const long long qd_bytes = (long long)n * D * 2;
   const __amdgpu_buffer_rsrc_t qres = make_rsrc(a.q + head, qd_bytes);
   const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dout + head, qd_bytes);
+  const __amdgpu_buffer_rsrc_t bres =
+      make_rsrc(kBias ? a.bias + (size_t)h * n * n : a.dq, kBias ? (long long)n * n * 4 : 0);
   bf16x8_v kb[KC], vb[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -252,7 +292,28 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   const bool key_ok = my_key < nvalid;  // keys past the length (or n) get no weight
   float kmask = 0.f;
   if constexpr (kMask) kmask = a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n + kc_key] * kLog2e;
-  const float* bcol = kBias ? a.bias + (size_t)h * n * n + kc_key : nullptr;  // + q * n
+
+  RowChunks<D> qn, dn;
+  float ln = 0.f, dln = 0.f;   // thread r < 64: lse2 and D of query q0 + r
+  float bn[kBias ? 16 : 1];    // bias[q0 + 16tt + 4g + i][my key]
+  auto prefetch = [&](int jq) {
+    const int q0 = jq * kTileRows;
+    qn.load(qres, q0);
+    dn.load(dres, q0);
+    if (threadIdx.x < kTileRows) {
+      const int q = min(q0 + (int)threadIdx.x, n - 1);
+      ln = a.lse[(size_t)t * n + q];
+      dln = a.delta[(size_t)t * n + q];
+    }
+    if constexpr (kBias) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bn[4 * tt + i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              bres, ((16 * tt + 4 * g + i) * n + kc_key) * 4, q0 * n * 4, 0));
+    }
+  };
 
   f32x4_v dk[OC], dv[OC];
 #pragma unroll
@@ -260,17 +321,22 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
     dk[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     dv[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
+  prefetch(0);
   for (int jq = 0; jq < ntiles; ++jq) {
     const int q0 = jq * kTileRows;
-    if (jq > 0) __syncthreads();  // every wave is done with query block jq-1
-    stage_rows<D, ST>(sm.x, qres, q0);
-    stage_rows<D, ST>(sm.y, dres, q0);
+    if (jq > 0) lds_barrier();  // every wave is done with query block jq-1
+    qn.template store<ST>(sm.x);
+    dn.template store<ST>(sm.y);
     if (threadIdx.x < kTileRows) {
-      const int q = q0 + threadIdx.x;
-      sm.lse2[threadIdx.x] = q < n ? lse2_of(a.lse[(size_t)t * n + q]) : INFINITY;
-      sm.delta[threadIdx.x] = q < n ? a.delta[(size_t)t * n + q] : 0.f;
+      const bool in = q0 + (int)threadIdx.x < n;
+      sm.lse2[threadIdx.x] = in ? lse2_of(ln) : INFINITY;
+      sm.delta[threadIdx.x] = in ? dln : 0.f;
     }
-    __syncthreads();
+    float bc[kBias ? 16 : 1];
+#pragma unroll
+    for (int u = 0; u < (kBias ? 16 : 1); ++u) bc[u] = kBias ? bn[u] : 0.f;
+    lds_barrier();                        // query block jq is staged for every wave
+    prefetch(min(jq + 1, ntiles - 1));    // in flight while block jq is computed
     // S = Q K^T and dP = dO V^T: lane holds queries 16tt + 4g + i of key c16
     f32x4_v s[4], dp[4];
 #pragma unroll
@@ -296,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int tt = 2 * c2 + hh, ql = 16 * tt + 4 * g + i, q = q0 + ql;
           float x = s[tt][i] * scale2 + kmask;
-          if constexpr (kBias) x = fmaf(bcol[(size_t)min(q, n - 1) * n], kLog2e, x);
+          if constexpr (kBias) x = fmaf(bc[4 * tt + i], kLog2e, x);
           const float p = key_ok ? __builtin_amdgcn_exp2f(x - sm.lse2[ql]) : 0.f;
           const float ds = p * (dp[tt][i] - sm.delta[ql]);
           p8[4 * hh + i] = p;
