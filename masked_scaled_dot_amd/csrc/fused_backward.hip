@@ -140,7 +140,7 @@ struct RowChunks {
 // 16 consecutive bytes per lane) are loaded one block ahead into registers, staged in LDS
 // behind a barrier, and the next block's loads stay in flight while this one is computed.
 template <int D, bool kBias, bool kMask>
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : 1))) void dq_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
   __shared__ BwdSmem<D> sm;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
 // Per query block: Q and dO rows, the block's lse and D, and the lane's bias column values
 // are loaded one block ahead into registers, then staged in LDS behind a barrier.
 template <int D, bool kBias, bool kMask>
-__global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
   __shared__ BwdSmem<D> sm;
