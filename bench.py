@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
-    ap.add_argument("--profile", choices=["pipeline", "backward", "fused_csr", "fused_bsr", "fused_dense", "copy"],
+    ap.add_argument("--profile", choices=["pipeline", "backward", "fused_csr", "fused_bsr", "fused_dense",
+                                          "fused_backward", "copy"],
                     help="run only this kernel family (steps iterations after warmup) and exit; "
                          "for rocprofv3 runs")
     return ap.parse_args()
@@ -502,6 +503,10 @@ def profile_only(args, torch, sa, gen):
         p = gen.make(args.workload)
         prob, t, nnz = to_device(p, torch, sa)
         run_backward_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d, args.steps, args.warmup, None)
+    elif args.profile == "fused_backward":
+        q = gen.make("evoformer_l384")
+        us = time_fused_backward(torch, sa, q, iters=args.steps, warmup=args.warmup)
+        log(f"fused_backward evoformer_l384: {us:.1f} us")
     else:
         name = {"fused_csr": args.workload, "fused_bsr": "bsr_n16384",
                 "fused_dense": "evoformer_l384"}[args.profile]
