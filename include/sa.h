@@ -203,19 +203,25 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  *   D_row = sum over the row's entries of W * dW; weights, dweights and dscores are fp32
  *   [B*H, nnz] (dscores may alias dweights). out_scale = scale gives the operand of dQ
  *   and dK; out_scale = 1 gives the gradient of the scores. */
-/* --- Backward of the fused dense forward -------------------------------------------------
+/* --- Backward of the fused forward ---------------------------------------------------------
  * sa_fused_backward: the gradients of the fused forward over the dense pattern (additive
  *   bias, key mask and key lengths as in sa_fused_forward; the AlphaFold2 pull request's
- *   training and bias-gradient questions), from its outputs: out fp32 [B*H, n, d] and lse
+ *   training and bias-gradient questions) or over block CSR of 64x64 tiles, from its
+ *   outputs: out fp32 [B*H, n, d] and lse
  *   fp32 [B*H, n]. dout is the gradient of out, in the dtype of q/k/v (bf16 only). The
  *   weights are recomputed from lse (P = exp(S - lse)), never stored: dQ = scale dS K,
  *   dK = scale dS^T Q, dV = P^T dO with dS = P (dO V^T - rowsum(dO * O)). dq, dk, dv fp32
  *   [B*H, n, d]. dscores (optional, fp32 [B*H, n, n]) receives dS, the gradient of the
- *   scores and so of the bias and key mask at each pair (sa_bias_grad with row_ptr = NULL
- *   sums it over the batches). workspace: fp32 [B*H*n], caller-owned scratch.
- *   Pattern: dense only (row_ptr = NULL); dtype bf16 (else SA_ERR_UNSUPPORTED). */
+ *   scores and so of the bias and key mask at each pair of the pattern (pairs outside a
+ *   block pattern are not written; sa_bias_grad with row_ptr = NULL sums it over the
+ *   batches). workspace: fp32 [B*H*n], caller-owned scratch.
+ *   Block CSR also needs the transposed block pattern, t_row_ptr [ceil(n/64)+1] and
+ *   t_col_idx [nnz] (the block-rows holding each block-column, e.g. sa_csr_transpose of a
+ *   descriptor whose n is the number of block-rows); they are ignored for the dense pattern.
+ *   Pattern: dense or block CSR (element CSR: SA_ERR_UNSUPPORTED); dtype bf16 only. */
 int sa_fused_backward(const sa_problem *p, const void *q, const void *k, const void *v,
-                      const float *out, const float *lse, const void *dout, float *dq, float *dk,
+                      const float *out, const float *lse, const void *dout,
+                      const int32_t *t_row_ptr, const int32_t *t_col_idx, float *dq, float *dk,
                       float *dv, float *dscores, float *workspace, hipStream_t stream);
 
 size_t sa_transpose_workspace_bytes(const sa_problem *p);

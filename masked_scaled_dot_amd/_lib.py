@@ -72,7 +72,7 @@ def _load():
         "sa_sparse_softmax": (ctypes.c_int, [P, vp, vp, vp]),
         "sa_spmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_fused_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
-        "sa_fused_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "sa_fused_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "sa_transpose_workspace_bytes": (sz, [P]),
         "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
@@ -252,7 +252,7 @@ def sa_fused_forward(prob, q, k, v, out, lse=None, stream=None):
 
 
 def sa_fused_backward(prob, q, k, v, out, lse, dout, dq, dk, dv, workspace, dscores=None,
-                      stream=None):
+                      t_row_ptr=None, t_col_idx=None, stream=None):
     c = _c(prob)
     qkv, f32 = _dtype_of(c), _torch().float32
     N = c.B * c.H * c.n * c.d
@@ -263,9 +263,14 @@ def sa_fused_backward(prob, q, k, v, out, lse, dout, dq, dk, dv, workspace, dsco
     _check(lse, "lse", c.B * c.H * c.n, f32)
     _check(workspace, "workspace", c.B * c.H * c.n, f32)
     _check(dscores, "dscores", c.B * c.H * c.n * c.n, f32)
+    if c.row_ptr:
+        nb = (c.n + 63) // 64
+        _check(t_row_ptr, "t_row_ptr", nb + 1, _torch().int32)
+        _check(t_col_idx, "t_col_idx", c.nnz, _torch().int32)
     _raise(_lib.sa_fused_backward(_p(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dscores),
-                                  _ptr(workspace), _stream(stream)), "sa_fused_backward")
+                                  _ptr(dout), _ptr(t_row_ptr), _ptr(t_col_idx), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(dscores), _ptr(workspace), _stream(stream)),
+           "sa_fused_backward")
 
 
 def sa_transpose_workspace_bytes(prob) -> int:

@@ -205,11 +205,13 @@ int sa_fused_forward(const sa_problem* p, const void* q, const void* k, const vo
 }
 
 int sa_fused_backward(const sa_problem* p, const void* q, const void* k, const void* v,
-                      const float* out, const float* lse, const void* dout, float* dq, float* dk,
-                      float* dv, float* dscores, float* workspace, hipStream_t stream) {
+                      const float* out, const float* lse, const void* dout, const int32_t* t_row_ptr,
+                      const int32_t* t_col_idx, float* dq, float* dk, float* dv, float* dscores,
+                      float* workspace, hipStream_t stream) {
   int st = check_problem(p, kOpFused);
   if (st != SA_OK) return st;
-  if (p->row_ptr) return SA_ERR_UNSUPPORTED;     // dense pattern only
+  if (p->row_ptr && p->block != 64) return SA_ERR_UNSUPPORTED;  // dense or block CSR
+  if (p->row_ptr && p->nnz > 0 && (!t_row_ptr || !t_col_idx)) return SA_ERR_NULL;
   if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (dscores && (long long)p->B * p->H * (long long)p->n * p->n > (1ll << 40)) return SA_ERR_SHAPE;
   if (empty_problem(p)) return SA_OK;
@@ -219,7 +221,7 @@ int sa_fused_backward(const sa_problem* p, const void* q, const void* k, const v
   if ((long long)p->n * p->d * 2 > 0x7ffffff0ll) return SA_ERR_SHAPE;  // raw buffer range of a head
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_fused_backward(*p, q, k, v, out, lse, dout, dq, dk, dv, dscores,
-                                              workspace, stream));
+                                              workspace, t_row_ptr, t_col_idx, stream));
 }
 
 size_t sa_transpose_workspace_bytes(const sa_problem* p) {

@@ -1,5 +1,6 @@
-// Backward of the fused dense forward (the dense pattern with additive pair bias [H, n, n],
-// key mask [B, 1|H, n] and key lengths), from the forward's saved lse: the gradients of the
+// Backward of the fused forward over the dense pattern (with additive pair bias [H, n, n],
+// key mask [B, 1|H, n] and key lengths) and over block CSR of 64x64 tiles (the block-sparse
+// replies of the gluon-nlp issue), from the forward's saved lse: the gradients of the
 // flash-attention pull request "support attentions in AlphaFold2" (its training question and
 // the bias gradient). The weights are recomputed, never stored: with s = scale q.k + bias +
 // mask (natural units) and P = exp(s - lse),
@@ -8,7 +9,8 @@
 //   dQ    = scale dS K                                     (dq_kernel, one 64-query tile)
 //   dK    = scale dS^T Q,  dV = P^T dO                     (dkdv_kernel, one 64-key tile)
 // and dS itself, if asked for, is the gradient of the scores (of the bias and key mask at
-// each pair). Splitting dQ from dK/dV recomputes P once more but needs no atomics, so the
+// each pair). With block CSR the dQ tile walks its block-row's stored blocks and the dK/dV
+// tile the block-rows that hold its block-column (the transposed block pattern). Splitting dQ from dK/dV recomputes P once more but needs no atomics, so the
 // results do not depend on timing.
 //
 // Layouts follow the forward tile (v_mfma_f32_16x16x32_bf16): the dQ tile forms S^T = K Q^T
@@ -50,6 +52,11 @@ struct BwdArgs {
   float* dv;
   float* dscores;  // [B*H, n, n] or null
   float* delta;    // [B*H, n]
+  const int* row_ptr;    // block CSR: stored block-columns of each block-row (null: dense)
+  const int* col_idx;
+  const int* t_row_ptr;  // block CSR transposed: block-rows holding each block-column
+  const int* t_col_idx;
+  long long nnz;         // stored blocks
   int B, H, n, km_heads;
   float scale;
 };
@@ -171,12 +178,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   const float dlt = a.delta[(size_t)t * n + my_q];
   const float scale2 = a.scale * kLog2e;
   const int nvalid = valid_keys(a, b);
-  const int nblk = (nvalid + kTileRows - 1) / kTileRows;
+  const bool bsr = a.row_ptr != nullptr;
+  long long bs = 0, be = 0;
+  if (bsr) {
+    bs = a.row_ptr[tile];
+    be = a.row_ptr[tile + 1];
+    bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
+    be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
+  }
+  const int nblk = bsr ? (int)(be - bs) : (nvalid + kTileRows - 1) / kTileRows;
+  auto block_k0 = [&](int jj) -> int {
+    if (!bsr) return jj * kTileRows;
+    return __builtin_amdgcn_readfirstlane(clampi(a.col_idx[bs + jj], 0, ntiles - 1)) * kTileRows;
+  };
 
   RowChunks<D> kn, vn;
   f32x4_v bn[kBias ? 4 : 1], mn[kMask ? 4 : 1];
   auto prefetch = [&](int jj) {
-    const int k0 = jj * kTileRows;
+    const int k0 = block_k0(jj);
     kn.load(kres, k0);
     vn.load(vres, k0);
 #pragma unroll
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   for (int c = 0; c < OC; ++c) dq[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   if (nblk > 0) prefetch(0);
   for (int j = 0; j < nblk; ++j) {
-    const int k0 = j * kTileRows;
+    const int k0 = block_k0(j);
     if (j > 0) lds_barrier();  // every wave is done with block j-1
     kn.template store<ST>(sm.x);
     vn.template store<ST>(sm.y);
@@ -290,6 +309,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   const float scale2 = a.scale * kLog2e;
   const int nvalid = valid_keys(a, b);
   const bool key_ok = my_key < nvalid;  // keys past the length (or n) get no weight
+  const bool bsr = a.row_ptr != nullptr;
+  long long ts = 0, te = 0;
+  if (bsr) {
+    ts = a.t_row_ptr[tile];
+    te = a.t_row_ptr[tile + 1];
+    ts = ts < 0 ? 0 : (ts > a.nnz ? a.nnz : ts);
+    te = te < ts ? ts : (te > a.nnz ? a.nnz : te);
+  }
+  const int nqb = bsr ? (int)(te - ts) : ntiles;
+  auto block_q0 = [&](int jj) -> int {
+    if (!bsr) return jj * kTileRows;
+    return __builtin_amdgcn_readfirstlane(clampi(a.t_col_idx[ts + jj], 0, ntiles - 1)) * kTileRows;
+  };
   float kmask = 0.f;
   if constexpr (kMask) kmask = a.key_mask[((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n + kc_key] * kLog2e;
 
@@ -297,7 +329,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   float ln = 0.f, dln = 0.f;   // thread r < 64: lse2 and D of query q0 + r
   float bn[kBias ? 16 : 1];    // bias[q0 + 16tt + 4g + i][my key]
   auto prefetch = [&](int jq) {
-    const int q0 = jq * kTileRows;
+    const int q0 = block_q0(jq);
     qn.load(qres, q0);
     dn.load(dres, q0);
     if (threadIdx.x < kTileRows) {
@@ -321,9 +353,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
     dk[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     dv[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
-  prefetch(0);
-  for (int jq = 0; jq < ntiles; ++jq) {
-    const int q0 = jq * kTileRows;
+  if (nqb > 0) prefetch(0);
+  for (int jq = 0; jq < nqb; ++jq) {
+    const int q0 = block_q0(jq);
     if (jq > 0) lds_barrier();  // every wave is done with query block jq-1
     qn.template store<ST>(sm.x);
     dn.template store<ST>(sm.y);
@@ -336,7 +368,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 #pragma unroll
     for (int u = 0; u < (kBias ? 16 : 1); ++u) bc[u] = kBias ? bn[u] : 0.f;
     lds_barrier();                        // query block jq is staged for every wave
-    prefetch(min(jq + 1, ntiles - 1));    // in flight while block jq is computed
+    prefetch(min(jq + 1, nqb - 1));       // in flight while block jq is computed
     // S = Q K^T and dP = dO V^T: lane holds queries 16tt + 4g + i of key c16
     f32x4_v s[4], dp[4];
 #pragma unroll
@@ -434,11 +466,13 @@ hipError_t launch_d(const sa_problem& p, const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fused_backward(const sa_problem& p, const void* q, const void* k, const void* v,
                                  const float* out, const float* lse, const void* dout, float* dq,
-                                 float* dk, float* dv, float* dscores, float* delta, hipStream_t s) {
+                                 float* dk, float* dv, float* dscores, float* delta,
+                                 const int* t_row_ptr, const int* t_col_idx, hipStream_t s) {
   if (p.B == 0 || p.H == 0 || p.n == 0) return hipSuccess;
   const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                   static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), out, lse,
                   p.bias, p.key_mask, p.seqlen_k, dq, dk, dv, dscores, delta,
+                  p.row_ptr, p.col_idx, t_row_ptr, t_col_idx, (long long)p.nnz,
                   p.B, p.H, p.n, p.key_mask_heads, p.scale};
   switch (p.d) {
     case 32: return launch_d<32>(p, a, s);

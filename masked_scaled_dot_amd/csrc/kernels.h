@@ -33,10 +33,12 @@ hipError_t launch_bias_grad(const sa_problem& p, const float* ds, float factor, 
 hipError_t launch_softmax_backward(const sa_problem& p, const float* w, const float* dw,
                                    float out_scale, float* ds, hipStream_t s);
 
-// Backward of the fused dense forward from the saved lse (delta: [B*H*n] workspace).
+// Backward of the fused forward (dense, or block CSR with its transposed block pattern) from
+// the saved lse (delta: [B*H*n] workspace).
 hipError_t launch_fused_backward(const sa_problem& p, const void* q, const void* k, const void* v,
                                  const float* out, const float* lse, const void* dout, float* dq,
-                                 float* dk, float* dv, float* dscores, float* delta, hipStream_t s);
+                                 float* dk, float* dv, float* dscores, float* delta,
+                                 const int* t_row_ptr, const int* t_col_idx, hipStream_t s);
 
 // Mask construction: COO -> CSR, key mask from key lengths, packed variable-length batches.
 size_t mask_workspace_bytes(long long n, long long nnz);

@@ -259,16 +259,20 @@ def test_mask_calls_check_sizes_and_buffers():
 
 def test_fused_backward_checks():
     f = _lib.raw("sa_fused_backward")
-    args = [FAKE] * 10 + [FAKE, None]  # q k v out lse dout dq dk dv dscores workspace stream
+    # q k v out lse dout t_row_ptr t_col_idx dq dk dv dscores workspace stream
+    args = [FAKE] * 12 + [FAKE, None]
     dense = _prob(row_ptr=None, col_idx=None, nnz=0)
-    assert f(ctypes.byref(_prob()), *args) == sa.SA_ERR_UNSUPPORTED            # CSR pattern
+    assert f(ctypes.byref(_prob()), *args) == sa.SA_ERR_UNSUPPORTED            # element CSR
+    bsr = list(args)
+    bsr[6] = None                                                            # no transposed pattern
+    assert f(ctypes.byref(_prob(block=64, nnz=4)), *bsr) == sa.SA_ERR_NULL
     assert f(ctypes.byref(_prob(row_ptr=None, col_idx=None, nnz=0, dtype=sa.SA_F32)), *args) \
         == sa.SA_ERR_UNSUPPORTED                                             # fp32 inputs
     bad = list(args)
-    bad[10] = None                                                           # no workspace
+    bad[12] = None                                                           # no workspace
     assert f(ctypes.byref(dense), *bad) == sa.SA_ERR_NULL
     bad = list(args)
-    bad[9] = None                                                            # dscores is optional
+    bad[11] = None                                                           # dscores is optional
     bad[1] = FAKE + 4                                                        # misaligned k
     assert f(ctypes.byref(dense), *bad) == sa.SA_ERR_ALIGN
     assert f(None, *args) == sa.SA_ERR_NULL

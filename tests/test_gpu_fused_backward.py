@@ -5,7 +5,8 @@ weights from lse; dQ, dK, dV and dS (summed over the batches into the bias gradi
 sa_bias_grad) are compared with torch autograd in fp64 of the dense definition
 (oracle.backward.grads_autograd, pinned in test_oracle_backward_pins.py) on the same
 bf16-rounded inputs, at the bf16 tolerances. Cases cover d = 32, 64, 128, a ragged last tile,
-bias with and without a key mask, key lengths, and a batch whose keys are all masked.
+bias with and without a key mask, key lengths, a batch whose keys are all masked, and block
+CSR (with the transposed block pattern from sa_csr_transpose).
 """
 import dataclasses
 
@@ -46,6 +47,32 @@ CASES = {
 }
 
 
+def _block_transpose(p):
+    """The transposed block pattern (block-rows of each block-column) by sa_csr_transpose on
+    a descriptor over the block grid."""
+    nb = (p.n + 63) // 64
+    rp = torch.from_numpy(p.row_ptr).to(DEV)
+    ci = torch.from_numpy(p.col_idx).to(DEV)
+    prob = sa.Problem(1, 1, nb, 32, sa.SA_BF16, rp, ci, p.nnz)
+    rpt = torch.empty(nb + 1, dtype=torch.int32, device=DEV)
+    cit = torch.empty(max(p.nnz, 1), dtype=torch.int32, device=DEV)
+    perm = torch.empty_like(cit)
+    ws = torch.empty(max(sa.sa_transpose_workspace_bytes(prob), 1), dtype=torch.uint8, device=DEV)
+    sa.sa_csr_transpose(prob, rpt, cit[:p.nnz], perm[:p.nnz], ws)
+    return rpt, cit
+
+
+CASES.update({
+    "bsr_d128_ragged": (lambda: gen.make("bsr_n16384", n=64 * 6 + 21, H=2, extra=3), None),
+    "bsr_d64_bias_mask": (lambda: gen.make("bsr_n16384", n=64 * 5 + 7, H=2, d=64, extra=2,
+                                           bias=True, key_mask=True, pmax=40), None),
+})
+
+
+def _pattern(p):
+    return ("dense",) if p.row_ptr is None else ("bsr", p.row_ptr, p.col_idx, 64)
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_fused_backward_parity(name):
     make, lens = CASES[name]
@@ -64,20 +91,49 @@ def test_fused_backward_parity(name):
     sa.sa_fused_forward(dp.prob, dp.q, dp.k, dp.v, out, lse)
     dO, dO_host = _bf16(np.random.default_rng(21).standard_normal(N))
     dq, dk, dv = (torch.full(N, float("nan"), device=DEV) for _ in range(3))
-    ds = torch.full((p.BH, p.n, p.n), float("nan"), device=DEV)
+    ds = torch.full((p.BH, p.n, p.n), float("nan") if p.row_ptr is None else 0.0, device=DEV)
     ws = torch.empty(p.BH * p.n, device=DEV)
-    sa.sa_fused_backward(dp.prob, dp.q, dp.k, dp.v, out, lse, dO, dq, dk, dv, ws, dscores=ds)
+    rpt, cit = _block_transpose(p) if p.row_ptr is not None else (None, None)
+    sa.sa_fused_backward(dp.prob, dp.q, dp.k, dp.v, out, lse, dO, dq, dk, dv, ws, dscores=ds,
+                         t_row_ptr=rpt, t_col_idx=cit)
     torch.cuda.synchronize()
     km = p.key_mask
     if lens is not None:
         km = omask.key_mask_from_lengths(lens, p.n)[:, None, :] + (0 if km is None else km)
-    ref = obw.grads_autograd(p.q, p.k, p.v, p.scale, p.H, ("dense",), dO_host, bias=p.bias,
+    ref = obw.grads_autograd(p.q, p.k, p.v, p.scale, p.H, _pattern(p), dO_host, bias=p.bias,
                              key_mask=km)
     check(dq.cpu().numpy(), ref["dQ"], p.dtype, "dQ")
     check(dk.cpu().numpy(), ref["dK"], p.dtype, "dK")
     check(dv.cpu().numpy(), ref["dV"], p.dtype, "dV")
     if p.bias is not None:
         dbias = torch.full((p.H, p.n, p.n), float("nan"), device=DEV)
-        sa.sa_bias_grad(dp.prob, ds, 1.0, dbias)
+        dense = sa.Problem(p.B, p.H, p.n, p.d, sa.SA_BF16, None, None, 0, scale=p.scale)
+        sa.sa_bias_grad(dense, ds, 1.0, dbias)
         torch.cuda.synchronize()
         check(dbias.cpu().numpy(), ref["dBias"], p.dtype, "dBias")
+
+
+def test_fused_backward_full_size_sampled_heads():
+    """The Evoformer-style workload at full size (32 x 8 heads, n = 384, d = 32, bias and key
+    padding): dQ, dK and dV of sampled heads against autograd of those heads alone (a head's
+    gradients depend on its own q, k, v, dO, its bias head and its batch's key mask)."""
+    p = gen.make("evoformer_l384")
+    say(f"fused backward full size: BH={p.BH} n={p.n} d={p.d}")
+    dp = DevProblem(p)
+    N = (p.BH, p.n, p.d)
+    out = torch.empty(N, device=DEV)
+    lse = torch.empty(p.BH, p.n, device=DEV)
+    sa.sa_fused_forward(dp.prob, dp.q, dp.k, dp.v, out, lse)
+    dO, dO_host = _bf16(np.random.default_rng(22).standard_normal(N))
+    dq, dk, dv = (torch.full(N, float("nan"), device=DEV) for _ in range(3))
+    ws = torch.empty(p.BH * p.n, device=DEV)
+    sa.sa_fused_backward(dp.prob, dp.q, dp.k, dp.v, out, lse, dO, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    got = {"dQ": dq.cpu().numpy(), "dK": dk.cpu().numpy(), "dV": dv.cpu().numpy()}
+    assert all(np.isfinite(x).all() for x in got.values())
+    for t in (0, 77, p.BH - 1):
+        b, h = divmod(t, p.H)
+        ref = obw.grads_autograd(p.q[t:t + 1], p.k[t:t + 1], p.v[t:t + 1], p.scale, 1, ("dense",),
+                                 dO_host[t:t + 1], bias=p.bias[h:h + 1], key_mask=p.key_mask[b:b + 1])
+        for name in ("dQ", "dK", "dV"):
+            check(got[name][t:t + 1], ref[name], p.dtype, f"{name} head {t}")
