@@ -428,11 +428,21 @@ def time_fused(torch, sa, p, iters=20, warmup=3, element=False, seqlen_k=None):
 
 
 def time_fused_backward(torch, sa, p, iters=20, warmup=3, with_dscores=False):
-    """Average HIP-event time of sa_fused_backward (dense pattern) over `iters` back-to-back
-    calls, from one forward's O and lse and a N(0,1) bf16 upstream gradient."""
-    prob, t, _ = to_device(p, torch, sa)
+    """Average HIP-event time of sa_fused_backward (dense or block CSR) over `iters`
+    back-to-back calls, from one forward's O and lse and a N(0,1) bf16 upstream gradient."""
+    prob, t, _ = to_device(p, torch, sa, element=False)
     dev = "cuda:0"
     shape = (p.BH, p.n, p.d)
+    rpt = cit = None
+    if p.row_ptr is not None:  # block CSR: the transposed block pattern, built once per mask
+        nb = (p.n + 63) // 64
+        bprob = sa.Problem(1, 1, nb, 32, sa.SA_BF16, t["row_ptr"], t["col_idx"], p.nnz)
+        rpt = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+        cit = torch.empty(p.nnz, dtype=torch.int32, device=dev)
+        perm = torch.empty_like(cit)
+        ws0 = torch.empty(sa.sa_transpose_workspace_bytes(bprob), dtype=torch.uint8, device=dev)
+        sa.sa_csr_transpose(bprob, rpt, cit, perm, ws0)
+        del perm, ws0
     out = torch.empty(shape, device=dev)
     lse = torch.empty(p.BH, p.n, device=dev)
     sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
@@ -442,7 +452,7 @@ def time_fused_backward(torch, sa, p, iters=20, warmup=3, with_dscores=False):
     ws = torch.empty(p.BH * p.n, device=dev)
     ds = torch.empty(p.BH, p.n, p.n, device=dev) if with_dscores else None
     call = lambda: sa.sa_fused_backward(prob, t["q"], t["k"], t["v"], out, lse, dO, dq, dk, dv, ws,
-                                        dscores=ds)
+                                        dscores=ds, t_row_ptr=rpt, t_col_idx=cit)
     us = _avg_us(torch, call, iters=iters, warmup=warmup)
     del t, out, lse, dO, dq, dk, dv, ws, ds
     return us
@@ -640,16 +650,17 @@ def main():
                 "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "warm": True}
             log(f"fused {name}: {us:.1f} us")
-            if q.row_ptr is None:  # the backward of the dense fused forward
-                bus = time_fused_backward(torch, sa, q)
-                bus_ds = time_fused_backward(torch, sa, q, with_dscores=True)
-                bflops = 10.0 * pr * q.d  # S again, dP, dV, dK, dQ: five products of 2 pairs d
-                extra["fused_backward_" + name] = {
-                    "us": round(bus, 2), "us_with_dscores": round(bus_ds, 2),
-                    "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
-                    "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "flops_model": "10 * attended pairs * d (five products of 2 * pairs * d)"}
-                log(f"fused backward {name}: {bus:.1f} us ({bus_ds:.1f} us writing dS)")
+            # the backward of the fused forward (dS written out too for the dense pattern,
+            # where it is [B*H, n, n]: the bias gradient's input)
+            bus = time_fused_backward(torch, sa, q)
+            bflops = 10.0 * pr * q.d  # S again, dP, dV, dK, dQ: five products of 2 pairs d
+            row = {"us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
+                   "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "flops_model": "10 * attended pairs * d (five products of 2 * pairs * d)"}
+            if q.row_ptr is None:
+                row["us_with_dscores"] = round(time_fused_backward(torch, sa, q, with_dscores=True), 2)
+            extra["fused_backward_" + name] = row
+            log(f"fused backward {name}: {bus:.1f} us")
             del q
 
         mc = time_mask_construction(torch, sa, p)
