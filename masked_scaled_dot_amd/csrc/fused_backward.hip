@@ -20,6 +20,8 @@
 // block in LDS and the wave's 16 keys in registers, so lane (g, c16) holds queries
 // 16tt + 4g + i of key c16, and P, dS packed to bf16 are the A operands of dV += P^T dO and
 // dK += dS^T Q with dO, Q read transposed from LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tile.h"
@@ -280,8 +282,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 // --------------------------------------------------------------------- dK, dV: 64 keys
 // Per query block: Q and dO rows, the block's lse and D, and the lane's bias column values
 // are loaded one block ahead into registers, then staged in LDS behind a barrier.
-template <int D, bool kBias, bool kMask>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : 1))) void dkdv_kernel(BwdArgs a) {
+// kPart: 3 = dK and dV in one pass; 1 = dV only (no dP needed); 2 = dK only. d = 128 runs
+// the two halves as separate passes: each holds half the accumulators, which doubles the
+// waves per SIMD for about a quarter more products.
+template <int D, bool kBias, bool kMask, int kPart>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : (kPart == 3 ? 1 : 2)))) void dkdv_kernel(BwdArgs a) {
+  constexpr bool kDV = (kPart & 1) != 0, kDK = (kPart & 2) != 0;
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
   __shared__ BwdSmem<D> sm;
@@ -347,11 +353,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
     }
   };
 
-  f32x4_v dk[OC], dv[OC];
+  f32x4_v dk[kDK ? OC : 1], dv[kDV ? OC : 1];
 #pragma unroll
   for (int c = 0; c < OC; ++c) {
-    dk[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-    dv[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kDK) dk[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kDV) dv[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
   if (nqb > 0) prefetch(0);
   for (int jq = 0; jq < nqb; ++jq) {
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
         const bf16x8_v qa = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.x[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
         const bf16x8_v da = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(&sm.y[(16 * tt + c16) * ST + 32 * kc + 8 * g]));
         s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb[kc], s[tt], 0, 0, 0);
-        dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vb[kc], dp[tt], 0, 0, 0);
+        if constexpr (kDK) dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vb[kc], dp[tt], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
           const float ds = p * (dp[tt][i] - sm.delta[ql]);
           p8[4 * hh + i] = p;
           d8[4 * hh + i] = ds;
-          if (a.dscores && q < n && my_key < n) a.dscores[((size_t)t * n + q) * n + my_key] = ds;
+          if (kDK && a.dscores && q < n && my_key < n) a.dscores[((size_t)t * n + q) * n + my_key] = ds;
         }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -417,8 +423,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 #pragma unroll
       for (int c = 0; c < OC; ++c) {
         const int col = 16 * c + 4 * (c16 % 4);
-        dv[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, read_t<ST>(sm.y, qr + c16 / 4, col), dv[c], 0, 0, 0);
-        dk[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, read_t<ST>(sm.x, qr + c16 / 4, col), dk[c], 0, 0, 0);
+        if constexpr (kDV) dv[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, read_t<ST>(sm.y, qr + c16 / 4, col), dv[c], 0, 0, 0);
+        if constexpr (kDK) dk[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, read_t<ST>(sm.x, qr + c16 / 4, col), dk[c], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -431,8 +437,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
     if (key >= n) continue;
 #pragma unroll
     for (int c = 0; c < OC; ++c) {
-      a.dk[head + (size_t)key * D + 16 * c + c16] = dk[c][i] * a.scale;
-      a.dv[head + (size_t)key * D + 16 * c + c16] = dv[c][i];
+      if constexpr (kDK) a.dk[head + (size_t)key * D + 16 * c + c16] = dk[c][i] * a.scale;
+      if constexpr (kDV) a.dv[head + (size_t)key * D + 16 * c + c16] = dv[c][i];
     }
   }
 }
@@ -446,19 +452,22 @@ hipError_t launch_d(const sa_problem& p, const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
   const dim3 grid((unsigned)(ntiles * p.B * p.H)), block(kThreads);
-  if (p.bias && p.key_mask) {
-    hipLaunchKernelGGL((dq_kernel<D, true, true>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, true, true>), grid, block, 0, s, a);
-  } else if (p.bias) {
-    hipLaunchKernelGGL((dq_kernel<D, true, false>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, true, false>), grid, block, 0, s, a);
-  } else if (p.key_mask) {
-    hipLaunchKernelGGL((dq_kernel<D, false, true>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, false, true>), grid, block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((dq_kernel<D, false, false>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((dkdv_kernel<D, false, false>), grid, block, 0, s, a);
-  }
+  auto dkdv = [&](auto bias_c, auto mask_c) {
+    constexpr bool kB = decltype(bias_c)::value, kM = decltype(mask_c)::value;
+    hipLaunchKernelGGL((dq_kernel<D, kB, kM>), grid, block, 0, s, a);
+    if constexpr (D == 128) {
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 1>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 2>), grid, block, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 3>), grid, block, 0, s, a);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (p.bias && p.key_mask) dkdv(T_{}, T_{});
+  else if (p.bias) dkdv(T_{}, F_{});
+  else if (p.key_mask) dkdv(F_{}, T_{});
+  else dkdv(F_{}, F_{});
   return hipGetLastError();
 }
 
