@@ -218,7 +218,8 @@ int sa_fused_forward(const sa_problem *p, const void *q, const void *k, const vo
  *   Block CSR also needs the transposed block pattern, t_row_ptr [ceil(n/64)+1] and
  *   t_col_idx [nnz] (the block-rows holding each block-column, e.g. sa_csr_transpose of a
  *   descriptor whose n is the number of block-rows); they are ignored for the dense pattern.
- *   Pattern: dense or block CSR (element CSR: SA_ERR_UNSUPPORTED); dtype bf16 only. */
+ *   Pattern: dense or block CSR (element CSR: SA_ERR_UNSUPPORTED); dtype bf16 only; with a
+ *   bias, n <= 23170 (a bias head addressed with 32-bit offsets; else SA_ERR_UNSUPPORTED). */
 int sa_fused_backward(const sa_problem *p, const void *q, const void *k, const void *v,
                       const float *out, const float *lse, const void *dout,
                       const int32_t *t_row_ptr, const int32_t *t_col_idx, float *dq, float *dk,

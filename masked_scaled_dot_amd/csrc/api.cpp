@@ -219,6 +219,8 @@ int sa_fused_backward(const sa_problem* p, const void* q, const void* k, const v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(out))
     return SA_ERR_ALIGN;
   if ((long long)p->n * p->d * 2 > 0x7ffffff0ll) return SA_ERR_SHAPE;  // raw buffer range of a head
+  // the tiles address a bias head [n, n] through one raw buffer with 32-bit offsets
+  if (p->bias && (long long)p->n * p->n * 4 > 0x7ffffff0ll) return SA_ERR_UNSUPPORTED;
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_fused_backward(*p, q, k, v, out, lse, dout, dq, dk, dv, dscores,
                                               workspace, t_row_ptr, t_col_idx, stream));

@@ -276,3 +276,5 @@ def test_fused_backward_checks():
     bad[1] = FAKE + 4                                                        # misaligned k
     assert f(ctypes.byref(dense), *bad) == sa.SA_ERR_ALIGN
     assert f(None, *args) == sa.SA_ERR_NULL
+    big = _prob(row_ptr=None, col_idx=None, nnz=0, n=30000, bias=FAKE)  # bias head past 2 GB
+    assert f(ctypes.byref(big), *args) == sa.SA_ERR_UNSUPPORTED
