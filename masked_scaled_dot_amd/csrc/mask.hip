@@ -269,6 +269,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   });
 }
 
+__global__ void zero_first_kernel(int* __restrict__ p) { p[0] = 0; }
+
 size_t sort_temp_bytes(long long nnz, int bits) {
   size_t temp = 0;
   if (hipcub::DeviceRadixSort::SortKeys(nullptr, temp, (const unsigned long long*)nullptr,
@@ -353,9 +355,8 @@ hipError_t launch_varlen_row_ptr(int B, int total, const int* cu, int window, in
 
 hipError_t launch_topk_mask(int n, int k, const float* scores, int* row_ptr, int* col_idx,
                             hipStream_t s) {
-  if (n == 0) {
-    hipLaunchKernelGGL(varlen_counts_kernel, dim3(1), dim3(kThreads), 0, s, nullptr, 0, 0, -1,
-                       nullptr, row_ptr);  // row_ptr[0] = 0 only
+  if (n == 0) {  // an empty pattern: row_ptr = {0}
+    hipLaunchKernelGGL(zero_first_kernel, dim3(1), dim3(1), 0, s, row_ptr);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((n + kTopkWaves - 1) / kTopkWaves);

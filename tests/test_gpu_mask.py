@@ -265,7 +265,7 @@ def _topk(S, k):
 
 def _topk_case(name):
     seeds = {"normal": 1, "ties": 2, "specials": 3, "k_past_n": 4, "k_zero": 5, "one_row": 6,
-             "ragged_n": 7}
+             "ragged_n": 7, "empty": 8}
     rng = np.random.default_rng(seeds[name])
     if name == "normal":
         return rng.standard_normal((300, 300)).astype(np.float32), 17
@@ -286,12 +286,15 @@ def _topk_case(name):
         return rng.standard_normal((20, 20)).astype(np.float32), 0
     if name == "one_row":
         return np.array([[2.5]], np.float32), 1
+    if name == "empty":
+        return np.zeros((0, 0), np.float32), 4
     if name == "ragged_n":
         return rng.standard_normal((777, 777)).astype(np.float32), 100
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["normal", "ties", "specials", "k_past_n", "k_zero", "one_row", "ragged_n"])
+@pytest.mark.parametrize("name", ["normal", "ties", "specials", "k_past_n", "k_zero", "one_row", "ragged_n",
+                                  "empty"])
 def test_topk_mask(name):
     S, k = _topk_case(name)
     say(f"topk {name}: n={S.shape[0]} k={k}")
