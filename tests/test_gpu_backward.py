@@ -202,3 +202,30 @@ def test_backward_full_size_identities():
     lhs = (dp.q.double() * got["dQ"].double()).sum()
     rhs = (dp.k.double() * got["dK"].double()).sum()
     assert abs(float(lhs - rhs)) <= 1e-4 * max(1.0, abs(float(lhs)))
+
+
+def test_backward_graph_replay_matches_eager():
+    """The backward pass captured as one HIP graph (SDDMM, softmax gradient, SpMM, ordered
+    gather, transposed SpMMs with their long-row merge counters): every replay, with eager
+    work in between, reproduces the eager gradients bit for bit."""
+    p = CASES["longformer_long_rows"]()
+    say(f"backward graph replay: BH={p.BH} n={p.n} nnz={p.nnz}")
+    dp = DevProblem(p, plan=True)
+    bw = Backward(dp, plan=True)
+    dO, _ = _grad_out(p, 13)
+    W = _forward_weights(dp)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in bw.run(W, dO).items()}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = bw.run(W, dO)
+    for rep in range(3):
+        for x in got.values():
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x in got.items():
+            assert torch.equal(x, ref[name]), f"replay {rep}: {name} differs from the eager result"
+        bw.run(W, dO)  # eager work between replays
