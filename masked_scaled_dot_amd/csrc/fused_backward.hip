@@ -4,7 +4,7 @@
 // flash-attention pull request "support attentions in AlphaFold2" (its training question and
 // the bias gradient). The weights are recomputed, never stored: with s = scale q.k + bias +
 // mask (natural units) and P = exp(s - lse),
-//   D[q]  = dO[q] . O[q]                                   (delta_kernel)
+//   D[q]  = dO[q] . O[q]                                   (dq_kernel, kept for dkdv_kernel)
 //   dP    = dO V^T,  dS = P (dP - D)                       (both kernels)
 //   dQ    = scale dS K                                     (dq_kernel, one 64-query tile)
 //   dK    = scale dS^T Q,  dV = P^T dO                     (dkdv_kernel, one 64-key tile)
@@ -75,31 +75,6 @@ __device__ __forceinline__ int valid_keys(const BwdArgs& a, int b) {
 // lse in log2 units; a row without a finite score (lse = -inf) gets +inf so that its
 // recomputed weights exp2(s - lse2) are 0
 __device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
-
-// D[t, q] = dO[t, q, :] . O[t, q, :], one thread per row
-template <int D>
-__global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a, long long rows) {
-  const long long r = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= rows) return;
-  const uint16_t* dor = a.dout + r * D;
-  const float* orow = a.out + r * D;
-  float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const u32x4_v d8 = *reinterpret_cast<const u32x4_v*>(dor + c);
-    const float4 o0 = *reinterpret_cast<const float4*>(orow + c);
-    const float4 o1 = *reinterpret_cast<const float4*>(orow + c + 4);
-    acc0 = fmaf(__uint_as_float(d8.x << 16), o0.x, acc0);
-    acc1 = fmaf(__uint_as_float(d8.x & 0xffff0000u), o0.y, acc1);
-    acc0 = fmaf(__uint_as_float(d8.y << 16), o0.z, acc0);
-    acc1 = fmaf(__uint_as_float(d8.y & 0xffff0000u), o0.w, acc1);
-    acc0 = fmaf(__uint_as_float(d8.z << 16), o1.x, acc0);
-    acc1 = fmaf(__uint_as_float(d8.z & 0xffff0000u), o1.y, acc1);
-    acc0 = fmaf(__uint_as_float(d8.w << 16), o1.z, acc0);
-    acc1 = fmaf(__uint_as_float(d8.w & 0xffff0000u), o1.w, acc1);
-  }
-  a.delta[r] = acc0 + acc1;
-}
 
 template <int D>
 struct BwdSmem {
@@ -177,7 +152,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
     db[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(a.dout + head + (size_t)my_q * D + 32 * kc + 8 * g));
   }
   const float lse2 = lse2_of(a.lse[(size_t)t * n + my_q]);
-  const float dlt = a.delta[(size_t)t * n + my_q];
+  // D = dO . O of the lane's query: its four lanes (g) hold dims 32kc + 8g .. +7 of dO in
+  // registers; the tile writes D for the dK/dV tiles, which run after it
+  float dlt = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const u32x4_v d8 = __builtin_bit_cast(u32x4_v, db[kc]);
+    const float* orow = a.out + head + (size_t)my_q * D + 32 * kc + 8 * g;
+    const float4 o0 = *reinterpret_cast<const float4*>(orow);
+    const float4 o1 = *reinterpret_cast<const float4*>(orow + 4);
+    dlt = fmaf(__uint_as_float(d8.x << 16), o0.x, dlt);
+    dlt = fmaf(__uint_as_float(d8.x & 0xffff0000u), o0.y, dlt);
+    dlt = fmaf(__uint_as_float(d8.y << 16), o0.z, dlt);
+    dlt = fmaf(__uint_as_float(d8.y & 0xffff0000u), o0.w, dlt);
+    dlt = fmaf(__uint_as_float(d8.z << 16), o1.x, dlt);
+    dlt = fmaf(__uint_as_float(d8.z & 0xffff0000u), o1.y, dlt);
+    dlt = fmaf(__uint_as_float(d8.w << 16), o1.z, dlt);
+    dlt = fmaf(__uint_as_float(d8.w & 0xffff0000u), o1.w, dlt);
+  }
+  dlt += shfl_xor(dlt, 16);
+  dlt += shfl_xor(dlt, 32);
+  if (g == 0 && row0 + wave * 16 + c16 < n) a.delta[(size_t)t * n + my_q] = dlt;
   const float scale2 = a.scale * kLog2e;
   const int nvalid = valid_keys(a, b);
   const bool bsr = a.row_ptr != nullptr;
@@ -445,11 +440,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 
 template <int D>
 hipError_t launch_d(const sa_problem& p, const BwdArgs& a, hipStream_t s) {
-  const long long rows = (long long)p.B * p.H * p.n;
-  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, a, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
   const dim3 grid((unsigned)(ntiles * p.B * p.H)), block(kThreads);
   auto dkdv = [&](auto bias_c, auto mask_c) {
