@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--profile", choices=["pipeline", "backward", "fused_csr", "fused_bsr", "fused_dense",
-                                          "fused_backward", "copy"],
+                                          "fused_backward", "fused_backward_cover", "copy"],
                     help="run only this kernel family (steps iterations after warmup) and exit; "
                          "for rocprofv3 runs")
     return ap.parse_args()
@@ -458,6 +458,34 @@ def time_fused_backward(torch, sa, p, iters=20, warmup=3, with_dscores=False):
     return us
 
 
+def time_fused_backward_cover(torch, sa, p, iters=20, warmup=3):
+    """Element CSR: HIP-event time of building the block cover once (four calls, one
+    read-back) and the average of `iters` back-to-back sa_fused_backward_cover calls."""
+    prob, t, _ = to_device(p, torch, sa)
+    dev = "cuda:0"
+    shape = (p.BH, p.n, p.d)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    cover = sa.block_cover(prob, device=dev)
+    b.record()
+    torch.cuda.synchronize()
+    build_us = a.elapsed_time(b) * 1000
+    out = torch.empty(shape, device=dev)
+    lse = torch.empty(p.BH, p.n, device=dev)
+    sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+    g = torch.Generator(device="cpu").manual_seed(79)
+    dO = torch.randn(shape, generator=g).to(dev, torch.bfloat16)
+    dq, dk, dv = (torch.empty(shape, device=dev) for _ in range(3))
+    ws = torch.empty(p.BH * p.n, device=dev)
+    call = lambda: sa.sa_fused_backward_cover(prob, cover, t["q"], t["k"], t["v"], out, lse, dO, dq, dk,
+                                              dv, ws)
+    us = _avg_us(torch, call, iters=iters, warmup=warmup)
+    nblk = cover.nnz
+    del t, out, lse, dO, dq, dk, dv, ws, cover
+    return us, build_us, nblk
+
+
 def cpu_baseline(p, budget_s):
     """The fp64 dense oracle (definition with -inf outside the mask), timed on whole heads
     until the budget is used; returns attended pairs/s on the host cores."""
@@ -517,6 +545,10 @@ def profile_only(args, torch, sa, gen):
         q = gen.make("evoformer_l384")
         us = time_fused_backward(torch, sa, q, iters=args.steps, warmup=args.warmup)
         log(f"fused_backward evoformer_l384: {us:.1f} us")
+    elif args.profile == "fused_backward_cover":
+        q = gen.make(args.workload)
+        us, _, _ = time_fused_backward_cover(torch, sa, q, iters=args.steps, warmup=args.warmup)
+        log(f"fused_backward_cover {args.workload}: {us:.1f} us")
     else:
         name = {"fused_csr": args.workload, "fused_bsr": "bsr_n16384",
                 "fused_dense": "evoformer_l384"}[args.profile]
@@ -662,6 +694,18 @@ def main():
             extra["fused_backward_" + name] = row
             log(f"fused backward {name}: {bus:.1f} us")
             del q
+
+        # the backward of the fused element-CSR forward, on the pattern's 64x64 block cover
+        bus, build_us, nblk = time_fused_backward_cover(torch, sa, p)
+        pr = p.BH * p.nnz
+        bflops = 10.0 * pr * p.d
+        extra["fused_backward_cover_" + args.workload] = {
+            "us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
+            "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_model": "10 * attended pairs * d", "cover_blocks_per_head": nblk,
+            "computed_pairs_per_head": nblk * 64 * 64, "cover_build_us_once": round(build_us, 1)}
+        log(f"fused backward over the block cover {args.workload}: {bus:.1f} us "
+            f"({nblk} blocks per head; cover built once in {build_us:.0f} us)")
 
         mc = time_mask_construction(torch, sa, p)
         extra["mask_construction"] = mc

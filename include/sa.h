@@ -225,6 +225,48 @@ int sa_fused_backward(const sa_problem *p, const void *q, const void *k, const v
                       const int32_t *t_row_ptr, const int32_t *t_col_idx, float *dq, float *dk,
                       float *dv, float *dscores, float *workspace, hipStream_t stream);
 
+/* --- Block cover of an element pattern; fused backward over element CSR -----------------
+ * The block-sparse replies of the gluon-nlp issue compute whole 64x64 blocks on fast
+ * kernels; the cover carries an element CSR pattern onto them. It is the set of 64x64 blocks
+ * of the (n, n) grid holding at least one entry, as block CSR over nb = ceil(n/64)
+ * block-rows, with two arrays of 64-bit words: bits [nnz * 64], word r of cover block
+ * (R, C) having bit c set when (64R + r, 64C + c) is an entry; bits_t [nnz * 64], word c of
+ * the block at position j of the transposed cover (block-column C, block-row R) having bit
+ * r set for the same entries. Built once per mask, on the device, in this order:
+ *   sa_block_cover_row_ptr: cover row_ptr int32 [nb+1]; its last value is the cover's nnz
+ *     (read it back to size the arrays below).
+ *   sa_block_cover_col_idx: cover col_idx int32 [cover_nnz], each block-row's block-columns
+ *     ascending.
+ *   sa_csr_transpose of an element-CSR descriptor over the cover (n = nb, nnz = cover_nnz):
+ *     t_row_ptr [nb+1], t_col_idx [cover_nnz] (the block-rows holding each block-column).
+ *   sa_block_cover_bits: fills c->bits and c->bits_t from the pattern and the four arrays.
+ * p: the element CSR pattern (block 1, columns ascending and unique), n <= 2^22 (SA_ERR_SHAPE).
+ * Entries with a column outside [0, n) are skipped. The caller owns every array.
+ *
+ * sa_fused_backward_cover: the gradients of sa_fused_forward over an element CSR pattern
+ *   (same inputs and outputs as sa_fused_backward) computed on its block cover: each cover
+ *   block is computed whole and the words give pairs outside the pattern no weight. dscores
+ *   (optional, fp32 [B*H, n, n]) is written at every pair of the cover's blocks (0 outside
+ *   the pattern). bf16 only; bias, key_mask and seqlen_k as in sa_fused_backward. */
+typedef struct sa_block_cover {
+  const int32_t *row_ptr;    /* [nb+1]                                             */
+  const int32_t *col_idx;    /* [nnz] block-columns                                */
+  const int32_t *t_row_ptr;  /* [nb+1] transposed cover                            */
+  const int32_t *t_col_idx;  /* [nnz] block-rows                                   */
+  uint64_t *bits;            /* [nnz * 64] per block row                           */
+  uint64_t *bits_t;          /* [nnz * 64] per transposed block column             */
+  int64_t nnz;               /* stored blocks                                      */
+} sa_block_cover;
+
+int sa_block_cover_row_ptr(const sa_problem *p, int32_t *cover_row_ptr, hipStream_t stream);
+int sa_block_cover_col_idx(const sa_problem *p, const int32_t *cover_row_ptr, int64_t cover_nnz,
+                           int32_t *cover_col_idx, hipStream_t stream);
+int sa_block_cover_bits(const sa_problem *p, const sa_block_cover *c, hipStream_t stream);
+int sa_fused_backward_cover(const sa_problem *p, const sa_block_cover *c, const void *q,
+                            const void *k, const void *v, const float *out, const float *lse,
+                            const void *dout, float *dq, float *dk, float *dv, float *dscores,
+                            float *workspace, hipStream_t stream);
+
 size_t sa_transpose_workspace_bytes(const sa_problem *p);
 int sa_csr_transpose(const sa_problem *p, int32_t *row_ptr_t, int32_t *col_idx_t, int32_t *perm,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);

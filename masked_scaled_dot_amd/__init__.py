@@ -12,4 +12,6 @@ from ._lib import (  # noqa: F401
     sa_key_mask_from_lengths, sa_varlen_row_ptr, sa_varlen_col_idx, sa_topk_mask,
     sa_bias_grad, sa_problem, sa_sddmm, sa_sparse_softmax, sa_sparse_softmax_backward, sa_spmm,
     sa_status_string, sa_transpose_workspace_bytes, sa_validate_csr,
+    BlockCover, block_cover, sa_block_cover, sa_block_cover_row_ptr, sa_block_cover_col_idx,
+    sa_block_cover_bits, sa_fused_backward_cover,
 )

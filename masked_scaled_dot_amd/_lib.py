@@ -34,7 +34,8 @@ EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "s
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
            "sa_sparse_softmax_backward", "sa_bias_grad", "sa_mask_workspace_bytes", "sa_coo_to_csr",
            "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_topk_mask",
-           "sa_validate_csr",
+           "sa_block_cover_row_ptr", "sa_block_cover_col_idx", "sa_block_cover_bits",
+           "sa_fused_backward_cover", "sa_validate_csr",
            "sa_status_string", "sa_last_hip_error_string")
 
 
@@ -49,6 +50,15 @@ class sa_problem(ctypes.Structure):
         ("bias", ctypes.c_void_p), ("key_mask", ctypes.c_void_p), ("plan", ctypes.c_void_p),
         ("seqlen_k", ctypes.c_void_p),
         ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class sa_block_cover(ctypes.Structure):
+    """Mirror of ``struct sa_block_cover`` in include/sa.h."""
+    _fields_ = [
+        ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+        ("t_row_ptr", ctypes.c_void_p), ("t_col_idx", ctypes.c_void_p),
+        ("bits", ctypes.c_void_p), ("bits_t", ctypes.c_void_p), ("nnz", ctypes.c_int64),
     ]
 
 
@@ -87,6 +97,11 @@ def _load():
         "sa_sparse_softmax_backward": (ctypes.c_int, [P, vp, vp, ctypes.c_float, vp, vp]),
         "sa_bias_grad": (ctypes.c_int, [P, vp, ctypes.c_float, vp, vp]),
         "sa_validate_csr": (ctypes.c_int, [P, vp]),
+        "sa_block_cover_row_ptr": (ctypes.c_int, [P, vp, vp]),
+        "sa_block_cover_col_idx": (ctypes.c_int, [P, vp, i64, vp, vp]),
+        "sa_block_cover_bits": (ctypes.c_int, [P, ctypes.POINTER(sa_block_cover), vp]),
+        "sa_fused_backward_cover": (ctypes.c_int, [P, ctypes.POINTER(sa_block_cover), vp, vp, vp, vp, vp,
+                                                   vp, vp, vp, vp, vp, vp, vp]),
         "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "sa_last_hip_error_string": (ctypes.c_char_p, []),
     }
@@ -405,6 +420,80 @@ def sa_validate_csr(prob, stream=None) -> int:
     if st not in (SA_OK, SA_ERR_CSR):
         _raise(st, "sa_validate_csr")
     return st
+
+
+def sa_block_cover_row_ptr(prob, cover_row_ptr, stream=None):
+    c = _c(prob)
+    _check(cover_row_ptr, "cover_row_ptr", (c.n + 63) // 64 + 1, _torch().int32)
+    _raise(_lib.sa_block_cover_row_ptr(_p(prob), _ptr(cover_row_ptr), _stream(stream)),
+           "sa_block_cover_row_ptr")
+
+
+def sa_block_cover_col_idx(prob, cover_row_ptr, cover_nnz, cover_col_idx, stream=None):
+    c = _c(prob)
+    _check(cover_row_ptr, "cover_row_ptr", (c.n + 63) // 64 + 1, _torch().int32)
+    _check(cover_col_idx, "cover_col_idx", int(cover_nnz), _torch().int32)
+    _raise(_lib.sa_block_cover_col_idx(_p(prob), _ptr(cover_row_ptr), int(cover_nnz), _ptr(cover_col_idx),
+                                       _stream(stream)), "sa_block_cover_col_idx")
+
+
+class BlockCover:
+    """The arrays of a block cover (device tensors, owned here) and their C struct."""
+
+    def __init__(self, row_ptr, col_idx, t_row_ptr, t_col_idx, bits, bits_t, nnz):
+        self.row_ptr, self.col_idx, self.t_row_ptr, self.t_col_idx = row_ptr, col_idx, t_row_ptr, t_col_idx
+        self.bits, self.bits_t, self.nnz = bits, bits_t, int(nnz)
+        self.c = sa_block_cover(_ptr(row_ptr), _ptr(col_idx), _ptr(t_row_ptr), _ptr(t_col_idx),
+                                _ptr(bits), _ptr(bits_t), self.nnz)
+
+
+def sa_block_cover_bits(prob, cover, stream=None):
+    n = cover.nnz * 64
+    _check(cover.bits, "bits", n, _torch().int64)
+    _check(cover.bits_t, "bits_t", n, _torch().int64)
+    _raise(_lib.sa_block_cover_bits(_p(prob), ctypes.byref(cover.c), _stream(stream)), "sa_block_cover_bits")
+
+
+def block_cover(prob, device="cuda", stream=None) -> BlockCover:
+    """Runs the four once-per-mask steps of the block cover in order (sa_block_cover_row_ptr,
+    sa_block_cover_col_idx, sa_csr_transpose over the cover, sa_block_cover_bits); reads the
+    cover's size back to the host in between (one synchronisation)."""
+    torch = _torch()
+    c = _c(prob)
+    nb = (c.n + 63) // 64
+    rp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
+    sa_block_cover_row_ptr(prob, rp, stream)
+    nnz = int(rp[nb].item()) if nb else 0
+    ci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    sa_block_cover_col_idx(prob, rp, nnz, ci, stream)
+    grid = Problem(1, 1, nb, 32, SA_F32, rp, ci[:nnz], nnz)
+    trp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
+    tci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    perm = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+    ws = torch.empty(max(sa_transpose_workspace_bytes(grid), 1), dtype=torch.uint8, device=device)
+    sa_csr_transpose(grid, trp, tci[:nnz], perm[:nnz], ws, stream=stream)
+    bits = torch.empty(max(nnz, 1) * 64, dtype=torch.int64, device=device)
+    bits_t = torch.empty_like(bits)
+    cover = BlockCover(rp, ci, trp, tci, bits, bits_t, nnz)
+    sa_block_cover_bits(prob, cover, stream)
+    return cover
+
+
+def sa_fused_backward_cover(prob, cover, q, k, v, out, lse, dout, dq, dk, dv, workspace, dscores=None,
+                            stream=None):
+    c = _c(prob)
+    qkv, f32 = _dtype_of(c), _torch().float32
+    N = c.B * c.H * c.n * c.d
+    for x, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(x, name, N, qkv)
+    for x, name in ((out, "out"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(x, name, N, f32)
+    _check(lse, "lse", c.B * c.H * c.n, f32)
+    _check(workspace, "workspace", c.B * c.H * c.n, f32)
+    _check(dscores, "dscores", c.B * c.H * c.n * c.n, f32)
+    _raise(_lib.sa_fused_backward_cover(_p(prob), ctypes.byref(cover.c), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dscores),
+                                        _ptr(workspace), _stream(stream)), "sa_fused_backward_cover")
 
 
 def _dtype_of(c: sa_problem):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["api.cpp", "plan.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "fused_valu.hip",
            "fused_tile.hip", "backward.hip", "mask.hip",
-           "fused_backward.hip"]
+           "fused_backward.hip", "cover.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,

@@ -373,6 +373,81 @@ int sa_topk_mask(int32_t n, int32_t k, const float* scores, int32_t* row_ptr, in
   return hip_status(sa::launch_topk_mask(n, kk, scores, row_ptr, col_idx, stream));
 }
 
+namespace {
+constexpr int32_t kCoverMaxN = 1 << 22;  // block-row bitmap of ceil(n/64) bits in LDS
+
+int check_cover_problem(const sa_problem* p) {
+  const int st = check_problem(p, kOpSoftmax);  // element CSR
+  if (st != SA_OK) return st;
+  if (p->n > kCoverMaxN) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+int check_cover(const sa_problem* p, const sa_block_cover* c) {
+  if (!c) return SA_ERR_NULL;
+  const long long nb = (p->n + 63) / 64;
+  if (c->nnz < 0 || c->nnz > nb * nb) return SA_ERR_SHAPE;
+  if (p->n > 0 && (!c->row_ptr || !c->t_row_ptr)) return SA_ERR_NULL;
+  if (c->nnz > 0 && (!c->col_idx || !c->t_col_idx || !c->bits || !c->bits_t)) return SA_ERR_NULL;
+  return SA_OK;
+}
+}  // namespace
+
+int sa_block_cover_row_ptr(const sa_problem* p, int32_t* cover_row_ptr, hipStream_t stream) {
+  int st = check_cover_problem(p);
+  if (st != SA_OK) return st;
+  if (!cover_row_ptr || (p->n > 0 && !p->row_ptr)) return SA_ERR_NULL;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_block_cover_rows(p->n, p->nnz, p->row_ptr, p->col_idx, cover_row_ptr, stream));
+}
+
+int sa_block_cover_col_idx(const sa_problem* p, const int32_t* cover_row_ptr, int64_t cover_nnz,
+                           int32_t* cover_col_idx, hipStream_t stream) {
+  int st = check_cover_problem(p);
+  if (st != SA_OK) return st;
+  const long long nb = (p->n + 63) / 64;
+  if (cover_nnz < 0 || cover_nnz > nb * nb) return SA_ERR_SHAPE;
+  if (!cover_row_ptr || (cover_nnz > 0 && !cover_col_idx)) return SA_ERR_NULL;
+  if (p->n == 0 || cover_nnz == 0) return SA_OK;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_block_cover_cols(p->n, p->nnz, p->row_ptr, p->col_idx, cover_row_ptr,
+                                                cover_nnz, cover_col_idx, stream));
+}
+
+int sa_block_cover_bits(const sa_problem* p, const sa_block_cover* c, hipStream_t stream) {
+  int st = check_cover_problem(p);
+  if (st != SA_OK) return st;
+  if ((st = check_cover(p, c)) != SA_OK) return st;
+  if (p->n == 0 || c->nnz == 0) return SA_OK;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_block_cover_bits(p->n, p->nnz, p->row_ptr, p->col_idx, c->row_ptr,
+                                                c->col_idx, c->t_row_ptr, c->t_col_idx, c->nnz,
+                                                c->bits, c->bits_t, stream));
+}
+
+int sa_fused_backward_cover(const sa_problem* p, const sa_block_cover* c, const void* q, const void* k,
+                            const void* v, const float* out, const float* lse, const void* dout,
+                            float* dq, float* dk, float* dv, float* dscores, float* workspace,
+                            hipStream_t stream) {
+  int st = check_problem(p, kOpFused);
+  if (st != SA_OK) return st;
+  if (!p->row_ptr || p->block != 1) return SA_ERR_UNSUPPORTED;  // element CSR
+  if ((st = check_cover(p, c)) != SA_OK) return st;
+  if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (dscores && (long long)p->B * p->H * (long long)p->n * p->n > (1ll << 40)) return SA_ERR_SHAPE;
+  if (empty_problem(p)) return SA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(out))
+    return SA_ERR_ALIGN;
+  if ((long long)p->n * p->d * 2 > 0x7ffffff0ll) return SA_ERR_SHAPE;
+  if (p->bias && (long long)p->n * p->n * 4 > 0x7ffffff0ll) return SA_ERR_UNSUPPORTED;
+  if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  return hip_status(sa::launch_fused_backward_cover(*p, c->row_ptr, c->col_idx, c->t_row_ptr,
+                                                    c->t_col_idx, c->nnz, c->bits, c->bits_t, q, k, v,
+                                                    out, lse, dout, dq, dk, dv, dscores, workspace,
+                                                    stream));
+}
+
 int sa_validate_csr(const sa_problem* p, hipStream_t stream) {
   const int st = check_problem(p, kOpValidate);
   if (st != SA_OK) return st;

@@ -10,7 +10,10 @@
 //   dK    = scale dS^T Q,  dV = P^T dO                     (dkdv_kernel, one 64-key tile)
 // and dS itself, if asked for, is the gradient of the scores (of the bias and key mask at
 // each pair). With block CSR the dQ tile walks its block-row's stored blocks and the dK/dV
-// tile the block-rows that hold its block-column (the transposed block pattern). Splitting dQ from dK/dV recomputes P once more but needs no atomics, so the
+// tile the block-rows that hold its block-column (the transposed block pattern). An element
+// CSR pattern runs as its block cover (the blocks holding at least one entry) with one
+// 64-bit word per query of each block and per key of each transposed block; a pair whose bit
+// is clear gets no weight (kBits). Splitting dQ from dK/dV recomputes P once more but needs no atomics, so the
 // results do not depend on timing.
 //
 // Layouts follow the forward tile (v_mfma_f32_16x16x32_bf16): the dQ tile forms S^T = K Q^T
@@ -59,6 +62,8 @@ struct BwdArgs {
   const int* t_row_ptr;  // block CSR transposed: block-rows holding each block-column
   const int* t_col_idx;
   long long nnz;         // stored blocks
+  const unsigned long long* bits;    // element pattern in a block cover: [nnz][64] words of
+  const unsigned long long* bits_t;  // each block's queries / each transposed block's keys
   int B, H, n, km_heads;
   float scale;
 };
@@ -123,7 +128,7 @@ struct RowChunks {
 // Per key block: K and V (and the query's bias and key-mask values of the block's keys,
 // 16 consecutive bytes per lane) are loaded one block ahead into registers, staged in LDS
 // behind a barrier, and the next block's loads stay in flight while this one is computed.
-template <int D, bool kBias, bool kMask>
+template <int D, bool kBias, bool kMask, bool kBits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : 1))) void dq_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
@@ -135,6 +140,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, g = lane / 16, c16 = lane % 16;
   const int row0 = tile * kTileRows;
+  const bool bsr = a.row_ptr != nullptr;
+  long long bs = 0, be = 0;
+  if (bsr) {
+    bs = a.row_ptr[tile];
+    be = a.row_ptr[tile + 1];
+    bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
+    be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
+  }
   const int my_q = min(row0 + wave * 16 + c16, n - 1);
   const size_t head = (size_t)t * n * D;
   const long long kv_bytes = (long long)n * D * 2;
@@ -175,14 +188,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   if (g == 0 && row0 + wave * 16 + c16 < n) a.delta[(size_t)t * n + my_q] = dlt;
   const float scale2 = a.scale * kLog2e;
   const int nvalid = valid_keys(a, b);
-  const bool bsr = a.row_ptr != nullptr;
-  long long bs = 0, be = 0;
-  if (bsr) {
-    bs = a.row_ptr[tile];
-    be = a.row_ptr[tile + 1];
-    bs = bs < 0 ? 0 : (bs > a.nnz ? a.nnz : bs);
-    be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
-  }
   const int nblk = bsr ? (int)(be - bs) : (nvalid + kTileRows - 1) / kTileRows;
   auto block_k0 = [&](int jj) -> int {
     if (!bsr) return jj * kTileRows;
@@ -191,10 +196,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 
   RowChunks<D> kn, vn;
   f32x4_v bn[kBias ? 4 : 1], mn[kMask ? 4 : 1];
+  unsigned long long wn = ~0ull;  // the query's word of the block (keys present)
   auto prefetch = [&](int jj) {
     const int k0 = block_k0(jj);
     kn.load(kres, k0);
     vn.load(vres, k0);
+    if constexpr (kBits) wn = a.bits[(size_t)(bs + jj) * kTileRows + wave * 16 + c16];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {  // keys k0 + 16tt + 4g .. +3
       if constexpr (kBias) bn[tt] = __builtin_bit_cast(f32x4_v, __builtin_amdgcn_raw_buffer_load_b128(bres, brow_off + (16 * tt + 4 * g) * 4, k0 * 4, 0));
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
       if constexpr (kBias) ad[tt] += bn[tt];
       if constexpr (kMask) ad[tt] += mn[tt];
     }
+    const unsigned long long wc = wn >> (4 * g);  // bit 16tt + i: key 16tt + 4g + i
     lds_barrier();                   // block j is staged for every wave
     prefetch(min(j + 1, nblk - 1));  // in flight while block j is computed
     // S^T = K Q^T and dP^T = V dO^T: lane holds keys 16tt + 4g + i of query c16
@@ -246,7 +254,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
           const int tt = 2 * c2 + hh, key = k0 + 16 * tt + 4 * g + i;
           float x = s[tt][i] * scale2;
           if constexpr (kBias || kMask) x = fmaf(ad[tt][i], kLog2e, x);
-          const float p = key < nvalid ? __builtin_amdgcn_exp2f(x - lse2) : 0.f;
+          const bool on = key < nvalid && (!kBits || ((wc >> (16 * tt + i)) & 1ull));
+          const float p = on ? __builtin_amdgcn_exp2f(x - lse2) : 0.f;
           ds[4 * hh + i] = p * (dp[tt][i] - dlt);
         }
 #pragma unroll
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 // kPart: 3 = dK and dV in one pass; 1 = dV only (no dP needed); 2 = dK only. d = 128 runs
 // the two halves as separate passes: each holds half the accumulators, which doubles the
 // waves per SIMD for about a quarter more products.
-template <int D, bool kBias, bool kMask, int kPart>
+template <int D, bool kBias, bool kMask, int kPart, bool kBits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : (kPart == 3 ? 1 : 2)))) void dkdv_kernel(BwdArgs a) {
   constexpr bool kDV = (kPart & 1) != 0, kDK = (kPart & 2) != 0;
   constexpr int ST = BwdSmem<D>::kTStride;
@@ -293,6 +302,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, g = lane / 16, c16 = lane % 16;
   const int key0 = tile * kTileRows;
+  const bool bsr = a.row_ptr != nullptr;
+  long long ts = 0, te = 0;
+  if (bsr) {
+    ts = a.t_row_ptr[tile];
+    te = a.t_row_ptr[tile + 1];
+    ts = ts < 0 ? 0 : (ts > a.nnz ? a.nnz : ts);
+    te = te < ts ? ts : (te > a.nnz ? a.nnz : te);
+  }
   const int my_key = key0 + wave * 16 + c16;  // the lane's key (B-operand column)
   const int kc_key = min(my_key, n - 1);
   const size_t head = (size_t)t * n * D;
@@ -310,14 +327,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   const float scale2 = a.scale * kLog2e;
   const int nvalid = valid_keys(a, b);
   const bool key_ok = my_key < nvalid;  // keys past the length (or n) get no weight
-  const bool bsr = a.row_ptr != nullptr;
-  long long ts = 0, te = 0;
-  if (bsr) {
-    ts = a.t_row_ptr[tile];
-    te = a.t_row_ptr[tile + 1];
-    ts = ts < 0 ? 0 : (ts > a.nnz ? a.nnz : ts);
-    te = te < ts ? ts : (te > a.nnz ? a.nnz : te);
-  }
   const int nqb = bsr ? (int)(te - ts) : ntiles;
   auto block_q0 = [&](int jj) -> int {
     if (!bsr) return jj * kTileRows;
@@ -329,10 +338,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
   RowChunks<D> qn, dn;
   float ln = 0.f, dln = 0.f;   // thread r < 64: lse2 and D of query q0 + r
   float bn[kBias ? 16 : 1];    // bias[q0 + 16tt + 4g + i][my key]
+  unsigned long long wn = ~0ull;  // the key's word of the transposed block (queries present)
   auto prefetch = [&](int jq) {
     const int q0 = block_q0(jq);
     qn.load(qres, q0);
     dn.load(dres, q0);
+    if constexpr (kBits) wn = a.bits_t[(size_t)(ts + jq) * kTileRows + wave * 16 + c16];
     if (threadIdx.x < kTileRows) {
       const int q = min(q0 + (int)threadIdx.x, n - 1);
       ln = a.lse[(size_t)t * n + q];
@@ -368,6 +379,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
     float bc[kBias ? 16 : 1];
 #pragma unroll
     for (int u = 0; u < (kBias ? 16 : 1); ++u) bc[u] = kBias ? bn[u] : 0.f;
+    const unsigned long long wc = wn >> (4 * g);  // bit 16tt + i: query 16tt + 4g + i
     lds_barrier();                        // query block jq is staged for every wave
     prefetch(min(jq + 1, nqb - 1));       // in flight while block jq is computed
     // S = Q K^T and dP = dO V^T: lane holds queries 16tt + 4g + i of key c16
@@ -396,7 +408,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
           const int tt = 2 * c2 + hh, ql = 16 * tt + 4 * g + i, q = q0 + ql;
           float x = s[tt][i] * scale2 + kmask;
           if constexpr (kBias) x = fmaf(bc[4 * tt + i], kLog2e, x);
-          const float p = key_ok ? __builtin_amdgcn_exp2f(x - sm.lse2[ql]) : 0.f;
+          const bool on = key_ok && (!kBits || ((wc >> (16 * tt + i)) & 1ull));
+          const float p = on ? __builtin_amdgcn_exp2f(x - sm.lse2[ql]) : 0.f;
           const float ds = p * (dp[tt][i] - sm.delta[ql]);
           p8[4 * hh + i] = p;
           d8[4 * hh + i] = ds;
@@ -442,22 +455,27 @@ template <int D>
 hipError_t launch_d(const sa_problem& p, const BwdArgs& a, hipStream_t s) {
   const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
   const dim3 grid((unsigned)(ntiles * p.B * p.H)), block(kThreads);
-  auto dkdv = [&](auto bias_c, auto mask_c) {
+  auto run = [&](auto bias_c, auto mask_c, auto bits_c) {
     constexpr bool kB = decltype(bias_c)::value, kM = decltype(mask_c)::value;
-    hipLaunchKernelGGL((dq_kernel<D, kB, kM>), grid, block, 0, s, a);
+    constexpr bool kW = decltype(bits_c)::value;
+    hipLaunchKernelGGL((dq_kernel<D, kB, kM, kW>), grid, block, 0, s, a);
     if constexpr (D == 128) {
-      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 1>), grid, block, 0, s, a);
-      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 2>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 1, kW>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 2, kW>), grid, block, 0, s, a);
     } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 3>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, kB, kM, 3, kW>), grid, block, 0, s, a);
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (p.bias && p.key_mask) dkdv(T_{}, T_{});
-  else if (p.bias) dkdv(T_{}, F_{});
-  else if (p.key_mask) dkdv(F_{}, T_{});
-  else dkdv(F_{}, F_{});
+  auto with_bits = [&](auto bits_c) {
+    if (p.bias && p.key_mask) run(T_{}, T_{}, bits_c);
+    else if (p.bias) run(T_{}, F_{}, bits_c);
+    else if (p.key_mask) run(F_{}, T_{}, bits_c);
+    else run(F_{}, F_{}, bits_c);
+  };
+  if (a.bits) with_bits(T_{});
+  else with_bits(F_{});
   return hipGetLastError();
 }
 
@@ -471,7 +489,29 @@ hipError_t launch_fused_backward(const sa_problem& p, const void* q, const void*
   const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                   static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), out, lse,
                   p.bias, p.key_mask, p.seqlen_k, dq, dk, dv, dscores, delta,
-                  p.row_ptr, p.col_idx, t_row_ptr, t_col_idx, (long long)p.nnz,
+                  p.row_ptr, p.col_idx, t_row_ptr, t_col_idx, (long long)p.nnz, nullptr, nullptr,
+                  p.B, p.H, p.n, p.key_mask_heads, p.scale};
+  switch (p.d) {
+    case 32: return launch_d<32>(p, a, s);
+    case 64: return launch_d<64>(p, a, s);
+    case 128: return launch_d<128>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_backward_cover(const sa_problem& p, const int* c_row_ptr, const int* c_col_idx,
+                                       const int* t_row_ptr, const int* t_col_idx, long long cover_nnz,
+                                       const uint64_t* bits, const uint64_t* bits_t, const void* q,
+                                       const void* k, const void* v, const float* out, const float* lse,
+                                       const void* dout, float* dq, float* dk, float* dv, float* dscores,
+                                       float* delta, hipStream_t s) {
+  if (p.B == 0 || p.H == 0 || p.n == 0) return hipSuccess;
+  const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                  static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), out, lse,
+                  p.bias, p.key_mask, p.seqlen_k, dq, dk, dv, dscores, delta,
+                  c_row_ptr, c_col_idx, t_row_ptr, t_col_idx, cover_nnz,
+                  reinterpret_cast<const unsigned long long*>(bits),
+                  reinterpret_cast<const unsigned long long*>(bits_t),
                   p.B, p.H, p.n, p.key_mask_heads, p.scale};
   switch (p.d) {
     case 32: return launch_d<32>(p, a, s);

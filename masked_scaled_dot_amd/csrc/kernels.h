@@ -39,6 +39,21 @@ hipError_t launch_fused_backward(const sa_problem& p, const void* q, const void*
                                  const float* out, const float* lse, const void* dout, float* dq,
                                  float* dk, float* dv, float* dscores, float* delta,
                                  const int* t_row_ptr, const int* t_col_idx, hipStream_t s);
+hipError_t launch_fused_backward_cover(const sa_problem& p, const int* c_row_ptr, const int* c_col_idx,
+                                       const int* t_row_ptr, const int* t_col_idx, long long cover_nnz,
+                                       const uint64_t* bits, const uint64_t* bits_t, const void* q,
+                                       const void* k, const void* v, const float* out, const float* lse,
+                                       const void* dout, float* dq, float* dk, float* dv, float* dscores,
+                                       float* delta, hipStream_t s);
+hipError_t launch_block_cover_rows(int n, long long nnz, const int* row_ptr, const int* col_idx,
+                                   int* cover_row_ptr, hipStream_t s);
+hipError_t launch_block_cover_cols(int n, long long nnz, const int* row_ptr, const int* col_idx,
+                                   const int* cover_row_ptr, long long cover_nnz, int* cover_col_idx,
+                                   hipStream_t s);
+hipError_t launch_block_cover_bits(int n, long long nnz, const int* row_ptr, const int* col_idx,
+                                   const int* c_row_ptr, const int* c_col_idx, const int* t_row_ptr,
+                                   const int* t_col_idx, long long cover_nnz, uint64_t* bits,
+                                   uint64_t* bits_t, hipStream_t s);
 
 // Mask construction: COO -> CSR, key mask from key lengths, packed variable-length batches.
 size_t mask_workspace_bytes(long long n, long long nnz);

@@ -278,3 +278,48 @@ def test_fused_backward_checks():
     assert f(None, *args) == sa.SA_ERR_NULL
     big = _prob(row_ptr=None, col_idx=None, nnz=0, n=30000, bias=FAKE)  # bias head past 2 GB
     assert f(ctypes.byref(big), *args) == sa.SA_ERR_UNSUPPORTED
+
+
+# ---- block cover and the fused backward over it (host checks only)
+
+def test_block_cover_calls_check_arguments():
+    f = _lib.raw
+    good = _prob()
+    for p, st in ((None, sa.SA_ERR_NULL), (_prob(row_ptr=None), sa.SA_ERR_UNSUPPORTED),
+                  (_prob(block=64, nnz=4), sa.SA_ERR_UNSUPPORTED), (_prob(n=(1 << 22) + 1), sa.SA_ERR_SHAPE)):
+        ref = ctypes.byref(p) if p is not None else None
+        assert f("sa_block_cover_row_ptr")(ref, FAKE, None) == st
+        assert f("sa_block_cover_col_idx")(ref, FAKE, 1, FAKE, None) == st
+    p = ctypes.byref(good)
+    assert f("sa_block_cover_row_ptr")(p, None, None) == sa.SA_ERR_NULL
+    assert f("sa_block_cover_col_idx")(p, FAKE, 1, None, None) == sa.SA_ERR_NULL
+    assert f("sa_block_cover_col_idx")(p, FAKE, -1, FAKE, None) == sa.SA_ERR_SHAPE
+    assert f("sa_block_cover_col_idx")(p, FAKE, 5, FAKE, None) == sa.SA_ERR_SHAPE  # > (ceil(100/64))^2
+    c = _lib.sa_block_cover(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4)
+    assert f("sa_block_cover_bits")(p, None, None) == sa.SA_ERR_NULL
+    for field in ("row_ptr", "col_idx", "t_row_ptr", "t_col_idx", "bits", "bits_t"):
+        bad = _lib.sa_block_cover(**{k: (None if k == field else FAKE) for k in
+                                     ("row_ptr", "col_idx", "t_row_ptr", "t_col_idx", "bits", "bits_t")}, nnz=4)
+        assert f("sa_block_cover_bits")(p, ctypes.byref(bad), None) == sa.SA_ERR_NULL, field
+    c.nnz = 5
+    assert f("sa_block_cover_bits")(p, ctypes.byref(c), None) == sa.SA_ERR_SHAPE
+
+
+def test_fused_backward_cover_checks_arguments():
+    f = _lib.raw("sa_fused_backward_cover")
+    c = ctypes.byref(_lib.sa_block_cover(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4))
+    bufs = [FAKE] * 10
+    assert f(None, c, *bufs, FAKE, None) == sa.SA_ERR_NULL
+    for p, st in ((_prob(row_ptr=None), sa.SA_ERR_UNSUPPORTED), (_prob(block=64, nnz=4), sa.SA_ERR_UNSUPPORTED),
+                  (_prob(dtype=sa.SA_F32), sa.SA_ERR_UNSUPPORTED), (_prob(dtype=7), sa.SA_ERR_DTYPE)):
+        assert f(ctypes.byref(p), c, *bufs, FAKE, None) == st
+    p = ctypes.byref(_prob())
+    assert f(p, None, *bufs, FAKE, None) == sa.SA_ERR_NULL
+    for i in range(10):
+        args = list(bufs)
+        if i == 9:  # dscores is optional; the workspace is not
+            assert f(p, c, *args, None, None) == sa.SA_ERR_NULL
+            continue
+        args[i] = None
+        assert f(p, c, *args, FAKE, None) == sa.SA_ERR_NULL, i
+    assert f(p, c, *([FAKE + 8] + bufs[1:]), FAKE, None) == sa.SA_ERR_ALIGN
