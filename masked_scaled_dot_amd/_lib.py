@@ -456,26 +456,33 @@ def sa_block_cover_bits(prob, cover, stream=None):
 
 def block_cover(prob, device="cuda", stream=None) -> BlockCover:
     """Runs the four once-per-mask steps of the block cover in order (sa_block_cover_row_ptr,
-    sa_block_cover_col_idx, sa_csr_transpose over the cover, sa_block_cover_bits); reads the
-    cover's size back to the host in between (one synchronisation)."""
+    sa_block_cover_col_idx, sa_csr_transpose over the cover, sa_block_cover_bits) on `stream`
+    (torch's current stream when None); reads the cover's size back to the host in between,
+    after synchronising that stream. The arrays are allocated while that stream is current,
+    so torch's allocator orders their reuse after the work queued on it."""
     torch = _torch()
-    c = _c(prob)
-    nb = (c.n + 63) // 64
-    rp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
-    sa_block_cover_row_ptr(prob, rp, stream)
-    nnz = int(rp[nb].item()) if nb else 0
-    ci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
-    sa_block_cover_col_idx(prob, rp, nnz, ci, stream)
-    grid = Problem(1, 1, nb, 32, SA_F32, rp, ci[:nnz], nnz)
-    trp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
-    tci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
-    perm = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
-    ws = torch.empty(max(sa_transpose_workspace_bytes(grid), 1), dtype=torch.uint8, device=device)
-    sa_csr_transpose(grid, trp, tci[:nnz], perm[:nnz], ws, stream=stream)
-    bits = torch.empty(max(nnz, 1) * 64, dtype=torch.int64, device=device)
-    bits_t = torch.empty_like(bits)
-    cover = BlockCover(rp, ci, trp, tci, bits, bits_t, nnz)
-    sa_block_cover_bits(prob, cover, stream)
+    s = torch.cuda.current_stream() if stream is None else stream
+    if not hasattr(s, "cuda_stream"):
+        s = torch.cuda.ExternalStream(int(s))
+    with torch.cuda.stream(s):
+        c = _c(prob)
+        nb = (c.n + 63) // 64
+        rp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
+        sa_block_cover_row_ptr(prob, rp, s)
+        s.synchronize()
+        nnz = int(rp[nb].item()) if nb else 0
+        ci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+        sa_block_cover_col_idx(prob, rp, nnz, ci, s)
+        grid = Problem(1, 1, nb, 32, SA_F32, rp, ci[:nnz], nnz)
+        trp = torch.zeros(nb + 1, dtype=torch.int32, device=device)
+        tci = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+        perm = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)
+        ws = torch.empty(max(sa_transpose_workspace_bytes(grid), 1), dtype=torch.uint8, device=device)
+        sa_csr_transpose(grid, trp, tci[:nnz], perm[:nnz], ws, stream=s)
+        bits = torch.empty(max(nnz, 1) * 64, dtype=torch.int64, device=device)
+        bits_t = torch.empty_like(bits)
+        cover = BlockCover(rp, ci, trp, tci, bits, bits_t, nnz)
+        sa_block_cover_bits(prob, cover, s)
     return cover
 
 

@@ -606,12 +606,15 @@ hipError_t launch_block_t(const sa_problem& p, const FusedArgs& a, hipStream_t s
 }  // namespace
 
 bool fused_tile_supported(const sa_problem& p) {
+  // Every tile kind addresses a head's K/V and a bias head [n, n] through raw buffers with
+  // 32-bit offsets; larger problems take the vector path, whose pointers are 64-bit.
+  const long long kv = (long long)p.n * p.d * (p.dtype == SA_BF16 ? 2 : 4);
+  const long long bias = p.bias ? (long long)p.n * p.n * 4 : 0;
+  if (kv > kMaxBufBytes || bias > kMaxBufBytes) return false;
   // plan-driven CSR (both dtypes); its tiles do not read key lengths
   if (p.row_ptr && p.block == 1) return p.plan != nullptr && p.seqlen_k == nullptr;
-  // block CSR and dense: bf16, with every buffer the tile addresses within 32-bit offsets
-  const long long kv = (long long)p.n * p.d * 2;
-  const long long bias = p.bias ? (long long)p.n * p.n * 4 : 0;
-  return p.dtype == SA_BF16 && kv <= kMaxBufBytes && bias <= kMaxBufBytes;
+  // block CSR and dense: bf16
+  return p.dtype == SA_BF16;
 }
 
 hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
