@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libsa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["api.cpp", "plan.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "fused_valu.hip",
-           "fused_tile.hip", "backward.hip", "mask.hip",
+           "fused_tile.hip", "fused_wide.hip", "backward.hip", "mask.hip",
            "fused_backward.hip", "cover.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -200,6 +200,8 @@ int sa_fused_forward(const sa_problem* p, const void* q, const void* k, const vo
   if (!q || !k || !v || !out) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_ALIGN;
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
+  if (sa::fused_resident_supported(*p))
+    return hip_status(sa::launch_fused_resident(*p, q, k, v, out, lse, stream));
   if (sa::fused_tile_supported(*p)) return hip_status(sa::launch_fused_tile(*p, q, k, v, out, lse, stream));
   return hip_status(sa::launch_fused_valu(*p, q, k, v, out, lse, stream));
 }

@@ -17,6 +17,10 @@ hipError_t launch_fused_valu(const sa_problem& p, const void* q, const void* k, 
 hipError_t launch_fused_tile(const sa_problem& p, const void* q, const void* k, const void* v,
                              float* out, float* lse, hipStream_t s);
 bool fused_tile_supported(const sa_problem& p);
+// Dense pattern with the head's K and V resident in LDS (bf16, small n).
+hipError_t launch_fused_resident(const sa_problem& p, const void* q, const void* k, const void* v,
+                                 float* out, float* lse, hipStream_t s);
+bool fused_resident_supported(const sa_problem& p);
 
 // Backward pass pieces: pattern transpose, per-entry gather, softmax gradient.
 size_t transpose_workspace_bytes(long long n, long long nnz);

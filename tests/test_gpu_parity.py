@@ -52,6 +52,9 @@ SMALL = {
     "evoformer_bf16_odd": lambda: gen.make("evoformer_l384", B=3, H=2, n=97),
     "evoformer_bf16": lambda: gen.make("evoformer_l384", B=2, H=8, n=384),
     "evoformer_f32_d64": lambda: gen.make("evoformer_l384", B=2, H=2, n=130, d=64, dtype="f32"),
+    "evoformer_bf16_d64": lambda: gen.make("evoformer_l384", B=2, H=2, n=130, d=64),
+    "evoformer_bf16_d128_bias": lambda: gen.make("evoformer_l384", B=1, H=2, n=70, d=128, key_mask=False),
+    "evoformer_bf16_d32_mask_only": lambda: gen.make("evoformer_l384", B=3, H=2, n=200, bias=False),
     "random_bias_keymask": lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
                                             bias=True, key_mask=True, pmax=40),
     # rows longer than the plan's split threshold (1024 entries): global-token rows, random
@@ -96,8 +99,10 @@ def test_fused_parity_small(name, plan):
     O, lse = dp.fused()
     ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), want_weights=False,
                                  **dp.oracle_args())
-    check(O, ref["O"], p.dtype, "context")
-    check(lse, ref["lse"], p.dtype, "lse")
+    eo = check(O, ref["O"], p.dtype, "context")
+    el = check(lse, ref["lse"], p.dtype, "lse")
+    say(f"PARITY {name} fused{'_plan' if plan else ''} context max_abs={eo[0]:.3e} mean_abs={eo[1]:.3e}"
+        f" lse max_abs={el[0]:.3e}")
 
 
 def test_fused_without_lse_and_scale_one():
