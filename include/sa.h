@@ -66,7 +66,8 @@ typedef enum sa_status {
                               not accepted by this call                                   */
   SA_ERR_ALIGN = -6,       /* q/k/v/out base pointer not 16-byte aligned                  */
   SA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed                  */
-  SA_ERR_WORKSPACE = -8    /* plan buffer too small or not built for this problem          */
+  SA_ERR_WORKSPACE = -8    /* plan or workspace too small (or the fixed scratch of the
+                              no-allocation entry point), or a plan for another problem    */
 } sa_status;
 
 typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -224,6 +225,20 @@ int sa_fused_backward(const sa_problem *p, const void *q, const void *k, const v
                       const float *out, const float *lse, const void *dout,
                       const int32_t *t_row_ptr, const int32_t *t_col_idx, float *dq, float *dk,
                       float *dv, float *dscores, float *workspace, hipStream_t stream);
+
+/* --- Fused backward without a workspace argument ---------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, arguments and outputs as
+ * sa_fused_backward without `workspace`; the row sums it needs live in a fixed device array of
+ * the library, 16 MiB on each GPU it runs on (held until the process ends), so B*H*n <= 4 Mi
+ * (else SA_ERR_WORKSPACE). Allocates nothing and calls no allocating routine; SA_FLAG_VALIDATE
+ * is refused (SA_ERR_UNSUPPORTED), since device validation allocates. Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams, other threads)
+ * race and give wrong gradients; serialise them. */
+int sa_fused_backward_noalloc(const sa_problem *p, const void *q, const void *k, const void *v,
+                              const float *out, const float *lse, const void *dout,
+                              const int32_t *t_row_ptr, const int32_t *t_col_idx, float *dq, float *dk,
+                              float *dv, float *dscores, hipStream_t stream);
 
 /* --- Block cover of an element pattern; fused backward over element CSR -----------------
  * The block-sparse replies of the gluon-nlp issue compute whole 64x64 blocks on fast

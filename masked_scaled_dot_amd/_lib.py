@@ -30,7 +30,8 @@ SA_BF16 = 1
 SA_FLAG_VALIDATE = 1
 
 EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
-           "sa_fused_forward", "sa_fused_backward", "sa_transpose_workspace_bytes", "sa_csr_transpose",
+           "sa_fused_forward", "sa_fused_backward", "sa_fused_backward_noalloc",
+           "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
            "sa_sparse_softmax_backward", "sa_bias_grad", "sa_mask_workspace_bytes", "sa_coo_to_csr",
            "sa_key_mask_from_lengths", "sa_varlen_row_ptr", "sa_varlen_col_idx", "sa_topk_mask",
@@ -83,6 +84,7 @@ def _load():
         "sa_spmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_fused_forward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "sa_fused_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "sa_fused_backward_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "sa_transpose_workspace_bytes": (sz, [P]),
         "sa_csr_transpose": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "sa_gather_entries": (ctypes.c_int, [P, vp, vp, vp, vp]),
@@ -286,6 +288,28 @@ def sa_fused_backward(prob, q, k, v, out, lse, dout, dq, dk, dv, workspace, dsco
                                   _ptr(dout), _ptr(t_row_ptr), _ptr(t_col_idx), _ptr(dq), _ptr(dk),
                                   _ptr(dv), _ptr(dscores), _ptr(workspace), _stream(stream)),
            "sa_fused_backward")
+
+
+def sa_fused_backward_noalloc(prob, q, k, v, out, lse, dout, dq, dk, dv, dscores=None,
+                              t_row_ptr=None, t_col_idx=None, stream=None):
+    """sa_fused_backward with the library's fixed device scratch instead of a workspace."""
+    c = _c(prob)
+    qkv, f32 = _dtype_of(c), _torch().float32
+    N = c.B * c.H * c.n * c.d
+    for x, name in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(x, name, N, qkv)
+    for x, name in ((out, "out"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(x, name, N, f32)
+    _check(lse, "lse", c.B * c.H * c.n, f32)
+    _check(dscores, "dscores", c.B * c.H * c.n * c.n, f32)
+    if c.row_ptr:
+        nb = (c.n + 63) // 64
+        _check(t_row_ptr, "t_row_ptr", nb + 1, _torch().int32)
+        _check(t_col_idx, "t_col_idx", c.nnz, _torch().int32)
+    _raise(_lib.sa_fused_backward_noalloc(_p(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                          _ptr(dout), _ptr(t_row_ptr), _ptr(t_col_idx), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(dscores), _stream(stream)),
+           "sa_fused_backward_noalloc")
 
 
 def sa_transpose_workspace_bytes(prob) -> int:

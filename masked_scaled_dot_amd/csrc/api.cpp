@@ -228,6 +228,25 @@ int sa_fused_backward(const sa_problem* p, const void* q, const void* k, const v
                                               workspace, t_row_ptr, t_col_idx, stream));
 }
 
+int sa_fused_backward_noalloc(const sa_problem* p, const void* q, const void* k, const void* v,
+                              const float* out, const float* lse, const void* dout,
+                              const int32_t* t_row_ptr, const int32_t* t_col_idx, float* dq, float* dk,
+                              float* dv, float* dscores, hipStream_t stream) {
+  int st = check_problem(p, kOpFused);
+  if (st != SA_OK) return st;
+  // device validation allocates a result flag: not available here
+  if (p->flags & SA_FLAG_VALIDATE) return SA_ERR_UNSUPPORTED;
+  if ((long long)p->B * p->H * (long long)p->n * 4 > (long long)sa::kNoAllocScratchBytes)
+    return SA_ERR_WORKSPACE;
+  if (empty_problem(p)) return SA_OK;
+  void* ws = nullptr;
+  clear_stale_error();
+  const hipError_t e = sa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return sa_fused_backward(p, q, k, v, out, lse, dout, t_row_ptr, t_col_idx, dq, dk, dv, dscores,
+                           static_cast<float*>(ws), stream);
+}
+
 size_t sa_transpose_workspace_bytes(const sa_problem* p) {
   if (check_problem(p, kOpSoftmax) != SA_OK) return 0;
   return sa::transpose_workspace_bytes(p->n, p->nnz);
@@ -470,7 +489,9 @@ const char* sa_status_string(int status) {
     case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: head size, block size, flag or pattern kind not supported by this call";
     case SA_ERR_ALIGN: return "SA_ERR_ALIGN: buffer not 16-byte aligned";
     case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime or launch failure";
-    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: plan buffer too small or built for another pattern";
+    case SA_ERR_WORKSPACE:
+      return "SA_ERR_WORKSPACE: plan or workspace too small (or the library's fixed scratch, for the "
+             "entry points that allocate nothing), or a plan built for another pattern";
   }
   return "unknown sa status";
 }

@@ -72,6 +72,11 @@ hipError_t launch_varlen_col_idx(int B, int total, const int* cu, int window, co
 hipError_t launch_topk_mask(int n, int k, const float* scores, int* row_ptr, int* col_idx,
                             hipStream_t s);
 
+// The library's fixed device scratch (16 MiB per GPU) for the entry points that allocate
+// nothing: its device address on the current device (looked up on the first call there).
+constexpr size_t kNoAllocScratchBytes = 16u << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // CSR row plan and validation.
 size_t plan_bytes_for(long long n, long long long_rows, long long segs, long long BH, long long d);
 hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_t s);
