@@ -1,17 +1,22 @@
-"""Benchmark of masked scaled dot-product attention over a CSR mask on one MI355X.
+"""Benchmark of masked scaled dot-product attention over a sparse mask on one MI355X.
 
-A step is one pass of the CSR path over one batch of synthetic input: SDDMM, sparse
-softmax and SpMM (scores, weights and context), replayed from a HIP graph of several steps,
-on the Longformer-style workload (12 heads, n=4096, d=64, bf16, window |i-j|<=128 plus
-global tokens 0 and 1).
-The row plan (a function of the mask alone) is built once before timing and reported
-separately. Inputs are resident in HBM before timing starts. The JSON line reports attended pairs/s
-(value), per-kernel durations from HIP events recorded on the stream the kernels run
-on, the roofline of the dominant kernel, the other fused variants measured on their own
-workloads, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Headline: a step is one fused forward pass (context O and lse) over the block-sparse
+workload bsr_n16384 (16 heads, n = 16384, d = 128, bf16, 64x64 blocks, each block-row its
+diagonal block plus 8 random block-columns), the largest of the five workloads named for the
+method, with inputs resident in HBM. `value` is attended pairs per second over K steps
+launched back to back; `roofline` is that kernel against the bf16 matrix-core peak (FLOP =
+4 * pairs * d); cold-cache (a 1 GiB write between launches) and warm medians are reported.
+
+Beside it, each other workload as a first-class entry (`workloads`): the Longformer-style
+pipeline (SDDMM -> softmax -> SpMM, the HBM-bound path, two streams and one), the random-row
+workload (pipeline and fused), the Evoformer-style dense + bias + key-padding fused forward
+(warm and cold), the 128-token window; the fp64 CPU oracle (dense definition and the CSR-only
+evaluation) timed on two whole heads of the headline workload (`cpu_baseline`,
+`cpu_baseline_csr`); whole-output parity of the headline's two heads and of the Longformer-style
+and Evoformer-style workloads against the oracle (`parity`); a plain copy's bandwidth.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extra] [--workload NAME]
+                       [--no-extra] [--profile FAMILY]
 """
 from __future__ import annotations
 
@@ -52,8 +57,7 @@ def parse():
     ap.add_argument("--streams", type=int, default=2,
                     help="independent batches in flight, one HIP stream (and graph) each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fused/BSR/bias rows")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--no-extra", action="store_true", help="the headline only (no other workloads)")
     ap.add_argument("--profile", choices=["pipeline", "backward", "fused_csr", "fused_bsr", "fused_dense",
                                           "fused_backward", "fused_backward_cover", "copy"],
                     help="run only this kernel family (steps iterations after warmup) and exit; "
@@ -486,31 +490,66 @@ def time_fused_backward_cover(torch, sa, p, iters=20, warmup=3):
     return us, build_us, nblk
 
 
-def cpu_baseline(p, budget_s):
-    """The fp64 dense oracle (definition with -inf outside the mask), timed on whole heads
-    until the budget is used; returns attended pairs/s on the host cores."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+        return max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = None
-    pattern = ("csr", p.row_ptr, p.col_idx)
-    done, t0 = 0, time.perf_counter()
-    while done < p.BH:
-        oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, pattern, heads=[done])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    pairs = done * p.nnz
-    return {"value": pairs / dt, "unit": "pairs/s",
-            "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
-            "kind": "oracle",
-            "sample": f"{done} of {p.BH} heads of {p.name} (all rows of each), dense fp64 "
-                      f"oracle with -inf outside the mask; {dt:.1f} s; exp and masking on one "
-                      f"thread, GEMMs on {blas_threads} BLAS threads; "
-                      f"{len(os.sched_getaffinity(0))} cores in the affinity mask"}
+        return None
+
+
+def _pattern_of(p):
+    if p.row_ptr is None:
+        return ("dense",)
+    if p.block == 64:
+        return ("bsr", p.row_ptr, p.col_idx, 64)
+    return ("csr", p.row_ptr, p.col_idx)
+
+
+def cpu_oracle_runs(p, heads):
+    """The fp64 oracle on whole heads of workload p, timed on the host cores: the dense
+    definition (-inf outside the mask, GEMMs on the BLAS threads) and the CSR-only evaluation of
+    the three steps on the element pattern (the fair sparse CPU baseline). Returns the two
+    baseline records and the CSR oracle's O and lse of those heads (for the parity block)."""
+    import oracle
+    blas = _blas_threads()
+    aff = len(os.sched_getaffinity(0))
+    sl = list(heads)
+    q, k, v = p.q[sl], p.k[sl], p.v[sl]
+    rp, ci = p.element_csr()
+    pairs_per_head = int(rp[-1])  # no key mask on the workloads timed here
+    t0 = time.perf_counter()
+    oracle.attention_dense(q, k, v, p.scale, p.H, _pattern_of(p), bias=p.bias, key_mask=None,
+                           want_weights=False)
+    t_dense = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ref = oracle.attention_csr(q, k, v, rp, ci, p.scale, p.H, bias=p.bias)
+    t_csr = time.perf_counter() - t0
+    pairs = len(sl) * pairs_per_head
+    what = (f"{len(sl)} of {p.BH} heads of {p.name} (heads {sl}, all rows of each)")
+    dense = {"value": pairs / t_dense, "unit": "pairs/s", "cores": blas if blas else aff,
+             "kind": "oracle",
+             "sample": f"{what}; dense fp64 definition with -inf outside the mask; {t_dense:.1f} s; "
+                       f"GEMMs on {blas} BLAS threads, exp and masking on one thread; {aff} cores "
+                       f"in the affinity mask"}
+    csr = {"value": pairs / t_csr, "unit": "pairs/s", "cores": blas if blas else aff,
+           "kind": "oracle",
+           "sample": f"{what}; CSR-only fp64 evaluation of the three steps (row loop, numpy); "
+                     f"{t_csr:.1f} s; {aff} cores in the affinity mask"}
+    return dense, csr, ref
+
+
+def parity_record(got, ref):
+    """max-abs / mean-abs of got against the fp64 reference over its finite entries, and
+    whether the -inf entries match exactly."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    fin = np.isfinite(r)
+    err = np.abs(g[fin] - r[fin])
+    return {"max_abs": float(err.max()) if err.size else 0.0,
+            "mean_abs": float(err.mean()) if err.size else 0.0,
+            "inf_pattern_equal": bool(np.array_equal(np.isfinite(g), fin)),
+            "values": int(r.size)}
 
 
 def load_traffic(kernel, src_hash):
@@ -558,6 +597,180 @@ def profile_only(args, torch, sa, gen):
     torch.cuda.synchronize()
 
 
+def time_cold_warm(torch, f, reps=30, flush_bytes=1 << 30):
+    """Median per-launch HIP-event time of f: warm (launches back to back, no flush) and cold
+    (a write of flush_bytes between launches, outside the events, so L2 and MALL hold none of
+    the inputs)."""
+    flush = torch.empty(flush_bytes // 4, device="cuda:0")
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        f()
+        b.record()
+    torch.cuda.synchronize()
+    warm = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    for a, b in ev:
+        flush.fill_(1.0)
+        a.record()
+        f()
+        b.record()
+    torch.cuda.synchronize()
+    cold = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    del flush
+    return warm, cold
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """GB/s of a plain device-to-device copy (bytes read + bytes written per second)."""
+    src = torch.ones(nbytes // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    us = _avg_us(torch, lambda: dst.copy_(src), iters=reps, warmup=2)
+    del src, dst
+    return 2 * nbytes / (us * 1e-6) / 1e9
+
+
+def headline_bsr(torch, sa, gen, steps, warmup):
+    """The block-sparse fused forward: `steps` launches back to back on one stream after
+    `warmup`, timed by HIP events on that stream and by the wall clock around them."""
+    p = gen.make("bsr_n16384")
+    prob, t, _ = to_device(p, torch, sa, element=False)
+    out = torch.empty(p.BH, p.n, p.d, device="cuda:0")
+    lse = torch.empty(p.BH, p.n, device="cuda:0")
+    f = lambda: sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_us = a.elapsed_time(b) * 1e3 / steps
+    warm, cold = time_cold_warm(torch, f)
+    pairs = p.BH * int(p.nnz) * 64 * 64
+    outs = (out.cpu().numpy(), lse.cpu().numpy())
+    del t, prob, out, lse
+    torch.cuda.empty_cache()
+    return p, pairs, wall, ev_us, warm, cold, outs
+
+
+def workload_longformer(torch, sa, gen, args):
+    """The three-step pipeline on the Longformer-style workload: two streams of graphed steps
+    (value of the entry), one stream, eager; per-kernel event times; the row plan's build time
+    and the rate when the plan is rebuilt every step (a mask generated at run time)."""
+    p = gen.make("longformer_n4096")
+    prob, t, nnz = to_device(p, torch, sa)
+    timer = EventTimer(torch)
+    steps = 100
+    wall, eager_wall, plan_us, chunk = run_pipeline_steps(torch, sa, prob, t, nnz, p.BH, p.n, p.d,
+                                                          steps, 10, timer)
+    kern_us = timer.result()
+    cwall, cchunk = run_concurrent_steps(torch, sa, p, steps, 10, max(1, args.streams))
+    pairs = p.BH * nnz
+    step_us = cwall * 1e6 / steps
+    algo = bytes_pipeline(p.BH, p.n, p.d, nnz, 2)
+    kernels = {}
+    for k_, us in kern_us.items():
+        gbs = algo[k_] / (us * 1e-6) / 1e9
+        kernels[k_] = {"us": round(us, 2), "algo_bytes": algo[k_], "GB_s": round(gbs, 1),
+                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    total_bytes = sum(algo[k_] for k_ in ("sddmm", "softmax", "spmm"))
+    total_us = sum(kern_us[k_] for k_ in ("sddmm", "softmax", "spmm"))
+    one_us = wall * 1e6 / steps
+    src_of = {"sddmm": ["sddmm.hip", "common.h", "tile.h", "plan_layout.h"],
+              "softmax": ["softmax.hip", "common.h"],
+              "spmm": ["spmm.hip", "common.h", "tile.h", "plan_layout.h"]}
+    for k_ in kernels:
+        kernels[k_]["traffic"] = load_traffic(k_, source_hash(src_of[k_]))
+    res = {"step": "sddmm + sparse_softmax + spmm (scores, weights, context); row plan built once per mask",
+           "pairs_per_step": pairs, "value": pairs / (step_us * 1e-6), "unit": "pairs/s",
+           "us_per_step_two_streams": round(step_us, 2), "us_per_step_one_stream": round(one_us, 2),
+           "us_per_step_eager": round(eager_wall * 1e6 / steps, 2),
+           "kernels": kernels,
+           "pipeline_hbm_frac_kernels": round(total_bytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "pipeline_hbm_frac_two_streams": round(total_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "plan_build_us": round(plan_us, 2),
+           "pairs_per_s_with_plan_per_step": pairs / ((one_us + plan_us) * 1e-6)}
+    log(f"longformer_n4096 pipeline: {step_us:.1f} us/step (2 streams), {one_us:.1f} (1 stream), plan "
+        f"{plan_us:.1f} us; " + "  ".join(f"{k_}={v:.1f}us" for k_, v in kern_us.items()))
+    del t, prob
+    return p, res
+
+
+def workload_random(torch, sa, gen):
+    q = gen.make("random_n8192")
+    prob, t, nnz = to_device(q, torch, sa)
+    timer = EventTimer(torch)
+    _, eager, plan_us, _ = run_pipeline_steps(torch, sa, prob, t, nnz, q.BH, q.n, q.d, 10, 2, timer)
+    rk = timer.result()
+    algo = bytes_pipeline(q.BH, q.n, q.d, nnz, 2)
+    pairs = q.BH * nnz
+    fused = time_fused(torch, sa, q)
+    res = {"pairs_per_step": pairs, "us_per_step_eager": round(eager * 1e6 / 10, 2),
+           "value": pairs / (eager / 10), "unit": "pairs/s",
+           "kernels_us": {k_: round(v, 2) for k_, v in rk.items()},
+           "hbm_frac": {k_: round(algo[k_] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k_, v in rk.items()},
+           "plan_build_us": round(plan_us, 2),
+           "fused_us": round(fused, 2), "fused_pairs_per_s": pairs / (fused * 1e-6),
+           "fused_TFLOP_s": round(4.0 * pairs * q.d / (fused * 1e-6) / 1e12, 2)}
+    log(f"random_n8192: pipeline {eager * 1e6 / 10:.1f} us/step (eager) " +
+        "  ".join(f"{k_}={v:.1f}us" for k_, v in rk.items()) + f", fused {fused:.1f} us")
+    del t, prob
+    return res
+
+
+def workload_evoformer(torch, sa, gen):
+    q = gen.make("evoformer_l384")
+    prob, t, _ = to_device(q, torch, sa, element=False)
+    out = torch.empty(q.BH, q.n, q.d, device="cuda:0")
+    lse = torch.empty(q.BH, q.n, device="cuda:0")
+    f = lambda: sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
+    us = _avg_us(torch, f, iters=100, warmup=5)
+    warm, cold = time_cold_warm(torch, f)
+    pr = q.attended_pairs()
+    flops = 4.0 * pr * q.d
+    res = {"pairs_per_step": pr, "us": round(us, 2), "warm_median_us": round(warm, 2),
+           "cold_median_us": round(cold, 2), "value": pr / (us * 1e-6), "unit": "pairs/s",
+           "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2),
+           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "traffic": load_traffic("fused_evoformer_l384", source_hash(["fused_wide.hip", "common.h", "tile.h", "fused_row.h"]))}
+    log(f"evoformer_l384 fused: {us:.1f} us (back to back), warm median {warm:.1f}, cold median {cold:.1f}")
+    outs = (out.cpu().numpy(), lse.cpu().numpy())
+    del t, prob, out, lse
+    return q, res, outs
+
+
+def workload_window(torch, sa, gen):
+    """The 128-token window workload (one head, fp32): pipeline and fused, launch-bound."""
+    q = gen.make("window_n128")
+    prob, t, nnz = to_device(q, torch, sa)
+    plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+    sa.sa_plan_build(prob, plan)
+    prob.set_plan(plan)
+    S = torch.empty(q.BH * nnz, device="cuda:0")
+    W = torch.empty_like(S)
+    O = torch.empty(q.BH, q.n, q.d, device="cuda:0")
+    lse = torch.empty(q.BH, q.n, device="cuda:0")
+
+    def pipe():
+        sa.sa_sddmm(prob, t["q"], t["k"], S)
+        sa.sa_sparse_softmax(prob, S, W)
+        sa.sa_spmm(prob, W, t["v"], O)
+    pus = _avg_us(torch, pipe, iters=50, warmup=5)
+    fus = _avg_us(torch, lambda: sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], O, lse), iters=50, warmup=5)
+    pairs = q.BH * nnz
+    del t, prob, plan
+    return {"pairs_per_step": pairs, "pipeline_us": round(pus, 2), "fused_us": round(fus, 2),
+            "note": "launch-bound (2,104 pairs); correctness workload"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -575,162 +788,145 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile:
         return profile_only(args, torch, sa, gen)
-    p = gen.make(args.workload)
-    BH, n, d = p.BH, p.n, p.d
-    prob, t, nnz = to_device(p, torch, sa)
-    pairs = BH * nnz
-    log(f"workload {p.name}: BH={BH} n={n} d={d} nnz/head={nnz} pairs/step={pairs}")
 
-    timer = EventTimer(torch)
-    wall, eager_wall, plan_us, chunk = run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d,
-                                                          args.steps, args.warmup, timer)
-    kern_us = timer.result()
-    single_ms = wall * 1e3 / args.steps
-    streams = args.streams if args.streams > 1 and args.steps % args.streams == 0 else 1
-    if streams > 1:
-        cwall, cchunk = run_concurrent_steps(torch, sa, p, args.steps, args.warmup, streams)
-        launch = (f"{streams} streams, each a HIP graph of {cchunk} steps on its own inputs, plan "
-                  f"and outputs, {args.steps // streams} steps per stream, replayed concurrently")
-    else:
-        cwall = wall
-        launch = f"one stream: a HIP graph of {chunk} steps, replayed {args.steps // chunk} times"
-    ms_per_step = cwall * 1e3 / args.steps
-    value = pairs / (cwall / args.steps)
-    log(f"pipeline: {ms_per_step * 1e3:.1f} us/step ({streams} streams), {single_ms * 1e3:.1f} us/step "
-        f"(one stream, graph of {chunk} steps), {eager_wall * 1e6 / args.steps:.1f} us/step (eager)  " +
-        "  ".join(f"{k}={v:.1f}us" for k, v in kern_us.items()))
+    # ---- headline: the block-sparse fused forward
+    p, pairs, wall, ev_us, warm, cold, bsr_out = headline_bsr(torch, sa, gen, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = pairs / (wall / args.steps)
+    flops = 4.0 * pairs * p.d
+    algo_bytes = bytes_fused(p)
+    achieved = flops / (ev_us * 1e-6) / 1e12
+    bsr_src = ["fused_tile.hip", "common.h", "tile.h", "fused_row.h", "plan_layout.h"]
+    roofline = {"bound": "mfma", "kernel": "fused_block_kernel (block CSR, d = 128)",
+                "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": load_traffic("fused_bsr_n16384", source_hash(bsr_src)),
+                "flops_per_launch": flops, "algo_bytes_per_launch": algo_bytes,
+                "avg_launch_us": round(ev_us, 2),
+                "hbm_frac": round(algo_bytes / (ev_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "source_hash": source_hash(bsr_src)}
+    log(f"bsr_n16384 fused: {ev_us:.1f} us per launch ({args.steps} back to back), warm median "
+        f"{warm:.1f}, cold median {cold:.1f}; {achieved:.0f} TFLOP/s")
 
-    algo = bytes_pipeline(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
-    kernels = {"plan_build_once": {"us": round(plan_us, 2), "algo_bytes": algo["plan"],
-                                   "note": "built once per mask, outside the timed step"}}
-    for k, us in kern_us.items():
-        gbs = algo[k] / (us * 1e-6) / 1e9
-        kernels[k] = {"us": round(us, 2), "algo_bytes": algo[k], "GB_s": round(gbs, 1),
-                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    total_bytes = sum(algo[k] for k in ("sddmm", "softmax", "spmm"))
-    total_us = sum(kern_us[k] for k in ("sddmm", "softmax", "spmm"))
-    dominant = max(("sddmm", "softmax", "spmm"), key=lambda k: kern_us[k])
-    src_of = {"sddmm": ["sddmm.hip", "common.h", "tile.h", "plan_layout.h"],
-              "softmax": ["softmax.hip", "common.h"],
-              "spmm": ["spmm.hip", "common.h", "tile.h", "plan_layout.h"]}
-    dom_hash = source_hash(src_of[dominant])
-    achieved = algo[dominant] / (kern_us[dominant] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(dominant, dom_hash),
-                "algo_bytes_per_launch": algo[dominant], "avg_launch_us": round(kern_us[dominant], 2),
-                "source_hash": dom_hash,
-                "pipeline_aggregate_frac": round(total_bytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-
-    extra = {}
-    if not args.no_extra:
-        fused_us = time_fused(torch, sa, p)
-        flops = 4.0 * pairs * d
-        extra["fused_csr_" + p.name] = {
-            "us": round(fused_us, 2), "pairs_per_s": pairs / (fused_us * 1e-6),
-            "TFLOP_s": round(flops / (fused_us * 1e-6) / 1e12, 2),
-            # the tiles of this workload run on the matrix cores (bf16); the vector-ALU
-            # fraction is the bound for tiles that take the vector path
-            "mfma_frac": round(flops / (fused_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "valu_frac": round(flops / (fused_us * 1e-6) / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
-            "hbm_frac": round(bytes_fused(p) / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del t
-        # the backward pass of the CSR pipeline on the main workload
-        bprob, bt, _ = to_device(p, torch, sa)
-        btimer = EventTimer(torch)
-        bwall = run_backward_steps(torch, sa, bprob, bt, nnz, BH, n, d, 20, 3, btimer)
-        bk = btimer.result()
-        balgo = bytes_backward(BH, n, d, nnz, 2 if p.dtype == "bf16" else 4)
-        extra["backward_" + p.name] = {
-            "us_per_step_eager": round(bwall * 1e6 / 20, 2), "pairs_per_s": pairs / (bwall / 20),
-            "kernels_us": {k: round(v, 2) for k, v in bk.items()},
-            "hbm_frac": {k: round(balgo[k] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k, v in bk.items()},
-            "aggregate_hbm_frac": round(sum(balgo.values()) / (sum(bk.values()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"backward {p.name}: {bwall * 1e6 / 20:.1f} us/step (eager) " +
-            "  ".join(f"{k}={v:.1f}us" for k, v in bk.items()))
-        del bt, bprob
-        # the random-row workload (rows of 32-512 random columns): every tile takes the
-        # vector path, whose key/value row gathers bound it
-        rq = gen.make("random_n8192")
-        rprob, rt, rnnz = to_device(rq, torch, sa)
-        rtimer = EventTimer(torch)
-        _, reager, _, _ = run_pipeline_steps(torch, sa, rprob, rt, rnnz, rq.BH, rq.n, rq.d, 10, 2, rtimer)
-        rk = rtimer.result()
-        ralgo = bytes_pipeline(rq.BH, rq.n, rq.d, rnnz, 2)
-        rpairs = rq.BH * rnnz
-        extra["pipeline_" + rq.name] = {
-            "us_per_step_eager": round(reager * 1e6 / 10, 2), "pairs_per_s": rpairs / (reager / 10),
-            "kernels_us": {k: round(v, 2) for k, v in rk.items()},
-            "hbm_frac": {k: round(ralgo[k] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k, v in rk.items()}}
-        fr = time_fused(torch, sa, rq)
-        extra["fused_csr_" + rq.name] = {
-            "us": round(fr, 2), "pairs_per_s": rpairs / (fr * 1e-6),
-            "TFLOP_s": round(4.0 * rpairs * rq.d / (fr * 1e-6) / 1e12, 2),
-            "hbm_frac": round(bytes_fused(rq) / (fr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"random_n8192: pipeline {reager * 1e6 / 10:.1f} us/step (eager) " +
-            "  ".join(f"{k}={v:.1f}us" for k, v in rk.items()) + f", fused {fr:.1f} us")
-        del rt, rprob
-        for name in ("bsr_n16384", "evoformer_l384"):
-            q = gen.make(name)
-            us = time_fused(torch, sa, q)
-            pr = q.attended_pairs() if q.row_ptr is None else q.BH * int(q.element_csr()[0][-1])
-            flops = 4.0 * pr * q.d
-            extra["fused_" + name] = {
-                "us": round(us, 2), "pairs_per_s": pr / (us * 1e-6),
-                "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2),
-                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "warm": True}
-            log(f"fused {name}: {us:.1f} us")
-            # the backward of the fused forward (dS written out too for the dense pattern,
-            # where it is [B*H, n, n]: the bias gradient's input)
-            bus = time_fused_backward(torch, sa, q)
-            bflops = 10.0 * pr * q.d  # S again, dP, dV, dK, dQ: five products of 2 pairs d
-            row = {"us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
-                   "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "flops_model": "10 * attended pairs * d (five products of 2 * pairs * d)"}
-            if q.row_ptr is None:
-                row["us_with_dscores"] = round(time_fused_backward(torch, sa, q, with_dscores=True), 2)
-            extra["fused_backward_" + name] = row
-            log(f"fused backward {name}: {bus:.1f} us")
-            del q
-
-        # the backward of the fused element-CSR forward, on the pattern's 64x64 block cover
-        bus, build_us, nblk = time_fused_backward_cover(torch, sa, p)
-        pr = p.BH * p.nnz
-        bflops = 10.0 * pr * p.d
-        extra["fused_backward_cover_" + args.workload] = {
-            "us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
-            "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "flops_model": "10 * attended pairs * d", "cover_blocks_per_head": nblk,
-            "computed_pairs_per_head": nblk * 64 * 64, "cover_build_us_once": round(build_us, 1)}
-        log(f"fused backward over the block cover {args.workload}: {bus:.1f} us "
-            f"({nblk} blocks per head; cover built once in {build_us:.0f} us)")
-
-        mc = time_mask_construction(torch, sa, p)
-        extra["mask_construction"] = mc
-        log("mask construction: " + ", ".join(f"{k} {v.get('us', v)}" for k, v in mc.items()))
-
-    cpu = None
+    workloads, parity, extra = {}, {}, {}
+    cpu = cpu_csr = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(p, args.cpu_seconds)
-        log(f"cpu oracle: {cpu['value']:.3e} pairs/s ({cpu['sample']})")
+        heads = (0, p.BH - 1)
+        cpu, cpu_csr, ref = cpu_oracle_runs(p, heads)
+        parity["bsr_n16384"] = {"heads": list(heads), "kernel": "fused forward, block CSR",
+                                "context": parity_record(bsr_out[0][list(heads)], ref["O"]),
+                                "lse": parity_record(bsr_out[1][list(heads)], ref["lse"])}
+        log(f"cpu oracle: dense {cpu['value']:.3e} pairs/s, csr {cpu_csr['value']:.3e} pairs/s")
+        del ref
+    del bsr_out
+
+    if not args.no_extra:
+        lp, workloads["longformer_n4096"] = workload_longformer(torch, sa, gen, args)
+        workloads["random_n8192"] = workload_random(torch, sa, gen)
+        ep, workloads["evoformer_l384"], evo_out = workload_evoformer(torch, sa, gen)
+        workloads["window_n128"] = workload_window(torch, sa, gen)
+        workloads["bsr_n16384"] = {"value": value, "unit": "pairs/s", "us": round(ev_us, 2),
+                                   "warm_median_us": round(warm, 2), "cold_median_us": round(cold, 2),
+                                   "note": "the headline"}
+        if not args.no_cpu_baseline:
+            import oracle
+            ref = oracle.attention_dense(ep.q, ep.k, ep.v, ep.scale, ep.H, ("dense",), bias=ep.bias,
+                                         key_mask=ep.key_mask, km_heads=ep.key_mask_heads,
+                                         want_weights=False)
+            parity["evoformer_l384"] = {"heads": "all", "kernel": "fused forward, dense + bias + key mask",
+                                        "context": parity_record(evo_out[0], ref["O"]),
+                                        "lse": parity_record(evo_out[1], ref["lse"])}
+            parity["longformer_n4096"] = longformer_parity(torch, sa, lp, oracle)
+        del evo_out
+        extra.update(extra_rows(torch, sa, gen, lp))
+        extra["copy_GB_s"] = round(copy_bandwidth(torch), 1)
 
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": p.name, "B": p.B, "H": p.H, "n": n, "d": d, "nnz_per_head": nnz,
-                   "pairs_per_step": pairs,
-                   "step": "sddmm + sparse_softmax + spmm (scores, weights, context); the row plan "
-                           "is built once per mask before timing",
-                   "launch": launch, "streams": streams,
-                   "single_stream_ms_per_step": round(single_ms, 5),
-                   "eager_ms_per_step": round(eager_wall * 1e3 / args.steps, 5),
-                   "inputs": "resident in HBM; caches not flushed between steps"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "extra": extra,
+        "config": {"workload": p.name, "B": p.B, "H": p.H, "n": p.n, "d": p.d, "block": 64,
+                   "blocks_per_block_row": 9, "pairs_per_step": pairs,
+                   "step": "fused forward over the 64x64 block CSR: context O [16, 16384, 128] fp32 "
+                           "and lse; the pattern is the input, nothing is built per mask",
+                   "launch": f"{args.steps} launches back to back on one stream",
+                   "inputs": "resident in HBM; value and roofline from launches back to back (warm)",
+                   "warm_median_us": round(warm, 2), "cold_median_us": round(cold, 2),
+                   "cold": "a 1 GiB write between launches, outside the timed events"},
+        "roofline": roofline, "cpu_baseline": cpu, "cpu_baseline_csr": cpu_csr,
+        "parity": parity, "workloads": workloads, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def longformer_parity(torch, sa, p, oracle):
+    """Whole outputs of the pipeline (weights, context) and of the fused forward (context, lse)
+    on the Longformer-style workload, with their row plans, against the CSR oracle."""
+    prob, t, nnz = to_device(p, torch, sa)
+    plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
+    sa.sa_plan_build(prob, plan)
+    prob.set_plan(plan)
+    S = torch.empty(p.BH * nnz, device="cuda:0")
+    W = torch.empty_like(S)
+    O = torch.empty(p.BH, p.n, p.d, device="cuda:0")
+    Of = torch.empty_like(O)
+    lse = torch.empty(p.BH, p.n, device="cuda:0")
+    sa.sa_sddmm(prob, t["q"], t["k"], S)
+    sa.sa_sparse_softmax(prob, S, W)
+    sa.sa_spmm(prob, W, t["v"], O)
+    sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], Of, lse)
+    torch.cuda.synchronize()
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H)
+    res = {"heads": "all", "kernel": "pipeline (weights, context) and fused forward (context, lse)",
+           "weights": parity_record(W.view(p.BH, nnz).cpu().numpy(), ref["W"]),
+           "context": parity_record(O.cpu().numpy(), ref["O"]),
+           "fused_context": parity_record(Of.cpu().numpy(), ref["O"]),
+           "fused_lse": parity_record(lse.cpu().numpy(), ref["lse"])}
+    del t, prob, plan, S, W, O, Of, lse
+    return res
+
+
+def extra_rows(torch, sa, gen, p):
+    """Backward passes and mask construction (the rows after the forward path)."""
+    extra = {}
+    n, d, BH = p.n, p.d, p.BH
+    bprob, bt, nnz = to_device(p, torch, sa)
+    btimer = EventTimer(torch)
+    bwall = run_backward_steps(torch, sa, bprob, bt, nnz, BH, n, d, 20, 3, btimer)
+    bk = btimer.result()
+    balgo = bytes_backward(BH, n, d, nnz, 2)
+    pairs = BH * nnz
+    extra["backward_" + p.name] = {
+        "us_per_step_eager": round(bwall * 1e6 / 20, 2), "pairs_per_s": pairs / (bwall / 20),
+        "kernels_us": {k: round(v, 2) for k, v in bk.items()},
+        "hbm_frac": {k: round(balgo[k] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k, v in bk.items()},
+        "aggregate_hbm_frac": round(sum(balgo.values()) / (sum(bk.values()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"backward {p.name}: {bwall * 1e6 / 20:.1f} us/step (eager)")
+    del bt, bprob
+    fused_csr = time_fused(torch, sa, p)
+    extra["fused_csr_" + p.name] = {"us": round(fused_csr, 2), "pairs_per_s": pairs / (fused_csr * 1e-6),
+                                    "TFLOP_s": round(4.0 * pairs * d / (fused_csr * 1e-6) / 1e12, 2)}
+    for name in ("bsr_n16384", "evoformer_l384"):
+        q = gen.make(name)
+        pr = q.attended_pairs() if q.row_ptr is None else q.BH * int(q.nnz) * 64 * 64
+        bus = time_fused_backward(torch, sa, q)
+        bflops = 10.0 * pr * q.d
+        row = {"us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
+               "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "flops_model": "10 * attended pairs * d (five products of 2 * pairs * d)"}
+        if q.row_ptr is None:
+            row["us_with_dscores"] = round(time_fused_backward(torch, sa, q, with_dscores=True), 2)
+        extra["fused_backward_" + name] = row
+        log(f"fused backward {name}: {bus:.1f} us")
+        del q
+    bus, build_us, nblk = time_fused_backward_cover(torch, sa, p)
+    bflops = 10.0 * pairs * d
+    extra["fused_backward_cover_" + p.name] = {
+        "us": round(bus, 2), "TFLOP_s": round(bflops / (bus * 1e-6) / 1e12, 2),
+        "mfma_frac": round(bflops / (bus * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "cover_blocks_per_head": nblk, "cover_build_us_once": round(build_us, 1)}
+    extra["mask_construction"] = time_mask_construction(torch, sa, p)
+    return extra
 
 
 if __name__ == "__main__":
