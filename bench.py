@@ -164,6 +164,8 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     out = torch.empty(BH, n, d, device="cuda:0")
     plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
     pt = EventTimer(torch)
+    sa.sa_plan_build(prob, plan)  # the first build also loads the plan kernels' code
+    torch.cuda.synchronize()
     a = pt.mark()
     sa.sa_plan_build(prob, plan)
     b = pt.mark()

@@ -34,8 +34,9 @@
  * DEVICE pointer (hipMalloc / torch CUDA tensor on the current device),
  * row-major and contiguous, owned by the caller. The library keeps no pointer
  * after a call returns. Calls are asynchronous on the given stream (0 = the
- * null stream); outputs are valid after the stream is synchronised. Calls on
- * different streams share no library state.
+ * null stream); outputs are valid after the stream is synchronised. The library
+ * keeps no state between calls; buffers the caller passes (a row plan among them, see
+ * below) are the caller's to order between streams.
  *
  * Errors: every call returns SA_OK (0) or a negative sa_status, and checks its
  * arguments on the host before touching the device. Host checks cover pointers,
@@ -120,14 +121,27 @@ typedef struct sa_problem {
  * The plan cuts every row of an element CSR into segments of at most a fixed
  * number of entries, so that rows of very different length (variable per-token
  * windows and global tokens, gluon-nlp issue replies; global tokens in the
- * "Sparse Attention" notes) become work units of similar size. It depends on
- * row_ptr, n and nnz only and serves every head and every call on that pattern.
+ * "Sparse Attention" notes) become work units of similar size, and classifies each
+ * 64-row tile (matrix-core tile, banded, gathered far columns, vector rows). Its
+ * schedule depends on the pattern only (row_ptr, col_idx, n, nnz); it also holds the
+ * merge counters and partial rows of split rows for B*H heads of d dimensions, which
+ * sa_spmm and sa_fused_forward write during a call. Hence a plan serves one call at a
+ * time: calls that may overlap (on other streams) need plans of their own, built from the
+ * same pattern; stream-ordered calls may share one, for any B*H and d up to those it was
+ * sized for (SA_ERR_WORKSPACE under SA_FLAG_VALIDATE otherwise).
  *
- * sa_plan_bytes: size in bytes of the plan buffer for problem p (host-only; 0 on a bad
- *   descriptor). Requires block == 1 and row_ptr != NULL.
- * sa_plan_build: fills plan (device buffer of at least sa_plan_bytes bytes, caller-owned)
- *   on stream. The plan stays valid while row_ptr's content is unchanged. */
+ * sa_plan_bytes: size in bytes of the plan buffer for problem p, from n, nnz, B*H and d
+ *   alone (host-only, no device access; 0 on a bad descriptor). Requires block == 1 and
+ *   row_ptr != NULL. It holds up to 1024 long-row segments; a pattern needing more gets a
+ *   plan without segments, and its long rows are then computed whole (slower, same results).
+ * sa_plan_bytes_segments: the same for up to max_segments segments. A row of len > 1024
+ *   entries takes ceil(len / 256) segments; the sum over the pattern's rows is the count
+ *   that keeps every long row split.
+ * sa_plan_build: fills plan (device buffer of at least the size of a plan without
+ *   segments, caller-owned) on stream. The plan stays valid while the pattern's content is
+ *   unchanged. */
 size_t sa_plan_bytes(const sa_problem *p);
+size_t sa_plan_bytes_segments(const sa_problem *p, int64_t max_segments);
 int sa_plan_build(const sa_problem *p, void *plan, size_t plan_bytes, hipStream_t stream);
 
 /* --- SDDMM: scores at the mask's nonzeros ----------------------------------------------

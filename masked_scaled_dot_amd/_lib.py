@@ -29,7 +29,7 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_FLAG_VALIDATE = 1
 
-EXPORTS = ("sa_plan_bytes", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
+EXPORTS = ("sa_plan_bytes", "sa_plan_bytes_segments", "sa_plan_build", "sa_sddmm", "sa_sparse_softmax", "sa_spmm",
            "sa_fused_forward", "sa_fused_backward", "sa_fused_backward_noalloc",
            "sa_transpose_workspace_bytes", "sa_csr_transpose",
            "sa_gather_entries", "sa_gather_order_build", "sa_gather_entries_ordered",
@@ -78,6 +78,7 @@ def _load():
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     sig = {
         "sa_plan_bytes": (sz, [P]),
+        "sa_plan_bytes_segments": (sz, [P, i64]),
         "sa_plan_build": (ctypes.c_int, [P, vp, sz, vp]),
         "sa_sddmm": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "sa_sparse_softmax": (ctypes.c_int, [P, vp, vp, vp]),
@@ -222,6 +223,10 @@ def _raise(st, where):
 
 def sa_plan_bytes(prob) -> int:
     return int(_lib.sa_plan_bytes(_p(prob)))
+
+
+def sa_plan_bytes_segments(prob, max_segments: int) -> int:
+    return int(_lib.sa_plan_bytes_segments(_p(prob), int(max_segments)))
 
 
 def sa_plan_build(prob, plan, plan_bytes: Optional[int] = None, stream=None):

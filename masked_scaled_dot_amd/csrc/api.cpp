@@ -5,7 +5,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <vector>
 
 #include "../../include/sa.h"
 #include "kernels.h"
@@ -130,28 +129,21 @@ int pre_launch(const sa_problem* p, hipStream_t s) {
 
 extern "C" {
 
-size_t sa_plan_bytes(const sa_problem* p) {
-  if (check_problem(p, kOpPlan) != SA_OK) return 0;
+size_t sa_plan_bytes_segments(const sa_problem* p, int64_t max_segments) {
+  if (check_problem(p, kOpPlan) != SA_OK || max_segments < 0) return 0;
   const long long BH = (long long)p->B * p->H;
-  if (p->n == 0) return sa::plan_bytes_for(0, 0, 0, BH, p->d);
-  // Exact count of long rows and their segments: one synchronous copy of row_ptr.
-  std::vector<int32_t> rp((size_t)p->n + 1);
-  clear_stale_error();
-  if (hipMemcpy(rp.data(), p->row_ptr, rp.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
-      hipSuccess)
-    return 0;
-  long long L = 0, S = 0;
-  for (int i = 0; i < p->n; ++i) {
-    long long a = rp[i], b = rp[i + 1];
-    a = a < 0 ? 0 : (a > p->nnz ? p->nnz : a);
-    b = b < a ? a : (b > p->nnz ? p->nnz : b);
-    if (b - a > sa::kLongRow) {
-      ++L;
-      S += (b - a + sa::kSeg - 1) / sa::kSeg;
-    }
-  }
-  return sa::plan_bytes_for(p->n, L, S, BH, p->d);
+  // a long row has more than kLongRow entries, so at least this many segments
+  const long long min_segs = (sa::kLongRow + 1 + sa::kSeg - 1) / sa::kSeg;
+  const long long n = p->n, nnz = p->nnz;
+  long long S = nnz / sa::kSeg + nnz / (sa::kLongRow + 1);  // segments cannot exceed this
+  S = S < max_segments ? S : max_segments;
+  long long L = nnz / (sa::kLongRow + 1);
+  L = L < n ? L : n;
+  L = L < S / min_segs ? L : S / min_segs;
+  return sa::plan_bytes_for(n, L, S, BH, p->d);
 }
+
+size_t sa_plan_bytes(const sa_problem* p) { return sa_plan_bytes_segments(p, sa::kPlanMaxSegs); }
 
 int sa_plan_build(const sa_problem* p, void* plan, size_t plan_bytes, hipStream_t stream) {
   int st = check_problem(p, kOpPlan);

@@ -43,11 +43,13 @@ __device__ __forceinline__ long long lower_bound(const int* col, long long lo, l
   return lo;
 }
 
-// Kernel A: per-row core ranges.
+// Kernel A: per-row core ranges, one wave per row: the lanes read the row's columns (64 at a
+// time) and count those below the two bounds of the core range.
 __global__ __launch_bounds__(256) void plan_rows_kernel(const int* __restrict__ row_ptr,
                                                         const int* __restrict__ col_idx, int n,
                                                         long long nnz, int* __restrict__ rows) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   if (i >= n) return;
   long long a, b;
   row_range(row_ptr, i, nnz, a, b);
@@ -55,11 +57,21 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int* __restrict__ 
   long long lo = a, hi = a;
   if (len > 0 && len <= kLongRow) {
     const long long med = col_idx[(a + b) >> 1], half = (len + 1) >> 1;
-    lo = lower_bound(col_idx, a, b, med - half);
-    hi = lower_bound(col_idx, lo, b, med + half + 1);
+    int below = 0, upto = 0;  // columns < med - half, columns <= med + half
+    for (long long e = a + lane; e < b; e += kWave) {
+      const long long c = col_idx[e];
+      below += c < med - half;
+      upto += c <= med + half;
+    }
+    below = (int)wave_reduce<OpSum>((float)below);
+    upto = (int)wave_reduce<OpSum>((float)upto);
+    lo = a + below;
+    hi = a + upto;
   }
-  rows[2 * i] = (int)lo;
-  rows[2 * i + 1] = (int)hi;
+  if (lane == 0) {
+    rows[2 * i] = (int)lo;
+    rows[2 * i + 1] = (int)hi;
+  }
 }
 
 // Kernel B (one workgroup): long-row segments and the header.
@@ -151,6 +163,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
                                                          long long nnz, const int* __restrict__ rows,
                                                          int* __restrict__ tiles, int ntiles) {
   __shared__ int s_far[kFarMax];
+  __shared__ int s_dist[kFarMax];
   __shared__ int s_pre[kTileRows + 1];
   __shared__ int s_min, s_max, s_core, s_far_total, s_banded;
   const int tile = blockIdx.x;
@@ -188,9 +201,15 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   }
   if (tid == 0) s_pre[0] = 0;
   __syncthreads();
-  if (tid == 0) {
-    for (int r = 0; r < kTileRows; ++r) s_pre[r + 1] += s_pre[r];
-    s_far_total = s_pre[kTileRows];
+  if (tid < kTileRows) {  // wave 0: inclusive prefix sum of the rows' far counts
+    int x = s_pre[tid + 1];
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __builtin_amdgcn_ds_bpermute((tid - off) << 2, x);
+      x += tid >= off ? y : 0;
+    }
+    s_pre[tid + 1] = x;
+    if (tid == kTileRows - 1) s_far_total = x;
   }
   __syncthreads();
   const int F = s_far_total;
@@ -222,18 +241,43 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
         __syncthreads();
       }
     }
+    // distinct values: a value starts a run when it differs from its predecessor; its slot in
+    // the compacted list is the number of run starts before it (ballot counts per 64 values,
+    // chunk offsets from a scan over the chunks), written to a second half of s_far's storage
+    __shared__ int s_chunk[kFarMax / kWave + 1];
+    int* s_uni = s_dist;
+    const int lane = tid % kWave;
+    for (int c0 = 0; c0 < F; c0 += (int)blockDim.x) {
+      const int i = c0 + tid;
+      const bool start = i < F && (i == 0 || s_far[i] != s_far[i - 1]);
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(start);
+      if (lane == 0) s_chunk[i / kWave] = __builtin_popcountll(bal);
+    }
+    __syncthreads();
     if (tid == 0) {
-      int u = 0;
-      for (int i = 0; i < F; ++i)
-        if (i == 0 || s_far[i] != s_far[i - 1]) {
-          if (u < kTileRows) tiles[kTileInfo * ntiles + kTileRows * tile + u] = s_far[i];
-          s_far[u] = s_far[i];  // compact in place (u <= i)
-          ++u;
-        }
-      s_far_total = u;
+      int acc = 0;
+      for (int c = 0; c < (F + kWave - 1) / kWave; ++c) {
+        const int x = s_chunk[c];
+        s_chunk[c] = acc;
+        acc += x;
+      }
+      s_far_total = acc;
+    }
+    __syncthreads();
+    for (int c0 = 0; c0 < F; c0 += (int)blockDim.x) {
+      const int i = c0 + tid;
+      const bool start = i < F && (i == 0 || s_far[i] != s_far[i - 1]);
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(start);
+      const int u = s_chunk[i / kWave] + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      if (start) {
+        if (u < kTileRows) tiles[kTileInfo * ntiles + kTileRows * tile + u] = s_far[i];
+        if (u < kFarMax) s_uni[u] = s_far[i];
+      }
     }
     __syncthreads();
     U = s_far_total;
+    for (int i = tid; i < min(U, kFarMax); i += blockDim.x) s_far[i] = s_uni[i];
+    __syncthreads();
     ok = U <= kTileRows;
   }
   if (tid == 0) {
@@ -257,47 +301,73 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
     s_far_total = mfma ? 1 : 0;  // reused: broadcast the decision
   }
   __syncthreads();
-  // block records of a matrix-core tile: per key block, each row's first entry and key mask
-  if (s_far_total && tid < kTileRows) {
-    const int kb_lo = tiles[kTileInfo * tile], kb_hi = tiles[kTileInfo * tile + 1];
-    const int nfar = tiles[kTileInfo * tile + 3];
-    int* blk = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
-    long long e = lo;
-    for (int j = 0; j < kb_hi - kb_lo; ++j) {
-      const long long k0 = (long long)(kb_lo + j) * kTileRows;
-      unsigned long long m = 0;
-      const long long first = e;
-      while (e < hi && col_idx[e] < k0 + kTileRows) {
-        const long long dk = col_idx[e] - k0;
-        if (dk >= 0) m |= 1ull << dk;
-        ++e;
+  // block records of a matrix-core tile: per key block, each row's first entry and key mask.
+  // One wave per row: lanes take the row's core entries 64 at a time and OR their key bits
+  // into the row's per-block masks in LDS; a block's first entry is the row's first core entry
+  // plus the entries of the blocks before it.
+  __shared__ unsigned long long s_mask[4][kMaxTileBlocks + 1];
+  const bool mfma_tile = s_far_total != 0;
+  const int kb_lo = tiles[kTileInfo * tile], kb_hi = tiles[kTileInfo * tile + 1];
+  const int nfar_t = tiles[kTileInfo * tile + 3];
+  int* blk = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
+  const int wv = tid / kWave, ln = tid % kWave;
+  for (int r = wv; mfma_tile && r < kTileRows; r += (int)blockDim.x / kWave) {
+    const int row = tile * kTileRows + r;
+    long long rrs = 0, rre = 0, rlo = 0, rhi = 0;
+    if (row < n) {
+      row_range(row_ptr, row, nnz, rrs, rre);
+      if (rre - rrs > kLongRow) {
+        rrs = rre = 0;
+      } else {
+        rlo = rows[2 * row];
+        rhi = rows[2 * row + 1];
       }
-      int* rec = blk + ((long long)j * kTileRows + tid) * kBlkWords;
+    }
+    if (ln <= kMaxTileBlocks) s_mask[wv][ln] = 0ull;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the clears are done before the ORs below
+    for (long long e = rlo + ln; e < rhi; e += kWave) {
+      const int dk = col_idx[e] - kb_lo * kTileRows;
+      const int j = dk >> 6;
+      if (dk >= 0 && j < kb_hi - kb_lo) atomicOr(&s_mask[wv][j], 1ull << (dk & 63));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    if (ln < kb_hi - kb_lo) {
+      long long first = rlo;
+      for (int jj = 0; jj < ln; ++jj) first += __builtin_popcountll(s_mask[wv][jj]);
+      const unsigned long long m = s_mask[wv][ln];
+      int* rec = blk + ((long long)ln * kTileRows + r) * kBlkWords;
       rec[0] = (int)first;
       rec[1] = (int)(m & 0xffffffffull);
       rec[2] = (int)(m >> 32);
       rec[3] = 0;
     }
-    if (nfar > 0) {  // the gathered block: slots are positions in the far list
+    if (nfar_t > 0) {  // the gathered block: slots are positions in the far list
       unsigned long long m = 0;
-      for (int side = 0; side < 2; ++side) {
-        const long long a = side ? hi : rs, b = side ? re : lo;
-        for (long long f = a; f < b; ++f) {
-          const int c = col_idx[f];
-          int l = 0, h = nfar;
-          while (l < h) {
-            const int mid = (l + h) >> 1;
-            if (s_far[mid] < c) l = mid + 1;
-            else h = mid;
-          }
-          m |= 1ull << l;
+      const long long nlow = rlo - rrs, nf = nlow + (rre - rhi);
+      for (long long q = ln; q < nf; q += kWave) {
+        const int c = col_idx[q < nlow ? rrs + q : rhi + (q - nlow)];
+        int l = 0, h = nfar_t;
+        while (l < h) {
+          const int mid = (l + h) >> 1;
+          if (s_far[mid] < c) l = mid + 1;
+          else h = mid;
         }
+        m |= 1ull << l;
       }
-      int* rec = blk + ((long long)(kb_hi - kb_lo) * kTileRows + tid) * kBlkWords;
-      rec[0] = (int)rs;
-      rec[1] = (int)(m & 0xffffffffull);
-      rec[2] = (int)(m >> 32);
-      rec[3] = (int)((lo - rs) | ((long long)(hi - lo) << 16));
+      // OR over the lanes
+      unsigned lo32 = (unsigned)m, hi32 = (unsigned)(m >> 32);
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        lo32 |= (unsigned)__builtin_amdgcn_ds_bpermute((ln ^ off) << 2, (int)lo32);
+        hi32 |= (unsigned)__builtin_amdgcn_ds_bpermute((ln ^ off) << 2, (int)hi32);
+      }
+      if (ln == 0) {
+        int* rec = blk + ((long long)(kb_hi - kb_lo) * kTileRows + r) * kBlkWords;
+        rec[0] = (int)rrs;
+        rec[1] = (int)lo32;
+        rec[2] = (int)hi32;
+        rec[3] = (int)((rlo - rrs) | ((long long)(rhi - rlo) << 16));
+      }
     }
   }
 }
@@ -356,7 +426,7 @@ hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_
   const long long off_tiles = off_rows + sz.rows;
   const int ntiles = (n + kTileRows - 1) / kTileRows;
   if (cap < off_tiles + sz.tiles) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(plan_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col_idx,
+  hipLaunchKernelGGL(plan_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, p.row_ptr, p.col_idx,
                      n, (long long)p.nnz, pl + off_rows);
   hipLaunchKernelGGL(plan_segs_kernel, dim3(1), dim3(kScanThreads), 0, s, p.row_ptr, n,
                      (long long)p.nnz, BH, p.d, cap, pl);

@@ -12,6 +12,7 @@ constexpr int kPlanHeaderWords = 16;
 constexpr int kTileRows = 64;           // rows per tile (and keys per key block)
 constexpr int kLongRow = 1024;          // rows with more entries are split into segments
 constexpr int kSeg = 256;               // entries per long-row segment
+constexpr long long kPlanMaxSegs = 1024; // segments a plan of sa_plan_bytes bytes holds
 constexpr float kDenseTile = 0.25f;     // tiles at least this dense run on matrix cores
 constexpr int kFarMax = 1024;           // far entries a tile may hold and still be gathered
 constexpr int kMaxTileBlocks = 12;      // contiguous key blocks a matrix-core tile may span

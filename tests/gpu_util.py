@@ -44,7 +44,11 @@ class DevProblem:
             self.build_plan()
 
     def build_plan(self):
-        nbytes = sa.sa_plan_bytes(self.prob)
+        # room for every long-row segment of the pattern (rows over 1024 entries take
+        # ceil(len / 256) each), so that the split paths run even on patterns with many
+        lens = np.diff(self.p.row_ptr.astype(np.int64))
+        segs = int(((lens[lens > 1024] + 255) // 256).sum())
+        nbytes = sa.sa_plan_bytes_segments(self.prob, max(segs, 1024))
         assert nbytes > 0
         self.plan = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=DEV)
         sa.sa_plan_build(self.prob, self.plan)

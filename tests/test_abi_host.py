@@ -323,3 +323,12 @@ def test_fused_backward_cover_checks_arguments():
         args[i] = None
         assert f(p, c, *args, FAKE, None) == sa.SA_ERR_NULL, i
     assert f(p, c, *([FAKE + 8] + bufs[1:]), FAKE, None) == sa.SA_ERR_ALIGN
+
+
+def test_plan_size_is_host_only_bound():
+    """sa_plan_bytes needs no device access (a descriptor whose row_ptr points nowhere valid
+    still gets a size) and grows with the head count and size, not with the pattern's content."""
+    fake = FAKE
+    a = sa.Problem(1, 12, 4096, 64, sa.SA_BF16, fake, fake, 1_052_026)
+    b = sa.Problem(1, 12, 4096, 128, sa.SA_BF16, fake, fake, 1_052_026)
+    assert 0 < sa.sa_plan_bytes(a) < sa.sa_plan_bytes(b)

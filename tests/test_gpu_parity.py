@@ -388,6 +388,35 @@ def test_plan_build_matches_host(name):
         assert ei.value.status == sa.SA_ERR_WORKSPACE
 
 
+def test_two_streams_one_pattern_own_plans():
+    """Two streams run the pipeline and the fused forward concurrently on the same pattern,
+    each with a plan of its own (a plan's long-row merge state serves one call at a time):
+    every result equals the stream-ordered one bit for bit."""
+    p = _elementwise(small("longformer_long_rows"))  # rows split into segments
+    dps = [DevProblem(p, plan=True) for _ in range(2)]
+    ref = [x.copy() for x in dps[0].pipeline()] + [dps[0].fused(want_lse=True)[0].copy()]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = []
+    for dp, st in zip(dps, streams):
+        outs.append((torch.empty(p.BH * p.nnz, device=DEV), torch.empty(p.BH * p.nnz, device=DEV),
+                     torch.empty(p.BH, p.n, p.d, device=DEV), torch.empty(p.BH, p.n, p.d, device=DEV),
+                     torch.empty(p.BH, p.n, device=DEV)))
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for dp, st, (S, W, O, Of, lse) in zip(dps, streams, outs):
+            with torch.cuda.stream(st):
+                sa.sa_sddmm(dp.prob, dp.q, dp.k, S)
+                sa.sa_sparse_softmax(dp.prob, S, W)
+                sa.sa_spmm(dp.prob, W, dp.v, O)
+                sa.sa_fused_forward(dp.prob, dp.q, dp.k, dp.v, Of, lse)
+    torch.cuda.synchronize()
+    for S, W, O, Of, _ in outs:
+        got = [S.view(p.BH, p.nnz).cpu().numpy(), W.view(p.BH, p.nnz).cpu().numpy(), O.cpu().numpy(),
+               Of.cpu().numpy()]
+        for what, g_, r_ in zip(("scores", "weights", "context", "fused"), got, ref):
+            assert np.array_equal(g_, r_), what
+
+
 # ------------------------------------------------------------------------------ full size
 
 FULL = ["longformer_n4096", "random_n8192", "bsr_n16384", "evoformer_l384"]
