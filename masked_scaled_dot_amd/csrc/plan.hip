@@ -15,7 +15,7 @@
 //   * rows longer than kLongRow, cut into segments of at most kSeg entries, so that such a
 //     row is spread over many waves; their partial results merge deterministically through
 //     a per-(row, head) counter and scratch space kept in the plan.
-// Building takes four small kernels on the caller's stream.
+// Building takes three small kernels on the caller's stream.
 #include "common.h"
 #include "kernels.h"
 #include "plan_layout.h"
@@ -134,6 +134,10 @@ __global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __re
       ++lr;
     }
   }
+  if (fits) {  // merge counters start at zero (a plain store loop, safe under graph capture)
+    int* cnt = plan + off_cnt;
+    for (long long i = tid; i < (long long)L * BH; i += kScanThreads) cnt[i] = 0;
+  }
   if (tid == 0) {
     plan[kHMagic] = kPlanMagic;
     plan[kHN] = n;
@@ -165,6 +169,10 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   __shared__ int s_far[kFarMax];
   __shared__ int s_dist[kFarMax];
   __shared__ int s_pre[kTileRows + 1];
+  __shared__ int s_lo[kTileRows], s_hi[kTileRows];  // rows' core ranges (empty for long rows)
+  __shared__ int s_rs[kTileRows], s_re[kTileRows];  // rows' entry ranges (empty for long rows)
+  __shared__ int s_c0[kTileRows], s_cons[kTileRows];  // first core column; core columns consecutive
+  __shared__ int s_rp[kTileRows + 1];                // row_ptr of the tile's rows (clamped)
   __shared__ int s_min, s_max, s_core, s_far_total, s_banded;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
     s_banded = 1;
   }
   __syncthreads();
-  int nfar = 0, lo = 0, hi = 0;
+  int nfar = 0, lo = 0, hi = 0, c0 = 0, c1 = -1;
   long long rs = 0, re = 0;
   if (tid < kTileRows) {
     const int row = tile * kTileRows + tid;
@@ -187,17 +195,32 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
         lo = rows[2 * row];
         hi = rows[2 * row + 1];
         if (hi > lo) {
-          atomicMin(&s_min, col_idx[lo]);
-          atomicMax(&s_max, col_idx[hi - 1]);
+          c0 = col_idx[lo];
+          c1 = col_idx[hi - 1];
+          atomicMin(&s_min, c0);
+          atomicMax(&s_max, c1);
           atomicAdd(&s_core, hi - lo);
         }
         nfar = (int)((lo - rs) + (re - hi));
         // banded row: the core range holds consecutive columns, so within every key block
         // the row's entries are one run of consecutive slots
-        if (hi > lo && col_idx[hi - 1] - col_idx[lo] != hi - lo - 1) atomicAnd(&s_banded, 0);
+        if (hi > lo && c1 - c0 != hi - lo - 1) atomicAnd(&s_banded, 0);
       }
     }
+    s_c0[tid] = c0;
+    s_cons[tid] = hi == lo || c1 - c0 == hi - lo - 1;
     s_pre[tid + 1] = nfar;
+    s_lo[tid] = lo;
+    s_hi[tid] = hi;
+    s_rs[tid] = (int)rs;
+    s_re[tid] = (int)re;
+    // the tile's row_ptr (rows below n; the last one also writes its end)
+    if (row < n) {
+      long long a0, b0;
+      row_range(row_ptr, row, nnz, a0, b0);
+      s_rp[tid] = (int)a0;
+      if (tid == kTileRows - 1 || row == n - 1) s_rp[tid + 1] = (int)b0;
+    }
   }
   if (tid == 0) s_pre[0] = 0;
   __syncthreads();
@@ -219,15 +242,35 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
     // gather the far columns, pad with INT_MAX, bitonic sort, count distinct values
     for (int i = tid; i < kFarMax; i += blockDim.x) s_far[i] = 0x7fffffff;
     __syncthreads();
-    if (tid < kTileRows && nfar > 0) {
-      int o = s_pre[tid];
-      for (long long e = rs; e < lo; ++e) s_far[o++] = col_idx[e];
-      for (long long e = hi; e < re; ++e) s_far[o++] = col_idx[e];
+    // far entry f of the tile belongs to the row r with s_pre[r] <= f < s_pre[r + 1]; every
+    // thread takes every 256th one, all its loads in flight at once
+    for (int f0 = tid; f0 < F; f0 += 4 * (int)blockDim.x) {
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + u * (int)blockDim.x;
+        c[u] = 0x7fffffff;
+        if (f < F) {
+          int l = 0, h = kTileRows;
+          while (h - l > 1) {
+            const int mid = (l + h) >> 1;
+            if (s_pre[mid] <= f) l = mid;
+            else h = mid;
+          }
+          const int q = f - s_pre[l], nlow = s_lo[l] - s_rs[l];
+          c[u] = col_idx[q < nlow ? s_rs[l] + q : s_hi[l] + (q - nlow)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (f0 + u * (int)blockDim.x < F) s_far[f0 + u * (int)blockDim.x] = c[u];
     }
     __syncthreads();
-    for (int k = 2; k <= kFarMax; k <<= 1) {
+    int span = 2;  // sort the first span >= F slots (the rest hold INT_MAX already)
+    while (span < F) span <<= 1;
+    for (int k = 2; k <= span; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < kFarMax; i += blockDim.x) {
+        for (int i = tid; i < span; i += blockDim.x) {
           const int ixj = i ^ j;
           if (ixj > i) {
             const int x = s_far[i], y = s_far[ixj];
@@ -302,84 +345,113 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   }
   __syncthreads();
   // block records of a matrix-core tile: per key block, each row's first entry and key mask.
-  // One wave per row: lanes take the row's core entries 64 at a time and OR their key bits
-  // into the row's per-block masks in LDS; a block's first entry is the row's first core entry
-  // plus the entries of the blocks before it.
-  __shared__ unsigned long long s_mask[4][kMaxTileBlocks + 1];
+  // The threads read the tile's entries in order (coalesced), find each entry's row by a
+  // binary search over the tile's row_ptr, and OR the key bit of a core entry into its row's
+  // mask for the entry's block in LDS; a block's first entry is then the row's first core
+  // entry plus the bits of the blocks before it.
+  __shared__ unsigned long long s_mask[kMaxTileBlocks][kTileRows];
   const bool mfma_tile = s_far_total != 0;
+  if (!mfma_tile) return;
   const int kb_lo = tiles[kTileInfo * tile], kb_hi = tiles[kTileInfo * tile + 1];
+  const int nb = kb_hi - kb_lo;
   const int nfar_t = tiles[kTileInfo * tile + 3];
   int* blk = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
+  const int last_row = min(kTileRows, n - tile * kTileRows);  // rows of this tile below n
+  // rows whose core columns are consecutive: a block's key slots are the run's overlap with it
+  for (int i = tid; i < nb * kTileRows; i += blockDim.x) {
+    const int j = i / kTileRows, r = i % kTileRows;
+    if (!s_cons[r]) continue;
+    const int k0 = (kb_lo + j) * kTileRows;
+    const int len = s_hi[r] - s_lo[r];
+    const int a = max(s_c0[r], k0), b = min(s_c0[r] + len - 1, k0 + kTileRows - 1);  // columns
+    unsigned long long m = 0ull;
+    if (len > 0 && a <= b) {
+      const int w = b - a + 1;
+      m = (w == 64 ? ~0ull : ((1ull << w) - 1ull)) << (a - k0);
+    }
+    const int first = s_lo[r] + (len > 0 ? min(max(k0 - s_c0[r], 0), len) : 0);
+    int* rec = blk + ((long long)j * kTileRows + r) * kBlkWords;
+    rec[0] = first;
+    rec[1] = (int)(m & 0xffffffffull);
+    rec[2] = (int)(m >> 32);
+    rec[3] = 0;
+  }
+  // other rows: a wave per row ORs the key bits of its core entries into LDS masks (loads of a
+  // pass in flight together); a block's first entry is the row's first core entry plus the
+  // bits of the blocks before it
   const int wv = tid / kWave, ln = tid % kWave;
-  for (int r = wv; mfma_tile && r < kTileRows; r += (int)blockDim.x / kWave) {
-    const int row = tile * kTileRows + r;
-    long long rrs = 0, rre = 0, rlo = 0, rhi = 0;
-    if (row < n) {
-      row_range(row_ptr, row, nnz, rrs, rre);
-      if (rre - rrs > kLongRow) {
-        rrs = rre = 0;
-      } else {
-        rlo = rows[2 * row];
-        rhi = rows[2 * row + 1];
+  for (int r = wv; r < last_row; r += (int)blockDim.x / kWave) {
+    if (s_cons[r]) continue;
+    if (ln < nb) s_mask[ln][r] = 0ull;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    for (int e0 = s_lo[r] + ln; e0 < s_hi[r]; e0 += 4 * kWave) {
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = e0 + u * kWave < s_hi[r] ? col_idx[e0 + u * kWave] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dk = c[u] - kb_lo * kTileRows;
+        const int j = dk >> 6;
+        if (c[u] >= 0 && dk >= 0 && j < nb) atomicOr(&s_mask[j][r], 1ull << (dk & 63));
       }
     }
-    if (ln <= kMaxTileBlocks) s_mask[wv][ln] = 0ull;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // the clears are done before the ORs below
-    for (long long e = rlo + ln; e < rhi; e += kWave) {
-      const int dk = col_idx[e] - kb_lo * kTileRows;
-      const int j = dk >> 6;
-      if (dk >= 0 && j < kb_hi - kb_lo) atomicOr(&s_mask[wv][j], 1ull << (dk & 63));
-    }
     __builtin_amdgcn_s_waitcnt(0xc07f);
-    if (ln < kb_hi - kb_lo) {
-      long long first = rlo;
-      for (int jj = 0; jj < ln; ++jj) first += __builtin_popcountll(s_mask[wv][jj]);
-      const unsigned long long m = s_mask[wv][ln];
+    if (ln < nb) {
+      long long first = s_lo[r];
+      for (int jj = 0; jj < ln; ++jj) first += __builtin_popcountll(s_mask[jj][r]);
+      const unsigned long long m = s_mask[ln][r];
       int* rec = blk + ((long long)ln * kTileRows + r) * kBlkWords;
       rec[0] = (int)first;
       rec[1] = (int)(m & 0xffffffffull);
       rec[2] = (int)(m >> 32);
       rec[3] = 0;
     }
-    if (nfar_t > 0) {  // the gathered block: slots are positions in the far list
-      unsigned long long m = 0;
-      const long long nlow = rlo - rrs, nf = nlow + (rre - rhi);
-      for (long long q = ln; q < nf; q += kWave) {
-        const int c = col_idx[q < nlow ? rrs + q : rhi + (q - nlow)];
+  }
+  if (nfar_t > 0) {  // the gathered block: slots are positions in the far list
+    __shared__ unsigned long long s_fm[kTileRows];
+    if (tid < kTileRows) s_fm[tid] = 0ull;
+    __syncthreads();
+    for (int f0 = tid; f0 < F; f0 += 4 * (int)blockDim.x) {
+      int c[4], rr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + u * (int)blockDim.x;
+        c[u] = 0;
+        rr[u] = -1;
+        if (f < F) {
+          int l = 0, h = kTileRows;
+          while (h - l > 1) {
+            const int mid = (l + h) >> 1;
+            if (s_pre[mid] <= f) l = mid;
+            else h = mid;
+          }
+          const int q = f - s_pre[l], nlow = s_lo[l] - s_rs[l];
+          c[u] = col_idx[q < nlow ? s_rs[l] + q : s_hi[l] + (q - nlow)];
+          rr[u] = l;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rr[u] < 0) continue;
         int l = 0, h = nfar_t;
         while (l < h) {
           const int mid = (l + h) >> 1;
-          if (s_far[mid] < c) l = mid + 1;
+          if (s_far[mid] < c[u]) l = mid + 1;
           else h = mid;
         }
-        m |= 1ull << l;
-      }
-      // OR over the lanes
-      unsigned lo32 = (unsigned)m, hi32 = (unsigned)(m >> 32);
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        lo32 |= (unsigned)__builtin_amdgcn_ds_bpermute((ln ^ off) << 2, (int)lo32);
-        hi32 |= (unsigned)__builtin_amdgcn_ds_bpermute((ln ^ off) << 2, (int)hi32);
-      }
-      if (ln == 0) {
-        int* rec = blk + ((long long)(kb_hi - kb_lo) * kTileRows + r) * kBlkWords;
-        rec[0] = (int)rrs;
-        rec[1] = (int)lo32;
-        rec[2] = (int)hi32;
-        rec[3] = (int)((rlo - rrs) | ((long long)(rhi - rlo) << 16));
+        atomicOr(&s_fm[rr[u]], 1ull << l);
       }
     }
+    __syncthreads();
+    if (tid < kTileRows) {
+      const unsigned long long m = s_fm[tid];
+      int* rec = blk + ((long long)nb * kTileRows + tid) * kBlkWords;
+      rec[0] = (int)rs;
+      rec[1] = (int)(m & 0xffffffffull);
+      rec[2] = (int)(m >> 32);
+      rec[3] = (int)((lo - rs) | ((long long)(hi - lo) << 16));
+    }
   }
-}
-
-// Kernel D: zero the merge counters (a plain fill kernel, safe under graph capture).
-__global__ __launch_bounds__(256) void plan_zero_kernel(int* __restrict__ plan) {
-  if (plan[kHValid] == 0) return;
-  const long long cnt = (long long)plan[kHLongRows] * plan[kHBH];
-  int* c = plan + plan[kHOffCounters];
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < cnt;
-       i += (long long)gridDim.x * blockDim.x)
-    c[i] = 0;
 }
 
 // Flags: bit 0 bad row_ptr, bit 1 column out of range, bit 2 columns not strictly ascending.
@@ -433,7 +505,6 @@ hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_
   if (ntiles > 0)
     hipLaunchKernelGGL(plan_tiles_kernel, dim3(ntiles), dim3(256), 0, s, p.row_ptr, p.col_idx, n,
                        (long long)p.nnz, pl + off_rows, pl + off_tiles, ntiles);
-  hipLaunchKernelGGL(plan_zero_kernel, dim3(64), dim3(256), 0, s, pl);
   return hipGetLastError();
 }
 
