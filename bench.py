@@ -827,9 +827,13 @@ def main():
         workloads["random_n8192"] = workload_random(torch, sa, gen)
         ep, workloads["evoformer_l384"], evo_out = workload_evoformer(torch, sa, gen)
         workloads["window_n128"] = workload_window(torch, sa, gen)
+        el_us = time_fused(torch, sa, p, element=True)
         workloads["bsr_n16384"] = {"value": value, "unit": "pairs/s", "us": round(ev_us, 2),
                                    "warm_median_us": round(warm, 2), "cold_median_us": round(cold, 2),
-                                   "note": "the headline"}
+                                   "note": "the headline",
+                                   "element_csr_plan_us": round(el_us, 2),
+                                   "element_csr_plan_over_block": round(el_us / ev_us, 3)}
+        log(f"bsr_n16384 as element CSR with a row plan: {el_us:.1f} us ({el_us / ev_us:.2f}x the block call)")
         if not args.no_cpu_baseline:
             import oracle
             ref = oracle.attention_dense(ep.q, ep.k, ep.v, ep.scale, ep.H, ("dense",), bias=ep.bias,

@@ -188,7 +188,11 @@ void fused_plan_kernel(FusedArgs a, int BH) {
   const int row0 = tile * kTileRows;
   const TileView tv = tile_view(plan, tile);
   if (sizeof(T) == 2 && tv.mfma && segs_ok) {
-    if constexpr (sizeof(T) == 2) fused_block_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, 0, 0);
+    if constexpr (sizeof(T) == 2) fused_block_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, nullptr, 0);
+    return;
+  }
+  if (sizeof(T) == 2 && tv.blocks > 0) {  // whole 64x64 blocks: the block-sparse tile
+    if constexpr (sizeof(T) == 2) fused_block_tile<D, kFusedBsr, kBias, kMask, false>(a, sm, tv, t, row0, tv.bcols, tv.blocks);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -204,7 +208,8 @@ void fused_plan_kernel(FusedArgs a, int BH) {
 
 // Matrix-core tile of 64 queries [row0, row0 + 64) of head t. Kind kFusedCsr: the blocks are
 // the plan tile's (tv): its contiguous key blocks, then its far columns; kFusedBsr: the
-// stored blocks [bs, be) of the block-row; kFusedDense: all key blocks. kBias / kMask: a bias
+// nbk block-columns bcols[0, nbk) (a block-row of a block CSR, or a plan tile made of whole
+// blocks); kFusedDense: all key blocks. kBias / kMask: a bias
 // / key mask is added; kVec4: their rows are 16-byte aligned (n % 4 == 0) and loaded as
 // float4. Each of the four waves owns 16 queries; per 64-key block it forms S^T = K Q^T on
 // the matrix cores (lane g = lane / 16, c16 = lane % 16 holds keys 16tt + 4g + i of query
@@ -220,7 +225,7 @@ void fused_plan_kernel(FusedArgs a, int BH) {
 //    ragged last block (a uniform test).
 template <int D, int K, bool kBias, bool kMask, bool kVec4>
 __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const TileView& tv, int t,
-                                 int row0, long long bs, long long be) {
+                                 int row0, const int* bcols, int nbk) {
   constexpr int KS = FusedSmem1<D>::kKStride, VS = FusedSmem1<D>::kVStride;
   constexpr int KC = D / 32;
   constexpr int OC = D / 16;
@@ -239,11 +244,11 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   // dense and block CSR: keys at or past the batch's key length (n without one) are masked,
   // and the dense kind stops at the block that holds the last valid key
   const int nvalid = K != kFusedCsr && a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
-  const int nblk = K == kFusedBsr ? (int)(be - bs)
+  const int nblk = K == kFusedBsr ? nbk
                    : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv))
                                     : (nvalid + kTileRows - 1) / kTileRows;
   if constexpr (K == kFusedBsr)
-    for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = a.col_idx[bs + i];
+    for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = bcols[i];
   if constexpr (K == kFusedCsr) {
     if (threadIdx.x < kTileRows) {
       const int r = threadIdx.x, row = row0 + r;
@@ -280,7 +285,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   auto block_k0 = [&](int jj) -> int {
     if constexpr (K == kFusedBsr)
       return __builtin_amdgcn_readfirstlane(
-          clampi(jj < kBsrCached ? sm.bcol[jj] : a.col_idx[bs + jj], 0, ntiles - 1) * kTileRows);
+          clampi(jj < kBsrCached ? sm.bcol[jj] : bcols[jj], 0, ntiles - 1) * kTileRows);
     else if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
     else return jj * kTileRows;
   };
@@ -557,7 +562,7 @@ void fused_block_kernel(FusedArgs a) {
     be = be < bs ? bs : (be > a.nnz ? a.nnz : be);
   }
   const TileView tv{};
-  fused_block_tile<D, K, kBias, kMask, kVec4>(a, sm, tv, t, tile * kTileRows, bs, be);
+  fused_block_tile<D, K, kBias, kMask, kVec4>(a, sm, tv, t, tile * kTileRows, a.col_idx + bs, (int)(be - bs));
 }
 
 template <typename T, int D>

@@ -173,6 +173,8 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   __shared__ int s_rs[kTileRows], s_re[kTileRows];  // rows' entry ranges (empty for long rows)
   __shared__ int s_c0[kTileRows], s_cons[kTileRows];  // first core column; core columns consecutive
   __shared__ int s_rp[kTileRows + 1];                // row_ptr of the tile's rows (clamped)
+  __shared__ int s_len[kTileRows];                   // row lengths (-1 for long rows)
+  __shared__ int s_isblk;
   __shared__ int s_min, s_max, s_core, s_far_total, s_banded;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
@@ -220,6 +222,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
       row_range(row_ptr, row, nnz, a0, b0);
       s_rp[tid] = (int)a0;
       if (tid == kTileRows - 1 || row == n - 1) s_rp[tid + 1] = (int)b0;
+      s_len[tid] = b0 - a0 > kLongRow ? -1 : (int)(b0 - a0);
     }
   }
   if (tid == 0) s_pre[0] = 0;
@@ -235,6 +238,55 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
     if (tid == kTileRows - 1) s_far_total = x;
   }
   __syncthreads();
+  // ---- a tile made of whole 64x64 blocks: every row holds the same columns, and these are
+  // full key blocks (64 consecutive columns from a multiple of 64; the last block-column may
+  // be cut at n). When such a tile does not run on matrix cores as a CSR tile, its
+  // block-columns go to its (otherwise unused) block-record space and their count to word 5:
+  // the fused forward computes it as a block-sparse tile.
+  const int last_row = min(kTileRows, n - tile * kTileRows);
+  if (tid < kWave) {
+    const int len0 = s_len[0];
+    const bool same = tid >= last_row || s_len[tid] == len0;
+    const bool all = __builtin_amdgcn_ballot_w64(!same) == 0ull;
+    if (tid == 0) s_isblk = all && len0 > 0 && (len0 + kTileRows - 1) / kTileRows <= kTileRows;
+  }
+  __syncthreads();
+  if (s_isblk) {
+    const int len0 = s_len[0], e_lo = s_rp[0], e_hi = s_rp[last_row];
+    bool ok = true;
+    for (int e0 = e_lo + tid; e0 < e_hi; e0 += 4 * (int)blockDim.x) {
+      int c[4], cref[4], cprev[4], qq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * (int)blockDim.x;
+        c[u] = cref[u] = cprev[u] = qq[u] = 0;
+        if (e < e_hi) {
+          int l = 0, h = last_row;  // the entry's row
+          while (h - l > 1) {
+            const int mid = (l + h) >> 1;
+            if (s_rp[mid] <= e) l = mid;
+            else h = mid;
+          }
+          const int q = e - s_rp[l];
+          qq[u] = q;
+          c[u] = col_idx[e];
+          cref[u] = col_idx[e_lo + min(q, len0 - 1)];
+          cprev[u] = col_idx[e_lo + max(q - 1, 0)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e0 + u * (int)blockDim.x >= e_hi) break;
+        const int q = qq[u];
+        ok = ok && c[u] == cref[u] && (c[u] & (kTileRows - 1)) == (q & (kTileRows - 1)) &&
+             ((q & (kTileRows - 1)) == 0 || c[u] == cprev[u] + 1) && c[u] < n;
+      }
+    }
+    // a cut last block must end at n
+    const int w = len0 - (len0 - 1) / kTileRows * kTileRows;
+    if (tid == 0 && w < kTileRows && col_idx[e_lo + len0 - 1] + 1 != n) ok = false;
+    if (!ok) atomicAnd(&s_isblk, 0);
+  }
   const int F = s_far_total;
   int U = 0;
   bool ok = F <= kFarMax;
@@ -351,12 +403,19 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   // entry plus the bits of the blocks before it.
   __shared__ unsigned long long s_mask[kMaxTileBlocks][kTileRows];
   const bool mfma_tile = s_far_total != 0;
-  if (!mfma_tile) return;
+  if (!mfma_tile) {
+    if (s_isblk) {
+      const int nbk = (s_len[0] + kTileRows - 1) / kTileRows;
+      int* bcols = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
+      if (tid < nbk) bcols[tid] = col_idx[s_rp[0] + kTileRows * tid] / kTileRows;
+      if (tid == 0) tiles[kTileInfo * tile + 5] = nbk;
+    }
+    return;
+  }
   const int kb_lo = tiles[kTileInfo * tile], kb_hi = tiles[kTileInfo * tile + 1];
   const int nb = kb_hi - kb_lo;
   const int nfar_t = tiles[kTileInfo * tile + 3];
   int* blk = tiles + (long long)(kTileInfo + kTileRows) * ntiles + (long long)kBoundsPerTile * tile;
-  const int last_row = min(kTileRows, n - tile * kTileRows);  // rows of this tile below n
   // rows whose core columns are consecutive: a block's key slots are the run's overlap with it
   for (int i = tid; i < nb * kTileRows; i += blockDim.x) {
     const int j = i / kTileRows, r = i % kTileRows;

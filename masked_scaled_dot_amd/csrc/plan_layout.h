@@ -34,9 +34,10 @@ enum PlanHeader {
 // records below are 16-byte aligned), tiles (kTileInfo per tile: first key block, one
 // past the last key block, 1 if the tile runs on matrix cores, number of far columns, 1 if
 // every row's core range holds consecutive columns (so a row's entries in a key block are one
-// run of slots), then unused), far columns (64 per tile: the sorted distinct columns of the
-// tile's entries
-// outside the rows' core ranges, when there are at most 64 of them), block records (for a
+// run of slots), the number of 64x64 blocks when the tile is made of whole blocks and is not
+// a matrix-core tile (its rows hold the same full key blocks; its block-record space then
+// starts with their block-columns, ascending), then unused), far columns (64 per tile: the
+// sorted distinct columns of the tile's entries outside the rows' core ranges, when there are at most 64 of them), block records (for a
 // matrix-core tile, per key block j -- the contiguous ones, then the gathered far block --
 // and row r: the row's first entry in the block and a 64-bit mask of the block's key slots
 // the row holds; the row's entries in the block are its set bits in ascending order; the

@@ -35,8 +35,10 @@ struct TileView {
   int kb_lo, kb_hi, nfar;
   bool mfma;
   bool banded;          // every row's entries in every contiguous block are one run of slots
+  int blocks;           // > 0: the tile is that many whole 64x64 blocks (not a matrix-core CSR tile)
   const int* far_cols;  // nfar ascending columns
   const i32x4_v* rec;   // block records [block][row]: first entry, mask low, mask high, aux
+  const int* bcols;     // whole-block tile: its block-columns, ascending (in the record space)
 };
 
 __device__ __forceinline__ TileView tile_view(const int* plan, int tile) {
@@ -49,9 +51,11 @@ __device__ __forceinline__ TileView tile_view(const int* plan, int tile) {
   v.mfma = ti[2] != 0;
   v.nfar = ti[3];
   v.banded = ti[4] != 0;
+  v.blocks = ti[5];
   v.far_cols = base + (long long)kTileInfo * ntiles + (long long)kTileRows * tile;
   v.rec = reinterpret_cast<const i32x4_v*>(base + (long long)(kTileInfo + kTileRows) * ntiles +
                                         (long long)kBoundsPerTile * tile);
+  v.bcols = reinterpret_cast<const int*>(v.rec);
   return v;
 }
 

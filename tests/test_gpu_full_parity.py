@@ -110,6 +110,12 @@ def test_full_block_sparse_two_whole_heads():
     report(name, "sddmm", "scores", S[list(heads)], ref["S"], p.dtype)
     report(name, "softmax", "weights", W[list(heads)], ref["W"], p.dtype)
     report(name, "spmm", "context", Oe[list(heads)], ref["O"], p.dtype)
+    del S, W, Oe
+    # the fused forward on the element expansion with its plan: every tile is whole blocks
+    say(f"full fused forward on the element expansion {name} (plan, whole-block tiles)")
+    Of, lsef = dpe.fused()
+    report(name, "fused_plan_blocks", "context", Of[list(heads)], ref["O"], p.dtype)
+    report(name, "fused_plan_blocks", "lse", lsef[list(heads)], ref["lse"], p.dtype)
 
 
 class _SampledBiasRows:

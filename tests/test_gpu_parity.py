@@ -105,6 +105,61 @@ def test_fused_parity_small(name, plan):
         f" lse max_abs={el[0]:.3e}")
 
 
+# element CSR patterns whose tiles are whole 64x64 blocks (expansions of block-sparse
+# patterns): the fused forward with a plan computes such tiles as block-sparse tiles
+BLOCKY = {
+    "bsr_bf16_d128_ragged": lambda: small("bsr_bf16_d128_ragged"),
+    "bsr_bf16_d64": lambda: small("bsr_bf16_d64"),
+    "bsr_bf16_d32_bias_keymask": lambda: gen.make("bsr_n16384", n=64 * 5 + 9, H=2, B=2, d=32, extra=2,
+                                                  bias=True, key_mask=True, pmax=50),
+    "bsr_bf16_d64_bias": lambda: gen.make("bsr_n16384", n=64 * 7, H=2, d=64, extra=3, bias=True),
+}
+
+
+def _drop_entry(p, row):
+    """p with the last entry of ``row`` removed (its tile is no longer whole blocks)."""
+    import copy
+    rp, ci = p.row_ptr.astype(np.int64), p.col_idx
+    keep = np.ones(len(ci), bool)
+    keep[rp[row + 1] - 1] = False
+    e = copy.copy(p)
+    e.col_idx = ci[keep].astype(np.int32)
+    e.row_ptr = (rp - (np.arange(len(rp)) > row)).astype(np.int32)
+    return e
+
+
+@pytest.mark.parametrize("mixed", [False, True], ids=["whole", "one_tile_csr"])
+@pytest.mark.parametrize("name", sorted(BLOCKY))
+def test_fused_plan_whole_block_tiles(name, mixed):
+    """Element expansion of a block-sparse pattern through the fused forward with a plan:
+    whole-block tiles run as block-sparse tiles, the rest as CSR tiles; all against the
+    oracle. ``one_tile_csr`` drops one entry of row 70, so tile 1 takes the CSR path."""
+    pb = BLOCKY[name]()
+    p = _elementwise(pb)
+    if mixed:
+        p = _drop_entry(p, 70)
+    dp = DevProblem(p, plan=True)
+    h = dp.plan.cpu().numpy()
+    T = h[4]
+    words = h[h[11]:h[11] + 8 * T].reshape(-1, 8)
+    nblock = int((words[:, 5] > 0).sum())
+    say(f"fused whole-block tiles {name} mixed={mixed}: n={p.n} d={p.d} tiles={T} block tiles={nblock}"
+        f" bias={p.bias is not None} key_mask={p.key_mask is not None}")
+    assert nblock >= 1
+    if mixed:
+        assert words[1, 5] == 0
+    O, lse = dp.fused()
+    ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, ("csr", p.row_ptr, p.col_idx),
+                                 want_weights=False, **dp.oracle_args())
+    eo = check(O, ref["O"], p.dtype, "context")
+    el = check(lse, ref["lse"], p.dtype, "lse")
+    say(f"PARITY {name}{'_mixed' if mixed else ''} fused_plan_blocks context max_abs={eo[0]:.3e}"
+        f" mean_abs={eo[1]:.3e} lse max_abs={el[0]:.3e}")
+    if not mixed:  # the same tiles through the block-sparse entry point
+        O2, lse2 = DevProblem(pb).fused()
+        check(O, O2, p.dtype, "context vs block-sparse call")
+
+
 def test_fused_without_lse_and_scale_one():
     p = small("longformer_bf16_d64")
     dp = DevProblem(p, scale=1.0)
@@ -278,7 +333,7 @@ def _host_plan(p, BH, d):
             rows[i] = lo, hi
         else:
             rows[i] = a, a
-    tiles, fars = [], []
+    tiles, fars, blks = [], [], []
     for t0 in range(0, n, 64):
         lo, hi, core, farcols, banded = None, None, 0, [], 1
         for i in range(t0, min(n, t0 + 64)):
@@ -298,8 +353,11 @@ def _host_plan(p, BH, d):
         kb0, kb1 = (0, 0) if hi is None else (lo // 64, hi // 64 + 1)
         nblk = (kb1 - kb0) + (1 if uniq else 0)
         mfma = ok and nblk > 0 and kb1 - kb0 <= 12 and core + len(farcols) >= 0.25 * 64 * 64 * nblk
-        tiles.append((kb0, kb1, int(mfma), len(uniq) if ok else 0, banded, 0, 0, 0))
+        blocks = _whole_blocks(rp, ci, n, t0)
+        nbk = len(blocks) if blocks and not mfma else 0
+        tiles.append((kb0, kb1, int(mfma), len(uniq) if ok else 0, banded, nbk, 0, 0))
         fars.append(uniq if ok else None)
+        blks.append(blocks if nbk else None)
     segs = []
     lr = 0
     for i in range(n):
@@ -310,17 +368,31 @@ def _host_plan(p, BH, d):
             for s_ in range(ns):
                 segs.append((i, a + L * s_ // ns, a + L * (s_ + 1) // ns, lr, s_, ns, 0, 0))
             lr += 1
-    return rows, np.array(tiles), fars, np.array(segs, dtype=np.int64).reshape(-1, 8), lr
+    return rows, np.array(tiles), fars, np.array(segs, dtype=np.int64).reshape(-1, 8), lr, blks
 
 
-@pytest.mark.parametrize("name", ["longformer_long_rows", "random_long_rows", "window_n128_f32"])
+def _whole_blocks(rp, ci, n, t0):
+    """Block-columns of tile t0 when its rows (at most 1024 entries each) all hold the same
+    columns and these are whole 64-key blocks (the block that holds key n - 1 may be cut at
+    n); else None."""
+    lists = [ci[rp[i]:rp[i + 1]] for i in range(t0, min(n, t0 + 64))]
+    first = lists[0]
+    if len(first) == 0 or len(first) > 1024 or any(not np.array_equal(x, first) for x in lists):
+        return None
+    blocks = sorted(set(int(c) // 64 for c in first))
+    full = np.concatenate([np.arange(64 * b, min(64 * b + 64, n)) for b in blocks])
+    return blocks if np.array_equal(full, first) else None
+
+
+@pytest.mark.parametrize("name", ["longformer_long_rows", "random_long_rows", "window_n128_f32",
+                                  "bsr_bf16_d128_ragged"])
 def test_plan_build_matches_host(name):
     p = _elementwise(small(name))
     dp = DevProblem(p)
     plan = dp.build_plan()
     torch.cuda.synchronize()
     h = plan.cpu().numpy().astype(np.int64)
-    rows, tiles, fars, segs, L = _host_plan(p, p.BH, p.d)
+    rows, tiles, fars, segs, L, blks = _host_plan(p, p.BH, p.d)
     assert h[0] == 0x53415032 and h[1] == p.n and h[2] == p.nnz and h[7] == 1
     assert h[4] == len(tiles) and h[5] == L and h[6] == len(segs)
     assert h[8] == p.BH and h[9] == p.d
@@ -337,6 +409,9 @@ def test_plan_build_matches_host(name):
     blk_base = h[11] + (8 + 64) * T
     per_tile = 13 * 64 * 4
     for ti in range(T):
+        if tiles[ti, 5]:  # whole-block tile: its block-columns open its record space
+            nbk = tiles[ti, 5]
+            assert list(h[blk_base + per_tile * ti: blk_base + per_tile * ti + nbk]) == blks[ti]
         if not tiles[ti, 2]:
             continue
         kb0, kb1 = tiles[ti, 0], tiles[ti, 1]
@@ -368,6 +443,9 @@ def test_plan_build_matches_host(name):
     if name == "longformer_long_rows":
         assert tiles[20, 2] == 1 and fars[20] == [0, 1]      # global-token columns gathered
         assert tiles[20, 4] == 1                             # window rows: banded
+    if name == "bsr_bf16_d128_ragged":                       # every tile is whole blocks
+        assert all(tiles[ti, 5] > 0 or tiles[ti, 2] == 1 for ti in range(T))
+        assert sum(tiles[:, 5] > 0) == 5                     # the other two: matrix-core CSR
     assert np.array_equal(h[h[12]:h[12] + 8 * len(segs)].reshape(-1, 8), segs)
     assert np.all(h[h[13]:h[13] + L * p.BH] == 0)                       # merge counters
     assert h[15] * 4 <= plan.numel() * 4
