@@ -65,6 +65,14 @@ def parse():
     return ap.parse_args()
 
 
+# sources of each kernel family: a traffic figure is used only while their hash matches
+PIPE_SRC = {"sddmm": ["sddmm.hip", "common.h", "tile.h", "plan_layout.h"],
+            "softmax": ["softmax.hip", "common.h"],
+            "spmm": ["spmm.hip", "common.h", "tile.h", "plan_layout.h"]}
+BSR_SRC = ["fused_tile.hip", "common.h", "tile.h", "fused_row.h", "plan_layout.h"]
+DENSE_SRC = ["fused_wide.hip", "common.h", "tile.h", "fused_row.h"]
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -685,11 +693,8 @@ def workload_longformer(torch, sa, gen, args):
     total_bytes = sum(algo[k_] for k_ in ("sddmm", "softmax", "spmm"))
     total_us = sum(kern_us[k_] for k_ in ("sddmm", "softmax", "spmm"))
     one_us = wall * 1e6 / steps
-    src_of = {"sddmm": ["sddmm.hip", "common.h", "tile.h", "plan_layout.h"],
-              "softmax": ["softmax.hip", "common.h"],
-              "spmm": ["spmm.hip", "common.h", "tile.h", "plan_layout.h"]}
     for k_ in kernels:
-        kernels[k_]["traffic"] = load_traffic(k_, source_hash(src_of[k_]))
+        kernels[k_]["traffic"] = load_traffic(k_, source_hash(PIPE_SRC[k_]))
     res = {"step": "sddmm + sparse_softmax + spmm (scores, weights, context); row plan built once per mask",
            "pairs_per_step": pairs, "value": pairs / (step_us * 1e-6), "unit": "pairs/s",
            "us_per_step_two_streams": round(step_us, 2), "us_per_step_one_stream": round(one_us, 2),
@@ -718,6 +723,9 @@ def workload_random(torch, sa, gen):
            "value": pairs / (eager / 10), "unit": "pairs/s",
            "kernels_us": {k_: round(v, 2) for k_, v in rk.items()},
            "hbm_frac": {k_: round(algo[k_] / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for k_, v in rk.items()},
+           "algo_bytes": {k_: algo[k_] for k_ in rk},
+           "traffic": {k_: load_traffic(k_ + "_random_n8192", source_hash(PIPE_SRC[k_])) for k_ in rk
+                       if k_ in PIPE_SRC},
            "plan_build_us": round(plan_us, 2),
            "fused_us": round(fused, 2), "fused_pairs_per_s": pairs / (fused * 1e-6),
            "fused_TFLOP_s": round(4.0 * pairs * q.d / (fused * 1e-6) / 1e12, 2)}
@@ -742,7 +750,7 @@ def workload_evoformer(torch, sa, gen):
            "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2),
            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "traffic": load_traffic("fused_evoformer_l384", source_hash(["fused_wide.hip", "common.h", "tile.h", "fused_row.h"]))}
+           "traffic": load_traffic("fused_evoformer_l384", source_hash(DENSE_SRC))}
     log(f"evoformer_l384 fused: {us:.1f} us (back to back), warm median {warm:.1f}, cold median {cold:.1f}")
     outs = (out.cpu().numpy(), lse.cpu().numpy())
     del t, prob, out, lse
@@ -798,7 +806,7 @@ def main():
     flops = 4.0 * pairs * p.d
     algo_bytes = bytes_fused(p)
     achieved = flops / (ev_us * 1e-6) / 1e12
-    bsr_src = ["fused_tile.hip", "common.h", "tile.h", "fused_row.h", "plan_layout.h"]
+    bsr_src = BSR_SRC
     roofline = {"bound": "mfma", "kernel": "fused_block_kernel (block CSR, d = 128)",
                 "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
