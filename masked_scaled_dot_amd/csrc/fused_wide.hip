@@ -9,11 +9,13 @@
 //     registers; lane l holds query l % 32 and keys 8(r/4) + 4(l/32) + r%4 of each 32-key
 //     half (r = 0..15), so a query's scores sit in lanes l and l + 32;
 //   O^T (dims x queries) += V^T P^T : B = P^T is the score accumulator itself, rounded to
-//     bf16 (no shuffle); A = V^T comes from the row-major V in LDS through the transposing
-//     read ds_read_b64_tr_b16 at exactly the keys the B slots hold; the output lane again
-//     holds query l % 32, so the running-max rescale of O is a per-lane multiply;
-//   the row sums of P come from one more product with an all-ones A operand (the matrix
-//     cores are mostly idle at this head size, the vector ALUs are not).
+//     fp16 (no shuffle); A = V^T comes from V in LDS, stored as fp16 after a power-of-two
+//     scaling that puts the head's largest |v| in [2^14, 2^15) (exact for the bf16 inputs
+//     down to 2^-29 of that maximum), through the transposing read ds_read_b64_tr_b16 at
+//     exactly the keys the B slots hold; the output lane again holds query l % 32, so the
+//     running-max rescale of O is a per-lane multiply. The weights enter the product with
+//     11 significant bits and the row sum is taken over the same rounded values (one dot2
+//     instruction per two weights), so that the normalisation matches the product.
 // The softmax is the running-max / running-sum form with one division at the end
 // (streaming-dataflow SDPA review on nubint.ai, "proposed method"); the running maximum is
 // moved only when a block's maximum exceeds it by more than kSlack (log2 units), so most
@@ -35,12 +37,16 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_w;
 typedef __attribute__((ext_vector_type(4))) short i16x4_v;
 typedef __attribute__((ext_vector_type(8))) short i16x8_v;
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
+
 constexpr float kSlack = 8.f;
 constexpr int kResidentLds = 160 << 10;  // LDS bytes a resident head may take (all of a CU's LDS)
-constexpr bool kResidentSumMfma = false;  // row sums on the matrix cores (ones operand)
-constexpr int kResidentMaxWaves = 12;     // waves per workgroup (32 queries each)
+// waves per workgroup (32 queries each): three per SIMD at d = 32; wider heads hold more
+// accumulator and Q registers per wave and run fewer waves
+template <int D>
+constexpr int resident_max_waves() { return D == 32 ? 12 : D == 64 ? 8 : 4; }
 constexpr int kRing = 3;                  // 32-key units of bias in flight per wave
-constexpr bool kResidentSplit = true;     // P as two bf16 planes in the product with V
 constexpr int kBiasRow = 32 + 4;          // floats per row of a wave's bias buffer (16-byte pad)
 
 template <int D>
@@ -65,33 +71,30 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 
 // Bytes of LDS a resident head of n keys takes: K and V rows (padded, rounded up to whole
 // 64-key blocks), then the key-mask values in log2 units, then the list of visited key
-// blocks and its length (padded to 16 bytes), then one bias buffer per wave when a bias is read.
+// blocks and its length (padded to 16 bytes), then the head's largest |v| (16 bytes), then one
+// bias buffer per wave when a bias is read.
 template <int D>
 __host__ __device__ constexpr long long resident_lds_bytes(int n, int bias_waves) {
   const long long rows = (long long)(n + kTileRows - 1) / kTileRows * kTileRows;
-  return rows * (WideLayout<D>::kKS + WideLayout<D>::kVS) * 2 + rows * 4 + (rows / kTileRows + 4) * 4 +
+  return rows * (WideLayout<D>::kKS + WideLayout<D>::kVS) * 2 + rows * 4 + (rows / kTileRows + 4) / 4 * 16 + 16 +
          (long long)bias_waves * 32 * kBiasRow * 4;
 }
 
 // Running state of a wave's 32 queries (lane l: query l % 32): O^T in D/32 accumulator
-// blocks, the row sums (all registers of a lane equal with the ones product, else a partial
-// per lane whose halves l and l + 32 are added at the end) and the running max (log2 units).
-template <int D, bool kSumMfma>
+// blocks, the lane's part of the row sum of the fp16 weights (lanes l and l + 32 are added at
+// the end) and the running max (log2 units).
+template <int D>
 struct WaveAcc {
   f32x16_v o[D / 32];
-  f32x16_v lsum;
-  float lpart;  // sum of the fp32 exponentials
-  float lq;     // sum of their bf16 roundings
+  float lq;   // sum of the fp16 weights the product used
   float m2;   // running max (log2 units), -inf while no finite score has been seen
   float ref;  // the reference the exponentials are taken against: m2, or 0 while m2 = -inf
 };
 
-template <int D, bool kSumMfma>
-__device__ __forceinline__ void wave_acc_init(WaveAcc<D, kSumMfma>& st) {
+template <int D>
+__device__ __forceinline__ void wave_acc_init(WaveAcc<D>& st) {
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) st.o[c] = f32x16_v{};
-  st.lsum = f32x16_v{};
-  st.lpart = 0.f;
   st.lq = 0.f;
   st.m2 = -INFINITY;
   st.ref = 0.f;
@@ -116,82 +119,69 @@ __device__ __forceinline__ void wide_qk(f32x16_v (&s)[NH], const uint16_t* kb, c
   if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
 }
 
-// Online-softmax update with the scores s of NH 32-key halves (log2 units, bias and masks
-// applied; slot r of half hh of lane l is key 32hh + 8(r/4) + 4(l/32) + r%4), then
-// O^T += V^T P^T with their V rows starting at vb in LDS (row stride VS bf16).
-// kRel: the scores arrive relative to st.ref (x - ref), so exponentials need no subtraction
-// unless the reference moves (a rare, wave-uniform branch). kSplit: P enters the product as
-// two bf16 planes, p = hi + lo (about 16 mantissa bits), so that O carries the fp32 weights
-// (for head sizes where the matrix cores have time to spare).
-template <int D, int VS, int NH, bool kSumMfma, bool kRel = false, bool kSplit = false>
-__device__ __forceinline__ void wide_softmax_pv(f32x16_v (&s)[NH], const uint16_t* vb, WaveAcc<D, kSumMfma>& st,
-                                                int lane) {
+// fp16 weights exp2(s) of NH 32-key halves (k-step ss of half hh takes registers 8ss .. 8ss + 7)
+// and the sum of the rounded values.
+template <int NH>
+__device__ __forceinline__ float weights_f16(const f32x16_v (&s)[NH], f16x8_v (&pb)[NH][2]) {
+  float pq = 0.f;
+  const f16x2_v ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2_v pp = {__builtin_amdgcn_exp2f(s[hh][8 * ss + 2 * i]),
+                            __builtin_amdgcn_exp2f(s[hh][8 * ss + 2 * i + 1])};
+        const f16x2_v h2 = __builtin_convertvector(pp, f16x2_v);
+        pb[hh][ss][2 * i] = h2[0];
+        pb[hh][ss][2 * i + 1] = h2[1];
+        pq = __builtin_amdgcn_fdot2(h2, ones, pq, false);
+      }
+  return pq;
+}
+
+// Online-softmax update with the scores s of NH 32-key halves, given in log2 units relative to
+// the lane's reference st.ref (bias and masks applied; slot r of half hh of lane l is key
+// 32hh + 8(r/4) + 4(l/32) + r%4), then O^T += V^T P^T with their fp16 V rows starting at vb in
+// LDS (row stride VS halves). The weights are taken against the current reference at once,
+// while the block maximum is formed beside them; only when that maximum exceeds the running
+// max by more than kSlack (a rare, wave-uniform branch: a lane's first finite scores, or a
+// large increase) does the reference move, O and the sum get rescaled, the weights get
+// recomputed and cref, the initial accumulator value -ref / scale2 that makes the next
+// scores relative, get reset. Otherwise every weight is at most 2^kSlack.
+template <int D, int VS, int NH>
+__device__ __forceinline__ void wide_softmax_pv(f32x16_v (&s)[NH], const uint16_t* vb, WaveAcc<D>& st,
+                                                f32x16_v& cref, float inv_scale2, int lane) {
   constexpr int OB = D / 32;
   const int g = lane / 32, c32 = lane % 32;
+  f16x8_v pb[NH][2];
+  float pq = weights_f16<NH>(s, pb);
   float mx = -INFINITY;
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][r]);
-  mx = across_halves<OpMax>(mx);
-  if constexpr (kRel) mx += st.ref;  // absolute block max
-  // the running max moves only when the block max exceeds it by more than kSlack
-  const float mn = (mx > st.m2 + kSlack) ? mx : st.m2;
-  const float ref = mn == -INFINITY ? 0.f : mn;
-  const float alpha = __builtin_amdgcn_exp2f(st.m2 - ref);  // 0 while nothing is accumulated
-  const float shift = kRel ? ref - st.ref : ref;  // subtracted from s before the exponential
-  st.m2 = mn;
-  st.ref = ref;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+  mx = across_halves<OpMax>(mx) + st.ref;  // absolute block max
+  const bool moves = mx > st.m2 + kSlack;
+  if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+    const float mn = moves ? mx : st.m2;
+    const float ref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(st.m2 - ref);  // 1 if unmoved, 0 if nothing yet
 #pragma unroll
     for (int c = 0; c < OB; ++c) st.o[c] *= alpha;
-    if constexpr (kSumMfma) {
-      st.lsum *= alpha;
-    } else {
-      st.lpart *= alpha;
-      st.lq *= alpha;
-    }
-    if constexpr (kRel) {
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh) s[hh] -= shift;
-    }
-  }
-  if constexpr (!kRel) {
+    st.lq *= alpha;
+    const float shift = ref - st.ref;
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) s[hh] -= shift;
+    st.m2 = mn;
+    st.ref = ref;
+    cref = f32x16_v{} - ref * inv_scale2;
+    pq = weights_f16<NH>(s, pb);
   }
-  // P^T to bf16: k-step ss of half hh takes registers 8ss .. 8ss + 7
-  bf16x8_v pb[NH][2], pl[NH][2];
-  float ps = 0.f, pq = 0.f;
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      uint32_t w[4], wl[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(s[hh][8 * ss + 2 * i]);
-        const float p1 = __builtin_amdgcn_exp2f(s[hh][8 * ss + 2 * i + 1]);
-        w[i] = pack2_bf16(p0, p1);
-        if constexpr (kSplit) wl[i] = pack2_bf16(p0 - bf16lo(w[i]), p1 - bf16hi(w[i]));
-        // two row sums: of the bf16 values the product uses (two per dot2 instruction), which
-        // normalises O, and of the fp32 values, from which lse = m + log(sum) is formed (the
-        // value a backward pass recomputing exp(s - lse) in fp32 expects)
-        if constexpr (!kSumMfma) {
-          if constexpr (!kSplit) pq = dot2_bf16(w[i], 0x3f803f80u, pq);
-          ps += p0 + p1;
-        }
-      }
-      pb[hh][ss] = __builtin_bit_cast(bf16x8_v, (u32x4_v){w[0], w[1], w[2], w[3]});
-      if constexpr (kSplit) pl[hh][ss] = __builtin_bit_cast(bf16x8_v, (u32x4_v){wl[0], wl[1], wl[2], wl[3]});
-    }
-  if constexpr (!kSumMfma) {
-    st.lpart += ps;
-    st.lq += kSplit ? ps : pq;
-  }
-  // O^T += V^T P^T (and row sums += 1 P^T). Slot i of lane l in k-step ss of half hh is key
+  st.lq += pq;
+  // O^T += V^T P^T. Slot i of lane l in k-step ss of half hh is key
   // 32hh + 16ss + 8(i/4) + 4(l/32) + i%4: two transposing reads of four keys each
-  const bf16x8_v ones = __builtin_bit_cast(bf16x8_v, (u32x4_v){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
@@ -203,30 +193,23 @@ __device__ __forceinline__ void wide_softmax_pv(f32x16_v (&s)[NH], const uint16_
         typedef __attribute__((address_space(3))) i16x4_v lds_v4;
         const i16x4_v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vb + key * VS + col));
         const i16x4_v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vb + (key + 8) * VS + col));
-        const bf16x8_v va = __builtin_bit_cast(
-            bf16x8_v, (i16x8_v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-        st.o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hh][ss], st.o[c], 0, 0, 0);
-        if constexpr (kSplit) st.o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pl[hh][ss], st.o[c], 0, 0, 0);
+        const f16x8_v va = __builtin_bit_cast(
+            f16x8_v, (i16x8_v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        st.o[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[hh][ss], st.o[c], 0, 0, 0);
       }
-      if constexpr (kSumMfma) st.lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[hh][ss], st.lsum, 0, 0, 0);
     }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// O = O^T / l and lse for the lane's query q of head t (if q < n).
-template <int D, bool kSumMfma>
-__device__ __forceinline__ void wide_store(WaveAcc<D, kSumMfma>& st, const FusedArgs& a, int t, int q,
-                                           int lane) {
+// O = O^T / l (times vunscale, which undoes the V scaling) and lse for the lane's query q of
+// head t (if q < n).
+template <int D>
+__device__ __forceinline__ void wide_store(WaveAcc<D>& st, const FusedArgs& a, int t, int q, int lane,
+                                           float vunscale) {
   const int g = lane / 32;
-  float ltot, lnorm;
-  if constexpr (kSumMfma) {
-    ltot = lnorm = st.lsum[0];
-  } else {
-    ltot = across_halves<OpSum>(st.lpart);
-    lnorm = across_halves<OpSum>(st.lq);
-  }
+  const float ltot = across_halves<OpSum>(st.lq);
   if (q >= a.n) return;
-  const float inv = (st.m2 == -INFINITY) ? 0.f : 1.0f / lnorm;
+  const float inv = (st.m2 == -INFINITY) ? 0.f : vunscale / ltot;
   if (a.lse && g == 0)
     a.lse[(size_t)t * a.n + q] = (st.m2 == -INFINITY) ? -INFINITY : (st.m2 / kLog2e + logf(ltot));
   float* orow = a.out + ((size_t)t * a.n + q) * D;
@@ -243,13 +226,12 @@ __device__ __forceinline__ void wide_store(WaveAcc<D, kSumMfma>& st, const Fused
 // One workgroup: head t, queries [q_base, q_base + 32 * waves). K, V (and the key mask) of the
 // head are staged into LDS once; then wave w computes queries q_base + 32w + (0..31).
 template <int D, bool kBias, bool kMask, bool kVec4>
-__global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_resident_kernel(FusedArgs a,
+__global__ __launch_bounds__(kWave * resident_max_waves<D>()) void fused_dense_resident_kernel(FusedArgs a,
                                                                                  int chunks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int KS = WideLayout<D>::kKS, VS = WideLayout<D>::kVS;
   constexpr int KC = D / 16;   // 16-dim k-steps of S^T = K Q^T
   constexpr int C8 = D / 8;    // 16-byte chunks per K/V row
-  constexpr bool kSum = kResidentSumMfma;
   const int n = a.n;
   const int nthreads = blockDim.x;
   const int nwaves = nthreads / kWave;
@@ -268,7 +250,8 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
   uint16_t* vs = ks + (size_t)rows * KS;
   float* mk = reinterpret_cast<float*>(vs + (size_t)rows * VS);
   int* lst = reinterpret_cast<int*>(mk + rows);  // visited blocks, then their count
-  float* bias_buf = reinterpret_cast<float*>(lst + (nblk_all + 4) / 4 * 4);
+  unsigned* vmax = reinterpret_cast<unsigned*>(lst + (nblk_all + 4) / 4 * 4);  // largest |v| (bf16 bits)
+  float* bias_buf = reinterpret_cast<float*>(vmax + 4);
 
   // keys at or past the batch's key length are masked; blocks past it are not visited
   const int nvalid = a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
@@ -293,8 +276,12 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
   // ---- stage K, V (rows past n are zero) and the key mask (log2 units) of head t
   const uint16_t* kt = static_cast<const uint16_t*>(a.k) + head;
   const uint16_t* vt = static_cast<const uint16_t*>(a.v) + head;
-  // four chunks of K and of V per thread and pass, all loads issued before the stores
+  // four chunks of K and of V per thread and pass, all loads issued before the stores; V is
+  // staged as bf16 first, and the thread's largest |v| (bf16 magnitude bits, which order as
+  // the magnitudes do) is kept for the head's scale
   constexpr int kU = 4;
+  if (threadIdx.x == 0) *vmax = 0u;
+  unsigned my_vmax = 0u;
   for (int i0 = threadIdx.x; i0 < rows * C8; i0 += kU * nthreads) {
     u32x4_v kx[kU], vx[kU];
 #pragma unroll
@@ -313,6 +300,8 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
         *reinterpret_cast<u32x4_v*>(&ks[r * KS + c]) = kx[u];
         *reinterpret_cast<u32x4_v*>(&vs[r * VS + c]) = vx[u];
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) my_vmax = max(my_vmax, max(vx[u][e] & 0x7fffu, (vx[u][e] >> 16) & 0x7fffu));
     }
   }
   const float* kmrow = kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
@@ -322,6 +311,7 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
     mk[j] = x;
   }
   __syncthreads();
+  atomicMax(vmax, my_vmax);
   // a key block is visited if one of its keys has a mask value above -inf; wave 0 writes the
   // list of visited blocks (ascending) and their count
   if (wave == 0) {
@@ -337,6 +327,26 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
   }
   __syncthreads();
   const int nlive = __builtin_amdgcn_readfirstlane(lst[nblk_all]);
+  // V to fp16 times 2^e, e = 15 - (exponent of the largest |v|): that value lands in
+  // [2^14, 2^15); a zero, infinite or NaN maximum leaves V unscaled
+  int vexp = 0;
+  {
+    const unsigned vm = *vmax;
+    const int bexp = (int)(vm >> 7) & 0xff;  // biased exponent of the bf16 maximum
+    if (vm != 0u && bexp != 0xff) vexp = clampi(141 - max(bexp, 1), -126, 126);
+  }
+  const float vscale = __uint_as_float((unsigned)(vexp + 127) << 23);
+  for (int i = threadIdx.x; i < rows * C8; i += nthreads) {
+    const int r = i / C8, c = (i % C8) * 8;
+    u32x4_v x = *reinterpret_cast<const u32x4_v*>(&vs[r * VS + c]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2_v f = {bf16lo(x[e]) * vscale, bf16hi(x[e]) * vscale};
+      x[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_v));
+    }
+    *reinterpret_cast<u32x4_v*>(&vs[r * VS + c]) = x;
+  }
+  __syncthreads();
 
   if (!active) return;
   // The visited key blocks are walked as 32-key units (two per block). The bias of a unit is
@@ -346,7 +356,12 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
   // which the lanes read their slots in the layout of the score accumulator. The loop is
   // unrolled by the ring length so that every slot is a fixed register set.
   const int nunits = 2 * nlive;
-  auto unit_k0 = [&](int i) -> int { return lst[i >> 1] * kTileRows + 32 * (i & 1); };
+  // the visited blocks, one per lane (a head here has at most 64 key blocks), so that a
+  // unit's first key is a scalar read of a lane instead of an LDS round trip
+  const int lst_lane = lane < nblk_all ? lst[lane] : 0;
+  auto unit_k0 = [&](int i) -> int {
+    return __builtin_amdgcn_readlane(lst_lane, i >> 1) * kTileRows + 32 * (i & 1);
+  };
   float* bbuf = bias_buf + (size_t)wave * 32 * kBiasRow;
   const int crow = lane / 8, cch = lane % 8;  // coalesced layout: rows crow + 8ii, keys 4 cch + e
   f32x4_v br[kRing][4];
@@ -378,18 +393,22 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
       }
     }
   };
+  // the loads are issued unconditionally (past the last unit they repeat it), so that the
+  // number of loads in flight at every wait is the same on every path through the loop
+  if (nunits > 0) {
 #pragma unroll
-  for (int r = 0; r < kRing - 1; ++r)
-    if (r < nunits) load_unit_bias(br[r], r);
-  if (nunits > 0) write_unit_bias(br[0], 0);
-  WaveAcc<D, kSum> st;
+    for (int r = 0; r < kRing - 1; ++r) load_unit_bias(br[r], min(r, nunits - 1));
+    write_unit_bias(br[0], 0);
+  }
+  WaveAcc<D> st;
   wave_acc_init(st);
+  const float inv_scale2 = 1.0f / scale2;
   // S^T starts from -ref / scale2 in every slot, so that the scores come out relative to the
   // reference of the exponentials (log2 units after the scale)
   f32x16_v cref = f32x16_v{};
   // step i: load unit i + kRing - 1 into slot bx, compute unit i, write unit i + 1 (slot bw)
   auto step = [&](int i, f32x4_v (&bw)[4], f32x4_v (&bx)[4]) {
-    if (i + kRing - 1 < nunits) load_unit_bias(bx, i + kRing - 1);
+    load_unit_bias(bx, min(i + kRing - 1, nunits - 1));
     const int k0 = unit_k0(i);
     f32x16_v su[1];
     wide_qk<D, KS, 1>(su, ks + (size_t)k0 * KS, qb, lane, cref);
@@ -404,26 +423,26 @@ __global__ __launch_bounds__(kWave * kResidentMaxWaves) void fused_dense_residen
 #pragma unroll
       for (int e = 0; e < 4; ++e) su[0][4 * u + e] = fmaf(su[0][4 * u + e], scale2, add[u][e]);
     if (i + 1 < nunits) write_unit_bias(bw, i + 1);  // after this unit's reads of the buffer
-    const float ref0 = st.ref;
-    wide_softmax_pv<D, VS, 1, kSum, true, kResidentSplit>(su, vs + (size_t)k0 * VS, st, lane);
-    if (st.ref != ref0) cref = f32x16_v{} - st.ref / scale2;  // (per lane; rare)
+    wide_softmax_pv<D, VS, 1>(su, vs + (size_t)k0 * VS, st, cref, inv_scale2, lane);
   };
-  static_assert(kRing == 3, "the unrolled loop below names three ring slots");
+  // unrolled by the ring length: step i + r writes slot (r + 1) % kRing and loads into slot
+  // (r + kRing - 1) % kRing, fixed registers in every copy of the body
   for (int i = 0; i < nunits; i += kRing) {
-    step(i, br[1], br[2]);
-    if (i + 1 >= nunits) break;
-    step(i + 1, br[2], br[0]);
-    if (i + 2 >= nunits) break;
-    step(i + 2, br[0], br[1]);
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      if (i + r >= nunits) break;
+      step(i + r, br[(r + 1) % kRing], br[(r + kRing - 1) % kRing]);
+    }
   }
   mfma_drain();
-  wide_store<D, kSum>(st, a, t, q0 + c32, lane);
+  wide_store<D>(st, a, t, q0 + c32, lane, __uint_as_float((unsigned)(127 - vexp) << 23));
 }
 
 template <int D, bool kBias, bool kMask, bool kVec4>
 hipError_t launch_resident(const sa_problem& p, const FusedArgs& a, hipStream_t s) {
   const int waves_per_head = (p.n + 31) / 32;
-  const int per_wg = (waves_per_head + kResidentMaxWaves - 1) / kResidentMaxWaves;  // per head
+  constexpr int kMaxW = resident_max_waves<D>();
+  const int per_wg = (waves_per_head + kMaxW - 1) / kMaxW;  // workgroups per head
   const int nw = (waves_per_head + per_wg - 1) / per_wg;             // waves per workgroup
   const long long lds = resident_lds_bytes<D>(p.n, kBias ? nw : 0);
   const dim3 grid((unsigned)((long long)p.B * p.H * per_wg)), block(kWave * nw);
@@ -457,16 +476,21 @@ bool fused_resident_supported(const sa_problem& p) {
   if (p.row_ptr || p.dtype != SA_BF16 || p.n <= 0) return false;
   if (p.bias && (long long)p.n * p.n * 4 > kMaxBufBytes) return false;
   const int waves_per_head = (p.n + 31) / 32;
-  const int per_wg = (waves_per_head + kResidentMaxWaves - 1) / kResidentMaxWaves;
-  const int bw = p.bias ? (waves_per_head + per_wg - 1) / per_wg : 0;  // waves with a bias buffer
+  auto lds_of = [&](auto dtag) -> long long {
+    constexpr int D = decltype(dtag)::value;
+    constexpr int kMaxW = resident_max_waves<D>();
+    const int per_wg = (waves_per_head + kMaxW - 1) / kMaxW;
+    const int bw = p.bias ? (waves_per_head + per_wg - 1) / per_wg : 0;  // waves with a bias buffer
+    return resident_lds_bytes<D>(p.n, bw);
+  };
   long long lds = 0;
   switch (p.d) {
-    case 32: lds = resident_lds_bytes<32>(p.n, bw); break;
-    case 64: lds = resident_lds_bytes<64>(p.n, bw); break;
-    case 128: lds = resident_lds_bytes<128>(p.n, bw); break;
+    case 32: lds = lds_of(std::integral_constant<int, 32>{}); break;
+    case 64: lds = lds_of(std::integral_constant<int, 64>{}); break;
+    case 128: lds = lds_of(std::integral_constant<int, 128>{}); break;
     default: return false;
   }
-  return lds <= kResidentLds;
+  return lds <= kResidentLds && (p.n + kTileRows - 1) / kTileRows <= kWave;
 }
 
 hipError_t launch_fused_resident(const sa_problem& p, const void* q, const void* k, const void* v,
