@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsa.so")
+# SA_LIBRARY names another build of the same library (e.g. one whose host code carries
+# address and undefined-behaviour sanitizers); by default the in-tree libsa.so
+LIB_PATH = os.environ.get("SA_LIBRARY") or os.path.join(_HERE, "libsa.so")
 
 SA_OK = 0
 SA_ERR_NULL = -1

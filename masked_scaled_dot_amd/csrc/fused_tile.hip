@@ -5,7 +5,8 @@
 //    sparse tiles run the vector routine of fused_row.h per row, and long rows are cut into
 //    segments whose partial states are merged by the last segment to finish;
 //  * block CSR of 64x64 tiles: the block-row's stored blocks (each a dense 64x64 product,
-//    block-sparse attention in the gluon-nlp issue replies);
+//    block-sparse attention in the gluon-nlp issue replies); a plan tile of element CSR whose
+//    rows hold the same whole 64x64 blocks takes this path with the plan's block list;
 //  * dense with additive pair bias [H, n, n] and key mask [B, 1|H, n] (flash-attention PR
 //    "support attentions in AlphaFold2": bias [1,H,Lq,Lk], key mask [B,1|H,1,Lk]).
 // The softmax is the running-max / running-sum form with one division at the end
@@ -14,7 +15,8 @@
 // A workgroup (4 waves) owns 64 queries of one head; wave w owns queries 16w..16w+15. For
 // every key block:
 //   1. the block's K and V rows (loaded into registers one block ahead) are stored
-//      row-major in a double-buffered LDS stage, behind one LDS-only barrier;
+//      row-major in a single LDS stage (one stage keeps more workgroups resident), between
+//      two LDS-only barriers;
 //   2. each wave forms S^T = K Q^T for its 16 queries with v_mfma_f32_16x16x32_bf16
 //      (A = K rows from LDS, B = the wave's Q held in registers); the accumulator gives lane
 //      l query l%16 and keys 16t + 4(l/16) + {0..3};

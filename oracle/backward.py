@@ -27,7 +27,7 @@ over them (the flash-attention PR's bias-gradient question):
 Rows without a finite score have W = 0, so all their terms vanish.
 
 Two evaluations, pinned against each other and against finite differences in
-``tests/test_oracle_pins.py``:
+``tests/test_oracle_backward_pins.py``:
 
 * :func:`grads_autograd` -- torch autograd, in fp64 on the CPU, of the dense
   definition written with torch operations (the forward's formulas, nothing else);
