@@ -253,39 +253,41 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__
   __syncthreads();
   if (s_isblk) {
     const int len0 = s_len[0], e_lo = s_rp[0], e_hi = s_rp[last_row];
-    bool ok = true;
-    for (int e0 = e_lo + tid; e0 < e_hi; e0 += 4 * (int)blockDim.x) {
-      int c[4], cref[4], cprev[4], qq[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * (int)blockDim.x;
-        c[u] = cref[u] = cprev[u] = qq[u] = 0;
-        if (e < e_hi) {
-          int l = 0, h = last_row;  // the entry's row
-          while (h - l > 1) {
-            const int mid = (l + h) >> 1;
-            if (s_rp[mid] <= e) l = mid;
-            else h = mid;
-          }
-          const int q = e - s_rp[l];
-          qq[u] = q;
-          c[u] = col_idx[e];
-          cref[u] = col_idx[e_lo + min(q, len0 - 1)];
-          cprev[u] = col_idx[e_lo + max(q - 1, 0)];
-        }
+    // first the first row's columns: whole key blocks (column = block start + slot), the cut
+    // last block ending at n; most tiles fail here, reading one row
+    if (tid < kWave) {
+      bool ok = true;
+      for (int q = tid; q < len0; q += kWave) {
+        const int c = col_idx[e_lo + q];
+        const int cp = col_idx[e_lo + max(q - 1, 0)];
+        ok = ok && c < n && (c & (kTileRows - 1)) == (q & (kTileRows - 1)) &&
+             ((q & (kTileRows - 1)) == 0 || c == cp + 1);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (e0 + u * (int)blockDim.x >= e_hi) break;
-        const int q = qq[u];
-        ok = ok && c[u] == cref[u] && (c[u] & (kTileRows - 1)) == (q & (kTileRows - 1)) &&
-             ((q & (kTileRows - 1)) == 0 || c[u] == cprev[u] + 1) && c[u] < n;
-      }
+      const int w = len0 - (len0 - 1) / kTileRows * kTileRows;
+      if (tid == 0 && w < kTileRows && col_idx[e_lo + len0 - 1] + 1 != n) ok = false;
+      if (__builtin_amdgcn_ballot_w64(!ok) != 0ull && tid == 0) s_isblk = 0;
     }
-    // a cut last block must end at n
-    const int w = len0 - (len0 - 1) / kTileRows * kTileRows;
-    if (tid == 0 && w < kTileRows && col_idx[e_lo + len0 - 1] + 1 != n) ok = false;
-    if (!ok) atomicAnd(&s_isblk, 0);
+    __syncthreads();
+    // then every other row holds the same columns (the row's length equals the first's)
+    if (s_isblk) {
+      bool ok = true;
+      for (int e0 = e_lo + len0 + tid; e0 < e_hi && ok; e0 += 4 * (int)blockDim.x) {
+        int c[4], cref[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = e0 + u * (int)blockDim.x;
+          c[u] = cref[u] = 0;
+          if (e < e_hi) {
+            const int q = (e - e_lo) % len0;  // rows are len0 entries each
+            c[u] = col_idx[e];
+            cref[u] = col_idx[e_lo + q];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ok = ok && c[u] == cref[u];
+      }
+      if (!ok) atomicAnd(&s_isblk, 0);
+    }
   }
   const int F = s_far_total;
   int U = 0;
