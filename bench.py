@@ -815,6 +815,9 @@ def main():
                 "avg_launch_us": round(ev_us, 2),
                 "hbm_frac": round(algo_bytes / (ev_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "source_hash": source_hash(bsr_src)}
+    if roofline["traffic"]:  # the bytes that cross the L2 boundary, per second of the launch
+        roofline["traffic_GB_s"] = round(roofline["traffic"] / (ev_us * 1e-6) / 1e9, 1)
+        roofline["traffic_hbm_frac"] = round(roofline["traffic_GB_s"] / HBM_PEAK_GBS, 4)
     log(f"bsr_n16384 fused: {ev_us:.1f} us per launch ({args.steps} back to back), warm median "
         f"{warm:.1f}, cold median {cold:.1f}; {achieved:.0f} TFLOP/s")
 
