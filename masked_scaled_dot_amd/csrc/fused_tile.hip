@@ -62,9 +62,11 @@ struct FusedSmem1 {
   static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
   alignas(16) uint16_t k[1][kTileRows * kKStride];
   alignas(16) uint16_t v[1][kTileRows * kVStride];
-  int bcol[kBsrCached];  // block CSR: the block-row's first stored block-columns
+  int bcol[kBsrCached];  // block CSR: the block-row's first stored block-columns; dense with a
+                         // key mask: the key blocks to visit
   int far[kTileRows];    // element CSR: the gathered block's key rows
   int live[kTileRows];   // element CSR: 1 if the tile writes this query's output
+  int nvis;              // dense with a key mask: number of key blocks to visit
 };
 
 // Waves per SIMD the block kernels are compiled for (caps the registers at 512 / waves).
@@ -246,11 +248,43 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   // dense and block CSR: keys at or past the batch's key length (n without one) are masked,
   // and the dense kind stops at the block that holds the last valid key
   const int nvalid = K != kFusedCsr && a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
-  const int nblk = K == kFusedBsr ? nbk
-                   : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv))
-                                    : (nvalid + kTileRows - 1) / kTileRows;
+  int nblk = K == kFusedBsr ? nbk
+             : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv))
+                              : (nvalid + kTileRows - 1) / kTileRows;
   if constexpr (K == kFusedBsr)
     for (int i = threadIdx.x; i < min(nblk, kBsrCached); i += kThreads) sm.bcol[i] = bcols[i];
+  // dense with a key mask: a key block whose mask values (below the key length) are all -inf
+  // is not visited (key-padding discussion of the AlphaFold2 pull request); the visited
+  // blocks are listed in ascending order
+  const bool listed = K == kFusedDense && kMask && nblk <= kBsrCached;
+  if constexpr (K == kFusedDense && kMask) {
+    if (listed) {
+      const float* kmr = a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n;
+      const int lane = threadIdx.x % kWave;
+      for (int j0 = 0; j0 < nblk; j0 += kThreads / 16) {  // 16 threads per block, 4 keys each
+        const int j = j0 + threadIdx.x / 16, key = kTileRows * j + 4 * (threadIdx.x % 16);
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) any = any || (j < nblk && key + e < nvalid && kmr[key + e] > -INFINITY);
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(any);
+        if (threadIdx.x % 16 == 0 && j < nblk) sm.bcol[j] = ((bal >> (lane & ~15)) & 0xffffull) != 0ull;
+      }
+      __syncthreads();
+      if (threadIdx.x < kWave) {  // compact in place: every flag of a chunk is read before any write
+        const int lane = threadIdx.x;
+        int base = 0;
+        for (int c0 = 0; c0 < nblk; c0 += kWave) {
+          const bool f = c0 + lane < nblk && sm.bcol[c0 + lane] != 0;
+          const unsigned long long bal = __builtin_amdgcn_ballot_w64(f);
+          if (f) sm.bcol[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = c0 + lane;
+          base += __builtin_popcountll(bal);
+        }
+        if (lane == 0) sm.nvis = base;
+      }
+      __syncthreads();
+      nblk = __builtin_amdgcn_readfirstlane(sm.nvis);
+    }
+  }
   if constexpr (K == kFusedCsr) {
     if (threadIdx.x < kTileRows) {
       const int r = threadIdx.x, row = row0 + r;
@@ -289,7 +323,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
       return __builtin_amdgcn_readfirstlane(
           clampi(jj < kBsrCached ? sm.bcol[jj] : bcols[jj], 0, ntiles - 1) * kTileRows);
     else if constexpr (K == kFusedCsr) return (tv.kb_lo + jj) * kTileRows;
-    else return jj * kTileRows;
+    else return __builtin_amdgcn_readfirstlane((listed ? sm.bcol[jj] : jj) * kTileRows);
   };
   // lane-constant parts of the offsets: chunk u of the thread is row i / (D/8), part i % (D/8)
   int kvoff[CH];

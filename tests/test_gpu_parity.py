@@ -215,6 +215,32 @@ def test_empty_and_fully_masked_rows(dtype):
     assert lse[2, 7] == -np.inf and lse[0, 0] == -np.inf
 
 
+@pytest.mark.parametrize("bias", [True, False], ids=["bias", "mask_only"])
+@pytest.mark.parametrize("n,d", [(1000, 32), (600, 64)])
+def test_dense_tile_skips_masked_key_blocks(n, d, bias):
+    """Dense pattern with heads too large to keep in LDS (the tile kernel): key blocks whose
+    key-mask values are all -inf are skipped -- an interior block, the padded tail, and a
+    batch whose keys are all masked (its rows give O = 0 and lse = -inf)."""
+    import dataclasses
+    p = gen.make("evoformer_l384", B=3, H=2, n=n, d=d, bias=bias)
+    km = np.zeros((3, 1, n), np.float32)
+    km[0, 0, 128:192] = -np.inf        # one whole interior key block
+    km[0, 0, 70:75] = -np.inf          # part of a block
+    km[1, 0, n - 300:] = -np.inf       # a tail longer than four blocks
+    km[2, 0, :] = -np.inf              # every key
+    p = dataclasses.replace(p, key_mask=km, key_mask_heads=1)
+    say(f"dense tile with masked key blocks: n={n} d={d} bias={bias}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, ("dense",), want_weights=False,
+                                 **dp.oracle_args())
+    eo = check(O, ref["O"], p.dtype, "context")
+    el = check(lse, ref["lse"], p.dtype, "lse")
+    assert np.all(O[4:6] == 0) and np.all(lse[4:6] == -np.inf)  # batch 2: heads 4 and 5
+    say(f"PARITY dense_tile_masked_blocks_n{n}_d{d} fused context max_abs={eo[0]:.3e} mean_abs={eo[1]:.3e}"
+        f" lse max_abs={el[0]:.3e}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_diagonal_only_rows_are_exact(dtype):
     n, d = 300, 32
