@@ -97,9 +97,8 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *            masked for every head and query of batch b, as if the key mask held -inf there
  *            (the one-int-per-batch key padding of the AlphaFold2 pull request, key-padding
  *            discussion). Read by sa_sddmm and sa_fused_forward (the dense and block-CSR
- *            tiles skip the key blocks past the length); it may be combined with key_mask.
- *            With an element-CSR plan, sa_sddmm and sa_fused_forward take their row
- *            kernels (no plan) when seqlen_k is set. */
+ *            tiles skip the key blocks past the length; the element-CSR plan tiles mask
+ *            the keys past it); it may be combined with key_mask. */
 typedef struct sa_problem {
   int32_t B, H, n, d;
   int32_t dtype;           /* sa_dtype of q, k, v                                     */

@@ -245,9 +245,9 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   // ALUs after the loop, more as one gathered block)
   const int nbc = K == kFusedCsr ? tv.kb_hi - tv.kb_lo : 0;
   const bool far_vec = K == kFusedCsr && tv.nfar > 0 && tv.nfar <= kFarVec;
-  // dense and block CSR: keys at or past the batch's key length (n without one) are masked,
-  // and the dense kind stops at the block that holds the last valid key
-  const int nvalid = K != kFusedCsr && a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
+  // keys at or past the batch's key length (n without one) are masked, and the dense kind
+  // stops at the block that holds the last valid key
+  const int nvalid = a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
   int nblk = K == kFusedBsr ? nbk
              : K == kFusedCsr ? (far_vec ? nbc : tile_blocks(tv))
                               : (nvalid + kTileRows - 1) / kTileRows;
@@ -445,6 +445,17 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sc[tt][i] = ((tt < 2 ? blo : bhi) >> ((16 * tt + 4 * g + i) & 31)) & 1u ? sc[tt][i] : -INFINITY;
+      if (nvalid < n) {  // and so do keys at or past the key length
+        const bool gat = j >= nbc;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int slot = 16 * tt + 4 * g + i;
+            const int key = gat ? sm.far[slot] : block_k0(j) + slot;
+            sc[tt][i] = key < nvalid ? sc[tt][i] : -INFINITY;
+          }
+      }
     } else if (lim < kTileRows) {  // ragged or last valid block: keys at or past lim score -inf
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -536,7 +547,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
       x *= scale2;
       if constexpr (kBias) x = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, brow_off + kf * 4, 0, 0)), kLog2e, x);
       if constexpr (kMask) x = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mres, kf * 4, 0, 0)), kLog2e, x);
-      x = (fm >> f) & 1ull ? x : -INFINITY;
+      x = ((fm >> f) & 1ull) && kf < nvalid ? x : -INFINITY;
       const float mn = fmaxf(m2, x);
       const float ref = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m2 - ref);
@@ -652,8 +663,8 @@ bool fused_tile_supported(const sa_problem& p) {
   const long long kv = (long long)p.n * p.d * (p.dtype == SA_BF16 ? 2 : 4);
   const long long bias = p.bias ? (long long)p.n * p.n * 4 : 0;
   if (kv > kMaxBufBytes || bias > kMaxBufBytes) return false;
-  // plan-driven CSR (both dtypes); its tiles do not read key lengths
-  if (p.row_ptr && p.block == 1) return p.plan != nullptr && p.seqlen_k == nullptr;
+  // plan-driven CSR (both dtypes)
+  if (p.row_ptr && p.block == 1) return p.plan != nullptr;
   // block CSR and dense: bf16
   return p.dtype == SA_BF16;
 }

@@ -253,7 +253,10 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
   for (int kc = 0; kc < KC; ++kc)
     qb[kc] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4_v*>(qt + (size_t)my_q * D + 32 * kc + 8 * g));
   const float* brow = kBias ? a.bias + ((size_t)h * n + my_q) * n : nullptr;
-  const float* kmr = kMask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
+  const float* kmr = kMask && a.key_mask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n
+                                         : nullptr;
+  // keys at or past the batch's key length score -inf (the kMask variant carries them)
+  const int nvalid = a.seqlen_k ? __builtin_amdgcn_readfirstlane(clampi(a.seqlen_k[b], 0, n)) : n;
 
   const __amdgpu_buffer_rsrc_t outb = make_rsrc(a.scores + (size_t)t * a.nnz + e_lo, (e_hi - e_lo) * 4);
   float* orow = sm.out + lr * OS;                    // this lane's compacted row (step 3)
@@ -285,7 +288,8 @@ __device__ void sddmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, i
           const int slot = 16 * tt + 4 * g + i;
           const int kf = sm.far[slot], kc = min(k0 + slot, n - 1);
           const int key = gat ? kf : kc;
-          an[tt][i] = (kBias ? brow[key] : 0.f) + (kMask ? kmr[key] : 0.f);
+          an[tt][i] = (kBias ? brow[key] : 0.f) + (kMask && kmr ? kmr[key] : 0.f);
+          if (kMask && (gat ? kf : k0 + slot) >= nvalid) an[tt][i] = -INFINITY;
         }
     }
   };
@@ -577,15 +581,16 @@ hipError_t launch_t(const sa_problem& p, const void* q, const void* k, float* sc
   Args a{q, k, p.row_ptr, p.col_idx, scores, p.bias, p.key_mask, static_cast<const int*>(p.plan),
          p.seqlen_k, p.B, p.H, p.n, (long long)p.nnz, p.key_mask_heads, p.scale};
   const int BH = p.B * p.H;
-  if (p.plan && !p.seqlen_k) {  // the plan's tiles do not read key lengths
+  if (p.plan) {  // key lengths are applied by the kMask variant of the tiles
+    const bool masked = p.key_mask || p.seqlen_k;
     const long long ntiles = (p.n + kTileRows - 1) / kTileRows;
     const long long blocks = kLongWGs + ntiles * BH;
     const dim3 grid((unsigned)blocks), block(kThreads);
     if constexpr (sizeof(T) == 4)
       hipLaunchKernelGGL((sddmm_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
-    else if (!p.bias && !p.key_mask)
+    else if (!p.bias && !masked)
       hipLaunchKernelGGL((sddmm_plan_kernel<T, D, false, false>), grid, block, 0, s, a, BH);
-    else if (p.bias && p.key_mask)
+    else if (p.bias && masked)
       hipLaunchKernelGGL((sddmm_plan_kernel<T, D, true, true>), grid, block, 0, s, a, BH);
     else if (p.bias)
       hipLaunchKernelGGL((sddmm_plan_kernel<T, D, true, false>), grid, block, 0, s, a, BH);

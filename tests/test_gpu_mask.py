@@ -202,7 +202,23 @@ SEQLEN = {
     "csr": (lambda: gen.make("longformer_n4096", n=700, H=2, window=40), [650], False),
     "csr_with_key_mask": (lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
                                            bias=True, key_mask=True, pmax=40), [250, 299], True),
+    # a global-token column past the length: the plan's far columns (the gathered block and
+    # the few-columns epilogue) must mask it
+    "csr_far_cols_past_length": (lambda: gen.make("longformer_n4096", n=700, H=2, window=40,
+                                                  global_tokens=(0, 1, 690)), [650], False),
+    # rows longer than the plan's split threshold (segments) with a length
+    "csr_long_rows": (lambda: gen.make("longformer_n4096", n=2500, H=2, window=100), [1800], False),
+    # the element expansion of a block pattern (the plan's whole-block tiles)
+    "csr_whole_blocks": (lambda: _element(gen.make("bsr_n16384", n=640, H=2, d=64, extra=3)), [500], False),
 }
+
+
+def _element(p):
+    import copy
+    rp, ci = p.element_csr()
+    e = copy.copy(p)
+    e.row_ptr, e.col_idx, e.block = rp.astype(np.int32), ci.astype(np.int32), 1
+    return e
 
 
 @pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
@@ -221,7 +237,7 @@ def test_seqlen_k_fused(name, plan):
 
 
 @pytest.mark.parametrize("plan", [False, True], ids=["rows", "plan"])
-@pytest.mark.parametrize("name", ["csr", "csr_with_key_mask"])
+@pytest.mark.parametrize("name", ["csr", "csr_with_key_mask", "csr_far_cols_past_length", "csr_long_rows"])
 def test_seqlen_k_pipeline(name, plan):
     """SDDMM reads the key lengths (masked scores are exactly -inf); softmax and SpMM then
     need nothing more."""
