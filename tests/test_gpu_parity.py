@@ -241,6 +241,40 @@ def test_dense_tile_skips_masked_key_blocks(n, d, bias):
         f" lse max_abs={el[0]:.3e}")
 
 
+TINY_N = [1, 2, 5, 31, 33, 63, 65]
+
+
+@pytest.mark.parametrize("n", TINY_N)
+def test_tiny_sizes(n):
+    """Degenerate sizes, one case each through every path: the dense pattern with bias and key
+    mask (resident kernel at d = 32, 64, 128; the vector path in fp32), a window pattern
+    through the pipeline and the fused forward with and without a plan, and a block CSR of
+    one ragged block-row."""
+    cases = [("dense_d32", gen.make("evoformer_l384", B=2, H=2, n=n, pmax=n)),
+             ("dense_d64", gen.make("evoformer_l384", B=1, H=2, n=n, d=64)),
+             ("dense_d128", gen.make("evoformer_l384", B=1, H=1, n=n, d=128)),
+             ("dense_f32", gen.make("evoformer_l384", B=1, H=2, n=n, dtype="f32")),
+             ("window_bf16", gen.make("window_n128", n=n, H=2, d=64, dtype="bf16", window=3)),
+             ("window_f32", gen.make("window_n128", n=n, H=1, window=3)),
+             ("bsr", gen.make("bsr_n16384", n=n, H=2, d=64, extra=2))]
+    for name, p in cases:
+        say(f"tiny n={n} {name}")
+        pat = _pattern(p)
+        for plan in ((False, True) if p.row_ptr is not None and p.block == 1 else (False,)):
+            dp = DevProblem(p, plan=plan)
+            O, lse = dp.fused()
+            ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, pat, want_weights=False,
+                                         **dp.oracle_args())
+            check(O, ref["O"], p.dtype, f"{name} fused context plan={plan}")
+            check(lse, ref["lse"], p.dtype, f"{name} fused lse plan={plan}")
+            if p.row_ptr is not None and p.block == 1:
+                S, W, Op = dp.pipeline()
+                refc = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H,
+                                            **dp.oracle_args())
+                check(W, refc["W"], p.dtype, f"{name} weights plan={plan}")
+                check(Op, refc["O"], p.dtype, f"{name} pipeline context plan={plan}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_diagonal_only_rows_are_exact(dtype):
     n, d = 300, 32
