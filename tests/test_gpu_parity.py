@@ -37,6 +37,21 @@ def _pattern(p):
     return ("csr", p.row_ptr, p.col_idx)
 
 
+def _empty_block_rows(p, rows):
+    """p (a block-sparse pattern) with the given block-rows emptied."""
+    import copy
+    rp, ci = p.row_ptr.astype(np.int64), p.col_idx
+    lens = np.diff(rp)
+    keep = np.ones(len(ci), bool)
+    for r in rows:
+        keep[rp[r]:rp[r + 1]] = False
+        lens[r] = 0
+    e = copy.copy(p)
+    e.col_idx = ci[keep].astype(np.int32)
+    e.row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return e
+
+
 SMALL = {
     "window_n128_f32": lambda: gen.make("window_n128"),
     "window_f32_d64_ragged": lambda: gen.make("window_n128", n=131, d=64, H=2),
@@ -49,6 +64,9 @@ SMALL = {
     "bsr_bf16_d128_ragged": lambda: gen.make("bsr_n16384", n=64 * 6 + 21, H=2, extra=3),
     "bsr_bf16_d64": lambda: gen.make("bsr_n16384", n=64 * 8, H=2, d=64, extra=2),
     "bsr_f32_d32": lambda: gen.make("bsr_n16384", n=64 * 5, H=1, d=32, dtype="f32", extra=2),
+    # block-rows 1 and 6 (the ragged last one) store no block: their outputs are zero
+    "bsr_bf16_d32_empty_rows": lambda: _empty_block_rows(gen.make("bsr_n16384", n=64 * 6 + 5, H=2, d=32,
+                                                                  extra=2), (1, 6)),
     "evoformer_bf16_odd": lambda: gen.make("evoformer_l384", B=3, H=2, n=97),
     "evoformer_bf16": lambda: gen.make("evoformer_l384", B=2, H=8, n=384),
     "evoformer_f32_d64": lambda: gen.make("evoformer_l384", B=2, H=2, n=130, d=64, dtype="f32"),
