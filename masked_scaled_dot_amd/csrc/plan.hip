@@ -15,15 +15,13 @@
 //   * rows longer than kLongRow, cut into segments of at most kSeg entries, so that such a
 //     row is spread over many waves; their partial results merge deterministically through
 //     a per-(row, head) counter and scratch space kept in the plan.
-// Building takes three small kernels on the caller's stream.
+// Building takes two small kernels on the caller's stream.
 #include "common.h"
 #include "kernels.h"
 #include "plan_layout.h"
 
 namespace sa {
 namespace {
-
-constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ void row_range(const int* row_ptr, int i, long long nnz, long long& a,
                                           long long& b) {
@@ -74,29 +72,51 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int* __restrict__ 
   }
 }
 
-// Kernel B (one workgroup): long-row segments and the header.
-__global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __restrict__ row_ptr,
-                                                                 int n, long long nnz, int BH, int d,
-                                                                 long long cap_words,
-                                                                 int* __restrict__ plan) {
-  __shared__ int part_rows[kScanThreads];
-  __shared__ int part_segs[kScanThreads];
+// Long-row segments and the header, by one workgroup of kPlanThreads threads (the last
+// workgroup of the tile kernel): thread tid walks rows [tid * per, (tid + 1) * per), eight
+// row bounds in flight at a time, counts its long rows and their segments, and after a
+// prefix sum over the threads writes the segment records of its long rows.
+constexpr int kPlanThreads = 256;
+
+// Rows [r0, r1): visit(i, a, b) for each, with the bounds of row_range, loading the row
+// pointers eight ahead.
+template <class F>
+__device__ __forceinline__ void walk_rows(const int* row_ptr, int n, long long nnz, int r0, int r1, F&& visit) {
+  int raw = r0 < r1 ? row_ptr[r0] : 0;
+  for (int i0 = r0; i0 < r1; i0 += 8) {
+    int nx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nx[u] = row_ptr[min(i0 + u + 1, n)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u >= r1) break;
+      long long a = raw, b = nx[u];
+      a = a < 0 ? 0 : (a > nnz ? nnz : a);
+      b = b < a ? a : (b > nnz ? nnz : b);
+      visit(i0 + u, a, b);
+      raw = nx[u];
+    }
+  }
+}
+
+__device__ void plan_segs(const int* __restrict__ row_ptr, int n, long long nnz, int BH, int d,
+                          long long cap_words, int* __restrict__ plan) {
+  __shared__ int part_rows[kPlanThreads];
+  __shared__ int part_segs[kPlanThreads];
   const int tid = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
   const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
   int cl = 0, cs = 0;
-  for (int i = r0; i < r1; ++i) {
-    long long a, b;
-    row_range(row_ptr, i, nnz, a, b);
+  walk_rows(row_ptr, n, nnz, r0, r1, [&](int, long long a, long long b) {
     if (b - a > kLongRow) {
       ++cl;
       cs += (int)((b - a + kSeg - 1) / kSeg);
     }
-  }
+  });
   part_rows[tid] = cl;
   part_segs[tid] = cs;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int xr = tid >= off ? part_rows[tid - off] : 0;
     const int xs = tid >= off ? part_segs[tid - off] : 0;
     __syncthreads();
@@ -104,21 +124,19 @@ __global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __re
     part_segs[tid] += xs;
     __syncthreads();
   }
-  const int L = part_rows[kScanThreads - 1], S = part_segs[kScanThreads - 1];
+  const int L = part_rows[kPlanThreads - 1], S = part_segs[kPlanThreads - 1];
   const PlanSizes sz = plan_sizes(n, L, S, BH, d);
   const long long off_rows = kPlanHeaderWords, off_tiles = off_rows + sz.rows;
   const long long off_segs = off_tiles + sz.tiles, off_cnt = off_segs + sz.segs;
   const long long off_scr = off_cnt + sz.counters + sz.pad;
   const bool fits = sz.total <= cap_words;
-  if (fits) {
+  if (fits && cl > 0) {
     int lr = part_rows[tid] - cl;
     long long sg = part_segs[tid] - cs;
     int* segs = plan + off_segs;
-    for (int i = r0; i < r1; ++i) {
-      long long a, b;
-      row_range(row_ptr, i, nnz, a, b);
+    walk_rows(row_ptr, n, nnz, r0, r1, [&](int i, long long a, long long b) {
       const long long len = b - a;
-      if (len <= kLongRow) continue;
+      if (len <= kLongRow) return;
       const int ns = (int)((len + kSeg - 1) / kSeg);
       for (int s = 0; s < ns; ++s, ++sg) {
         int* it = segs + 8 * sg;
@@ -132,11 +150,11 @@ __global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __re
         it[7] = 0;
       }
       ++lr;
-    }
+    });
   }
   if (fits) {  // merge counters start at zero (a plain store loop, safe under graph capture)
     int* cnt = plan + off_cnt;
-    for (long long i = tid; i < (long long)L * BH; i += kScanThreads) cnt[i] = 0;
+    for (long long i = tid; i < (long long)L * BH; i += kPlanThreads) cnt[i] = 0;
   }
   if (tid == 0) {
     plan[kHMagic] = kPlanMagic;
@@ -162,10 +180,17 @@ __global__ __launch_bounds__(kScanThreads) void plan_segs_kernel(const int* __re
 // sorted distinct far columns (entries outside the core ranges, long rows excluded), and
 // whether the tile runs on matrix cores: at most 64 far columns (one gathered key block)
 // and core + far entries filling at least kDenseTile of the blocks' cells.
-__global__ __launch_bounds__(256) void plan_tiles_kernel(const int* __restrict__ row_ptr,
-                                                         const int* __restrict__ col_idx, int n,
-                                                         long long nnz, const int* __restrict__ rows,
-                                                         int* __restrict__ tiles, int ntiles) {
+__global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int* __restrict__ row_ptr,
+                                                                  const int* __restrict__ col_idx, int n,
+                                                                  long long nnz, int BH, int d,
+                                                                  long long cap_words, int* __restrict__ plan,
+                                                                  int ntiles) {
+  if ((int)blockIdx.x == ntiles) {  // the last workgroup: segments and header
+    plan_segs(row_ptr, n, nnz, BH, d, cap_words, plan);
+    return;
+  }
+  const int* rows = plan + kPlanHeaderWords;
+  int* tiles = plan + kPlanHeaderWords + plan_sizes(n, 0, 0, 0, d).rows;
   __shared__ int s_far[kFarMax];
   __shared__ int s_dist[kFarMax];
   __shared__ int s_pre[kTileRows + 1];
@@ -561,11 +586,9 @@ hipError_t launch_plan(const sa_problem& p, void* plan, size_t bytes, hipStream_
   if (cap < off_tiles + sz.tiles) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, p.row_ptr, p.col_idx,
                      n, (long long)p.nnz, pl + off_rows);
-  hipLaunchKernelGGL(plan_segs_kernel, dim3(1), dim3(kScanThreads), 0, s, p.row_ptr, n,
-                     (long long)p.nnz, BH, p.d, cap, pl);
-  if (ntiles > 0)
-    hipLaunchKernelGGL(plan_tiles_kernel, dim3(ntiles), dim3(256), 0, s, p.row_ptr, p.col_idx, n,
-                       (long long)p.nnz, pl + off_rows, pl + off_tiles, ntiles);
+  // the tiles and, in one more workgroup beside them, the segments and the header
+  hipLaunchKernelGGL(plan_tiles_kernel, dim3(ntiles + 1), dim3(kPlanThreads), 0, s, p.row_ptr, p.col_idx, n,
+                     (long long)p.nnz, BH, p.d, cap, pl, ntiles);
   return hipGetLastError();
 }
 
