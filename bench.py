@@ -171,14 +171,10 @@ def run_pipeline_steps(torch, sa, prob, t, nnz, BH, n, d, steps, warmup, timer):
     weights = torch.empty_like(scores)
     out = torch.empty(BH, n, d, device="cuda:0")
     plan = torch.zeros(sa.sa_plan_bytes(prob) // 4 + 1, dtype=torch.int32, device="cuda:0")
-    pt = EventTimer(torch)
     sa.sa_plan_build(prob, plan)  # the first build also loads the plan kernels' code
     torch.cuda.synchronize()
-    a = pt.mark()
-    sa.sa_plan_build(prob, plan)
-    b = pt.mark()
-    pt.add("plan", a, b)
-    plan_us = pt.result()["plan"]
+    # ten builds back to back (the cost per step when every step brings a new mask)
+    plan_us = _avg_us(torch, lambda: sa.sa_plan_build(prob, plan), iters=10, warmup=1)
     prob.set_plan(plan)
 
     calls = {"sddmm": lambda: sa.sa_sddmm(prob, t["q"], t["k"], scores),
@@ -732,6 +728,25 @@ def workload_random(torch, sa, gen):
     log(f"random_n8192: pipeline {eager * 1e6 / 10:.1f} us/step (eager) " +
         "  ".join(f"{k_}={v:.1f}us" for k_, v in rk.items()) + f", fused {fused:.1f} us")
     del t, prob
+    # The same calls without a plan: every tile of this pattern is sparse, and the LDS-free
+    # row kernels run such rows at a higher occupancy than the plan's tile kernels do.
+    prob0, t0, _ = to_device(q, torch, sa)
+    S0 = torch.empty(q.BH * nnz, device="cuda:0")
+    W0 = torch.empty_like(S0)
+    O0 = torch.empty(q.BH, q.n, q.d, device="cuda:0")
+    L0 = torch.empty(q.BH, q.n, device="cuda:0")
+    rows = {"sddmm": _avg_us(torch, lambda: sa.sa_sddmm(prob0, t0["q"], t0["k"], S0), iters=10, warmup=2),
+            "softmax": _avg_us(torch, lambda: sa.sa_sparse_softmax(prob0, S0, W0), iters=10, warmup=2),
+            "spmm": _avg_us(torch, lambda: sa.sa_spmm(prob0, W0, t0["v"], O0), iters=10, warmup=2)}
+    fused0 = _avg_us(torch, lambda: sa.sa_fused_forward(prob0, t0["q"], t0["k"], t0["v"], O0, L0),
+                     iters=10, warmup=2)
+    res["without_plan"] = {"kernels_us": {k_: round(v, 2) for k_, v in rows.items()},
+                           "pipeline_kernels_us": round(sum(rows.values()), 2),
+                           "pipeline_pairs_per_s": pairs / (sum(rows.values()) * 1e-6),
+                           "fused_us": round(fused0, 2), "fused_pairs_per_s": pairs / (fused0 * 1e-6)}
+    log("random_n8192 without a plan: " + "  ".join(f"{k_}={v:.1f}us" for k_, v in rows.items()) +
+        f", fused {fused0:.1f} us")
+    del t0, prob0, S0, W0, O0, L0
     return res
 
 

@@ -138,7 +138,11 @@ typedef struct sa_problem {
  *   that keeps every long row split.
  * sa_plan_build: fills plan (device buffer of at least the size of a plan without
  *   segments, caller-owned) on stream. The plan stays valid while the pattern's content is
- *   unchanged. */
+ *   unchanged.
+ * A plan pays off where 64-row tiles are dense enough for the matrix cores (windows, blocks,
+ * dense rows). A pattern that is sparse everywhere (e.g. a few hundred random columns per row
+ * out of thousands) runs about 10-25% faster with plan = NULL, whose row kernels need no LDS
+ * and keep more waves per compute unit; rows longer than 1024 entries are then not split. */
 size_t sa_plan_bytes(const sa_problem *p);
 size_t sa_plan_bytes_segments(const sa_problem *p, int64_t max_segments);
 int sa_plan_build(const sa_problem *p, void *plan, size_t plan_bytes, hipStream_t stream);
