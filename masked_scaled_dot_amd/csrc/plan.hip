@@ -81,7 +81,8 @@ constexpr int kPlanThreads = 256;
 // Rows [r0, r1): visit(i, a, b) for each, with the bounds of row_range, loading the row
 // pointers eight ahead.
 template <class F>
-__device__ __forceinline__ void walk_rows(const int* row_ptr, int n, long long nnz, int r0, int r1, F&& visit) {
+__device__ __forceinline__ void walk_rows(const int* row_ptr, int n, long long nnz, int r0, int r1,
+                                          F&& visit) {
   int raw = r0 < r1 ? row_ptr[r0] : 0;
   for (int i0 = r0; i0 < r1; i0 += 8) {
     int nx[8];
@@ -176,10 +177,11 @@ __device__ void plan_segs(const int* __restrict__ row_ptr, int n, long long nnz,
   }
 }
 
-// Kernel C (one workgroup per tile): key-block span of the rows' core entries, the
-// sorted distinct far columns (entries outside the core ranges, long rows excluded), and
-// whether the tile runs on matrix cores: at most 64 far columns (one gathered key block)
-// and core + far entries filling at least kDenseTile of the blocks' cells.
+// Kernel B (one workgroup per tile, and one more for the segments and the header): key-block
+// span of the rows' core entries, the sorted distinct far columns (entries outside the core
+// ranges, long rows excluded), and whether the tile runs on matrix cores: at most 64 far
+// columns (one gathered key block) and core + far entries filling at least kDenseTile of the
+// blocks' cells.
 __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int* __restrict__ row_ptr,
                                                                   const int* __restrict__ col_idx, int n,
                                                                   long long nnz, int BH, int d,
