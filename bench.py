@@ -758,15 +758,27 @@ def workload_evoformer(torch, sa, gen):
     f = lambda: sa.sa_fused_forward(prob, t["q"], t["k"], t["v"], out, lse)
     us = _avg_us(torch, f, iters=100, warmup=5)
     warm, cold = time_cold_warm(torch, f)
+    # the same launch captured 20 times in a HIP graph: per-launch time of the replays, and
+    # the replayed output against the eager one (the kernel allocates and clears nothing)
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(20):
+            f()
+    graph_us = _avg_us(torch, graph.replay, iters=5, warmup=1) / 20
+    graph_same = bool(torch.equal(out, eager))
+    del graph
     pr = q.attended_pairs()
     flops = 4.0 * pr * q.d
     res = {"pairs_per_step": pr, "us": round(us, 2), "warm_median_us": round(warm, 2),
-           "cold_median_us": round(cold, 2), "value": pr / (us * 1e-6), "unit": "pairs/s",
+           "cold_median_us": round(cold, 2), "graph_us": round(graph_us, 2),
+           "graph_output_equals_eager": graph_same, "value": pr / (us * 1e-6), "unit": "pairs/s",
            "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2),
            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "hbm_frac": round(bytes_fused(q) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "traffic": load_traffic("fused_evoformer_l384", source_hash(DENSE_SRC))}
-    log(f"evoformer_l384 fused: {us:.1f} us (back to back), warm median {warm:.1f}, cold median {cold:.1f}")
+    log(f"evoformer_l384 fused: {us:.1f} us (back to back), {graph_us:.1f} us (graph), warm median "
+        f"{warm:.1f}, cold median {cold:.1f}")
     outs = (out.cpu().numpy(), lse.cpu().numpy())
     del t, prob, out, lse
     return q, res, outs
