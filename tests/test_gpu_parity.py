@@ -293,6 +293,34 @@ def test_tiny_sizes(n):
                 check(Op, refc["O"], p.dtype, f"{name} pipeline context plan={plan}")
 
 
+@pytest.mark.parametrize("kind", ["bsr", "dense_key_mask"])
+def test_rows_beyond_the_lds_block_list(kind):
+    """n = 33,280 (520 key blocks): more block-columns than the tile kernel keeps in LDS (512).
+    Block CSR: block-row 0 holds all 520 blocks, block-row 1 the first and the last, the others
+    their diagonal block. Dense with a key-padding mask: the list of visited key blocks does
+    not fit either, and every block is visited. Rows sampled from each kind of block-row are
+    compared with the oracle."""
+    import copy
+    n, nb = 33280, 520
+    if kind == "bsr":
+        base = gen.make("bsr_n16384", n=n, H=1, d=32, extra=0)
+        rows = [list(range(nb)), [0, nb - 1]] + [[r] for r in range(2, nb)]
+        p = copy.copy(base)
+        p.row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+        p.col_idx = np.concatenate([np.asarray(r, np.int32) for r in rows])
+        picks = [0, 31, 63, 64, 100, 127, 128, 20000, n - 1]
+    else:
+        p = gen.make("evoformer_l384", B=1, H=1, n=n, d=32, bias=False, pmax=200)
+        picks = [0, 1, 16000, 33000, n - 1]
+    say(f"rows beyond the LDS block list: {kind} n={n} nnz={p.nnz}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    pairs = [(0, i) for i in picks]
+    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), pairs, **dp.oracle_args())
+    check(O[0, picks], ref["O"], p.dtype, f"{kind} context")
+    check(lse[0, picks], ref["lse"], p.dtype, f"{kind} lse")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_diagonal_only_rows_are_exact(dtype):
     n, d = 300, 32
