@@ -293,6 +293,34 @@ def test_tiny_sizes(n):
                 check(Op, refc["O"], p.dtype, f"{name} pipeline context plan={plan}")
 
 
+@pytest.mark.parametrize("name", ["longformer_long_rows", "random_long_rows"])
+def test_plan_without_segment_room(name):
+    """A plan sized for no long-row segments (sa_plan_bytes_segments(p, 0)) is built without
+    them (header word 7 = 0); every kernel then computes the long rows whole, and the outputs
+    still match the oracle."""
+    p = small(name)
+    dp = DevProblem(p)
+    nbytes = sa.sa_plan_bytes_segments(dp.prob, 0)
+    assert 0 < nbytes < sa.sa_plan_bytes(dp.prob)
+    plan = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=DEV)
+    sa.sa_plan_build(dp.prob, plan)
+    dp.prob.set_plan(plan)
+    dp.plan = plan
+    hdr = plan[:16].cpu().numpy()
+    assert hdr[7] == 0 and hdr[6] > 0, hdr  # segments counted but not written
+    say(f"plan without segment room: {name} n={p.n} segments={hdr[6]}")
+    S, W, O = dp.pipeline()
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H, **dp.oracle_args())
+    check(S, ref["S"], p.dtype, "scores")
+    check(W, ref["W"], p.dtype, "weights")
+    check(O, ref["O"], p.dtype, "context")
+    Of, lse = dp.fused()
+    refd = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), want_weights=False,
+                                  **dp.oracle_args())
+    check(Of, refd["O"], p.dtype, "fused context")
+    check(lse, refd["lse"], p.dtype, "fused lse")
+
+
 @pytest.mark.parametrize("kind", ["bsr", "dense_key_mask"])
 def test_rows_beyond_the_lds_block_list(kind):
     """n = 33,280 (520 key blocks): more block-columns than the tile kernel keeps in LDS (512).
