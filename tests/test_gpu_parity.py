@@ -600,6 +600,28 @@ def test_plan_build_matches_host(name):
         assert ei.value.status == sa.SA_ERR_WORKSPACE
 
 
+def test_plan_serves_smaller_shapes():
+    """A plan built for B*H = 2 heads of d = 64 serves, stream-ordered, a problem on the same
+    pattern with one head of d = 32 (its split rows use the plan's scratch at the plan's
+    stride); pipeline and fused forward match the oracle."""
+    big = small("longformer_long_rows")
+    assert big.BH == 2 and big.d == 64
+    owner = DevProblem(big, plan=True)
+    p = gen.make("longformer_n4096", n=big.n, H=1, d=32, window=100)
+    assert np.array_equal(p.row_ptr, big.row_ptr) and np.array_equal(p.col_idx, big.col_idx)
+    dp = DevProblem(p)
+    dp.prob.set_plan(owner.plan)
+    dp.plan = owner.plan
+    S, W, O = dp.pipeline()
+    ref = oracle.attention_csr(p.q, p.k, p.v, p.row_ptr, p.col_idx, p.scale, p.H)
+    check(W, ref["W"], p.dtype, "weights")
+    check(O, ref["O"], p.dtype, "context")
+    Of, lse = dp.fused()
+    refd = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, _pattern(p), want_weights=False)
+    check(Of, refd["O"], p.dtype, "fused context")
+    check(lse, refd["lse"], p.dtype, "fused lse")
+
+
 def test_two_streams_one_pattern_own_plans():
     """Two streams run the pipeline and the fused forward concurrently on the same pattern,
     each with a plan of its own (a plan's long-row merge state serves one call at a time):
