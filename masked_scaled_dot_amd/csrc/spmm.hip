@@ -167,7 +167,6 @@ struct TileSmem {
   static constexpr int kWStride = kTileRows + 4;  // fp32 per weight row: conflict-free 16-row reads
   alignas(16) uint16_t v[2][kTileRows * kVStride];  // double-buffered V block
   alignas(16) float w[kTileRows * kWStride];        // the waves' weight rows of one block
-  i32x4_v rec[(kMaxTileBlocks + 1) * kTileRows];    // the tile's block records
   int far[kTileRows];                               // the gathered block's key rows
   int live[kTileRows];                              // 1: the tile writes this row's output
 };
@@ -190,20 +189,6 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
   // than as one more gathered 64-key block
   const bool far_vec = tv.nfar > 0 && tv.nfar <= kFarVec;
   const int nblk = far_vec ? nbc : tile_blocks(tv);
-  {
-    // loads clamped to the tile's records (unconditional, so they are all in flight at once)
-    constexpr int kRecs = (kMaxTileBlocks + 1) * kTileRows;
-    const int last = max(tile_blocks(tv) * kTileRows - 1, 0);  // the gathered block's records too
-    i32x4_v r[(kRecs + kThreads - 1) / kThreads];
-#pragma unroll
-    for (int u = 0; u < (kRecs + kThreads - 1) / kThreads; ++u)
-      r[u] = tv.rec[min((int)threadIdx.x + u * kThreads, last)];
-#pragma unroll
-    for (int u = 0; u < (kRecs + kThreads - 1) / kThreads; ++u) {
-      const int i = threadIdx.x + u * kThreads;
-      if (i < kRecs) sm.rec[i] = r[u];
-    }
-  }
   if (threadIdx.x < kTileRows) {
     const int r = threadIdx.x, row = row0 + r;
     sm.far[r] = clampi(tv.far_cols[min(r, max(tv.nfar - 1, 0))], 0, a.n - 1);
@@ -228,6 +213,14 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
   // each present slot is loaded alone and absent ones read 0
   const int wq_row = lane / 16, wq_part = lane % 16;
   f32x4_v wn[4];
+  // the block records of those rows (first entry, key-slot mask, aux) come from global
+  // memory one block ahead of the weights they address
+  i32x4_v rcn[4];
+  auto load_recs = [&](int jj) {
+    const int b = min(jj, max(nblk - 1, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rcn[i] = tv.rec[b * kTileRows + wave * 16 + 4 * i + wq_row];
+  };
   auto prefetch = [&](int jj) {
     const bool gat = jj >= nbc;
     const int k0 = (tv.kb_lo + jj) * kTileRows;
@@ -244,7 +237,7 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
     bool any_slow = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const i32x4_v rc = sm.rec[jj * kTileRows + wave * 16 + 4 * i + wq_row];
+      const i32x4_v rc = rcn[i];
       const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
       const int s0 = 4 * wq_part;
       const unsigned bits = (unsigned)(m >> s0) & 0xfu;
@@ -273,12 +266,14 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
           if (slow[i] != 0u) wn[i][c] = x;
         }
     }
+    load_recs(jj + 1);
   };
 
   f32x4_v o[OC];
 #pragma unroll
   for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float* wrows = sm.w + wave * 16 * WS;
+  load_recs(0);
   prefetch(0);
   for (int j = 0; j < nblk; ++j) {
     uint16_t* vb = sm.v[j & 1];
@@ -329,7 +324,7 @@ __device__ void spmm_tile(const Args& a, TileSmem<D>& sm, const TileView& tv, in
       for (int c = 0; c < OC; ++c) vf[c] = __uint_as_float((uint32_t)vt[(size_t)kf * D + 16 * c + c16] << 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const i32x4_v rc = sm.rec[nbc * kTileRows + wave * 16 + 4 * g + i];
+        const i32x4_v rc = tv.rec[nbc * kTileRows + wave * 16 + 4 * g + i];
         const unsigned long long m = ((unsigned long long)(unsigned)rc.z << 32) | (unsigned)rc.y;
         const int rank = __builtin_popcountll(m & ((1ull << f) - 1ull));
         const int e = rc.x - (int)e_lo + rank + gathered_skip(rank, rc.w);
@@ -514,8 +509,14 @@ __device__ void spmm_tile_banded(const Args& a, TileSmem<D>& sm, const TileView&
   }
 }
 
+// Waves per SIMD the tile kernel is compiled for: four workgroups per compute unit fit the
+// LDS (38 KB each at d = 64) when the registers stay within 512 / 4.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void spmm_plan_kernel(Args a, int BH) {
+constexpr int kSpmmWaves = (sizeof(T) == 2 && D <= 64) ? 4 : 1;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSpmmWaves<T, D>)))
+void spmm_plan_kernel(Args a, int BH) {
   __shared__ TileSmem<D> sm;
   const int* plan = a.plan;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
