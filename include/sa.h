@@ -65,7 +65,7 @@ typedef enum sa_status {
   SA_ERR_DTYPE = -4,       /* dtype is not SA_F32 / SA_BF16                               */
   SA_ERR_UNSUPPORTED = -5, /* d not in {32,64,128}, block not in {1,64}, or pattern kind
                               not accepted by this call                                   */
-  SA_ERR_ALIGN = -6,       /* q/k/v/out base pointer not 16-byte aligned                  */
+  SA_ERR_ALIGN = -6,       /* q/k/v/out (or plan) base pointer not 16-byte aligned        */
   SA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed                  */
   SA_ERR_WORKSPACE = -8    /* plan or workspace too small (or the fixed scratch of the
                               no-allocation entry point), or a plan for another problem    */
@@ -91,8 +91,9 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  * bias     : NULL or fp32 [H, n, n] (the [1, H, seq_q, seq_k] bias), added to S.
  * key_mask : NULL or fp32 [B, key_mask_heads, n] (the [B, 1 or H, 1, seq_k] additive
  *            key mask, usually 0 / -inf); key_mask_heads is 1 or H.
- * plan     : NULL, or a buffer filled by sa_plan_build for this same pattern; calls that
- *            schedule rows read it instead of building their own.
+ * plan     : NULL, or a buffer filled by sa_plan_build for this same pattern (16-byte aligned,
+ *            SA_ERR_ALIGN otherwise); calls that schedule rows read it instead of building
+ *            their own.
  * seqlen_k : NULL or int32 [B] on the device: keys j >= seqlen_k[b] (clamped to [0, n]) are
  *            masked for every head and query of batch b, as if the key mask held -inf there
  *            (the one-int-per-batch key padding of the AlphaFold2 pull request, key-padding
@@ -136,8 +137,8 @@ typedef struct sa_problem {
  * sa_plan_bytes_segments: the same for up to max_segments segments. A row of len > 1024
  *   entries takes ceil(len / 256) segments; the sum over the pattern's rows is the count
  *   that keeps every long row split.
- * sa_plan_build: fills plan (device buffer of at least the size of a plan without
- *   segments, caller-owned) on stream. The plan stays valid while the pattern's content is
+ * sa_plan_build: fills plan (16-byte aligned device buffer of at least the size of a plan
+ *   without segments, caller-owned) on stream. The plan stays valid while the pattern's content is
  *   unchanged.
  * A plan pays off where 64-row tiles are dense enough for the matrix cores (windows, blocks,
  * dense rows). A pattern that is sparse everywhere (e.g. a few hundred random columns per row

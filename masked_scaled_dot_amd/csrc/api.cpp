@@ -51,6 +51,7 @@ int check_problem(const sa_problem* p, Op op) {
     }
   }
   if (p->key_mask && p->key_mask_heads != 1 && p->key_mask_heads != p->H) return SA_ERR_SHAPE;
+  if (p->plan && !aligned16(p->plan)) return SA_ERR_ALIGN;  // its records are read 16 bytes at a time
   // Buffer element counts must fit in 64-bit byte offsets used by the kernels.
   const long long bh = (long long)p->B * p->H;
   if (bh > INT32_MAX) return SA_ERR_SHAPE;
@@ -149,6 +150,7 @@ int sa_plan_build(const sa_problem* p, void* plan, size_t plan_bytes, hipStream_
   int st = check_problem(p, kOpPlan);
   if (st != SA_OK) return st;
   if (!plan) return SA_ERR_NULL;
+  if (!aligned16(plan)) return SA_ERR_ALIGN;
   if (plan_bytes < sa::plan_bytes_for(p->n, 0, 0, 0, p->d)) return SA_ERR_WORKSPACE;  // header, rows, tiles
   if ((st = pre_launch(p, stream)) != SA_OK) return st;
   return hip_status(sa::launch_plan(*p, plan, plan_bytes, stream));

@@ -186,11 +186,11 @@ void fused_plan_kernel(FusedArgs a, int BH) {
     if (segs_ok) fused_segments<T, D>(a, BH);
     return;
   }
-  const int ntiles = plan[kHTiles];
+  const int ntiles = (a.n + kTileRows - 1) / kTileRows;
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const TileView tv = tile_view(plan, tile);
+  const TileView tv = tile_view(plan, tile, a.n);
   if (sizeof(T) == 2 && tv.mfma && segs_ok) {
     if constexpr (sizeof(T) == 2) fused_block_tile<D, kFusedCsr, kBias, kMask, false>(a, sm, tv, t, row0, nullptr, 0);
     return;

@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int* __restrict__ 
     hi = a + upto;
   }
   if (lane == 0) {
-    rows[2 * i] = (int)lo;
-    rows[2 * i + 1] = (int)hi;
+    const int c0 = hi > lo ? col_idx[lo] : 0;
+    *reinterpret_cast<i32x4_v*>(rows + 4ll * i) = i32x4_v{(int)lo, (int)hi, c0, 0};
   }
 }
 
@@ -191,8 +191,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int* __r
     plan_segs(row_ptr, n, nnz, BH, d, cap_words, plan);
     return;
   }
-  const int* rows = plan + kPlanHeaderWords;
-  int* tiles = plan + kPlanHeaderWords + plan_sizes(n, 0, 0, 0, d).rows;
+  const int* rows = plan + plan_rows_offset();
+  int* tiles = plan + plan_tiles_offset(n);
   __shared__ int s_far[kFarMax];
   __shared__ int s_dist[kFarMax];
   __shared__ int s_pre[kTileRows + 1];
@@ -221,10 +221,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int* __r
       if (re - rs > kLongRow) {
         rs = re = 0;  // handled by segments: no entries in this tile's records
       } else {
-        lo = rows[2 * row];
-        hi = rows[2 * row + 1];
+        const i32x4_v pr = *reinterpret_cast<const i32x4_v*>(rows + 4ll * row);
+        lo = pr.x;
+        hi = pr.y;
         if (hi > lo) {
-          c0 = col_idx[lo];
+          c0 = pr.z;
           c1 = col_idx[hi - 1];
           atomicMin(&s_min, c0);
           atomicMax(&s_max, c1);

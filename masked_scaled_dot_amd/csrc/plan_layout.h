@@ -29,9 +29,9 @@ enum PlanHeader {
 // After the tile records (kTileInfo words each) come the far-column lists (kTileRows ints per
 // tile) and the block records (kBoundsPerTile ints per tile, laid out [block][row][4]).
 
-// Word counts of the parts, in layout order: header, rows (2 per row: first and one past
-// the last entry of the row's core range; padded to a multiple of 4 words so that the
-// records below are 16-byte aligned), tiles (kTileInfo per tile: first key block, one
+// Word counts of the parts, in layout order: header, rows (4 per row, 16-byte aligned: first
+// and one past the last entry of the row's core range, the column of its first core entry
+// (0 when the range is empty), 0), tiles (kTileInfo per tile: first key block, one
 // past the last key block, 1 if the tile runs on matrix cores, number of far columns, 1 if
 // every row's core range holds consecutive columns (so a row's entries in a key block are one
 // run of slots), the number of 64x64 blocks when the tile is made of whole blocks and is not
@@ -51,6 +51,11 @@ enum PlanHeader {
 // starting on a 16-byte boundary.
 __host__ __device__ constexpr long long slot_floats(long long d) { return d + 4; }
 
+// The row and tile tables sit at offsets that depend on n alone (the header records them too),
+// so that kernels can address them without first reading the header.
+__host__ __device__ constexpr long long plan_rows_offset() { return kPlanHeaderWords; }
+__host__ __device__ constexpr long long plan_tiles_offset(long long n) { return kPlanHeaderWords + 4 * n; }
+
 struct PlanSizes {
   long long rows, tiles, segs, counters, pad, scratch, total;
 };
@@ -59,7 +64,7 @@ __host__ __device__ inline PlanSizes plan_sizes(long long n, long long long_rows
                             long long d) {
   PlanSizes s;
   const long long tiles = (n + kTileRows - 1) / kTileRows;
-  s.rows = (2 * n + 3) / 4 * 4;
+  s.rows = 4 * n;
   s.tiles = (long long)(kTileInfo + kTileRows + kBoundsPerTile) * tiles;
   s.segs = 8 * segs;
   s.counters = long_rows * BH;

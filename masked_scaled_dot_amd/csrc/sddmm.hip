@@ -552,11 +552,11 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
   }
 
   // ---- tiles: one workgroup per (head, tile)
-  const int ntiles = plan[kHTiles];
+  const int ntiles = (a.n + kTileRows - 1) / kTileRows;
   const int lb = xcd_logical_block(blockIdx.x - kLongWGs, gridDim.x - kLongWGs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const TileView tv = tile_view(plan, tile);
+  const TileView tv = tile_view(plan, tile, a.n);
   long long e_lo, e_hi;
   tile_entry_span(a.row_ptr, row0, a.n, a.nnz, e_lo, e_hi);
   const bool dense =

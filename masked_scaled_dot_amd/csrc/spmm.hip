@@ -383,10 +383,11 @@ __device__ void spmm_tile_banded(const Args& a, TileSmem<D>& sm, const TileView&
   if (arow < a.n) {
     long long rs, re;
     row_bounds(a, arow, rs, re);
-    const int* prow = a.plan + a.plan[kHOffRows];
-    const long long lo = prow[2 * arow], hi = prow[2 * arow + 1];
+    // the plan's row entry: core range [lo, hi) and the column of its first entry
+    const i32x4_v pr = *reinterpret_cast<const i32x4_v*>(a.plan + plan_rows_offset() + 4ll * arow);
+    const long long lo = pr.x, hi = pr.y;
     if (re - rs <= kLongRow && hi > lo && lo >= e_lo && hi <= e_hi) {
-      c0 = clampi(a.col_idx[lo], 0, a.n - 1);
+      c0 = clampi(pr.z, 0, a.n - 1);
       len = (int)(hi - lo);
       base = (int)(lo - e_lo) - c0;
     }
@@ -594,11 +595,11 @@ void spmm_plan_kernel(Args a, int BH) {
   }
 
   // ---- tiles
-  const int ntiles = plan[kHTiles];
+  const int ntiles = (a.n + kTileRows - 1) / kTileRows;
   const int lb = xcd_logical_block(blockIdx.x, ntile_wgs);
   const int t = lb / ntiles, tile = lb % ntiles;
   const int row0 = tile * kTileRows;
-  const TileView tv = tile_view(plan, tile);
+  const TileView tv = tile_view(plan, tile, a.n);
   long long e_lo, e_hi;
   tile_entry_span(a.row_ptr, row0, a.n, a.nnz, e_lo, e_hi);
   const bool dense = (sizeof(T) == 2) && tv.mfma && split && (e_hi - e_lo) * 4 <= kMaxBufBytes;

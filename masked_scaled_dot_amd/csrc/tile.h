@@ -41,9 +41,9 @@ struct TileView {
   const int* bcols;     // whole-block tile: its block-columns, ascending (in the record space)
 };
 
-__device__ __forceinline__ TileView tile_view(const int* plan, int tile) {
-  const int ntiles = plan[kHTiles];
-  const int* base = plan + plan[kHOffTiles];
+__device__ __forceinline__ TileView tile_view(const int* plan, int tile, int n) {
+  const int ntiles = (n + kTileRows - 1) / kTileRows;
+  const int* base = plan + plan_tiles_offset(n);
   const int* ti = base + kTileInfo * tile;
   TileView v;
   v.kb_lo = ti[0];

@@ -144,9 +144,16 @@ def test_plan_bytes_and_build_checks():
     assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(block=64, nnz=4))) == 0
     assert _lib.raw("sa_plan_bytes")(ctypes.byref(_prob(n=0, nnz=0))) == 4 * 16
     assert _lib.raw("sa_plan_build")(ctypes.byref(p), None, 1 << 20, None) == sa.SA_ERR_NULL
-    # header, row core ranges, per tile: info, far columns, 13 x 64 block records of 4 words
-    minimal = 4 * (16 + 2 * 4096 + (8 + 64 + 13 * 64 * 4) * 64)
+    # header, row entries (4 words each), per tile: info, far columns, 13 x 64 block records of
+    # 4 words
+    minimal = 4 * (16 + 4 * 4096 + (8 + 64 + 13 * 64 * 4) * 64)
     assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE, minimal - 4, None) == sa.SA_ERR_WORKSPACE
+    # the plan is read 16 bytes at a time: a buffer off that alignment is refused, by the build
+    # and by every call that carries it, before any device access
+    assert _lib.raw("sa_plan_build")(ctypes.byref(p), FAKE + 4, minimal, None) == sa.SA_ERR_ALIGN
+    q = _prob(n=4096, nnz=1052026)
+    q.plan = FAKE + 8
+    assert _lib.raw("sa_sddmm")(ctypes.byref(q), FAKE, FAKE, FAKE, None) == sa.SA_ERR_ALIGN
 
 
 def test_validate_requires_a_pattern():

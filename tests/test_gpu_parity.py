@@ -530,7 +530,11 @@ def test_plan_build_matches_host(name):
     assert h[0] == 0x53415032 and h[1] == p.n and h[2] == p.nnz and h[7] == 1
     assert h[4] == len(tiles) and h[5] == L and h[6] == len(segs)
     assert h[8] == p.BH and h[9] == p.d
-    assert np.array_equal(h[h[10]:h[10] + 2 * p.n].reshape(-1, 2), rows)
+    rows4 = np.zeros((p.n, 4), np.int64)
+    rows4[:, :2] = rows
+    rows4[:, 2] = [p.col_idx[lo] if hi > lo else 0 for lo, hi in rows]  # column of the first core entry
+    assert h[10] == 16 and h[11] == 16 + 4 * p.n                   # offsets from n alone
+    assert np.array_equal(h[h[10]:h[10] + 4 * p.n].reshape(-1, 4), rows4)
     T = len(tiles)
     assert np.array_equal(h[h[11]:h[11] + 8 * T].reshape(-1, 8), tiles)
     far_base = h[11] + 8 * T
