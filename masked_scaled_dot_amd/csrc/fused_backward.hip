@@ -128,8 +128,11 @@ struct RowChunks {
 // Per key block: K and V (and the query's bias and key-mask values of the block's keys,
 // 16 consecutive bytes per lane) are loaded one block ahead into registers, staged in LDS
 // behind a barrier, and the next block's loads stay in flight while this one is computed.
+// Waves per SIMD: three at d = 32, and at d = 128 without a bias or a key mask (148-164
+// registers).
 template <int D, bool kBias, bool kMask, bool kBits>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : 1))) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 32 || (D == 128 && !kBias && !kMask) ? 3 : 1))) void dq_kernel(BwdArgs a) {
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
   __shared__ BwdSmem<D> sm;
@@ -289,8 +292,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 3
 // kPart: 3 = dK and dV in one pass; 1 = dV only (no dP needed); 2 = dK only. d = 128 runs
 // the two halves as separate passes: each holds half the accumulators, which doubles the
 // waves per SIMD for about a quarter more products.
+// Waves per SIMD: three at d = 32, and for the split passes at d = 128 without a bias or a
+// cover (126-168 registers); two otherwise.
 template <int D, bool kBias, bool kMask, int kPart, bool kBits>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 32 ? 3 : (kPart == 3 ? 1 : 2)))) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 32 || (kPart != 3 && D == 128 && !kBias && !kBits) ? 3 : (kPart == 3 ? 1 : 2))))
+void dkdv_kernel(BwdArgs a) {
   constexpr bool kDV = (kPart & 1) != 0, kDK = (kPart & 2) != 0;
   constexpr int ST = BwdSmem<D>::kTStride;
   constexpr int KC = D / 32, OC = D / 16;
