@@ -259,6 +259,34 @@ def test_dense_tile_skips_masked_key_blocks(n, d, bias):
         f" lse max_abs={el[0]:.3e}")
 
 
+@pytest.mark.parametrize("n,d", [(384, 32), (200, 64), (97, 128)])
+def test_dense_running_max_jumps(n, d):
+    """Dense pattern with a pair bias that moves each row's maximum in steps across the 32-key
+    units: a first unit hundreds below the rest (its exponentials underflow against any early
+    reference), rises of 3-6 (under the slack the running maximum allows, but enough to lift
+    a unit's sum of weights past it), and jumps of 12-60 in later units. Every step of the
+    online softmax (first reference, no move, move and rescale) is taken; context and lse
+    match the oracle."""
+    import dataclasses
+    p = gen.make("evoformer_l384", B=2, H=2, n=n, d=d)
+    rng = np.random.default_rng(77)
+    steps = np.array([-200.0, -5.0, 0.0, 3.0, 6.0, 12.0, 60.0])
+    units = (n + 31) // 32
+    shift = np.cumsum(rng.choice(steps, size=(p.H, n, units)), axis=2)
+    shift[:, :, 0] = -300.0
+    bias = p.bias + np.repeat(shift, 32, axis=2)[:, :, :n].astype(np.float32)
+    p = dataclasses.replace(p, bias=bias.astype(np.float32))
+    say(f"dense running-max jumps: n={n} d={d}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, ("dense",), want_weights=False,
+                                 **dp.oracle_args())
+    eo = check(O, ref["O"], p.dtype, "context")
+    el = check(lse, ref["lse"], p.dtype, "lse")
+    say(f"PARITY dense_running_max_jumps_n{n}_d{d} fused context max_abs={eo[0]:.3e} mean_abs={eo[1]:.3e}"
+        f" lse max_abs={el[0]:.3e}")
+
+
 TINY_N = [1, 2, 5, 31, 33, 63, 65]
 
 
