@@ -377,6 +377,54 @@ def test_rows_beyond_the_lds_block_list(kind):
     check(lse[0, picks], ref["lse"], p.dtype, f"{kind} lse")
 
 
+def test_block_sparse_tiles_in_several_rounds():
+    """Block CSR with more (head, block-row) tiles than the device runs at once (4500 tiles at
+    n = 95,987, three heads: the tiles run in several rounds), whose block-rows cycle through
+    every shape a tile can have: empty, one block, two blocks, 25 blocks, and 3-9 random ones;
+    the last block is ragged. Rows sampled from each kind of block-row in every head are
+    compared with the oracle; every row of an empty block-row must give O = 0 and lse = -inf."""
+    import copy
+    nb = 1500
+    n = 64 * nb - 13
+    base = gen.make("bsr_n16384", n=n, H=3, d=32, extra=0)
+    rng = np.random.default_rng(2024)
+    rows = []
+    for r in range(nb):
+        kind = r % 7
+        if kind == 0 and r != nb - 1:
+            cols = []
+        elif kind == 1:
+            cols = [r]
+        elif kind == 2:
+            cols = [max(r - 1, 0), r] if r > 0 else [0, 1]
+        elif kind == 3:
+            cols = rng.choice(nb, size=25, replace=False).tolist()
+        else:
+            cols = rng.choice(nb, size=int(rng.integers(3, 10)), replace=False).tolist() + [r]
+        rows.append(sorted(set(cols)))
+    p = copy.copy(base)
+    p.row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    p.col_idx = np.concatenate([np.asarray(r, np.int32) for r in rows])
+    say(f"block CSR, tiles in several rounds: n={n} H={p.H} block nnz={p.nnz}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    picks = []
+    for br in [0, 1, 2, 3, 4, 5, 6, 700, 701, 702, 703, 704, 1493, 1494, 1495, 1496, nb - 1]:
+        picks += [64 * br, min(64 * br + 37, n - 1), min(64 * br + 63, n - 1)]
+    pairs = [(t, i) for t in range(p.H) for i in picks]
+    ref = oracle.attention_rows(p.q, p.k, p.v, p.scale, p.H, _pattern(p), pairs, **dp.oracle_args())
+    got_o = np.stack([O[t, i] for t, i in pairs])
+    got_l = np.array([lse[t, i] for t, i in pairs])
+    eo = check(got_o, ref["O"], p.dtype, "context")
+    el = check(got_l, ref["lse"], p.dtype, "lse")
+    empty = np.concatenate([np.arange(64 * br, min(64 * br + 64, n)) for br in range(nb) if not rows[br]])
+    assert np.all(O[:, empty] == 0) and np.all(lse[:, empty] == -np.inf)
+    live = np.setdiff1d(np.arange(n), empty)
+    assert np.all(np.isfinite(O[:, live])) and np.all(np.isfinite(lse[:, live]))
+    say(f"PARITY bsr_tiles_in_several_rounds fused context max_abs={eo[0]:.3e} mean_abs={eo[1]:.3e}"
+        f" lse max_abs={el[0]:.3e}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_diagonal_only_rows_are_exact(dtype):
     n, d = 300, 32
