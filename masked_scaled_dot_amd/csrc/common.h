@@ -86,4 +86,18 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+
+// The long-row segments of the heads whose tiles an XCD runs are walked by segment
+// workgroups on that XCD, so the K/V rows a segment gathers are the ones already in that
+// XCD's L2. Head t belongs to the XCD that xcd_logical_block gives its middle tile (logical
+// index t * ntiles + ntiles / 2 of ntiles * BH); the heads of XCD x are [first, next first).
+__device__ __forceinline__ int first_head_on_xcd(int x, int ntiles, int BH) {
+  const long long nblocks = (long long)ntiles * BH;
+  const long long per = nblocks / kXcds, rem = nblocks % kXcds;
+  const long long start = x * per + (x < rem ? x : rem);  // first logical block of XCD x
+  const long long num = start - ntiles / 2;                // t * ntiles >= num
+  const long long t = num <= 0 ? 0 : (num + ntiles - 1) / ntiles;
+  return (int)(t < BH ? t : BH);
+}
+
 }  // namespace sa

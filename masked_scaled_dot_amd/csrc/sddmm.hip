@@ -539,11 +539,15 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     // each plan segment as kSegSplit tasks: scores need no merge, so shorter tasks only add
     // parallelism
     constexpr int kSegSplit = 2;
-    const long long tasks = (long long)S * BH * kSegSplit;
-    for (long long task = (long long)blockIdx.x * (kThreads / kWave) + wave; task < tasks;
-         task += (long long)kLongWGs * (kThreads / kWave)) {
+    // this XCD's heads; the workgroup is number blockIdx.x / kXcds of the XCD's segment workgroups
+    const int ntiles = (a.n + kTileRows - 1) / kTileRows;
+    const int x = (int)blockIdx.x % kXcds;
+    const int ta = first_head_on_xcd(x, ntiles, BH), tb = first_head_on_xcd(x + 1, ntiles, BH);
+    const long long tasks = (long long)S * (tb - ta) * kSegSplit;
+    for (long long task = (long long)(blockIdx.x / kXcds) * (kThreads / kWave) + wave; task < tasks;
+         task += (long long)(kLongWGs / kXcds) * (kThreads / kWave)) {
       const int part = (int)(task % kSegSplit);
-      const int sg = (int)(task / kSegSplit % S), t = (int)(task / kSegSplit / S);
+      const int sg = (int)(task / kSegSplit % S), t = ta + (int)(task / kSegSplit / S);
       const int* it = segs + 8 * sg;
       const long long len = it[2] - it[1];
       valu_row<T, D>(a, t, it[0], it[1] + len * part / kSegSplit, it[1] + len * (part + 1) / kSegSplit);

@@ -538,11 +538,15 @@ void spmm_plan_kernel(Args a, int BH) {
     int* counters = const_cast<int*>(plan) + plan[kHOffCounters];
     float* scratch = reinterpret_cast<float*>(const_cast<int*>(plan) + plan[kHOffScratch]);
     const int pBH = plan[kHBH], pD = plan[kHD];
-    const long long tasks = (long long)S * BH;
+    // this XCD's heads; the workgroup is number lwg / kXcds of the XCD's segment workgroups
+    const int ntiles = (a.n + kTileRows - 1) / kTileRows;
+    const int x = (int)blockIdx.x % kXcds;
+    const int ta = first_head_on_xcd(x, ntiles, BH), tb = first_head_on_xcd(x + 1, ntiles, BH);
+    const long long tasks = (long long)S * (tb - ta);
     using L = Layout<T, D>;
-    for (long long task = (long long)lwg * (kThreads / kWave) + wave; task < tasks;
-         task += (long long)kLongWGs * (kThreads / kWave)) {
-      const int sg = (int)(task % S), t = (int)(task / S);
+    for (long long task = (long long)(lwg / kXcds) * (kThreads / kWave) + wave; task < tasks;
+         task += (long long)(kLongWGs / kXcds) * (kThreads / kWave)) {
+      const int sg = (int)(task % S), t = ta + (int)(task / S);
       const int* it = segs + 8 * sg;
       const int row = it[0], lr = it[3], sidx = it[4], ns = it[5];
       float acc[L::kEPC];
