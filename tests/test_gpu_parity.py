@@ -259,6 +259,31 @@ def test_dense_tile_skips_masked_key_blocks(n, d, bias):
         f" lse max_abs={el[0]:.3e}")
 
 
+@pytest.mark.parametrize("bias", [True, False], ids=["bias", "mask_only"])
+@pytest.mark.parametrize("n,d", [(384, 32), (200, 64)])
+def test_dense_resident_skips_leading_key_blocks(n, d, bias):
+    """Dense pattern whose heads fit in LDS: a key-padding mask hides all of key block 0 in
+    batch 0 (the first visited block is block 1) and all of block 1 plus a few single keys in
+    batch 1; batch 2 keeps every key. Context and lse match the oracle."""
+    import dataclasses
+    p = gen.make("evoformer_l384", B=3, H=2, n=n, d=d, bias=bias)
+    km = np.zeros((3, 1, n), np.float32)
+    km[0, 0, :64] = -np.inf
+    km[0, 0, 100:131] = -np.inf
+    km[1, 0, 64:128] = -np.inf
+    km[1, 0, [3, 17, n - 1]] = -np.inf
+    p = dataclasses.replace(p, key_mask=km, key_mask_heads=1)
+    say(f"dense resident, leading key blocks masked: n={n} d={d} bias={bias}")
+    dp = DevProblem(p)
+    O, lse = dp.fused()
+    ref = oracle.attention_dense(p.q, p.k, p.v, p.scale, p.H, ("dense",), want_weights=False,
+                                 **dp.oracle_args())
+    eo = check(O, ref["O"], p.dtype, "context")
+    el = check(lse, ref["lse"], p.dtype, "lse")
+    say(f"PARITY dense_resident_leading_blocks_n{n}_d{d} fused context max_abs={eo[0]:.3e}"
+        f" mean_abs={eo[1]:.3e} lse max_abs={el[0]:.3e}")
+
+
 @pytest.mark.parametrize("n,d", [(384, 32), (200, 64), (97, 128)])
 def test_dense_running_max_jumps(n, d):
     """Dense pattern with a pair bias that moves each row's maximum in steps across the 32-key
