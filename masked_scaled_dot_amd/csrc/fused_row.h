@@ -1,21 +1,25 @@
-// Fused forward on the vector ALUs over the entries of one row: a running maximum and a
-// running sum, rescaling the partial sums whenever the maximum grows, and a single
-// division at the end (streaming-dataflow SDPA review on nubint.ai, "proposed method":
-// reordering the softmax division by the distributive law; running max / running sum with
-// delta rescaling). Scores and weights are never stored.
+// Fused forward on the vector ALUs over the entries of one row: a running reference
+// maximum and a running sum, rescaling the partial sums when the reference moves, and a
+// single division at the end (streaming-dataflow SDPA review on nubint.ai, "proposed
+// method": reordering the softmax division by the distributive law; running max / running
+// sum with delta rescaling). Scores and weights are never stored.
 //
 // A K/V row of d elements is LPR 16-byte chunks; the wave is split into 64/LPR slots. Each
 // slot walks every (64/LPR)-th entry of the range: its lanes multiply their chunk of q by
 // the same chunk of the gathered key row, sum the chunk products within the slot with DPP,
-// update the slot's running (m, l) and rescale-and-add the gathered value chunk into an
-// fp32 accumulator. At the end the slots are merged with the same rescaling (slot maxima to
-// the range maximum).
+// and add the weighted value chunk into an fp32 accumulator. The slot's reference (m, l)
+// moves only when a score exceeds it by more than a fixed slack (then the sums are
+// rescaled), so a weight never exceeds 2^slack and most entries cost one exponential and
+// the multiply-adds. At the end the slots are merged by rescaling each to the largest
+// reference.
 //
 // Pattern kinds: element CSR, block CSR of 64x64 tiles (entry e of row i is column
 // 64*col_idx[blk] + e%64 for the e/64-th stored block of block-row i/64), and dense.
 #pragma once
 
 #include "common.h"
+
+#include <cfloat>
 
 namespace sa {
 
@@ -64,16 +68,16 @@ __device__ __forceinline__ float chunk_dot(const u32x4_v& a, const u32x4_v& b) {
 }
 
 template <typename T, int EPC>
-__device__ __forceinline__ void chunk_axpy(float (&acc)[EPC], float a, float p, const u32x4_v& v) {
+__device__ __forceinline__ void chunk_axpy(float (&acc)[EPC], float p, const u32x4_v& v) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      acc[2 * c] = fmaf(p, bf16lo(v[c]), acc[2 * c] * a);
-      acc[2 * c + 1] = fmaf(p, bf16hi(v[c]), acc[2 * c + 1] * a);
+      acc[2 * c] = fmaf(p, bf16lo(v[c]), acc[2 * c]);
+      acc[2 * c + 1] = fmaf(p, bf16hi(v[c]), acc[2 * c + 1]);
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = fmaf(p, __uint_as_float(v[c]), acc[c] * a);
+    for (int c = 0; c < 4; ++c) acc[c] = fmaf(p, __uint_as_float(v[c]), acc[c]);
   }
 }
 
@@ -122,8 +126,13 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
   const float* km = a.key_mask ? a.key_mask + ((size_t)b * a.km_heads + (a.km_heads > 1 ? h : 0)) * n : nullptr;
   const int ncols = a.seqlen_k ? clampi(a.seqlen_k[b], 0, n) : n;  // keys at or past it are masked
   if constexpr (K == kFusedDense) e_end = e_end < ncols ? e_end : ncols;
-
-  float m = -INFINITY, l = 0.f;
+  // Scores in log2 units against a reference m that moves only when a score exceeds it by
+  // more than kRowSlack, so every weight is at most 2^kRowSlack and most entries skip the
+  // rescale. m starts at -FLT_MAX rather than -inf: a masked score's weight is then exp2(-inf)
+  // = 0 with no special case, and the first finite score always moves it.
+  constexpr float kRowSlack = 8.f;
+  const float scale2 = a.scale * kLog2e;
+  float m = -FLT_MAX, l = 0.f;
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
 
@@ -151,26 +160,30 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float s = group_reduce<LPR, OpSum>(chunk_dot<T>(qc, kc[u])) * a.scale;
-      if (brow) s += brow[j[u]];
-      if (km) s += km[j[u]];
+      float s = group_reduce<LPR, OpSum>(chunk_dot<T>(qc, kc[u])) * scale2;
+      if (brow) s = fmaf(brow[j[u]], kLog2e, s);
+      if (km) s = fmaf(km[j[u]], kLog2e, s);
       s = ok[u] ? s : -INFINITY;
-      const float mn = fmaxf(m, s);
-      if (mn != -INFINITY) {  // uniform within the slot
-        const float al = exp_fast(m - mn);
-        const float p = exp_fast(s - mn);
-        l = fmaf(l, al, p);
-        chunk_axpy<T, EPC>(acc, al, p, vc[u]);
-        m = mn;
+      if (s > m + kRowSlack) {  // uniform within the slot; rare after a row's first entries
+        const float al = __builtin_amdgcn_exp2f(m - s);
+        l *= al;
+#pragma unroll
+        for (int c = 0; c < EPC; ++c) acc[c] *= al;
+        m = s;
       }
+      const float p = __builtin_amdgcn_exp2f(s - m);
+      l += p;
+      chunk_axpy<T, EPC>(acc, p, vc[u]);
     }
   }
 
-  // Merge the slots: rescale each to the range maximum and sum.
-  M = m;
+  // Merge the slots: rescale each to the largest reference and sum; M in natural-log units
+  // (-inf if no entry has a finite score).
+  float m2 = m;
 #pragma unroll
-  for (int s = LPR; s < kWave; s <<= 1) M = fmaxf(M, shfl_xor(M, s));
-  const float f = (M == -INFINITY || m == -INFINITY) ? 0.f : exp_fast(m - M);
+  for (int s = LPR; s < kWave; s <<= 1) m2 = fmaxf(m2, shfl_xor(m2, s));
+  const float f = (m2 == -FLT_MAX) ? 0.f : __builtin_amdgcn_exp2f(m - m2);
+  M = m2 == -FLT_MAX ? -INFINITY : m2 / kLog2e;
   Lsum = l * f;
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] *= f;
