@@ -137,6 +137,20 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
   for (int c = 0; c < EPC; ++c) acc[c] = 0.f;
 
   constexpr int U = 4;
+  // column of entry e (entries past the range read the range's first one, never used); an
+  // iteration's U columns are loaded one iteration ahead, so that its K/V gathers wait for
+  // nothing but themselves
+  auto entry_col = [&](long long e) -> int {
+    const long long ee = e < e_end ? e : e_begin;
+    if constexpr (K == kFusedCsr) return a.col_idx[base + ee];
+    else if constexpr (K == kFusedBsr) return a.col_idx[base + ee / 64] * 64 + (int)(ee % 64);
+    else return (int)ee;
+  };
+  int cn[U] = {};
+  if (e_begin < e_end) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) cn[u] = entry_col(e_begin + slot + (long long)u * SLOTS);
+  }
   for (long long e0 = e_begin + slot; e0 < e_end; e0 += (long long)U * SLOTS) {
     int j[U];
     bool ok[U];
@@ -144,20 +158,14 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long long e = e0 + (long long)u * SLOTS;
-      const long long ee = e < e_end ? e : e_begin;
-      int col;
-      if constexpr (K == kFusedCsr) {
-        col = a.col_idx[base + ee];
-      } else if constexpr (K == kFusedBsr) {
-        col = a.col_idx[base + ee / 64] * 64 + (int)(ee % 64);
-      } else {
-        col = (int)ee;
-      }
+      const int col = cn[u];
       ok[u] = e < e_end && col >= 0 && col < ncols;
       j[u] = clampi(col, 0, n - 1);
       kc[u] = reinterpret_cast<const u32x4_v*>(kt + (size_t)j[u] * D)[r];
       vc[u] = reinterpret_cast<const u32x4_v*>(vt + (size_t)j[u] * D)[r];
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) cn[u] = entry_col(e0 + (long long)(U + u) * SLOTS);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float s = group_reduce<LPR, OpSum>(chunk_dot<T>(qc, kc[u])) * scale2;
