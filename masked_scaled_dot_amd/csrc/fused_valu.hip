@@ -10,8 +10,10 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
+// Compiled for at least six waves per SIMD (80 registers for element CSR, no spills): the
+// rows are gather-bound and more waves keep more K/V rows in flight.
 template <typename T, int D, int K>
-__global__ __launch_bounds__(256) void fused_valu_kernel(FusedArgs a, int BH) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void fused_valu_kernel(FusedArgs a, int BH) {
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const long long unit = (long long)lb * kRowsPerBlock + wave;
