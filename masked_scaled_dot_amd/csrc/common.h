@@ -100,4 +100,16 @@ __device__ __forceinline__ int first_head_on_xcd(int x, int ntiles, int BH) {
   return (int)(t < BH ? t : BH);
 }
 
+
+// Bounds [rs, re) of row row0 + r (r < 64, wave-uniform) of a tile, from the two row_ptr
+// values each lane of the wave loaded for row row0 + lane (rp0 = row_ptr[row], rp1 =
+// row_ptr[row + 1], rows past n repeat row n), clamped to [0, nnz] as everywhere else.
+__device__ __forceinline__ void tile_row_bounds(int rp0, int rp1, int r, long long nnz, long long& rs,
+                                                long long& re) {
+  rs = __builtin_amdgcn_readlane(rp0, r);
+  re = __builtin_amdgcn_readlane(rp1, r);
+  rs = rs < 0 ? 0 : (rs > nnz ? nnz : rs);
+  re = re < rs ? rs : (re > nnz ? nnz : re);
+}
+
 }  // namespace sa

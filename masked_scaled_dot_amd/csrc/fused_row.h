@@ -205,12 +205,10 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
 
 // The whole row: O = acc / Lsum (0 for a row without a finite score) and lse = M + log Lsum.
 template <typename T, int D, int K>
-__device__ __forceinline__ void fused_row(const FusedArgs& a, int t, int row) {
+__device__ __forceinline__ void fused_row_span(const FusedArgs& a, int t, int row, long long base, long long len) {
   using L = FusedLayout<T, D>;
   constexpr int EPC = L::kEPC, LPR = L::kLPR;
   const int lane = threadIdx.x % kWave;
-  long long base, len;
-  fused_row_entries<K>(a, row, base, len);
   float M, Lsum, acc[EPC];
   fused_range<T, D, K>(a, t, row, base, 0, len, M, Lsum, acc);
   if (lane < LPR) {
@@ -222,6 +220,13 @@ __device__ __forceinline__ void fused_row(const FusedArgs& a, int t, int row) {
                          acc[4 * c + 3] * inv);
     if (a.lse && lane == 0) a.lse[(size_t)t * a.n + row] = M == -INFINITY ? -INFINITY : M + logf(Lsum);
   }
+}
+
+template <typename T, int D, int K>
+__device__ __forceinline__ void fused_row(const FusedArgs& a, int t, int row) {
+  long long base, len;
+  fused_row_entries<K>(a, row, base, len);
+  fused_row_span<T, D, K>(a, t, row, base, len);
 }
 
 }  // namespace sa

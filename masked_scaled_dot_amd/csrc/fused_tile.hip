@@ -204,13 +204,17 @@ void fused_plan_kernel(FusedArgs a, int BH) {
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // the row_ptr values of the tile's rows, loaded once (row row0 + lane per lane)
+  const int tl = min(row0 + (int)(threadIdx.x % kWave), a.n);
+  const int rp0 = a.row_ptr[tl], rp1 = a.row_ptr[min(tl + 1, a.n)];
   for (int r = wave; r < kTileRows; r += kThreads / kWave) {
     const int row = row0 + r;
     if (row >= a.n) break;
-    long long base, len;
-    fused_row_entries<kFusedCsr>(a, row, base, len);
+    long long base, re;
+    tile_row_bounds(rp0, rp1, r, a.nnz, base, re);
+    const long long len = re - base;
     if (segs_ok && len > kLongRow) continue;  // a segment task covers it
-    fused_row<T, D, kFusedCsr>(a, t, row);
+    fused_row_span<T, D, kFusedCsr>(a, t, row, base, len);
   }
 }
 

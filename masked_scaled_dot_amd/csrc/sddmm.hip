@@ -567,11 +567,14 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
       (sizeof(T) == 2) && tv.mfma && segs_ok && (e_hi - e_lo) * 4 <= kMaxBufBytes;
 
   if (!dense) {
+    // the row_ptr values of the tile's rows, loaded once (row row0 + lane per lane)
+    const int tl = min(row0 + (int)(threadIdx.x % kWave), a.n);
+    const int rp0 = a.row_ptr[tl], rp1 = a.row_ptr[min(tl + 1, a.n)];
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
       const int row = row0 + r;
       if (row >= a.n) break;
       long long rs, re;
-      row_bounds(a, row, rs, re);
+      tile_row_bounds(rp0, rp1, r, a.nnz, rs, re);
       if (segs_ok && re - rs > kLongRow) continue;  // a long-row segment task covers it
       valu_row<T, D>(a, t, row, rs, re);
     }

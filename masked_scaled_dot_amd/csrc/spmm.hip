@@ -144,12 +144,17 @@ __device__ __forceinline__ void store_chunk(float* orow, const float (&acc)[Layo
 }
 
 template <typename T, int D>
-__device__ void valu_row(const Args& a, int t, int row) {
-  long long rs, re;
-  row_bounds(a, row, rs, re);
+__device__ void valu_row(const Args& a, int t, int row, long long rs, long long re) {
   float acc[Layout<T, D>::kEPC];
   valu_segment<T, D>(a, t, rs, re, acc);
   store_chunk<T, D>(a.out + ((size_t)t * a.n + row) * D, acc);
+}
+
+template <typename T, int D>
+__device__ void valu_row(const Args& a, int t, int row) {
+  long long rs, re;
+  row_bounds(a, row, rs, re);
+  valu_row<T, D>(a, t, row, rs, re);
 }
 
 template <typename T, int D>
@@ -609,13 +614,16 @@ void spmm_plan_kernel(Args a, int BH) {
   const bool dense = (sizeof(T) == 2) && tv.mfma && split && (e_hi - e_lo) * 4 <= kMaxBufBytes;
 
   if (!dense) {
+    // the row_ptr values of the tile's rows, loaded once (row row0 + lane per lane)
+    const int tl = min(row0 + (int)(threadIdx.x % kWave), a.n);
+    const int rp0 = a.row_ptr[tl], rp1 = a.row_ptr[min(tl + 1, a.n)];
     for (int r = wave; r < kTileRows; r += kThreads / kWave) {
       const int row = row0 + r;
       if (row >= a.n) break;
       long long rs, re;
-      row_bounds(a, row, rs, re);
+      tile_row_bounds(rp0, rp1, r, a.nnz, rs, re);
       if (split && re - rs > kLongRow) continue;
-      valu_row<T, D>(a, t, row);
+      valu_row<T, D>(a, t, row, rs, re);
     }
     return;
   }
