@@ -87,10 +87,12 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 
-// The long-row segments of the heads whose tiles an XCD runs are walked by segment
-// workgroups on that XCD, so the K/V rows a segment gathers are the ones already in that
-// XCD's L2. Head t belongs to the XCD that xcd_logical_block gives its middle tile (logical
-// index t * ntiles + ntiles / 2 of ntiles * BH); the heads of XCD x are [first, next first).
+// Long-row segment tasks. With at least kXcds heads, a segment workgroup walks the tasks of
+// the heads whose tiles run on its own XCD, so the K/V rows a segment gathers are the ones
+// already in that XCD's L2; head t belongs to the XCD that xcd_logical_block gives its middle
+// tile (logical index t * ntiles + ntiles / 2 of ntiles * BH), and the heads of XCD x are
+// [first_head_on_xcd(x), first_head_on_xcd(x + 1)). With fewer heads, every workgroup walks
+// every head's tasks (one XCD's workgroups alone would hold them all).
 __device__ __forceinline__ int first_head_on_xcd(int x, int ntiles, int BH) {
   const long long nblocks = (long long)ntiles * BH;
   const long long per = nblocks / kXcds, rem = nblocks % kXcds;
@@ -98,6 +100,29 @@ __device__ __forceinline__ int first_head_on_xcd(int x, int ntiles, int BH) {
   const long long num = start - ntiles / 2;                // t * ntiles >= num
   const long long t = num <= 0 ? 0 : (num + ntiles - 1) / ntiles;
   return (int)(t < BH ? t : BH);
+}
+
+// The walk of segment workgroup wg of nwgs (contiguous in the grid, nwgs a multiple of kXcds),
+// wave `wave` of `waves`: heads [t0, t1), task indices first, first + stride, ...
+struct SegWalk {
+  int t0, t1;
+  long long first, stride;
+};
+__device__ __forceinline__ SegWalk seg_walk(int wg, int nwgs, int ntiles, int BH, int waves, int wave) {
+  SegWalk w;
+  if (BH >= kXcds) {
+    const int x = (int)blockIdx.x % kXcds;
+    w.t0 = first_head_on_xcd(x, ntiles, BH);
+    w.t1 = first_head_on_xcd(x + 1, ntiles, BH);
+    w.first = (long long)(wg / kXcds) * waves + wave;  // wg / kXcds: its index among the XCD's
+    w.stride = (long long)(nwgs / kXcds) * waves;
+  } else {
+    w.t0 = 0;
+    w.t1 = BH;
+    w.first = (long long)wg * waves + wave;
+    w.stride = (long long)nwgs * waves;
+  }
+  return w;
 }
 
 

@@ -50,6 +50,7 @@ typedef __attribute__((ext_vector_type(8))) short i16x8_v;
 
 constexpr int kThreads = 256;
 constexpr int kLongWGs = 256;   // workgroups that walk the long-row segments (CSR)
+static_assert(kLongWGs % kXcds == 0, "segment workgroups split evenly over the XCDs");
 constexpr float kSlack = 8.f;   // lazy running-max threshold, log2 units
 
 constexpr int kBsrCached = 512;  // block-columns of a block-row kept in LDS (n <= 32768 fully)
@@ -96,14 +97,11 @@ __device__ void fused_segments(const FusedArgs& a, int BH) {
   int* counters = const_cast<int*>(plan) + plan[kHOffCounters];
   float* scratch = reinterpret_cast<float*>(const_cast<int*>(plan) + plan[kHOffScratch]);
   const int pBH = plan[kHBH], pD = plan[kHD];
-  // this XCD's heads; the workgroup is number blockIdx.x / kXcds of the XCD's segment workgroups
-  const int ntiles = (a.n + kTileRows - 1) / kTileRows;
-  const int x = (int)blockIdx.x % kXcds;
-  const int ta = first_head_on_xcd(x, ntiles, BH), tb = first_head_on_xcd(x + 1, ntiles, BH);
-  const long long tasks = (long long)S * (tb - ta);
-  for (long long task = (long long)(blockIdx.x / kXcds) * (kThreads / kWave) + wave; task < tasks;
-       task += (long long)(kLongWGs / kXcds) * (kThreads / kWave)) {
-    const int sg = (int)(task % S), t = ta + (int)(task / S);
+  const SegWalk sw = seg_walk((int)blockIdx.x, kLongWGs, (a.n + kTileRows - 1) / kTileRows, BH,
+                              kThreads / kWave, wave);
+  const long long tasks = (long long)S * (sw.t1 - sw.t0);
+  for (long long task = sw.first; task < tasks; task += sw.stride) {
+    const int sg = (int)(task % S), t = sw.t0 + (int)(task / S);
     const int* it = segs + 8 * sg;
     const int row = it[0], lr = it[3], sidx = it[4], ns = it[5];
     float M, Lsum, acc[L::kEPC];

@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLongWGs = 256;  // workgroups that walk the long-row segments
+static_assert(kLongWGs % kXcds == 0, "segment workgroups split evenly over the XCDs");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
@@ -539,15 +540,12 @@ __global__ __launch_bounds__(kThreads) void sddmm_plan_kernel(Args a, int BH) {
     // each plan segment as kSegSplit tasks: scores need no merge, so shorter tasks only add
     // parallelism
     constexpr int kSegSplit = 2;
-    // this XCD's heads; the workgroup is number blockIdx.x / kXcds of the XCD's segment workgroups
-    const int ntiles = (a.n + kTileRows - 1) / kTileRows;
-    const int x = (int)blockIdx.x % kXcds;
-    const int ta = first_head_on_xcd(x, ntiles, BH), tb = first_head_on_xcd(x + 1, ntiles, BH);
-    const long long tasks = (long long)S * (tb - ta) * kSegSplit;
-    for (long long task = (long long)(blockIdx.x / kXcds) * (kThreads / kWave) + wave; task < tasks;
-         task += (long long)(kLongWGs / kXcds) * (kThreads / kWave)) {
+    const SegWalk sw = seg_walk((int)blockIdx.x, kLongWGs, (a.n + kTileRows - 1) / kTileRows, BH,
+                                kThreads / kWave, wave);
+    const long long tasks = (long long)S * (sw.t1 - sw.t0) * kSegSplit;
+    for (long long task = sw.first; task < tasks; task += sw.stride) {
       const int part = (int)(task % kSegSplit);
-      const int sg = (int)(task / kSegSplit % S), t = ta + (int)(task / kSegSplit / S);
+      const int sg = (int)(task / kSegSplit % S), t = sw.t0 + (int)(task / kSegSplit / S);
       const int* it = segs + 8 * sg;
       const long long len = it[2] - it[1];
       valu_row<T, D>(a, t, it[0], it[1] + len * part / kSegSplit, it[1] + len * (part + 1) / kSegSplit);

@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLongWGs = 256;
+static_assert(kLongWGs % kXcds == 0, "segment workgroups split evenly over the XCDs");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
@@ -543,15 +544,11 @@ void spmm_plan_kernel(Args a, int BH) {
     int* counters = const_cast<int*>(plan) + plan[kHOffCounters];
     float* scratch = reinterpret_cast<float*>(const_cast<int*>(plan) + plan[kHOffScratch]);
     const int pBH = plan[kHBH], pD = plan[kHD];
-    // this XCD's heads; the workgroup is number lwg / kXcds of the XCD's segment workgroups
-    const int ntiles = (a.n + kTileRows - 1) / kTileRows;
-    const int x = (int)blockIdx.x % kXcds;
-    const int ta = first_head_on_xcd(x, ntiles, BH), tb = first_head_on_xcd(x + 1, ntiles, BH);
-    const long long tasks = (long long)S * (tb - ta);
+    const SegWalk sw = seg_walk(lwg, kLongWGs, (a.n + kTileRows - 1) / kTileRows, BH, kThreads / kWave, wave);
+    const long long tasks = (long long)S * (sw.t1 - sw.t0);
     using L = Layout<T, D>;
-    for (long long task = (long long)(lwg / kXcds) * (kThreads / kWave) + wave; task < tasks;
-         task += (long long)(kLongWGs / kXcds) * (kThreads / kWave)) {
-      const int sg = (int)(task % S), t = ta + (int)(task / S);
+    for (long long task = sw.first; task < tasks; task += sw.stride) {
+      const int sg = (int)(task % S), t = sw.t0 + (int)(task / S);
       const int* it = segs + 8 * sg;
       const int row = it[0], lr = it[3], sidx = it[4], ns = it[5];
       float acc[L::kEPC];
