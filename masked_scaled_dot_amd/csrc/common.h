@@ -86,7 +86,6 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-
 // Long-row segment tasks. With at least kXcds heads, a segment workgroup walks the tasks of
 // the heads whose tiles run on its own XCD, so the K/V rows a segment gathers are the ones
 // already in that XCD's L2; head t belongs to the XCD that xcd_logical_block gives its middle
@@ -124,7 +123,6 @@ __device__ __forceinline__ SegWalk seg_walk(int wg, int nwgs, int ntiles, int BH
   }
   return w;
 }
-
 
 // Bounds [rs, re) of row row0 + r (r < 64, wave-uniform) of a tile, from the two row_ptr
 // values each lane of the wave loaded for row row0 + lane (rp0 = row_ptr[row], rp1 =

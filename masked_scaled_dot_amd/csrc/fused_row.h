@@ -185,13 +185,15 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
     }
   }
 
-  // Merge the slots: rescale each to the largest reference and sum; M in natural-log units
-  // (-inf if no entry has a finite score).
+  // Merge the slots: rescale each to the largest reference and sum. A slot that has seen a
+  // finite score has a weight sum of at least 1 (the score that set its reference weighs 1,
+  // and a rescale is always followed by that weight), and the slot with the largest
+  // reference keeps its sum unscaled, so a range without a finite score is exactly the one
+  // whose weights sum to zero; its M is -inf. M is in natural-log units.
   float m2 = m;
 #pragma unroll
   for (int s = LPR; s < kWave; s <<= 1) m2 = fmaxf(m2, shfl_xor(m2, s));
-  const float f = (m2 == -FLT_MAX) ? 0.f : __builtin_amdgcn_exp2f(m - m2);
-  M = m2 == -FLT_MAX ? -INFINITY : m2 / kLog2e;
+  const float f = __builtin_amdgcn_exp2f(m - m2);  // m <= m2, both finite
   Lsum = l * f;
 #pragma unroll
   for (int c = 0; c < EPC; ++c) acc[c] *= f;
@@ -201,6 +203,7 @@ __device__ __forceinline__ void fused_range(const FusedArgs& a, int t, int row, 
 #pragma unroll
     for (int c = 0; c < EPC; ++c) acc[c] += shfl_xor(acc[c], s);
   }
+  M = Lsum > 0.f ? m2 / kLog2e : -INFINITY;
 }
 
 // The whole row: O = acc / Lsum (0 for a row without a finite score) and lse = M + log Lsum.
