@@ -77,6 +77,8 @@ SMALL = {
                                             bias=True, key_mask=True, pmax=40),
     # rows longer than the plan's split threshold (1024 entries): global-token rows, random
     "longformer_long_rows": lambda: gen.make("longformer_n4096", n=2500, H=2, window=100),
+    # the same with eight heads: each XCD's segment workgroups take the segments of its own heads
+    "longformer_long_rows_8heads": lambda: gen.make("longformer_n4096", n=1300, H=8, window=60),
     "random_long_rows": lambda: gen.make("random_n8192", n=2100, H=2, kmin=1, kmax=1800),
     "longformer_bias_keymask": lambda: gen.make("longformer_n4096", n=600, H=2, B=2, window=50,
                                                 bias=True, key_mask=True, pmax=100),
