@@ -59,7 +59,7 @@ constexpr int kBsrCached = 512;  // block-columns of a block-row kept in LDS (n 
 // so that three or four workgroups fit on a compute unit and more loads are in flight.
 template <int D>
 struct FusedSmem1 {
-  static constexpr int kKStride = D + 8;   // bf16 per K row (+16 B: conflict-free A reads)
+  static constexpr int kKStride = D + 16;  // bf16 per K row (+32 B: no LDS bank conflicts, by counters)
   static constexpr int kVStride = D + 16;  // bf16 per V row (conflict-free transposing reads)
   alignas(16) uint16_t k[1][kTileRows * kKStride];
   alignas(16) uint16_t v[1][kTileRows * kVStride];

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void sddmm_rows_kernel(Args a, int BH) {
 // grows with the number of separate segments its lanes touch.
 template <int D>
 struct TileSmem {
-  static constexpr int kKStride = D + 8;     // bf16 per K row (+16 B: conflict-free reads)
+  static constexpr int kKStride = D + 16;    // bf16 per K row (+32 B: no LDS bank conflicts, by counters)
   static constexpr int kOStride = kTileRows + 4;  // fp32 per compacted row
   alignas(16) uint16_t k[2][kTileRows * kKStride];   // double-buffered K block
   alignas(16) float out[kTileRows * kOStride + kTileRows];  // one block's scores per row (+ slack
