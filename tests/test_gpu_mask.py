@@ -199,6 +199,11 @@ SEQLEN = {
     "dense_ragged_n": (lambda: gen.make("evoformer_l384", B=2, H=2, n=200), [130, 200], False),
     "dense_f32": (lambda: gen.make("evoformer_l384", B=2, H=2, n=160, dtype="f32"), [100, 7], False),
     "bsr": (lambda: gen.make("bsr_n16384", n=640, H=2, d=64, extra=3), [500], False),
+    # lengths that end in the first key half of a block (its second half all masked), at a
+    # block boundary, inside the ragged last block, and 0
+    "bsr_d128_half_blocks": (lambda: gen.make("bsr_n16384", n=64 * 6 + 21, H=2, B=4, d=128, extra=3),
+                             [340, 320, 400, 0], False),
+    "bsr_d32_half_blocks": (lambda: gen.make("bsr_n16384", n=64 * 5, H=1, B=2, d=32, extra=2), [275, 1], False),
     "csr": (lambda: gen.make("longformer_n4096", n=700, H=2, window=40), [650], False),
     "csr_with_key_mask": (lambda: gen.make("random_n8192", n=300, H=2, B=2, kmin=1, kmax=120,
                                            bias=True, key_mask=True, pmax=40), [250, 299], True),
