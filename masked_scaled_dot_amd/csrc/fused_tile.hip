@@ -489,11 +489,14 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
         p[i] = __builtin_amdgcn_exp2f(sc[2 * c][i] - ref);
         p[4 + i] = __builtin_amdgcn_exp2f(sc[2 * c + 1][i] - ref);
       }
-      ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pk[c][0] = pack_bf16(p[0], p[1]);
       pk[c][1] = pack_bf16(p[2], p[3]);
       pk[c][2] = pack_bf16(p[4], p[5]);
       pk[c][3] = pack_bf16(p[6], p[7]);
+      // the row sum is taken over the rounded weights the product uses, so that O is divided
+      // by the sum of the weights it holds (exact for a row whose weight sits on one key)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ps = dot2_bf16(pk[c][w], 0x3f803f80u, ps);  // bf16 pair (1, 1)
     }
     lsum = fmaf(lsum, alpha, ps);
     m2 = mn;
