@@ -392,7 +392,8 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   };
 
   float m2 = -INFINITY;  // running max of the lane's query, log2 units
-  float lsum = 0.f;      // partial running sum over this lane's keys
+  float lsum = 0.f;      // partial running sum over this lane's keys (fp32 weights: the lse)
+  float lsumr = 0.f;     // the same over the bf16-rounded weights the products use (divides O)
   f32x4_v o[OC];
 #pragma unroll
   for (int c = 0; c < OC; ++c) o[c] = f32x4_v{0.f, 0.f, 0.f, 0.f};
@@ -479,7 +480,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
     const float mn = (mx > m2 + kSlack) ? mx : m2;
     const float ref = mn == -INFINITY ? 0.f : mn;
     const float alpha = __builtin_amdgcn_exp2f(m2 - ref);  // 0 while nothing is accumulated
-    float ps = 0.f;
+    float ps = 0.f, pr = 0.f;
     uint32_t pk[2][4];  // bf16 P: [32-key chunk][dword]
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -489,16 +490,18 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
         p[i] = __builtin_amdgcn_exp2f(sc[2 * c][i] - ref);
         p[4 + i] = __builtin_amdgcn_exp2f(sc[2 * c + 1][i] - ref);
       }
+      ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pk[c][0] = pack_bf16(p[0], p[1]);
       pk[c][1] = pack_bf16(p[2], p[3]);
       pk[c][2] = pack_bf16(p[4], p[5]);
       pk[c][3] = pack_bf16(p[6], p[7]);
-      // the row sum is taken over the rounded weights the product uses, so that O is divided
-      // by the sum of the weights it holds (exact for a row whose weight sits on one key)
+      // O is divided by the sum of the rounded weights it holds (exact for a row whose weight
+      // sits on one key); the lse keeps the sum of the fp32 weights
 #pragma unroll
-      for (int w = 0; w < 4; ++w) ps = dot2_bf16(pk[c][w], 0x3f803f80u, ps);  // bf16 pair (1, 1)
+      for (int w = 0; w < 4; ++w) pr = dot2_bf16(pk[c][w], 0x3f803f80u, pr);  // bf16 pair (1, 1)
     }
     lsum = fmaf(lsum, alpha, ps);
+    lsumr = fmaf(lsumr, alpha, pr);
     m2 = mn;
     // rescale O rows when some query's max moved (query 4g+i is owned by lane 4g+i)
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
@@ -562,6 +565,7 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
       const float alpha = __builtin_amdgcn_exp2f(m2 - ref);
       const float p = __builtin_amdgcn_exp2f(x - ref);
       lsum = fmaf(lsum, alpha, g == 0 ? p : 0.f);  // the query's four lanes share the sum
+      lsumr = fmaf(lsumr, alpha, g == 0 ? p : 0.f);  // V_f enters O with the fp32 weight
       m2 = mn;
       float vf[OC];
 #pragma unroll
@@ -578,7 +582,9 @@ __device__ void fused_block_tile(const FusedArgs& a, FusedSmem1<D>& sm, const Ti
   // finish: total sum per query, divide, store O and lse
   float ltot = lsum + shfl_xor(lsum, 16);
   ltot += shfl_xor(ltot, 32);
-  const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltot;
+  float ltotr = lsumr + shfl_xor(lsumr, 16);
+  ltotr += shfl_xor(ltotr, 32);
+  const float inv = (m2 == -INFINITY) ? 0.f : 1.0f / ltotr;
   auto live = [&](int lr) {
     if constexpr (K == kFusedCsr) return sm.live[lr] != 0;
     else return row0 + lr < n;

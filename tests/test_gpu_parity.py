@@ -125,30 +125,42 @@ def test_fused_parity_small(name, plan):
         f" lse max_abs={el[0]:.3e}")
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("scale", [2.0, 0.02])
-def test_block_sparse_extreme_scales(d, scale):
-    """Block CSR without bias under extreme score ranges: a large scale puts the scores of
-    one row hundreds of log2 units apart (most weights underflow to 0, the running maximum
-    moves far past its lazy threshold from block to block), a tiny scale keeps every weight
-    near 1. The block-rows hold 1 to 6 blocks, the last one ragged."""
+def _extreme_problem(kind, d):
     import copy
-    n = 64 * 6 + 37
-    base = gen.make("bsr_n16384", n=n, H=2, d=d, extra=0)
-    rng = np.random.default_rng(77 + d)
-    nb = (n + 63) // 64
-    rows = [sorted(set(rng.choice(nb, size=int(rng.integers(1, 6)), replace=False).tolist() + [r]))
-            for r in range(nb)]
-    p = copy.copy(base)
-    p.row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
-    p.col_idx = np.concatenate([np.asarray(r, np.int32) for r in rows])
-    dp = DevProblem(p, scale=scale)
+    if kind == "bsr":  # block-rows of 1 to 6 blocks, the last one ragged
+        n = 64 * 6 + 37
+        base = gen.make("bsr_n16384", n=n, H=2, d=d, extra=0)
+        rng = np.random.default_rng(77 + d)
+        nb = (n + 63) // 64
+        rows = [sorted(set(rng.choice(nb, size=int(rng.integers(1, 6)), replace=False).tolist() + [r]))
+                for r in range(nb)]
+        p = copy.copy(base)
+        p.row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+        p.col_idx = np.concatenate([np.asarray(r, np.int32) for r in rows])
+        return p, False
+    if kind == "csr_plan":  # window + global tokens: banded matrix-core tiles and far columns
+        return gen.make("longformer_n4096", n=64 * 5 + 11, H=2, d=d, window=40), True
+    # dense, too long for the LDS-resident kernel at d = 128: the 64-query tile
+    return gen.make("evoformer_l384", B=1, H=2, n=64 * 5 + 3, d=d, bias=False, key_mask=False), False
+
+
+@pytest.mark.parametrize("kind,d", [("bsr", 32), ("bsr", 64), ("bsr", 128), ("csr_plan", 64),
+                                    ("csr_plan", 128), ("dense", 128)])
+@pytest.mark.parametrize("scale", [2.0, 0.02])
+def test_fused_extreme_scales(kind, d, scale):
+    """The matrix-core fused tiles under extreme score ranges: a large scale puts the scores
+    of one row hundreds of log2 units apart (most weights underflow to 0, a row's weight sits
+    on one key, the running maximum moves far past its lazy threshold from block to block), a
+    tiny scale keeps every weight near 1."""
+    p, plan = _extreme_problem(kind, d)
+    dp = DevProblem(p, scale=scale, plan=plan)
     O, lse = dp.fused()
-    ref = oracle.attention_dense(p.q, p.k, p.v, scale, p.H, _pattern(p), want_weights=False)
+    ref = oracle.attention_dense(p.q, p.k, p.v, scale, p.H, _pattern(p), want_weights=False,
+                                 **dp.oracle_args())
     eo = check(O, ref["O"], p.dtype, "context")
     el = check(lse, ref["lse"], p.dtype, "lse")
-    say(f"PARITY bsr_extreme_scales d={d} scale={scale} context max_abs={eo[0]:.3e} mean_abs={eo[1]:.3e}"
-        f" lse max_abs={el[0]:.3e}")
+    say(f"PARITY extreme_scales {kind} d={d} scale={scale} context max_abs={eo[0]:.3e}"
+        f" mean_abs={eo[1]:.3e} lse max_abs={el[0]:.3e}")
 
 
 # element CSR patterns whose tiles are whole 64x64 blocks (expansions of block-sparse
